@@ -1,0 +1,206 @@
+// C ABI of the ISPA hot path: argument validation, workspace sizing and launches.
+// The operations, layouts and error behaviour are documented in include/ispa.h.
+#include "../../include/ispa.h"
+#include "kernels.hpp"
+
+#include <math.h>
+
+using namespace ispa;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+bool valid_dtype(int t) { return t == ISPA_F32 || t == ISPA_BF16 || t == ISPA_F16; }
+
+int check_shape(const ispa_attn_shape* s) {
+  if (!s) return ISPA_EINVAL;
+  if (s->n_q < 1 || s->n_sink < 0 || s->n_hist < 0 || s->n_cur < 0 || s->n_heads < 1) return ISPA_EINVAL;
+  if ((int64_t)s->n_sink + s->n_cur < 1) return ISPA_EINVAL;
+  if ((int64_t)s->n_sink + s->n_hist + s->n_cur > INT32_MAX) return ISPA_EINVAL;
+  if (s->head_dim != 64 && s->head_dim != 128) return ISPA_EUNSUPPORTED;
+  if ((int64_t)s->n_heads * s->head_dim > 65536) return ISPA_EINVAL;
+  if (!(s->scale == s->scale)) return ISPA_EINVAL;
+  return ISPA_OK;
+}
+
+float eff_scale(const ispa_attn_shape* s) { return s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ISPA_OK : ISPA_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int ispa_version(void) { return 100; }
+
+const char* ispa_status_string(int status) {
+  switch (status) {
+    case ISPA_OK: return "ok";
+    case ISPA_EINVAL: return "invalid argument";
+    case ISPA_EUNSUPPORTED: return "unsupported head_dim or dtype combination";
+    case ISPA_EWORKSPACE: return "workspace missing or too small";
+    case ISPA_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t ispa_workspace_bytes(int call_id, const ispa_attn_shape* shape, int d) {
+  switch (call_id) {
+    case ISPA_CALL_DUAL_ATTN: return 0;
+    case ISPA_CALL_ABSORB_SOLVE: return d > 0 ? solve_workspace_bytes(d) : 0;
+    case ISPA_CALL_LOCAL_ATTN_PROJ:
+      if (!shape || shape->n_q < 1 || shape->n_heads < 1) return 0;
+      return (size_t)shape->n_q * shape->n_heads * shape->head_dim * 2 + 256;
+    default: return (size_t)-1;
+  }
+}
+
+int ispa_dual_attn(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k, const void* v,
+                   void* a_full, int stat_dtype, void* a_loc_t, void* delta_a_t, int64_t ld_stat, float* lse_loc,
+                   float* lse_hist, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int st = check_shape(shape);
+  if (st) return st;
+  if (!valid_dtype(io_dtype)) return ISPA_EUNSUPPORTED;
+  if (!q || !k || !v) return ISPA_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(a_full)) return ISPA_EINVAL;
+  const bool dual = a_loc_t || delta_a_t || lse_loc || lse_hist;
+  if (!dual && !a_full) return ISPA_EINVAL;
+  if (a_loc_t || delta_a_t) {
+    if (!valid_dtype(stat_dtype)) return ISPA_EUNSUPPORTED;
+    if (ld_stat < shape->n_q || ld_stat % 8 != 0) return ISPA_EINVAL;
+    if (!aligned16(a_loc_t) || !aligned16(delta_a_t)) return ISPA_EINVAL;
+  }
+  if (!aligned4(lse_loc) || !aligned4(lse_hist)) return ISPA_EINVAL;
+  if (io_dtype == ISPA_F32) {
+    if ((a_loc_t || delta_a_t) && stat_dtype != ISPA_F32) return ISPA_EUNSUPPORTED;
+  } else {
+    if (shape->head_dim != 128) return ISPA_EUNSUPPORTED;
+  }
+  AttnLaunch L;
+  L.mode = dual ? 0 : 1;
+  L.io = io_dtype;
+  L.stat = stat_dtype;
+  L.q = q;
+  L.k = k;
+  L.v = v;
+  L.a_full = a_full;
+  L.a_loc_t = a_loc_t;
+  L.delta_a_t = delta_a_t;
+  L.ld_stat = ld_stat;
+  L.lse_loc = lse_loc;
+  L.lse_hist = lse_hist;
+  L.n_q = shape->n_q;
+  L.n_sink = shape->n_sink;
+  L.n_hist = shape->n_hist;
+  L.n_cur = shape->n_cur;
+  L.n_heads = shape->n_heads;
+  L.head_dim = shape->head_dim;
+  L.scale = eff_scale(shape);
+  return hip_status(launch_attention(L, (hipStream_t)stream));
+}
+
+int ispa_gram_accum(int d, int n, int stat_dtype, const void* a_loc_t, const void* delta_a_t, int64_t ld,
+                    int accumulate, float* G, float* C, float* D, void* stream) {
+  if (d < 32 || d > 16384 || d % 32 != 0 || n < 1) return ISPA_EINVAL;
+  if (!valid_dtype(stat_dtype)) return ISPA_EUNSUPPORTED;
+  if (!a_loc_t || !delta_a_t || !G || !C) return ISPA_EINVAL;
+  if (ld < n || ld % 8 != 0) return ISPA_EINVAL;
+  if (!aligned16(a_loc_t) || !aligned16(delta_a_t) || !aligned16(G) || !aligned16(C) || !aligned16(D))
+    return ISPA_EINVAL;
+  if (accumulate != 0 && accumulate != 1) return ISPA_EINVAL;
+  GramLaunch L;
+  L.d = d;
+  L.n = n;
+  L.stat = stat_dtype;
+  L.a_t = a_loc_t;
+  L.da_t = delta_a_t;
+  L.ld = ld;
+  L.accumulate = accumulate;
+  L.G = G;
+  L.C = C;
+  L.D = D;
+  return hip_status(launch_gram(L, (hipStream_t)stream));
+}
+
+int ispa_absorb_solve(int d, const float* G, const float* C, const float* D, int w_dtype, const void* W,
+                      float lambda, int lambda_relative, int refine, float* delta_w, void* w_new, float* eps,
+                      float* lambda_out, int* info, void* workspace, size_t workspace_bytes, void* stream) {
+  if (d < 32 || d > 16384 || d % 32 != 0) return ISPA_EINVAL;
+  if (!valid_dtype(w_dtype)) return ISPA_EUNSUPPORTED;
+  if (!G || !C || !W || !delta_w || !info) return ISPA_EINVAL;
+  if (eps && !D) return ISPA_EINVAL;
+  if (!(lambda == lambda) || (lambda_relative != 0 && lambda_relative != 1) || (refine != 0 && refine != 1))
+    return ISPA_EINVAL;
+  if (!aligned16(G) || !aligned16(C) || !aligned16(D) || !aligned16(W) || !aligned16(delta_w) || !aligned16(w_new) ||
+      !aligned4(eps) || !aligned4(lambda_out) || !aligned4(info))
+    return ISPA_EINVAL;
+  if (!workspace || workspace_bytes < solve_workspace_bytes(d) || !aligned16(workspace)) return ISPA_EWORKSPACE;
+  SolveLaunch L;
+  L.d = d;
+  L.G = G;
+  L.C = C;
+  L.D = D;
+  L.w_dtype = w_dtype;
+  L.W = W;
+  L.lambda = lambda;
+  L.lambda_relative = lambda_relative;
+  L.refine = refine;
+  L.delta_w = delta_w;
+  L.w_new = w_new;
+  L.eps = eps;
+  L.lambda_out = lambda_out;
+  L.info = info;
+  L.ws = workspace;
+  return hip_status(launch_solve(L, (hipStream_t)stream));
+}
+
+int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k,
+                               const void* v, const void* w_new, void* out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if (io_dtype != ISPA_BF16 && io_dtype != ISPA_F16) return ISPA_EUNSUPPORTED;
+  if (shape->head_dim != 128) return ISPA_EUNSUPPORTED;
+  if (!q || !k || !v || !w_new || !out) return ISPA_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(w_new) || !aligned16(out)) return ISPA_EINVAL;
+  const size_t need = ispa_workspace_bytes(ISPA_CALL_LOCAL_ATTN_PROJ, shape, 0);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return ISPA_EWORKSPACE;
+  const hipStream_t s = (hipStream_t)stream;
+  AttnLaunch L;
+  L.mode = 2;
+  L.io = io_dtype;
+  L.stat = ISPA_F16;
+  L.q = q;
+  L.k = k;
+  L.v = v;
+  L.a_full = workspace;
+  L.a_loc_t = nullptr;
+  L.delta_a_t = nullptr;
+  L.ld_stat = 0;
+  L.lse_loc = nullptr;
+  L.lse_hist = nullptr;
+  L.n_q = shape->n_q;
+  L.n_sink = shape->n_sink;
+  L.n_hist = shape->n_hist;
+  L.n_cur = shape->n_cur;
+  L.n_heads = shape->n_heads;
+  L.head_dim = shape->head_dim;
+  L.scale = eff_scale(shape);
+  hipError_t e = launch_attention(L, s);
+  if (e != hipSuccess) return ISPA_EHIP;
+  const int d = shape->n_heads * shape->head_dim;
+  ProjLaunch P;
+  P.io = io_dtype;
+  P.m = shape->n_q;
+  P.n = d;
+  P.k = d;
+  P.a = workspace;
+  P.b = w_new;
+  P.out = out;
+  return hip_status(launch_proj(P, s));
+}
+
+}  // extern "C"

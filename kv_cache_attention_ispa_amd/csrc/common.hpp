@@ -1,0 +1,97 @@
+// Shared device helpers for the ISPA kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ispa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, work-groups dispatched round-robin
+
+// Element tags.  Storage is 16-bit patterns (uint16_t) for both half types.
+struct BF16 { typedef uint16_t storage; };
+struct F16 { typedef uint16_t storage; };
+struct F32 { typedef float storage; };
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+  __bf16 h = (__bf16)f;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float f16_bits_to_float(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+__device__ __forceinline__ uint16_t float_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+template <typename T> struct Cvt;
+template <> struct Cvt<BF16> {
+  static __device__ __forceinline__ float to_f(uint16_t b) { return bf16_bits_to_float(b); }
+  static __device__ __forceinline__ uint16_t from_f(float f) { return float_to_bf16_bits(f); }
+};
+template <> struct Cvt<F16> {
+  static __device__ __forceinline__ float to_f(uint16_t b) { return f16_bits_to_float(b); }
+  static __device__ __forceinline__ uint16_t from_f(float f) { return float_to_f16_bits(f); }
+};
+template <> struct Cvt<F32> {
+  static __device__ __forceinline__ float to_f(float b) { return b; }
+  static __device__ __forceinline__ float from_f(float f) { return f; }
+};
+
+// Pack two floats into one dword of two 16-bit values (low = a).
+template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return (uint32_t)Cvt<T>::from_f(a) | ((uint32_t)Cvt<T>::from_f(b) << 16);
+}
+
+// 32x32x16 MFMA with 16-bit inputs given as raw dword quads (8 values per lane).
+// A: lane l holds A[m = l%32][k = 8*(l/32) + 0..7]; B: B[k = 8*(l/32) + 0..7][n = l%32];
+// C/D: register r of lane l is D[8*(r/4) + 4*(l/32) + r%4][l%32].
+template <typename T> __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c);
+template <> __device__ __forceinline__ f32x16 mfma32x32x16<BF16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x16 mfma32x32x16<F16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                0, 0, 0);
+}
+
+// LDS transposing read of four 16-bit values.  Within each group of 16 lanes,
+// lane j receives element (j % 4) of the 8-byte chunk addressed by lane 4*e + j/4,
+// for e = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const lds_void* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Work-group id -> logical tile id such that each XCD receives a contiguous range
+// of logical ids (work-groups are dispatched round-robin over the XCDs).
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  int xcd = bid % kNumXcd;
+  int local = bid / kNumXcd;
+  int per = n / kNumXcd;
+  int rem = n % kNumXcd;
+  return xcd * per + (xcd < rem ? xcd : rem) + local;
+}
+
+__device__ __forceinline__ float wave_max_xor32(float x) {
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+}  // namespace ispa

@@ -1,0 +1,72 @@
+// Internal launch interface between the C ABI layer (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ispa {
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+struct AttnLaunch {
+  int mode;  // 0: dual stream, 1: single stream over all rows, 2: single stream over the local rows
+  int io, stat;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* a_full;
+  void* a_loc_t;
+  void* delta_a_t;
+  int64_t ld_stat;
+  float* lse_loc;
+  float* lse_hist;
+  int n_q, n_sink, n_hist, n_cur, n_heads, head_dim;
+  float scale;
+};
+hipError_t launch_attention(const AttnLaunch& L, hipStream_t s);
+
+// Gram statistics: out_z (+)= X_z Y_z^T for z in {G: (A, A), C: (A, dA), D: (dA, dA)}.
+struct GramLaunch {
+  int d, n, stat;
+  const void* a_t;
+  const void* da_t;
+  int64_t ld;
+  int accumulate;
+  float* G;
+  float* C;
+  float* D;
+};
+hipError_t launch_gram(const GramLaunch& L, hipStream_t s);
+
+// out[m, n] = in0 @ in1 for 16-bit row-major operands (local-layer projection), fp32 accumulate.
+struct ProjLaunch {
+  int io;
+  int m, n, k;
+  const void* a;   // [m, k]
+  const void* b;   // [k, n]
+  void* out;       // [m, n]
+};
+hipError_t launch_proj(const ProjLaunch& L, hipStream_t s);
+
+struct SolveLaunch {
+  int d;
+  const float* G;
+  const float* C;
+  const float* D;
+  int w_dtype;
+  const void* W;
+  float lambda;
+  int lambda_relative;
+  int refine;
+  float* delta_w;
+  void* w_new;
+  float* eps;
+  float* lambda_out;
+  int* info;
+  void* ws;
+};
+size_t solve_workspace_bytes(int d);
+hipError_t launch_solve(const SolveLaunch& L, hipStream_t s);
+
+}  // namespace ispa

@@ -1,0 +1,489 @@
+// Closed-form ridge absorption for gfx950.
+//
+// ISPA technical summary (gist.science, nl/pt), section 2, stage 2 "Layer
+// Absorb": the weight modulation minimising ||A_loc (W + dW) - A_full W||^2 +
+// lambda ||dW||^2 is dW = (A_loc^T A_loc + lambda I)^-1 A_loc^T (A_full - A_loc) W,
+// computed once, without iteration.  With G = A_loc^T A_loc and C = A_loc^T dA:
+//
+//   R = C W;   G + lambda I = L L^T (blocked right-looking Cholesky, fp32);
+//   the forward solve runs inside the same sweep on the augmented right-hand
+//   side [R | I], which leaves Y = L^-1 R and L^-1 when the sweep ends, so the
+//   backward solve is one triangular GEMM: dW = (L^-1)^T Y.
+//   Optional refinement: r = R - (G + lambda I) dW accumulated in fp64, then
+//   dW += (L^-1)^T (L^-1 r).
+//
+// "Dynamic layer selection" ranks layers by the reconstruction error epsilon;
+// it is evaluated here from the statistics alone (D = dA^T dA, P = W W^T):
+//   ||A_loc dW - dA W||^2 = <D, P> - <dW, R> - lambda ||dW||^2   (at the optimum)
+//   ||A_full W||^2        = <G, P> + 2 <W, R> + <D, P>.
+//
+// Every step is a HIP kernel enqueued on the caller's stream; the host never
+// waits.  A non-positive pivot sets *info to its 1-based index.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ispa {
+
+namespace {
+
+constexpr int NB = 64;          // Cholesky panel width
+constexpr int TB = 64;          // GEMM output tile
+constexpr int TK = 16;          // GEMM k-step
+constexpr int NT = 256;
+
+// ------------------------------------------------------------------------------------------
+// fp32 GEMM on MFMA (32x32x2): C = alpha * op(A) op(B) + beta * C, 64 x 64 tiles, 4 waves.
+// op(A)[m][k] = transA ? A[k*lda + m] : A[m*lda + k];  op(B)[k][n] = transB ? B[n*ldb + k] : B[k*ldb + n].
+// kmode: 0 full k range; 1 k >= m0 (op(A) upper triangular); 2 k < m0 + 64 (op(A) lower triangular).
+// lower_only: skip output tiles strictly above the diagonal.
+// ------------------------------------------------------------------------------------------
+struct Gemm {
+  const float* A;
+  const float* B;
+  float* C;
+  int64_t lda, ldb, ldc;
+  int M, N, K;
+  int transA, transB, kmode, lower_only;
+  float alpha, beta;
+};
+struct GemmBatch {
+  Gemm g[3];
+  int tiles_n[3];
+  int tile_start[4];
+  int count;
+};
+
+__global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmBatch b) {
+  __shared__ float As[2][TK][TB + 4];
+  __shared__ float Bs[2][TK][TB + 4];
+  int pid = 0;
+  while (pid + 1 < b.count && (int)blockIdx.x >= b.tile_start[pid + 1]) ++pid;
+  const Gemm g = b.g[pid];
+  const int t = blockIdx.x - b.tile_start[pid];
+  const int bm = t / b.tiles_n[pid], bn = t % b.tiles_n[pid];
+  if (g.lower_only && bn > bm) return;
+  const int m0 = bm * TB, n0 = bn * TB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  int k_begin = 0, k_end = g.K;
+  if (g.kmode == 1) k_begin = (m0 / TK) * TK;
+  if (g.kmode == 2) k_end = min(g.K, m0 + TB);
+  f32x16 acc = {};
+  float ra[4], rb[4];
+  auto gload = [&](int k0) {
+    if (!g.transA) {
+      const int m = tid >> 2, kk = (tid & 3) * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int gm = m0 + m, gk = k0 + kk + j;
+        ra[j] = (gm < g.M && gk < k_end) ? g.A[(int64_t)gm * g.lda + gk] : 0.f;
+      }
+    } else {
+      const int kk = tid >> 4, m = (tid & 15) * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int gm = m0 + m + j, gk = k0 + kk;
+        ra[j] = (gm < g.M && gk < k_end) ? g.A[(int64_t)gk * g.lda + gm] : 0.f;
+      }
+    }
+    if (!g.transB) {
+      const int kk = tid >> 4, n = (tid & 15) * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int gn = n0 + n + j, gk = k0 + kk;
+        rb[j] = (gn < g.N && gk < k_end) ? g.B[(int64_t)gk * g.ldb + gn] : 0.f;
+      }
+    } else {
+      const int n = tid >> 2, kk = (tid & 3) * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int gn = n0 + n, gk = k0 + kk + j;
+        rb[j] = (gn < g.N && gk < k_end) ? g.B[(int64_t)gn * g.ldb + gk] : 0.f;
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+    if (!g.transA) {
+      const int m = tid >> 2, kk = (tid & 3) * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) As[buf][kk + j][m] = ra[j];
+    } else {
+      const int kk = tid >> 4, m = (tid & 15) * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) As[buf][kk][m + j] = ra[j];
+    }
+    if (!g.transB) {
+      const int kk = tid >> 4, n = (tid & 15) * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Bs[buf][kk][n + j] = rb[j];
+    } else {
+      const int n = tid >> 2, kk = (tid & 3) * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Bs[buf][kk + j][n] = rb[j];
+    }
+  };
+  if (k_begin < k_end) {
+    gload(k_begin);
+    sstore(0);
+    __syncthreads();
+    int buf = 0;
+    for (int k0 = k_begin; k0 < k_end; k0 += TK) {
+      const bool nxt = k0 + TK < k_end;
+      if (nxt) gload(k0 + TK);
+#pragma unroll
+      for (int s = 0; s < TK / 2; ++s) {
+        const float a = As[buf][2 * s + (lane >> 5)][32 * wm + (lane & 31)];
+        const float bb = Bs[buf][2 * s + (lane >> 5)][32 * wn + (lane & 31)];
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bb, acc, 0, 0, 0);
+      }
+      if (nxt) sstore(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+  const int col = n0 + 32 * wn + (lane & 31);
+  if (col >= g.N) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = m0 + 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    if (row >= g.M) continue;
+    float* c = g.C + (int64_t)row * g.ldc + col;
+    *c = g.beta == 0.f ? g.alpha * acc[r] : fmaf(g.alpha, acc[r], g.beta * *c);
+  }
+}
+
+hipError_t run_gemms(const Gemm* gs, int count, hipStream_t s) {
+  GemmBatch b;
+  b.count = count;
+  int total = 0;
+  for (int i = 0; i < count; ++i) {
+    b.g[i] = gs[i];
+    const int tm = (gs[i].M + TB - 1) / TB, tn = (gs[i].N + TB - 1) / TB;
+    b.tiles_n[i] = tn;
+    b.tile_start[i] = total;
+    total += (gs[i].M > 0 && gs[i].N > 0) ? tm * tn : 0;
+  }
+  b.tile_start[count] = total;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_f32_kernel, dim3(total), dim3(NT), 0, s, b);
+  return hipGetLastError();
+}
+
+Gemm mk(const float* A, int64_t lda, int transA, const float* B, int64_t ldb, int transB, float* C, int64_t ldc, int M,
+        int N, int K, float alpha, float beta, int kmode = 0, int lower_only = 0) {
+  Gemm g;
+  g.A = A; g.B = B; g.C = C;
+  g.lda = lda; g.ldb = ldb; g.ldc = ldc;
+  g.M = M; g.N = N; g.K = K;
+  g.transA = transA; g.transB = transB;
+  g.kmode = kmode; g.lower_only = lower_only;
+  g.alpha = alpha; g.beta = beta;
+  return g;
+}
+
+// ------------------------------------------------------------------------------------------
+// Small kernels
+// ------------------------------------------------------------------------------------------
+struct Scalars {
+  float lambda;
+  int pad;
+  double dots[8];
+};
+
+// lambda (absolute or lambda * tr(G) / d), info = 0.
+__global__ __launch_bounds__(NT) void lambda_kernel(const float* G, int d, float lam, int relative, Scalars* sc,
+                                                    float* lambda_out, int* info) {
+  __shared__ double part[NT];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < d; i += NT) s += (double)G[(int64_t)i * d + i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = NT / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) part[threadIdx.x] += part[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float l = relative ? (float)((double)lam * part[0] / (double)d) : lam;
+    sc->lambda = l;
+    if (lambda_out) *lambda_out = l;
+    *info = 0;
+  }
+}
+
+// Mx = G + lambda I; Rc, Bx[:, :d] hold R (filled later), Bx[:, d:] = I; Wf = W as fp32.
+template <typename WT>
+__global__ __launch_bounds__(NT) void setup_kernel(const float* G, const typename WT::storage* W, int d,
+                                                   const Scalars* sc, float* Mx, float* Bx, float* Wf) {
+  const int64_t n = (int64_t)d * d;
+  const float lam = sc->lambda;
+  for (int64_t e = blockIdx.x * (int64_t)NT + threadIdx.x; e < n; e += (int64_t)gridDim.x * NT) {
+    const int i = (int)(e / d), j = (int)(e % d);
+    Mx[e] = G[e] + (i == j ? lam : 0.f);
+    Bx[(int64_t)i * 2 * d + d + j] = (i == j) ? 1.f : 0.f;
+    Wf[e] = Cvt<WT>::to_f(W[e]);
+  }
+}
+
+// Factor the diagonal block Mx[k0:k0+nb, k0:k0+nb] = L L^T in place (lower), and write T = L^-1.
+// One wave; the block lives in LDS.
+__global__ __launch_bounds__(64) void diag_kernel(float* Mx, int d, int k0, int nb, float* T, int* info) {
+  __shared__ float a[NB][NB + 1];
+  __shared__ float x[NB][NB + 1];
+  __shared__ int bad;
+  const int l = threadIdx.x;
+  for (int i = 0; i < nb; ++i)
+    if (l < nb) a[i][l] = Mx[(int64_t)(k0 + i) * d + k0 + l];
+  if (l == 0) bad = 0;
+  __syncthreads();
+  for (int j = 0; j < nb; ++j) {
+    if (l == 0) {
+      const float piv = a[j][j];
+      if (!(piv > 0.f)) {
+        if (!bad) {
+          bad = 1;
+          if (*info == 0) *info = k0 + j + 1;
+        }
+        a[j][j] = 1.f;
+      } else {
+        a[j][j] = sqrtf(piv);
+      }
+    }
+    __syncthreads();
+    const float ljj = a[j][j];
+    if (l > j && l < nb) a[l][j] = a[l][j] / ljj;
+    __syncthreads();
+    if (l > j && l < nb) {
+      const float lij = a[l][j];
+      for (int k = j + 1; k <= l; ++k) a[l][k] = fmaf(-lij, a[k][j], a[l][k]);
+    }
+    __syncthreads();
+  }
+  // inverse of the lower-triangular factor, one column per lane
+  if (l < nb) {
+    for (int i = 0; i < nb; ++i) {
+      float v = (i == l) ? 1.f : 0.f;
+      if (i >= l) {
+        for (int k = l; k < i; ++k) v = fmaf(-a[i][k], x[k][l], v);
+        v = v / a[i][i];
+      }
+      x[i][l] = (i >= l) ? v : 0.f;
+    }
+  }
+  __syncthreads();
+  for (int i = 0; i < nb; ++i)
+    if (l < nb) {
+      Mx[(int64_t)(k0 + i) * d + k0 + l] = (l <= i) ? a[i][l] : 0.f;
+      T[i * NB + l] = x[i][l];
+    }
+}
+
+// r = R - (G + lambda I) dW with fp64 accumulation; 64 x 64 tile per work-group, 4 x 4 per thread.
+__global__ __launch_bounds__(NT) void resid64_kernel(const float* G, const float* dW, const float* R, int d,
+                                                     const Scalars* sc, float* r) {
+  __shared__ float gs[16][65];
+  __shared__ float ws[16][65];
+  const int tpd = (d + 63) / 64;
+  const int i0 = (blockIdx.x / tpd) * 64, j0 = (blockIdx.x % tpd) * 64;
+  const int tid = threadIdx.x, ti = tid / 16, tj = tid % 16;
+  double acc[4][4] = {};
+  for (int k0 = 0; k0 < d; k0 += 16) {
+    __syncthreads();
+    for (int e = tid; e < 64 * 16; e += NT) {
+      const int a = e / 16, kk = e % 16;
+      gs[kk][a] = (i0 + a < d && k0 + kk < d) ? G[(int64_t)(i0 + a) * d + k0 + kk] : 0.f;
+      const int kk2 = e / 64, b = e % 64;
+      ws[kk2][b] = (j0 + b < d && k0 + kk2 < d) ? dW[(int64_t)(k0 + kk2) * d + j0 + b] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc[u][w] = fma((double)gs[kk][ti * 4 + u], (double)ws[kk][tj * 4 + w], acc[u][w]);
+  }
+  const double lam = sc->lambda;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int i = i0 + ti * 4 + u, j = j0 + tj * 4 + w;
+      if (i < d && j < d) {
+        const int64_t e = (int64_t)i * d + j;
+        r[e] = (float)((double)R[e] - lam * (double)dW[e] - acc[u][w]);
+      }
+    }
+}
+
+// Partial dot products for epsilon: <D,P>, <G,P>, <W,R>, <dW,R>, <dW,dW>.
+__global__ __launch_bounds__(NT) void dots_kernel(const float* D, const float* G, const float* P, const float* Wf,
+                                                  const float* R, const float* dW, int64_t n, double* part) {
+  double s[5] = {0, 0, 0, 0, 0};
+  for (int64_t e = blockIdx.x * (int64_t)NT + threadIdx.x; e < n; e += (int64_t)gridDim.x * NT) {
+    const double p = P[e], r = R[e], dw = dW[e];
+    s[0] += (double)D[e] * p;
+    s[1] += (double)G[e] * p;
+    s[2] += (double)Wf[e] * r;
+    s[3] += dw * r;
+    s[4] += dw * dw;
+  }
+  __shared__ double red[5][NT];
+  for (int q = 0; q < 5; ++q) red[q][threadIdx.x] = s[q];
+  __syncthreads();
+  for (int o = NT / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o)
+      for (int q = 0; q < 5; ++q) red[q][threadIdx.x] += red[q][threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x < 5) part[blockIdx.x * 5 + threadIdx.x] = red[threadIdx.x][0];
+}
+
+__global__ void eps_kernel(const double* part, int nblk, const Scalars* sc, float* eps) {
+  if (threadIdx.x != 0) return;
+  double t[5] = {0, 0, 0, 0, 0};
+  for (int b = 0; b < nblk; ++b)
+    for (int q = 0; q < 5; ++q) t[q] += part[b * 5 + q];
+  const double lam = sc->lambda;
+  const double num2 = t[0] - t[3] - lam * t[4];
+  const double den2 = t[1] + 2.0 * t[2] + t[0];
+  *eps = (float)sqrt((num2 > 0.0 ? num2 : 0.0) / den2);
+}
+
+template <typename WT>
+__global__ __launch_bounds__(NT) void fold_kernel(const typename WT::storage* W, const float* dW, int64_t n,
+                                                  typename WT::storage* out) {
+  for (int64_t e = blockIdx.x * (int64_t)NT + threadIdx.x; e < n; e += (int64_t)gridDim.x * NT)
+    out[e] = Cvt<WT>::from_f(Cvt<WT>::to_f(W[e]) + dW[e]);
+}
+
+constexpr int DOT_BLOCKS = 512;
+
+struct WsLayout {
+  float* Mx;   // d x d
+  float* Bx;   // d x 2d
+  float* Rc;   // d x d
+  float* Wf;   // d x d
+  float* P;    // d x d (W W^T, also the refinement residual)
+  float* T;    // NB x NB
+  Scalars* sc;
+  double* part;
+};
+
+WsLayout carve(void* ws, int d) {
+  char* p = (char*)ws;
+  const size_t dd = (size_t)d * d * sizeof(float);
+  WsLayout w;
+  w.Mx = (float*)p; p += dd;
+  w.Bx = (float*)p; p += 2 * dd;
+  w.Rc = (float*)p; p += dd;
+  w.Wf = (float*)p; p += dd;
+  w.P = (float*)p; p += dd;
+  w.T = (float*)p; p += NB * NB * sizeof(float);
+  w.sc = (Scalars*)p; p += 256;
+  w.part = (double*)p;
+  return w;
+}
+
+#define ISPA_TRY(x)                      \
+  do {                                   \
+    hipError_t e_ = (x);                 \
+    if (e_ != hipSuccess) return e_;     \
+  } while (0)
+
+}  // namespace
+
+size_t solve_workspace_bytes(int d) {
+  return (size_t)d * d * sizeof(float) * 6 + NB * NB * sizeof(float) + 256 + DOT_BLOCKS * 5 * sizeof(double) + 256;
+}
+
+hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
+  const int d = L.d;
+  WsLayout w = carve(L.ws, d);
+  const int64_t dd = (int64_t)d * d;
+  const int eb = (int)((dd + NT - 1) / NT > 2048 ? 2048 : (dd + NT - 1) / NT);
+
+  hipLaunchKernelGGL(lambda_kernel, dim3(1), dim3(NT), 0, s, L.G, d, L.lambda, L.lambda_relative, w.sc, L.lambda_out,
+                     L.info);
+  ISPA_TRY(hipGetLastError());
+  if (L.w_dtype == DT_BF16)
+    hipLaunchKernelGGL(setup_kernel<BF16>, dim3(eb), dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, w.sc, w.Mx, w.Bx,
+                       w.Wf);
+  else if (L.w_dtype == DT_F16)
+    hipLaunchKernelGGL(setup_kernel<F16>, dim3(eb), dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, w.sc, w.Mx, w.Bx,
+                       w.Wf);
+  else
+    hipLaunchKernelGGL(setup_kernel<F32>, dim3(eb), dim3(NT), 0, s, L.G, (const float*)L.W, d, w.sc, w.Mx, w.Bx, w.Wf);
+  ISPA_TRY(hipGetLastError());
+
+  // R = C W into Rc and into the left half of the augmented right-hand side
+  {
+    Gemm g[2] = {mk(L.C, d, 0, w.Wf, d, 0, w.Rc, d, d, d, d, 1.f, 0.f),
+                 mk(L.C, d, 0, w.Wf, d, 0, w.Bx, 2 * d, d, d, d, 1.f, 0.f)};
+    ISPA_TRY(run_gemms(g, 2, s));
+  }
+  const int64_t ldb = 2 * (int64_t)d;
+  for (int k0 = 0; k0 < d; k0 += NB) {
+    const int nb = d - k0 < NB ? d - k0 : NB;
+    const int below = d - k0 - nb;
+    hipLaunchKernelGGL(diag_kernel, dim3(1), dim3(64), 0, s, w.Mx, d, k0, nb, w.T, L.info);
+    ISPA_TRY(hipGetLastError());
+    // panel: L21 = A21 T^T; Y_k = T B_k (R part, and the nonzero columns of the identity part)
+    {
+      Gemm g[3];
+      int c = 0;
+      if (below > 0) g[c++] = mk(w.Mx + (int64_t)(k0 + nb) * d + k0, d, 0, w.T, NB, 1, w.Mx + (int64_t)(k0 + nb) * d + k0, d,
+                                 below, nb, nb, 1.f, 0.f);
+      g[c++] = mk(w.T, NB, 0, w.Bx + (int64_t)k0 * ldb, ldb, 0, w.Bx + (int64_t)k0 * ldb, ldb, nb, d, nb, 1.f, 0.f);
+      g[c++] = mk(w.T, NB, 0, w.Bx + (int64_t)k0 * ldb + d, ldb, 0, w.Bx + (int64_t)k0 * ldb + d, ldb, nb, k0 + nb, nb,
+                  1.f, 0.f);
+      ISPA_TRY(run_gemms(g, c, s));
+    }
+    if (below > 0) {
+      // trailing update: A22 -= L21 L21^T (lower tiles); B_below -= L21 Y_k
+      const float* L21 = w.Mx + (int64_t)(k0 + nb) * d + k0;
+      Gemm g[3] = {
+          mk(L21, d, 0, L21, d, 1, w.Mx + (int64_t)(k0 + nb) * d + k0 + nb, d, below, below, nb, -1.f, 1.f, 0, 1),
+          mk(L21, d, 0, w.Bx + (int64_t)k0 * ldb, ldb, 0, w.Bx + (int64_t)(k0 + nb) * ldb, ldb, below, d, nb, -1.f, 1.f),
+          mk(L21, d, 0, w.Bx + (int64_t)k0 * ldb + d, ldb, 0, w.Bx + (int64_t)(k0 + nb) * ldb + d, ldb, below, k0 + nb,
+             nb, -1.f, 1.f)};
+      ISPA_TRY(run_gemms(g, 3, s));
+    }
+  }
+  // dW = (L^-1)^T Y   (L^-1 lower triangular: only k >= m contributes)
+  {
+    Gemm g = mk(w.Bx + d, ldb, 1, w.Bx, ldb, 0, L.delta_w, d, d, d, d, 1.f, 0.f, 1);
+    ISPA_TRY(run_gemms(&g, 1, s));
+  }
+  if (L.refine) {
+    const int tpd = (d + 63) / 64;
+    hipLaunchKernelGGL(resid64_kernel, dim3(tpd * tpd), dim3(NT), 0, s, L.G, L.delta_w, w.Rc, d, w.sc, w.P);
+    ISPA_TRY(hipGetLastError());
+    // t = L^-1 r (into Mx, no longer needed), dW += (L^-1)^T t
+    Gemm g1 = mk(w.Bx + d, ldb, 0, w.P, d, 0, w.Mx, d, d, d, d, 1.f, 0.f, 2);
+    ISPA_TRY(run_gemms(&g1, 1, s));
+    Gemm g2 = mk(w.Bx + d, ldb, 1, w.Mx, d, 0, L.delta_w, d, d, d, d, 1.f, 1.f, 1);
+    ISPA_TRY(run_gemms(&g2, 1, s));
+  }
+  if (L.eps) {
+    Gemm g = mk(w.Wf, d, 0, w.Wf, d, 1, w.P, d, d, d, d, 1.f, 0.f);
+    ISPA_TRY(run_gemms(&g, 1, s));
+    hipLaunchKernelGGL(dots_kernel, dim3(DOT_BLOCKS), dim3(NT), 0, s, L.D, L.G, w.P, w.Wf, w.Rc, L.delta_w, dd, w.part);
+    ISPA_TRY(hipGetLastError());
+    hipLaunchKernelGGL(eps_kernel, dim3(1), dim3(64), 0, s, w.part, DOT_BLOCKS, w.sc, L.eps);
+    ISPA_TRY(hipGetLastError());
+  }
+  if (L.w_new) {
+    if (L.w_dtype == DT_BF16)
+      hipLaunchKernelGGL(fold_kernel<BF16>, dim3(eb), dim3(NT), 0, s, (const uint16_t*)L.W, L.delta_w, dd,
+                         (uint16_t*)L.w_new);
+    else if (L.w_dtype == DT_F16)
+      hipLaunchKernelGGL(fold_kernel<F16>, dim3(eb), dim3(NT), 0, s, (const uint16_t*)L.W, L.delta_w, dd,
+                         (uint16_t*)L.w_new);
+    else
+      hipLaunchKernelGGL(fold_kernel<F32>, dim3(eb), dim3(NT), 0, s, (const float*)L.W, L.delta_w, dd, (float*)L.w_new);
+    ISPA_TRY(hipGetLastError());
+  }
+  return hipSuccess;
+}
+
+}  // namespace ispa

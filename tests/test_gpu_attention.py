@@ -1,0 +1,180 @@
+"""GPU parity: ispa_dual_attn and ispa_local_attn_fused_proj against the CPU oracle.
+
+Inputs are seeded N(0,1) tensors rounded to the storage type the kernel reads;
+the oracle sees exactly those values in float64.  Tolerances (max-rel =
+max|x - ref| / max|ref|): 1e-4 for fp32 inputs, 2e-2 for 16-bit inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gpu_util import dev, host, maxrel, run_dual, torch, tdtype
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 2e-2}
+
+
+def _inputs(shape, dtype, seed, q_scale=1.0):
+    rng = np.random.default_rng(seed)
+    d = shape.d
+    q = wl.round_to(rng.standard_normal((shape.n_q, d)) * q_scale, dtype)
+    k = wl.round_to(rng.standard_normal((shape.n_k, d)), dtype)
+    v = wl.round_to(rng.standard_normal((shape.n_k, d)), dtype)
+    return q, k, v
+
+
+def _check_dual(shape, q, k, v, io, stat, tol):
+    got = run_dual(shape, q, k, v, io, stat, ld_extra=5)
+    ref = oracle.dual_stream(q, k, v, shape.n_sink, shape.n_hist, shape.n_cur, shape.n_heads)
+    errs = {
+        "a_full": maxrel(got["a_full"], ref["a_full"]),
+        "a_loc": maxrel(got["a_loc"], ref["a_loc"]),
+        "delta_a": maxrel(got["delta_a"], ref["delta_a"]) if shape.n_hist > 0 else float(np.max(np.abs(got["delta_a"]))),
+        "lse_loc": maxrel(got["lse_loc"], ref["lse_loc"]),
+    }
+    if shape.n_hist > 0:
+        errs["lse_hist"] = maxrel(got["lse_hist"], ref["lse_hist"])
+    else:
+        assert np.all(np.isneginf(got["lse_hist"])), "empty history must give LSE_hist = -inf"
+    for name, e in errs.items():
+        assert e <= tol, f"{name}: max-rel {e:.3e} > {tol} ({shape})"
+    # the kernel writes no stat column past n_q
+    assert np.all(np.isnan(got["a_loc_pad"]))
+    return errs
+
+
+SHAPES_16 = [
+    wl.AttnShape(200, 70, 150, 100, 2, 128),    # ragged everywhere: 2 query blocks, 3 + 3 key tiles
+    wl.AttnShape(128, 64, 256, 64, 2, 128),     # aligned
+    wl.AttnShape(77, 33, 0, 50, 3, 128),        # empty history
+    wl.AttnShape(65, 0, 130, 65, 1, 128),       # no sink
+    wl.AttnShape(40, 64, 100, 0, 1, 128),       # local set = sink only
+    wl.AttnShape(1, 1, 1, 1, 1, 128),           # one query, one key per segment
+    wl.AttnShape(300, 1, 1000, 7, 2, 128),      # long history, tiny local set
+]
+
+
+@pytest.mark.parametrize("io,stat", [("bf16", "f16"), ("f16", "f16"), ("bf16", "bf16"), ("bf16", "f32")])
+@pytest.mark.parametrize("si", range(len(SHAPES_16)))
+def test_dual_attn_16bit(si, io, stat):
+    shape = SHAPES_16[si]
+    q, k, v = _inputs(shape, io, 100 + si)
+    _check_dual(shape, q, k, v, io, stat, TOL[io])
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_dual_attn_f32(head_dim):
+    shape = wl.AttnShape(150, 30, 97, 64, 2, head_dim)
+    q, k, v = _inputs(shape, "f32", 7)
+    _check_dual(shape, q, k, v, "f32", "f32", TOL["f32"])
+
+
+@pytest.mark.parametrize("chunk", range(4))
+def test_dual_attn_tiny_workload(chunk):
+    """The tiny fp32 workload (hidden 128 = 2 x 64, 64-token frames), every warmup chunk."""
+    w = wl.TINY
+    x = wl.layer_inputs(w, chunk=chunk, with_w=False)
+    _check_dual(w.shape, x["q"], x["k"], x["v"], "f32", "f32", TOL["f32"])
+
+
+def test_peaky_scores():
+    """Large scores (|s| up to ~60): the online softmax must neither overflow nor lose the merge."""
+    shape = wl.AttnShape(96, 40, 200, 56, 2, 128)
+    q, k, v = _inputs(shape, "bf16", 11, q_scale=6.0)
+    _check_dual(shape, q, k, v, "bf16", "f16", TOL["bf16"])
+
+
+def test_duplicate_history_gives_zero_delta():
+    """History rows an exact copy of the local rows: A_full = A_loc and dA = 0 (up to rounding)."""
+    rng = np.random.default_rng(5)
+    n_sink, n_cur, H = 48, 80, 2
+    d = H * 128
+    ks = wl.round_to(rng.standard_normal((n_sink, d)), "bf16")
+    kc = wl.round_to(rng.standard_normal((n_cur, d)), "bf16")
+    vs = wl.round_to(rng.standard_normal((n_sink, d)), "bf16")
+    vc = wl.round_to(rng.standard_normal((n_cur, d)), "bf16")
+    k = np.concatenate([ks, kc, ks, kc])
+    v = np.concatenate([vs, vc, vs, vc])
+    shape = wl.AttnShape(n_cur, n_sink, n_sink + n_cur, n_cur, H, 128)
+    q = wl.round_to(rng.standard_normal((n_cur, d)), "bf16")
+    got = run_dual(shape, q, k, v, "bf16", "f32")
+    scale = np.max(np.abs(got["a_loc"]))
+    assert np.max(np.abs(got["delta_a"])) <= 2e-2 * scale
+    assert np.allclose(got["lse_hist"], got["lse_loc"], atol=1e-4)
+
+
+def test_zero_queries_average_values():
+    shape = wl.AttnShape(33, 20, 50, 40, 2, 128)
+    rng = np.random.default_rng(6)
+    q = np.zeros((shape.n_q, shape.d))
+    k = wl.round_to(rng.standard_normal((shape.n_k, shape.d)), "bf16")
+    v = wl.round_to(rng.standard_normal((shape.n_k, shape.d)), "bf16")
+    got = run_dual(shape, q, k, v, "bf16", "f32")
+    loc = oracle.branch_rows(shape.n_sink, shape.n_hist, shape.n_cur)["local"]
+    assert maxrel(got["a_loc"], np.broadcast_to(v[loc].mean(0), got["a_loc"].shape)) <= 2e-2
+    assert np.allclose(got["lse_loc"], math.log(shape.n_loc), atol=1e-5)
+    assert np.allclose(got["lse_hist"], math.log(shape.n_hist), atol=1e-5)
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_full_only_mode(io):
+    """No local outputs requested: single-stream attention over all rows (an F-layer after warmup)."""
+    shape = wl.AttnShape(140, 50, 300, 90, 2, 128 if io == "bf16" else 64)
+    q, k, v = _inputs(shape, io, 21)
+    got = run_dual(shape, q, k, v, io, "f16" if io == "bf16" else "f32", want=("a_full",))
+    ref, _ = oracle.softmax_attention(q, k, v, np.arange(shape.n_k), shape.n_heads)
+    assert maxrel(got["a_full"], ref) <= TOL[io]
+
+
+def test_dual_attn_is_deterministic():
+    shape = SHAPES_16[0]
+    q, k, v = _inputs(shape, "bf16", 3)
+    a = run_dual(shape, q, k, v, "bf16", "f16")
+    b = run_dual(shape, q, k, v, "bf16", "f16")
+    for key in ("a_full", "a_loc", "delta_a", "lse_loc", "lse_hist"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("io", ["bf16", "f16"])
+@pytest.mark.parametrize("n_hist", [0, 90])
+def test_local_attn_fused_proj(io, n_hist):
+    import kv_cache_attention_ispa_amd as ispa
+    t = torch()
+    shape = wl.AttnShape(150, 70, n_hist, 150, 2, 128)
+    q, k, v = _inputs(shape, io, 31 + n_hist)
+    rng = np.random.default_rng(99)
+    w_new = wl.round_to(rng.standard_normal((shape.d, shape.d)) / math.sqrt(shape.d), io)
+    s = ispa.AttnShape.of(shape)
+    ws = t.empty(ispa.workspace_bytes(ispa.CALL_LOCAL_ATTN_PROJ, s), dtype=t.uint8, device="cuda")
+    out = t.empty((shape.n_q, shape.d), dtype=tdtype(io), device="cuda")
+    ispa.local_attn_fused_proj(s, dev(q, io), dev(k, io), dev(v, io), dev(w_new, io), out, ws)
+    t.cuda.synchronize()
+    ref = oracle.local_layer_output(q, np.concatenate([k[:shape.n_sink], k[shape.n_sink + n_hist:]]),
+                                    np.concatenate([v[:shape.n_sink], v[shape.n_sink + n_hist:]]),
+                                    shape.n_sink, shape.n_cur, shape.n_heads, w_new)
+    assert maxrel(host(out), ref) <= TOL[io]
+
+
+def test_layer_1p3b_sampled_rows():
+    """The 1.3B-shaped layer at full size (4680 queries, 20280 cached rows, 12 heads), in the launch
+    configuration the bench times; 64 sampled query rows checked against the oracle."""
+    w = wl.LAYER_1P3B
+    s = w.shape
+    x = wl.layer_inputs(w, with_w=False)
+    got = run_dual(s, x["q"], x["k"], x["v"], "bf16", "f16")
+    rows = np.unique(np.concatenate([np.arange(0, 4680, 97), [4679, 4678, 128, 127]]))[:64]
+    r = {}
+    loc = oracle.branch_rows(s.n_sink, s.n_hist, s.n_cur)
+    qs = x["q"][rows]
+    r["a_loc"], r["lse_loc"] = oracle.softmax_attention(qs, x["k"], x["v"], loc["local"], s.n_heads, threads=8)
+    r["a_full"], _ = oracle.softmax_attention(qs, x["k"], x["v"], loc["full"], s.n_heads, threads=8)
+    _, r["lse_hist"] = oracle.softmax_attention(qs, x["k"], x["v"], loc["hist"], s.n_heads, threads=8)
+    assert maxrel(got["a_full"][rows], r["a_full"]) <= 2e-2
+    assert maxrel(got["a_loc"][rows], r["a_loc"]) <= 2e-2
+    assert maxrel(got["delta_a"][rows], r["a_full"] - r["a_loc"]) <= 2e-2
+    assert maxrel(got["lse_loc"][:, rows], r["lse_loc"]) <= 2e-2
+    assert maxrel(got["lse_hist"][:, rows], r["lse_hist"]) <= 2e-2
