@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark of the ISPA hot path on one MI355X.
+
+One step is one pass of the whole hot path over the 1.3B-shaped layer
+(hidden 1536 = 12 heads x 128; 4680 query tokens = one 3-frame chunk of 1560
+tokens/frame; cache = 1560 sink rows + 14040 history rows + 4680 current rows):
+
+  1. ispa_dual_attn            A_full (bf16), A_loc and dA (fp16, feature-major), both LSEs
+  2. ispa_gram_accum           G = A_loc^T A_loc, C = A_loc^T dA, D = dA^T dA (fp32)
+  3. ispa_absorb_solve         lambda = 1e-3 tr(G)/d, dW, epsilon, W_new = W + dW (bf16)
+  4. ispa_local_attn_fused_proj   the converted layer's step: local attention @ W_new
+
+Inputs are synthetic (seeded N(0,1) Q/K/V, W ~ N(0, 1/d)), resident in HBM
+before timing starts.  Prints one JSON line.  The headline value is the
+dual-stream attention throughput in TFLOP/s of algorithmic work
+(4 n_q n_k head_dim heads, one full attention: the local/history split adds no
+MFMA work); the absorb time per layer (steps 2 + 3) is reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dual_attn_layer_1p3b_traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "kv_cache_attention_ispa_amd", "csrc", "attn.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-queries", type=int, default=768, help="query rows in the CPU oracle sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also launch one plain 1 GiB device copy (for HBM counter calibration)")
+    return p.parse_args()
+
+
+def attn_source_hash() -> str:
+    with open(ATTN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per dual-attention launch from committed rocprofv3 counters, if they match this kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("attn_source_sha256_16") != attn_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(x, s, n_rows: int):
+    """The oracle, as it stands, on a bounded sample: dual-stream attention for n_rows queries
+    (all heads, all cached rows) plus the float64 ridge solve at full size."""
+    import numpy as np
+    import oracle
+    threads = min(len(os.sched_getaffinity(0)), 16)
+    rows = np.linspace(0, s.n_q - 1, n_rows).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.dual_stream(x["q"][rows], x["k"], x["v"], s.n_sink, s.n_hist, s.n_cur, s.n_heads, threads=threads)
+    t_attn = time.perf_counter() - t0
+    flops = 4.0 * n_rows * s.n_k * s.head_dim * s.n_heads
+    return {"value": round(flops / t_attn / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"float64 dual-stream attention (local, full and history passes) for {n_rows} of "
+                      f"{s.n_q} queries x {s.n_heads} heads x {s.n_k} cached rows, {t_attn:.2f} s; rate on the "
+                      f"same algorithmic FLOP count as the GPU value"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import kv_cache_attention_ispa_amd as ispa
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w = wl.LAYER_1P3B
+    s = w.shape
+    d = s.d
+    x = wl.layer_inputs(w)
+    dev = lambda a, dt=torch.bfloat16: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(dt)
+    q, k, v, W = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["w"])
+    loc_rows = np.concatenate([np.arange(s.n_sink), np.arange(s.n_sink + s.n_hist, s.n_k)])
+    k_loc = k[torch.from_numpy(loc_rows).cuda()].contiguous()
+    v_loc = v[torch.from_numpy(loc_rows).cuda()].contiguous()
+    shape = ispa.AttnShape.of(s)
+    shape_l = ispa.AttnShape(s.n_q, s.n_sink, 0, s.n_cur, s.n_heads, s.head_dim, 0.0)
+
+    a_full = torch.empty((s.n_q, d), dtype=torch.bfloat16, device="cuda")
+    ld = ((s.n_q + 7) // 8) * 8
+    a_loc_t = torch.empty((d, ld), dtype=torch.float16, device="cuda")
+    da_t = torch.empty((d, ld), dtype=torch.float16, device="cuda")
+    lse_l = torch.empty((s.n_heads, s.n_q), device="cuda")
+    lse_h = torch.empty((s.n_heads, s.n_q), device="cuda")
+    G = torch.empty((d, d), device="cuda")
+    C = torch.empty((d, d), device="cuda")
+    D = torch.empty((d, d), device="cuda")
+    dW = torch.empty((d, d), device="cuda")
+    W_new = torch.empty((d, d), dtype=torch.bfloat16, device="cuda")
+    eps = torch.empty((1,), device="cuda")
+    lam = torch.empty((1,), device="cuda")
+    info = torch.empty((1,), dtype=torch.int32, device="cuda")
+    ws_solve = torch.empty(ispa.workspace_bytes(ispa.CALL_ABSORB_SOLVE, None, d), dtype=torch.uint8, device="cuda")
+    ws_loc = torch.empty(ispa.workspace_bytes(ispa.CALL_LOCAL_ATTN_PROJ, shape_l), dtype=torch.uint8, device="cuda")
+    out = torch.empty((s.n_q, d), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    n_ev = 5
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        ispa.dual_attn(shape, q, k, v, a_full=a_full, a_loc_t=a_loc_t, delta_a_t=da_t, ld_stat=ld, lse_loc=lse_l,
+                       lse_hist=lse_h, stream=stream)
+        if ev: ev[1].record(stream)
+        ispa.gram_accum(a_loc_t, da_t, s.n_q, G, C, D, accumulate=False, stream=stream)
+        if ev: ev[2].record(stream)
+        ispa.absorb_solve(G, C, W, w.lam, w.lam_relative, dW, info, ws_solve, D=D, w_new=W_new, eps=eps,
+                          lambda_out=lam, refine=False, stream=stream)
+        if ev: ev[3].record(stream)
+        ispa.local_attn_fused_proj(shape_l, q, k_loc, v_loc, W_new, out, ws_loc, stream=stream)
+        if ev: ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(info.item()) != 0:
+        print(f"solve reported info={int(info.item())}", file=sys.stderr)
+        sys.exit(1)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(events[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    seg = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(n_ev - 1)] for i in range(args.steps)])
+    attn_ms, gram_ms, solve_ms, local_ms = seg.mean(axis=0)
+    attn_flops = s.attn_flops()
+    attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    gram_flops = 3 * 2.0 * s.n_q * d * d            # G, C, D computed as full d x d products
+    solve_flops = (13.0 / 3.0) * d ** 3              # R = CW, Cholesky, two triangular solves
+    local_flops = s.local_flops() + 2.0 * s.n_q * d * d
+    step_flops = attn_flops + gram_flops + solve_flops + local_flops
+
+    traffic = measured_traffic()
+    result = {
+        "metric": "dual-stream attn TFLOP/s (% MFMA peak) + dW absorb ms/layer, 1.3B-shape",
+        "value": round(attn_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_q": s.n_q, "n_sink": s.n_sink, "n_hist": s.n_hist, "n_cur": s.n_cur,
+                   "heads": s.n_heads, "head_dim": s.head_dim, "d": d, "stat_dtype": w.stat_dtype,
+                   "lambda": "1e-3*tr(G)/d", "parallelism": "none (1 GPU)"},
+        "attn_pct_mfma_peak": round(100.0 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+        "absorb_ms_per_layer": round(gram_ms + solve_ms, 4),
+        "attn_ms": round(attn_ms, 4),
+        "gram_ms": round(gram_ms, 4),
+        "solve_ms": round(solve_ms, 4),
+        "local_layer_step_ms": round(local_ms, 4),
+        "step_tflops": round(step_flops / (total_ms / args.steps * 1e-3) / 1e12, 2),
+        "eps": round(float(eps.item()), 6),
+        "roofline": {"bound": "mfma", "kernel": "attn_mfma_kernel (dual stream)",
+                     "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "flops_per_launch": attn_flops, "avg_launch_ms": round(attn_ms, 4)},
+    }
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(x, s, args.cpu_queries)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
