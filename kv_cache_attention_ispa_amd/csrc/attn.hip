@@ -11,7 +11,8 @@
 // Kernel design (bf16 / fp16, head_dim 128):
 //  * one work-group = 128 queries of one head, 4 waves x 32 queries;
 //  * keys stream through LDS in tiles of 64 rows (K and V, double-buffered,
-//    padded row pitches); a branch is a virtual row range made of
+//    padded row pitches) with direct global-to-LDS loads issued one tile ahead;
+//    a branch is a virtual row range made of
 //    up to two physical segments, so the sink + current-chunk local set is
 //    one contiguous loop and only its last tile needs a mask;
 //  * S^T = K Q^T with 32x32x16 MFMA: every lane owns one query, so the softmax
@@ -34,14 +35,15 @@ constexpr int HD = 128;          // head dim of the MFMA path
 constexpr int BM = 128;          // queries per work-group
 constexpr int BN = 64;           // keys per tile
 constexpr int NTHREADS = 256;
+constexpr float kRescaleSlack = 8.f;   // log2 units: probabilities stay below 2^8 between rescales
 // LDS tiles are row-major with padded pitches: every MFMA operand read is a per-lane base
 // address plus an immediate offset, and the read patterns below hit distinct banks.
 constexpr int K_PITCH = HD * 2 + 16;              // 272 bytes per key row
-constexpr int V_PITCH = HD * 2 + 32;              // 288 bytes per value row
+constexpr int V_PITCH = HD * 2 + 64;              // 320 bytes per value row
 constexpr int K_TILE = BN * K_PITCH;
 constexpr int V_TILE = BN * V_PITCH;
 constexpr int STAGE_BYTES = K_TILE + V_TILE;
-constexpr int LDS_BYTES = 2 * STAGE_BYTES;        // double-buffered: 70 KiB
+constexpr int LDS_BYTES = 2 * STAGE_BYTES;        // double-buffered: 74 KiB
 
 // A branch: virtual rows [0, len) mapped onto up to two physical row segments.
 struct Branch {
@@ -49,25 +51,53 @@ struct Branch {
   __device__ __forceinline__ int row(int v) const { return v < len0 ? start0 + v : start1 + (v - len0); }
 };
 
-// Global -> register -> LDS staging of one 64-row tile of K or V for one head:
-// 256 threads x 4 chunks of 16 bytes; 16 consecutive threads cover one 256-byte row.
-struct TileLoader {
-  u32x4 r[4];
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int d, int col0, const Branch& br,
-                                       int tile_start, int tid) {
-    const int c = tid & 15;
+// Global -> LDS staging of one 64-row tile of K or V for one head with direct-to-LDS loads
+// (global_load_lds_dwordx4: lane l of a wave instruction writes 16 bytes at base + 16 l).  A padded
+// row of PITCH bytes is PITCH/16 slots, 16 of them data; the tile is a run of 64 * PITCH/16 slots
+// filled 64 at a time by every lane.  A lane that falls on a padding slot loads its row's last
+// chunk again (padding is never read).  Rows past the end of the branch are filled with the
+// branch's last row, so the values stay finite (their probabilities are zero).
+template <int PITCH>
+struct DmaTile {
+  static constexpr int SLOTS = PITCH / 16;                   // slots per row
+  static constexpr int NINST = SLOTS;                        // 64 rows x SLOTS slots / 64 lanes
+  static constexpr int PER_WAVE = (NINST + 3) / 4;
+  uint32_t off[PER_WAVE];   // byte offset of this lane's chunk from the tile's first row
+  __device__ __forceinline__ void init(int wave, int lane, int d) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = (tid >> 4) + 16 * i;
-      const int vi = tile_start + rr;
-      r[i] = vi < br.len ? *(const u32x4*)(src + (int64_t)br.row(vi) * d + col0 + c * 8) : u32x4{0, 0, 0, 0};
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int p = 64 * (wave + 4 * j) + lane;
+      const int r = p / SLOTS, c = min(p % SLOTS, 15);
+      off[j] = (uint32_t)(r * d + c * 8) * 2u;
     }
   }
-  template <int PITCH>
-  __device__ __forceinline__ void store(char* tile, int tid) const {
-    char* base = tile + (tid >> 4) * PITCH + (tid & 15) * 16;
+  // Issue the loads of tile rows [tile_start, tile_start + 64) of branch br (column block col0).
+  __device__ __forceinline__ void issue(const uint16_t* __restrict__ src, int d, int col0, const Branch& br,
+                                        int tile_start, char* tile, int wave, int lane) const {
+    const bool contiguous = tile_start + 64 <= br.len &&
+                            (tile_start + 64 <= br.len0 || tile_start >= br.len0);
+    if (contiguous) {
+      const char* base = (const char*)(src + (int64_t)br.row(tile_start) * d + col0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4*)(base + 16 * i * PITCH) = r[i];
+      for (int j = 0; j < PER_WAVE; ++j) {
+        const int inst = wave + 4 * j;
+        if (inst < NINST)
+          __builtin_amdgcn_global_load_lds((const void*)(base + off[j]), (lds_void*)(tile + 1024 * inst), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER_WAVE; ++j) {
+        const int inst = wave + 4 * j;
+        if (inst < NINST) {
+          const int p = 64 * inst + lane;
+          const int r = p / SLOTS, c = min(p % SLOTS, 15);
+          int vi = tile_start + r;
+          vi = vi < br.len ? vi : br.len - 1;
+          const uint16_t* g = src + (int64_t)br.row(vi) * d + col0 + c * 8;
+          __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(tile + 1024 * inst), 16, 0, 0);
+        }
+      }
+    }
   }
 };
 
@@ -107,12 +137,15 @@ __device__ __forceinline__ void run_branch(const AttnParams& p, const Branch& br
   const int n_tiles = (br.len + BN - 1) / BN;
   if (n_tiles == 0) return;
 
-  TileLoader ld;
+  const int wave = tid >> 6;
+  DmaTile<K_PITCH> kd;
+  DmaTile<V_PITCH> vd;
+  kd.init(wave, lane, p.d);
+  vd.init(wave, lane, p.d);
   __syncthreads();  // previous users of the LDS stages are done
-  ld.load(p.k, p.d, col0, br, 0, tid);
-  ld.store<K_PITCH>(lds, tid);
-  ld.load(p.v, p.d, col0, br, 0, tid);
-  ld.store<V_PITCH>(lds + K_TILE, tid);
+  kd.issue(p.k, p.d, col0, br, 0, lds, wave, lane);
+  vd.issue(p.v, p.d, col0, br, 0, lds + K_TILE, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // per-lane LDS bases; every read below adds a compile-time offset
@@ -121,10 +154,13 @@ __device__ __forceinline__ void run_branch(const AttnParams& p, const Branch& br
   const int vbase = (4 * (g >> 1) + (i16 >> 2)) * V_PITCH + (16 * (g & 1) + 4 * (i16 & 3)) * 2;
   for (int t = 0; t < n_tiles; ++t) {
     char* stage = lds + (t & 1) * STAGE_BYTES;
-    char* next = lds + ((t + 1) & 1) * STAGE_BYTES;
     const bool has_next = t + 1 < n_tiles;
-    // K of the next tile lands while this tile's QK^T and softmax run
-    if (has_next) ld.load(p.k, p.d, col0, br, (t + 1) * BN, tid);
+    // the next tile streams into the other stage while this one is computed
+    if (has_next) {
+      char* next = lds + ((t + 1) & 1) * STAGE_BYTES;
+      kd.issue(p.k, p.d, col0, br, (t + 1) * BN, next, wave, lane);
+      vd.issue(p.v, p.d, col0, br, (t + 1) * BN, next + K_TILE, wave, lane);
+    }
 
     // ---- S^T = K Q^T for two 32-key sub-tiles.  Accumulator register r of lane l holds
     // key 32 kt + 8 (r/4) + 4 (l/32) + r%4 of this tile for query l%32.
@@ -151,17 +187,28 @@ __device__ __forceinline__ void run_branch(const AttnParams& p, const Branch& br
           if (key >= valid) s[kt][r] = -INFINITY;
         }
     }
-    // ---- online softmax (log2 domain)
+    // ---- online softmax (log2 domain).  The reference max m only moves when this tile's max
+    // exceeds it by more than kRescaleSlack (then O and the row sum are rescaled, for the whole
+    // wave at once); otherwise the probabilities are taken against the stale reference and stay
+    // below 2^kRescaleSlack.  The final normalisation uses the same reference, so this is exact.
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    mx = wave_max_xor32(mx);
-    const float m_new = fmaxf(st.m, mx * p.scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-    st.m = m_new;
-    float rs = 0.f;
+    mx = wave_max_xor32(mx) * p.scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > st.m + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(st.m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+      st.m = m_new;
+      st.lsum *= alpha;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.o[tt][r] *= alpha;
+    }
+    const float m_ref = st.m;
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
     u32x4 pf[2][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -170,21 +217,13 @@ __device__ __forceinline__ void run_branch(const AttnParams& p, const Branch& br
         float e[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          e[j] = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * u + j], p.scale_log2, -m_new));
-          rs += e[j];
+          e[j] = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * u + j], p.scale_log2, -m_ref));
+          rs[j & 3] += e[j];
         }
         pf[kt][u] = u32x4{pack2<T>(e[0], e[1]), pack2<T>(e[2], e[3]), pack2<T>(e[4], e[5]), pack2<T>(e[6], e[7])};
       }
-    st.lsum = fmaf(st.lsum, alpha, rs);
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.o[tt][r] *= alpha;
+    st.lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 
-    if (has_next) {
-      ld.store<K_PITCH>(next, tid);
-      ld.load(p.v, p.d, col0, br, (t + 1) * BN, tid);  // V of the next tile lands during PV
-    }
     // ---- O^T += V^T P^T.  MFMA step (kt, u) of lane half h uses the probabilities of keys
     // 32 kt + 16 u + 4 h + 0..3 and 32 kt + 16 u + 8 + 4 h + 0..3 (registers 8u..8u+7); the
     // matching V^T operand is two transposing reads of 4 keys x 16 columns per 16-lane group.
@@ -202,7 +241,7 @@ __device__ __forceinline__ void run_branch(const AttnParams& p, const Branch& br
         }
       }
 
-    if (has_next) ld.store<V_PITCH>(next + K_TILE, tid);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
     __syncthreads();
   }
 }

@@ -54,9 +54,18 @@ template <> struct Cvt<F32> {
   static __device__ __forceinline__ float from_f(float f) { return f; }
 };
 
-// Pack two floats into one dword of two 16-bit values (low = a).
-template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return (uint32_t)Cvt<T>::from_f(a) | ((uint32_t)Cvt<T>::from_f(b) << 16);
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+
+// Pack two floats into one dword of two 16-bit values (low = a), round to nearest even;
+// one v_cvt_pk_{bf16,f16}_f32 each.
+template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b);
+template <> __device__ __forceinline__ uint32_t pack2<BF16>(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+template <> __device__ __forceinline__ uint32_t pack2<F16>(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
 }
 
 // 32x32x16 MFMA with 16-bit inputs given as raw dword quads (8 values per lane).

@@ -28,7 +28,7 @@ namespace {
 
 constexpr int NB = 64;          // Cholesky panel width
 constexpr int TB = 64;          // GEMM output tile
-constexpr int TK = 16;          // GEMM k-step
+constexpr int TK = 32;          // GEMM k-step
 constexpr int NT = 256;
 
 // ------------------------------------------------------------------------------------------
@@ -69,57 +69,54 @@ __global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmBatch b) {
   if (g.kmode == 1) k_begin = (m0 / TK) * TK;
   if (g.kmode == 2) k_end = min(g.K, m0 + TB);
   f32x16 acc = {};
-  float ra[4], rb[4];
+  // Each thread moves two 16-byte vectors of op(A) and two of op(B) per k-step (all sizes are
+  // multiples of 4, so a vector is either fully inside or fully outside the matrix).
+  f32x4 ra[2], rb[2];
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
   auto gload = [&](int k0) {
-    if (!g.transA) {
-      const int m = tid >> 2, kk = (tid & 3) * 4;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int gm = m0 + m, gk = k0 + kk + j;
-        ra[j] = (gm < g.M && gk < k_end) ? g.A[(int64_t)gm * g.lda + gk] : 0.f;
+    for (int h = 0; h < 2; ++h) {
+      const int e = tid + NT * h;                // 512 vectors per operand tile
+      if (!g.transA) {                           // A[m][k]: vector along k
+        const int m = e >> 3, kk = (e & 7) * 4;
+        const int gm = m0 + m, gk = k0 + kk;
+        ra[h] = (gm < g.M && gk < k_end) ? *(const f32x4*)(g.A + (int64_t)gm * g.lda + gk) : z4;
+      } else {                                   // A[k][m]: vector along m
+        const int kk = e >> 4, m = (e & 15) * 4;
+        const int gm = m0 + m, gk = k0 + kk;
+        ra[h] = (gm < g.M && gk < k_end) ? *(const f32x4*)(g.A + (int64_t)gk * g.lda + gm) : z4;
       }
-    } else {
-      const int kk = tid >> 4, m = (tid & 15) * 4;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int gm = m0 + m + j, gk = k0 + kk;
-        ra[j] = (gm < g.M && gk < k_end) ? g.A[(int64_t)gk * g.lda + gm] : 0.f;
-      }
-    }
-    if (!g.transB) {
-      const int kk = tid >> 4, n = (tid & 15) * 4;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int gn = n0 + n + j, gk = k0 + kk;
-        rb[j] = (gn < g.N && gk < k_end) ? g.B[(int64_t)gk * g.ldb + gn] : 0.f;
-      }
-    } else {
-      const int n = tid >> 2, kk = (tid & 3) * 4;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int gn = n0 + n, gk = k0 + kk + j;
-        rb[j] = (gn < g.N && gk < k_end) ? g.B[(int64_t)gn * g.ldb + gk] : 0.f;
+      if (!g.transB) {                           // B[k][n]: vector along n
+        const int kk = e >> 4, n = (e & 15) * 4;
+        const int gn = n0 + n, gk = k0 + kk;
+        rb[h] = (gn < g.N && gk < k_end) ? *(const f32x4*)(g.B + (int64_t)gk * g.ldb + gn) : z4;
+      } else {                                   // B[n][k]: vector along k
+        const int n = e >> 3, kk = (e & 7) * 4;
+        const int gn = n0 + n, gk = k0 + kk;
+        rb[h] = (gn < g.N && gk < k_end) ? *(const f32x4*)(g.B + (int64_t)gn * g.ldb + gk) : z4;
       }
     }
   };
   auto sstore = [&](int buf) {
-    if (!g.transA) {
-      const int m = tid >> 2, kk = (tid & 3) * 4;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) As[buf][kk + j][m] = ra[j];
-    } else {
-      const int kk = tid >> 4, m = (tid & 15) * 4;
+    for (int h = 0; h < 2; ++h) {
+      const int e = tid + NT * h;
+      if (!g.transA) {
+        const int m = e >> 3, kk = (e & 7) * 4;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) As[buf][kk][m + j] = ra[j];
-    }
-    if (!g.transB) {
-      const int kk = tid >> 4, n = (tid & 15) * 4;
+        for (int j = 0; j < 4; ++j) As[buf][kk + j][m] = ra[h][j];
+      } else {
+        const int kk = e >> 4, m = (e & 15) * 4;
+        *(f32x4*)&As[buf][kk][m] = ra[h];
+      }
+      if (!g.transB) {
+        const int kk = e >> 4, n = (e & 15) * 4;
+        *(f32x4*)&Bs[buf][kk][n] = rb[h];
+      } else {
+        const int n = e >> 3, kk = (e & 7) * 4;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Bs[buf][kk][n + j] = rb[j];
-    } else {
-      const int n = tid >> 2, kk = (tid & 3) * 4;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) Bs[buf][kk + j][n] = rb[j];
+        for (int j = 0; j < 4; ++j) Bs[buf][kk + j][n] = rb[h][j];
+      }
     }
   };
   if (k_begin < k_end) {
@@ -224,57 +221,78 @@ __global__ __launch_bounds__(NT) void setup_kernel(const float* G, const typenam
   }
 }
 
-// Factor the diagonal block Mx[k0:k0+nb, k0:k0+nb] = L L^T in place (lower), and write T = L^-1.
-// One wave; the block lives in LDS.
-__global__ __launch_bounds__(64) void diag_kernel(float* Mx, int d, int k0, int nb, float* T, int* info) {
-  __shared__ float a[NB][NB + 1];
-  __shared__ float x[NB][NB + 1];
-  __shared__ int bad;
-  const int l = threadIdx.x;
-  for (int i = 0; i < nb; ++i)
-    if (l < nb) a[i][l] = Mx[(int64_t)(k0 + i) * d + k0 + l];
-  if (l == 0) bad = 0;
-  __syncthreads();
-  for (int j = 0; j < nb; ++j) {
-    if (l == 0) {
-      const float piv = a[j][j];
-      if (!(piv > 0.f)) {
-        if (!bad) {
-          bad = 1;
-          if (*info == 0) *info = k0 + j + 1;
+// Factor the diagonal block Mx[k0:k0+nb, k0:k0+nb] = L L^T in place (lower) and write T = L^-1.
+// 256 threads: thread t owns row i = t/4, columns 16 (t%4) .. +15 of the block A (kept symmetric,
+// so row j also holds column j) and of the augmented block U that starts as I.  Step j broadcasts
+// row j through LDS (one barrier) and records it; then every row i > j applies
+//   a_ik -= (a_ij / p_j) a_jk,      u_i -= (a_ij / p_j) u_j,      p_j = a_jj,
+// i.e. right-looking Cholesky and forward substitution with the divisions by l_jj = sqrt(p_j)
+// deferred.  Entries a_ik with k <= j are finished after step j and may take garbage afterwards:
+// the factor is read back from the recorded rows, L_ij = rec_j[i] / sqrt(p_j) for i > j.
+// U's row j is final at step j and rows i <= j are never updated again; (L^-1)_i = u_i / sqrt(p_i).
+// Rows past nb (last panel) are padded with the identity.
+__global__ __launch_bounds__(256) void diag_kernel(float* Mx, int d, int k0, int nb, float* T, int* info) {
+  __shared__ __attribute__((aligned(16))) float rec[NB][NB + 4];   // row j as broadcast at step j
+  __shared__ __attribute__((aligned(16))) float rowu[2][NB];
+  __shared__ float pivs[NB];
+  const int t = threadIdx.x;
+  const int i = t >> 2, c0 = (t & 3) * 16;
+  float ar[16], ur[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int k = c0 + m;
+    float v;
+    if (i < nb && k < nb)
+      v = (k <= i) ? Mx[(int64_t)(k0 + i) * d + k0 + k] : Mx[(int64_t)(k0 + k) * d + k0 + i];
+    else
+      v = (i == k) ? 1.f : 0.f;
+    ar[m] = v;
+    ur[m] = (i == k) ? 1.f : 0.f;
+  }
+  for (int j = 0; j < NB; ++j) {
+    const int b = j & 1;
+    if (i == j) {
+#pragma unroll
+      for (int m = 0; m < 16; m += 4) {
+        *(f32x4*)&rec[j][c0 + m] = f32x4{ar[m], ar[m + 1], ar[m + 2], ar[m + 3]};
+        *(f32x4*)&rowu[b][c0 + m] = f32x4{ur[m], ur[m + 1], ur[m + 2], ur[m + 3]};
+      }
+    }
+    __syncthreads();
+    float piv = rec[j][j];
+    if (!(piv > 0.f)) {
+      if (t == 0 && j < nb && *info == 0) *info = k0 + j + 1;
+      piv = 1.f;
+    }
+    if (i > j) {
+      const float f = rec[j][i] * __builtin_amdgcn_rcpf(piv);
+#pragma unroll
+      for (int m = 0; m < 16; m += 4) {
+        const f32x4 ra = *(const f32x4*)&rec[j][c0 + m];
+        const f32x4 ru = *(const f32x4*)&rowu[b][c0 + m];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ar[m + e] = fmaf(-f, ra[e], ar[m + e]);
+          ur[m + e] = fmaf(-f, ru[e], ur[m + e]);
         }
-        a[j][j] = 1.f;
-      } else {
-        a[j][j] = sqrtf(piv);
       }
     }
-    __syncthreads();
-    const float ljj = a[j][j];
-    if (l > j && l < nb) a[l][j] = a[l][j] / ljj;
-    __syncthreads();
-    if (l > j && l < nb) {
-      const float lij = a[l][j];
-      for (int k = j + 1; k <= l; ++k) a[l][k] = fmaf(-lij, a[k][j], a[l][k]);
-    }
-    __syncthreads();
-  }
-  // inverse of the lower-triangular factor, one column per lane
-  if (l < nb) {
-    for (int i = 0; i < nb; ++i) {
-      float v = (i == l) ? 1.f : 0.f;
-      if (i >= l) {
-        for (int k = l; k < i; ++k) v = fmaf(-a[i][k], x[k][l], v);
-        v = v / a[i][i];
-      }
-      x[i][l] = (i >= l) ? v : 0.f;
-    }
+    if (t == 0) pivs[j] = piv;
   }
   __syncthreads();
-  for (int i = 0; i < nb; ++i)
-    if (l < nb) {
-      Mx[(int64_t)(k0 + i) * d + k0 + l] = (l <= i) ? a[i][l] : 0.f;
-      T[i * NB + l] = x[i][l];
+  if (i < nb) {
+    const float inv_i = 1.f / sqrtf(pivs[i]);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const int k = c0 + m;
+      if (k >= nb) continue;
+      float l = 0.f;
+      if (k < i) l = rec[k][i] / sqrtf(pivs[k]);
+      else if (k == i) l = sqrtf(pivs[i]);
+      Mx[(int64_t)(k0 + i) * d + k0 + k] = l;
+      T[i * NB + k] = ur[m] * inv_i;
     }
+  }
 }
 
 // r = R - (G + lambda I) dW with fp64 accumulation; 64 x 64 tile per work-group, 4 x 4 per thread.
@@ -338,15 +356,24 @@ __global__ __launch_bounds__(NT) void dots_kernel(const float* D, const float* G
   if (threadIdx.x < 5) part[blockIdx.x * 5 + threadIdx.x] = red[threadIdx.x][0];
 }
 
-__global__ void eps_kernel(const double* part, int nblk, const Scalars* sc, float* eps) {
-  if (threadIdx.x != 0) return;
+__global__ __launch_bounds__(NT) void eps_kernel(const double* part, int nblk, const Scalars* sc, float* eps) {
+  __shared__ double red[5][NT];
   double t[5] = {0, 0, 0, 0, 0};
-  for (int b = 0; b < nblk; ++b)
+  for (int b = threadIdx.x; b < nblk; b += NT)
     for (int q = 0; q < 5; ++q) t[q] += part[b * 5 + q];
-  const double lam = sc->lambda;
-  const double num2 = t[0] - t[3] - lam * t[4];
-  const double den2 = t[1] + 2.0 * t[2] + t[0];
-  *eps = (float)sqrt((num2 > 0.0 ? num2 : 0.0) / den2);
+  for (int q = 0; q < 5; ++q) red[q][threadIdx.x] = t[q];
+  __syncthreads();
+  for (int o = NT / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o)
+      for (int q = 0; q < 5; ++q) red[q][threadIdx.x] += red[q][threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double lam = sc->lambda;
+    const double num2 = red[0][0] - red[3][0] - lam * red[4][0];
+    const double den2 = red[1][0] + 2.0 * red[2][0] + red[0][0];
+    *eps = (float)sqrt((num2 > 0.0 ? num2 : 0.0) / den2);
+  }
 }
 
 template <typename WT>
@@ -415,17 +442,18 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
     hipLaunchKernelGGL(setup_kernel<F32>, dim3(eb), dim3(NT), 0, s, L.G, (const float*)L.W, d, w.sc, w.Mx, w.Bx, w.Wf);
   ISPA_TRY(hipGetLastError());
 
-  // R = C W into Rc and into the left half of the augmented right-hand side
+  // R = C W into the left half of the augmented right-hand side, and a copy kept in Rc
   {
-    Gemm g[2] = {mk(L.C, d, 0, w.Wf, d, 0, w.Rc, d, d, d, d, 1.f, 0.f),
-                 mk(L.C, d, 0, w.Wf, d, 0, w.Bx, 2 * d, d, d, d, 1.f, 0.f)};
-    ISPA_TRY(run_gemms(g, 2, s));
+    Gemm g = mk(L.C, d, 0, w.Wf, d, 0, w.Bx, 2 * d, d, d, d, 1.f, 0.f);
+    ISPA_TRY(run_gemms(&g, 1, s));
+    ISPA_TRY(hipMemcpy2DAsync(w.Rc, (size_t)d * sizeof(float), w.Bx, (size_t)2 * d * sizeof(float),
+                              (size_t)d * sizeof(float), (size_t)d, hipMemcpyDeviceToDevice, s));
   }
   const int64_t ldb = 2 * (int64_t)d;
   for (int k0 = 0; k0 < d; k0 += NB) {
     const int nb = d - k0 < NB ? d - k0 : NB;
     const int below = d - k0 - nb;
-    hipLaunchKernelGGL(diag_kernel, dim3(1), dim3(64), 0, s, w.Mx, d, k0, nb, w.T, L.info);
+    hipLaunchKernelGGL(diag_kernel, dim3(1), dim3(256), 0, s, w.Mx, d, k0, nb, w.T, L.info);
     ISPA_TRY(hipGetLastError());
     // panel: L21 = A21 T^T; Y_k = T B_k (R part, and the nonzero columns of the identity part)
     {
@@ -469,7 +497,7 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
     ISPA_TRY(run_gemms(&g, 1, s));
     hipLaunchKernelGGL(dots_kernel, dim3(DOT_BLOCKS), dim3(NT), 0, s, L.D, L.G, w.P, w.Wf, w.Rc, L.delta_w, dd, w.part);
     ISPA_TRY(hipGetLastError());
-    hipLaunchKernelGGL(eps_kernel, dim3(1), dim3(64), 0, s, w.part, DOT_BLOCKS, w.sc, L.eps);
+    hipLaunchKernelGGL(eps_kernel, dim3(1), dim3(NT), 0, s, w.part, DOT_BLOCKS, w.sc, L.eps);
     ISPA_TRY(hipGetLastError());
   }
   if (L.w_new) {
