@@ -121,6 +121,7 @@ def main():
     eps = torch.empty((1,), device="cuda")
     lam = torch.empty((1,), device="cuda")
     info = torch.empty((1,), dtype=torch.int32, device="cuda")
+    ws_attn = torch.empty(ispa.workspace_bytes(ispa.CALL_DUAL_ATTN, shape), dtype=torch.uint8, device="cuda")
     ws_solve = torch.empty(ispa.workspace_bytes(ispa.CALL_ABSORB_SOLVE, None, d), dtype=torch.uint8, device="cuda")
     ws_loc = torch.empty(ispa.workspace_bytes(ispa.CALL_LOCAL_ATTN_PROJ, shape_l), dtype=torch.uint8, device="cuda")
     out = torch.empty((s.n_q, d), dtype=torch.bfloat16, device="cuda")
@@ -130,7 +131,7 @@ def main():
     def step(ev=None):
         if ev: ev[0].record(stream)
         ispa.dual_attn(shape, q, k, v, a_full=a_full, a_loc_t=a_loc_t, delta_a_t=da_t, ld_stat=ld, lse_loc=lse_l,
-                       lse_hist=lse_h, stream=stream)
+                       lse_hist=lse_h, workspace=ws_attn, stream=stream)
         if ev: ev[1].record(stream)
         ispa.gram_accum(a_loc_t, da_t, s.n_q, G, C, D, accumulate=False, stream=stream)
         if ev: ev[2].record(stream)

@@ -99,7 +99,12 @@ typedef struct ispa_attn_shape {
  * warmup); otherwise it runs the dual stream and writes the non-NULL outputs.
  * dtypes: io_dtype BF16 or F16 (MFMA path; stat_dtype F16, BF16 or F32) or
  * F32 (stat_dtype F32).  Requires n_q >= 1, n_sink + n_cur >= 1 (an empty local
- * set is EINVAL), n_hist >= 0.  No workspace (workspace may be NULL).
+ * set is EINVAL), n_hist >= 0.
+ * Precision: QK^T and PV run on MFMA with fp32 accumulation.  With BF16 inputs
+ * and F16 statistics the PV product uses fp16 probabilities and an fp16 copy of
+ * V made in the workspace (exact for |v| < 65504; larger values become inf);
+ * this needs ispa_workspace_bytes(ISPA_CALL_DUAL_ATTN, shape, 0) bytes of
+ * workspace.  Every other combination needs none (workspace may be NULL).
  */
 int ispa_dual_attn(const ispa_attn_shape* shape, int io_dtype,
                    const void* q, const void* k, const void* v,

@@ -107,8 +107,10 @@ def workspace_bytes(call_id: int, shape: Optional[AttnShape] = None, d: int = 0)
 
 
 def dual_attn(shape: AttnShape, q, k, v, a_full=None, a_loc_t=None, delta_a_t=None, ld_stat: Optional[int] = None,
-              lse_loc=None, lse_hist=None, stream=None) -> None:
-    """ispa_dual_attn: see include/ispa.h.  Stat outputs are feature-major [d, ld_stat] views."""
+              lse_loc=None, lse_hist=None, workspace=None, stream=None) -> None:
+    """ispa_dual_attn: see include/ispa.h.  Stat outputs are feature-major [d, ld_stat] views;
+    workspace (bytes from workspace_bytes(CALL_DUAL_ATTN, shape)) is needed for bf16 inputs with
+    fp16 statistics."""
     for n, t in (("q", q), ("k", k), ("v", v), ("a_full", a_full), ("lse_loc", lse_loc), ("lse_hist", lse_hist)):
         _dense(t, n)
     stat = a_loc_t if a_loc_t is not None else delta_a_t
@@ -120,7 +122,8 @@ def dual_attn(shape: AttnShape, q, k, v, a_full=None, a_loc_t=None, delta_a_t=No
     st = _dtype_code(stat) if stat is not None else F16
     _check(lib().ispa_dual_attn(ctypes.byref(shape), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(a_full), st,
                                 _ptr(a_loc_t), _ptr(delta_a_t), int(ld_stat or 0), _ptr(lse_loc), _ptr(lse_hist),
-                                None, 0, _stream(stream)), "ispa_dual_attn")
+                                _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                _stream(stream)), "ispa_dual_attn")
 
 
 def gram_accum(a_loc_t, delta_a_t, n: int, G, C, D=None, accumulate: bool = False, stream=None) -> None:

@@ -47,7 +47,10 @@ const char* ispa_status_string(int status) {
 
 size_t ispa_workspace_bytes(int call_id, const ispa_attn_shape* shape, int d) {
   switch (call_id) {
-    case ISPA_CALL_DUAL_ATTN: return 0;
+    case ISPA_CALL_DUAL_ATTN:
+      if (!shape || shape->n_heads < 1) return 0;
+      return attn_f16_values_bytes((int64_t)shape->n_sink + shape->n_hist + shape->n_cur,
+                                   (int64_t)shape->n_heads * shape->head_dim) + 256;
     case ISPA_CALL_ABSORB_SOLVE: return d > 0 ? solve_workspace_bytes(d) : 0;
     case ISPA_CALL_LOCAL_ATTN_PROJ:
       if (!shape || shape->n_q < 1 || shape->n_heads < 1) return 0;
@@ -59,8 +62,6 @@ size_t ispa_workspace_bytes(int call_id, const ispa_attn_shape* shape, int d) {
 int ispa_dual_attn(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k, const void* v,
                    void* a_full, int stat_dtype, void* a_loc_t, void* delta_a_t, int64_t ld_stat, float* lse_loc,
                    float* lse_hist, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   int st = check_shape(shape);
   if (st) return st;
   if (!valid_dtype(io_dtype)) return ISPA_EUNSUPPORTED;
@@ -99,6 +100,13 @@ int ispa_dual_attn(const ispa_attn_shape* shape, int io_dtype, const void* q, co
   L.n_heads = shape->n_heads;
   L.head_dim = shape->head_dim;
   L.scale = eff_scale(shape);
+  L.ws = workspace;
+  L.ws_bytes = workspace_bytes;
+  if (attn_needs_f16_values(L)) {
+    const size_t need = attn_f16_values_bytes((int64_t)shape->n_sink + shape->n_hist + shape->n_cur,
+                                              (int64_t)shape->n_heads * shape->head_dim);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return ISPA_EWORKSPACE;
+  }
   return hip_status(launch_attention(L, (hipStream_t)stream));
 }
 
@@ -189,6 +197,8 @@ int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype, const
   L.n_heads = shape->n_heads;
   L.head_dim = shape->head_dim;
   L.scale = eff_scale(shape);
+  L.ws = nullptr;
+  L.ws_bytes = 0;
   hipError_t e = launch_attention(L, s);
   if (e != hipSuccess) return ISPA_EHIP;
   const int d = shape->n_heads * shape->head_dim;

@@ -22,6 +22,10 @@
 //    ordered as two groups of 4 consecutive keys), V^T comes from the row-major
 //    V tile through transposing LDS reads;
 //  * exp2 with the softmax scale folded into log2(e); fp32 accumulation;
+//  * when the statistics are requested in fp16 from bf16 inputs, V is copied to
+//    fp16 first and the probabilities are rounded to fp16 (11-bit mantissa) for
+//    the PV product, which keeps dA accurate enough for ill-conditioned
+//    absorption problems; QK^T stays in bf16;
 //  * blockIdx -> (head, query block) is XCD-aware so the work-groups of one head
 //    share an L2.
 #include "common.hpp"
@@ -122,7 +126,8 @@ struct BranchState {
   float lsum;      // partial row sum over this lane's keys
 };
 
-template <typename T>
+// T: element type of Q and K (QK^T MFMA); TP: element type of P and V (PV MFMA).
+template <typename T, typename TP>
 __device__ __forceinline__ void run_branch(const AttnParams& p, const Branch& br, const u32x4 (&qf)[8], int col0,
                                            char* lds, BranchState& st) {
   const int tid = threadIdx.x;
@@ -220,7 +225,7 @@ __device__ __forceinline__ void run_branch(const AttnParams& p, const Branch& br
           e[j] = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * u + j], p.scale_log2, -m_ref));
           rs[j & 3] += e[j];
         }
-        pf[kt][u] = u32x4{pack2<T>(e[0], e[1]), pack2<T>(e[2], e[3]), pack2<T>(e[4], e[5]), pack2<T>(e[6], e[7])};
+        pf[kt][u] = u32x4{pack2<TP>(e[0], e[1]), pack2<TP>(e[2], e[3]), pack2<TP>(e[4], e[5]), pack2<TP>(e[6], e[7])};
       }
     st.lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 
@@ -237,7 +242,7 @@ __device__ __forceinline__ void run_branch(const AttnParams& p, const Branch& br
           const u32x2 h0 = lds_read_tr16((const lds_void*)(vb + (32 * kt + 16 * u) * V_PITCH + 64 * tt));
           const u32x2 h1 = lds_read_tr16((const lds_void*)(vb + (32 * kt + 16 * u + 8) * V_PITCH + 64 * tt));
           const u32x4 a = u32x4{h0.x, h0.y, h1.x, h1.y};
-          st.o[tt] = mfma32x32x16<T>(a, pf[kt][u], st.o[tt]);
+          st.o[tt] = mfma32x32x16<TP>(a, pf[kt][u], st.o[tt]);
         }
       }
 
@@ -291,7 +296,8 @@ __device__ __forceinline__ void store_token_major(void* out, int d, int col0, in
 }
 
 // MODE 0: dual stream; MODE 1: single stream over all rows; MODE 2: single stream over the local rows.
-template <typename T, typename ST, int MODE>
+// T: type of Q, K and of the token-major output; TP: type of P and V in the PV product; ST: statistics.
+template <typename T, typename TP, typename ST, int MODE>
 __global__ __launch_bounds__(NTHREADS, 2) void attn_mfma_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const int n_blocks = p.n_qblk * p.n_heads;
@@ -316,10 +322,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_mfma_kernel(AttnParams p) {
   BranchState st;
   if (MODE == 1) {
     Branch all{0, n_k, 0, n_k};
-    run_branch<T>(p, all, qf, col0, lds, st);
+    run_branch<T, TP>(p, all, qf, col0, lds, st);
   } else {
     Branch loc{0, p.n_sink, p.n_sink + p.n_hist, p.n_sink + p.n_cur};
-    run_branch<T>(p, loc, qf, col0, lds, st);
+    run_branch<T, TP>(p, loc, qf, col0, lds, st);
   }
   float L = st.lsum + __shfl_xor(st.lsum, 32);
   float inv = 1.f / L;
@@ -351,7 +357,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_mfma_kernel(AttnParams p) {
   ol.save(st.o);
 
   Branch hist{p.n_sink, p.n_hist, 0, p.n_hist};
-  run_branch<T>(p, hist, qf, col0, lds, st);
+  run_branch<T, TP>(p, hist, qf, col0, lds, st);
   const float l_h = st.lsum + __shfl_xor(st.lsum, 32);
   const float m_h = st.m;
   // merge through the log-sum-exp states
@@ -538,17 +544,47 @@ AttnParams make_params(const AttnLaunch& L) {
   return p;
 }
 
-template <typename T, int MODE>
-hipError_t launch_mfma_mode(AttnParams p, int stat, hipStream_t s) {
-  p.n_qblk = (p.n_q + BM - 1) / BM;
+// bf16 -> fp16 copy of V (exact for |v| < 65504), so the PV product of the statistics path can run
+// with fp16 probabilities.
+__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
+                                                          int64_t n8) {
+  for (int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    const u32x4 x = ((const u32x4*)in)[i];
+    u32x4 y;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      y[j] = pack2<F16>(bf16_bits_to_float((uint16_t)(x[j] & 0xFFFFu)), bf16_bits_to_float((uint16_t)(x[j] >> 16)));
+    ((u32x4*)out)[i] = y;
+  }
+}
+
+template <typename T, typename TP, int MODE>
+hipError_t launch_mfma_stat(AttnParams p, int stat, hipStream_t s) {
   dim3 grid(p.n_qblk * p.n_heads), block(NTHREADS);
   if (MODE != 0 || stat == DT_F16)
-    hipLaunchKernelGGL((attn_mfma_kernel<T, F16, MODE>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((attn_mfma_kernel<T, TP, F16, MODE>), grid, block, 0, s, p);
   else if (stat == DT_BF16)
-    hipLaunchKernelGGL((attn_mfma_kernel<T, BF16, MODE>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((attn_mfma_kernel<T, TP, BF16, MODE>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<T, F32, MODE>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((attn_mfma_kernel<T, TP, F32, MODE>), grid, block, 0, s, p);
   return hipGetLastError();
+}
+
+template <typename T, int MODE>
+hipError_t launch_mfma_mode(AttnParams p, const AttnLaunch& L, hipStream_t s) {
+  p.n_qblk = (p.n_q + BM - 1) / BM;
+  if (attn_needs_f16_values(L)) {
+    // statistics requested in fp16 from bf16 inputs: P and V in fp16 for the PV product
+    const int64_t n = (int64_t)(L.n_sink + L.n_hist + L.n_cur) * L.n_heads * L.head_dim;
+    const int64_t n8 = n / 8;
+    const int blocks = (int)((n8 + 255) / 256 < 2048 ? (n8 + 255) / 256 : 2048);
+    hipLaunchKernelGGL(bf16_to_f16_kernel, dim3(blocks), dim3(256), 0, s, (const uint16_t*)L.v, (uint16_t*)L.ws, n8);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    p.v = (const uint16_t*)L.ws;
+    return launch_mfma_stat<T, F16, MODE>(p, L.stat, s);
+  }
+  return launch_mfma_stat<T, T, MODE>(p, L.stat, s);
 }
 
 template <int HDF, int MODE>
@@ -574,13 +610,13 @@ hipError_t launch_attention(const AttnLaunch& L, hipStream_t s) {
     return launch_f32_mode<128, 2>(p, s);
   }
   if (L.io == DT_BF16) {
-    if (L.mode == 0) return launch_mfma_mode<BF16, 0>(p, L.stat, s);
-    if (L.mode == 1) return launch_mfma_mode<BF16, 1>(p, L.stat, s);
-    return launch_mfma_mode<BF16, 2>(p, L.stat, s);
+    if (L.mode == 0) return launch_mfma_mode<BF16, 0>(p, L, s);
+    if (L.mode == 1) return launch_mfma_mode<BF16, 1>(p, L, s);
+    return launch_mfma_mode<BF16, 2>(p, L, s);
   }
-  if (L.mode == 0) return launch_mfma_mode<F16, 0>(p, L.stat, s);
-  if (L.mode == 1) return launch_mfma_mode<F16, 1>(p, L.stat, s);
-  return launch_mfma_mode<F16, 2>(p, L.stat, s);
+  if (L.mode == 0) return launch_mfma_mode<F16, 0>(p, L, s);
+  if (L.mode == 1) return launch_mfma_mode<F16, 1>(p, L, s);
+  return launch_mfma_mode<F16, 2>(p, L, s);
 }
 
 }  // namespace ispa

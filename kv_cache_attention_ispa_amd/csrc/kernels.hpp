@@ -23,7 +23,14 @@ struct AttnLaunch {
   float* lse_hist;
   int n_q, n_sink, n_hist, n_cur, n_heads, head_dim;
   float scale;
+  void* ws;          // device workspace (fp16 copy of V when attn_needs_f16_values)
+  size_t ws_bytes;
 };
+// Dual stream from bf16 inputs with fp16 statistics: the PV product runs on an fp16 copy of V.
+inline bool attn_needs_f16_values(const AttnLaunch& L) {
+  return L.mode == 0 && L.io == DT_BF16 && L.stat == DT_F16 && (L.a_loc_t || L.delta_a_t);
+}
+inline size_t attn_f16_values_bytes(int64_t n_k, int64_t d) { return (size_t)(n_k * d * 2); }
 hipError_t launch_attention(const AttnLaunch& L, hipStream_t s);
 
 // Gram statistics: out_z (+)= X_z Y_z^T for z in {G: (A, A), C: (A, dA), D: (dA, dA)}.

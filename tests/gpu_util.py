@@ -53,8 +53,11 @@ def run_dual(shape, q, k, v, io: str, stat: str, ld_extra: int = 0, want=("a_ful
     da_t = t.full((d, ld), float("nan"), device="cuda", dtype=tdtype(stat)) if "delta_a" in want else None
     lse_l = t.full((shape.n_heads, shape.n_q), float("nan"), device="cuda") if "lse" in want else None
     lse_h = t.full((shape.n_heads, shape.n_q), float("nan"), device="cuda") if "lse" in want else None
-    ispa.dual_attn(ispa.AttnShape.of(shape), qd, kd, vd, a_full=a_full, a_loc_t=a_loc_t, delta_a_t=da_t,
-                   ld_stat=ld if (a_loc_t is not None or da_t is not None) else 0, lse_loc=lse_l, lse_hist=lse_h)
+    s = ispa.AttnShape.of(shape)
+    ws = t.empty(ispa.workspace_bytes(ispa.CALL_DUAL_ATTN, s), dtype=t.uint8, device="cuda")
+    ispa.dual_attn(s, qd, kd, vd, a_full=a_full, a_loc_t=a_loc_t, delta_a_t=da_t,
+                   ld_stat=ld if (a_loc_t is not None or da_t is not None) else 0, lse_loc=lse_l, lse_hist=lse_h,
+                   workspace=ws)
     t.cuda.synchronize()
     out = {}
     if a_full is not None:

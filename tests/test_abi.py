@@ -48,7 +48,7 @@ def test_status_strings_and_version(L):
 
 def test_workspace_queries(L):
     s = ispa.AttnShape(4680, 1560, 14040, 4680, 12, 128, 0.0)
-    assert ispa.workspace_bytes(ispa.CALL_DUAL_ATTN, s) == 0
+    assert ispa.workspace_bytes(ispa.CALL_DUAL_ATTN, s) >= 20280 * 1536 * 2
     assert ispa.workspace_bytes(ispa.CALL_LOCAL_ATTN_PROJ, s) >= 4680 * 1536 * 2
     assert ispa.workspace_bytes(ispa.CALL_ABSORB_SOLVE, None, 1536) >= 6 * 1536 * 1536 * 4
     assert L.ispa_workspace_bytes(42, None, 0) == ctypes.c_size_t(-1).value
@@ -78,6 +78,7 @@ def test_dual_attn_rejects_empty_local_set(L):
 
 def test_dual_attn_rejects_bad_arguments(L):
     s = ispa.AttnShape(64, 8, 16, 64, 2, 128, 0.0)
+    assert _dual(L, s, io=1, stat=2) == EWORKSPACE        # bf16 inputs + fp16 statistics need the V copy
     assert _dual(L, s, q=0) == EINVAL                       # NULL q
     assert _dual(L, s, q=FAKE + 4) == EINVAL                # misaligned
     assert _dual(L, s, ld=60) == EINVAL                     # ld_stat < n_q

@@ -141,8 +141,10 @@ def _warmup_chain(w, chunks, layer=0, refine=False):
         ld = ((s.n_q + 7) // 8) * 8
         a_t = t.empty((d, ld), dtype=tdtype(w.stat_dtype), device="cuda")
         da_t = t.empty((d, ld), dtype=tdtype(w.stat_dtype), device="cuda")
-        ispa.dual_attn(ispa.AttnShape.of(s), dev(x["q"], w.dtype), dev(x["k"], w.dtype), dev(x["v"], w.dtype),
-                       a_loc_t=a_t, delta_a_t=da_t, ld_stat=ld)
+        sh = ispa.AttnShape.of(s)
+        ws = t.empty(ispa.workspace_bytes(ispa.CALL_DUAL_ATTN, sh), dtype=t.uint8, device="cuda")
+        ispa.dual_attn(sh, dev(x["q"], w.dtype), dev(x["k"], w.dtype), dev(x["v"], w.dtype),
+                       a_loc_t=a_t, delta_a_t=da_t, ld_stat=ld, workspace=ws)
         ispa.gram_accum(a_t, da_t, s.n_q, G, C, D, accumulate=i > 0)
         r = oracle.dual_stream(x["q"], x["k"], x["v"], s.n_sink, s.n_hist, s.n_cur, s.n_heads)
         ref_chunks.append((r["a_loc"], r["delta_a"], r["a_full"]))

@@ -191,11 +191,17 @@ def frames(w: Workload, layer: int, tensor: int, n_frames: int, rows: Optional[i
         yield x
 
 
-def rollout_frames(w: Workload, layer: int, n_frames: int) -> Dict[str, np.ndarray]:
-    """Stored (rounded) Q, K, V for frames 0..n_frames-1 of one layer, each [n_frames*frame, d]."""
+def rollout_frames(w: Workload, layer: int, n_frames: int, tensors=("q", "k", "v"),
+                   as_f32: bool = False) -> Dict[str, np.ndarray]:
+    """Stored (rounded) Q, K, V for frames 0..n_frames-1 of one layer, each [n_frames*frame, d].
+
+    as_f32 returns float32 arrays (exact for bf16 storage) to halve host memory on long rollouts.
+    """
     out = {}
-    for name, t in (("q", T_Q), ("k", T_K), ("v", T_V)):
-        out[name] = round_to(np.concatenate(list(frames(w, layer, t, n_frames))), w.dtype)
+    ids = {"q": T_Q, "k": T_K, "v": T_V}
+    for name in tensors:
+        x = np.concatenate([round_to(f, w.dtype).astype(np.float32) for f in frames(w, layer, ids[name], n_frames)])
+        out[name] = x if as_f32 else x.astype(np.float64)
     return out
 
 
