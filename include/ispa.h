@@ -135,8 +135,10 @@ int ispa_gram_accum(int d, int n, int stat_dtype, const void* a_loc_t, const voi
  * ||A_loc (W + dW) - A_full W||_F^2 + lambda ||dW||_F^2 is
  * dW = (G + lambda I)^-1 C W, obtained without iteration.  Computed as
  * R = C W, a blocked Cholesky factorisation G + lambda I = L L^T, and the two
- * triangular solves, all in fp32; refine = 1 adds one refinement step whose
- * residual R - (G + lambda I) dW is accumulated in fp64.
+ * triangular solves, all in fp32; refine = n (0..8) adds n steps of iterative
+ * refinement whose residual C W - (G + lambda I) dW is accumulated in fp64 (C W
+ * formed once in fp64).  Ill-conditioned systems (features > warmup tokens)
+ * need refinement to reach fp64-solve accuracy.
  *
  *   G, C [d, d] fp32 (from ispa_gram_accum); D [d, d] fp32, needed only for eps.
  *   W [d, d] in w_dtype (F32, BF16 or F16).

@@ -138,8 +138,8 @@ def gram_accum(a_loc_t, delta_a_t, n: int, G, C, D=None, accumulate: bool = Fals
 
 
 def absorb_solve(G, C, W, lam: float, relative: bool, delta_w, info, workspace, D=None, w_new=None, eps=None,
-                 lambda_out=None, refine: bool = False, stream=None) -> None:
-    """ispa_absorb_solve: dW = (G + lambda I)^-1 C W (+ eps, W_new)."""
+                 lambda_out=None, refine: int = 0, stream=None) -> None:
+    """ispa_absorb_solve: dW = (G + lambda I)^-1 C W (+ eps, W_new); refine = refinement steps."""
     for n_, t in (("G", G), ("C", C), ("D", D), ("W", W), ("delta_w", delta_w), ("w_new", w_new)):
         _dense(t, n_)
     d = G.shape[0]

@@ -140,7 +140,7 @@ int ispa_absorb_solve(int d, const float* G, const float* C, const float* D, int
   if (!valid_dtype(w_dtype)) return ISPA_EUNSUPPORTED;
   if (!G || !C || !W || !delta_w || !info) return ISPA_EINVAL;
   if (eps && !D) return ISPA_EINVAL;
-  if (!(lambda == lambda) || (lambda_relative != 0 && lambda_relative != 1) || (refine != 0 && refine != 1))
+  if (!(lambda == lambda) || (lambda_relative != 0 && lambda_relative != 1) || refine < 0 || refine > 8)
     return ISPA_EINVAL;
   if (!aligned16(G) || !aligned16(C) || !aligned16(D) || !aligned16(W) || !aligned16(delta_w) || !aligned16(w_new) ||
       !aligned4(eps) || !aligned4(lambda_out) || !aligned4(info))

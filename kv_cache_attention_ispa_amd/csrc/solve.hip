@@ -9,8 +9,8 @@
 //   the forward solve runs inside the same sweep on the augmented right-hand
 //   side [R | I], which leaves Y = L^-1 R and L^-1 when the sweep ends, so the
 //   backward solve is one triangular GEMM: dW = (L^-1)^T Y.
-//   Optional refinement: r = R - (G + lambda I) dW accumulated in fp64, then
-//   dW += (L^-1)^T (L^-1 r).
+//   Optional iterative refinement (a given number of steps): r = C W - (G + lambda I) dW
+//   accumulated in fp64 (C W formed once in fp64), then dW += (L^-1)^T (L^-1 r).
 //
 // "Dynamic layer selection" ranks layers by the reconstruction error epsilon;
 // it is evaluated here from the statistics alone (D = dA^T dA, P = W W^T):
@@ -295,11 +295,14 @@ __global__ __launch_bounds__(256) void diag_kernel(float* Mx, int d, int k0, int
   }
 }
 
-// r = R - (G + lambda I) dW with fp64 accumulation; 64 x 64 tile per work-group, 4 x 4 per thread.
-__global__ __launch_bounds__(NT) void resid64_kernel(const float* G, const float* dW, const float* R, int d,
-                                                     const Scalars* sc, float* r) {
-  __shared__ float gs[16][65];
-  __shared__ float ws[16][65];
+// out = A B accumulated in fp64 (A, B fp32 [d, d] row-major); 64 x 64 tile per work-group,
+// 4 x 4 outputs per thread.  MODE 0: R64 = A B (fp64 store).  MODE 1: the refinement residual
+// r = R64 - lambda dW - A B with A = G and B = dW (fp32 store).
+template <int MODE>
+__global__ __launch_bounds__(NT) void gemm64_kernel(const float* A, const float* B, int d, const Scalars* sc,
+                                                    double* R64, float* r) {
+  __shared__ float as[16][65];
+  __shared__ float bs[16][65];
   const int tpd = (d + 63) / 64;
   const int i0 = (blockIdx.x / tpd) * 64, j0 = (blockIdx.x % tpd) * 64;
   const int tid = threadIdx.x, ti = tid / 16, tj = tid % 16;
@@ -308,9 +311,9 @@ __global__ __launch_bounds__(NT) void resid64_kernel(const float* G, const float
     __syncthreads();
     for (int e = tid; e < 64 * 16; e += NT) {
       const int a = e / 16, kk = e % 16;
-      gs[kk][a] = (i0 + a < d && k0 + kk < d) ? G[(int64_t)(i0 + a) * d + k0 + kk] : 0.f;
+      as[kk][a] = (i0 + a < d && k0 + kk < d) ? A[(int64_t)(i0 + a) * d + k0 + kk] : 0.f;
       const int kk2 = e / 64, b = e % 64;
-      ws[kk2][b] = (j0 + b < d && k0 + kk2 < d) ? dW[(int64_t)(k0 + kk2) * d + j0 + b] : 0.f;
+      bs[kk2][b] = (j0 + b < d && k0 + kk2 < d) ? B[(int64_t)(k0 + kk2) * d + j0 + b] : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -318,9 +321,8 @@ __global__ __launch_bounds__(NT) void resid64_kernel(const float* G, const float
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) acc[u][w] = fma((double)gs[kk][ti * 4 + u], (double)ws[kk][tj * 4 + w], acc[u][w]);
+        for (int w = 0; w < 4; ++w) acc[u][w] = fma((double)as[kk][ti * 4 + u], (double)bs[kk][tj * 4 + w], acc[u][w]);
   }
-  const double lam = sc->lambda;
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -328,7 +330,10 @@ __global__ __launch_bounds__(NT) void resid64_kernel(const float* G, const float
       const int i = i0 + ti * 4 + u, j = j0 + tj * 4 + w;
       if (i < d && j < d) {
         const int64_t e = (int64_t)i * d + j;
-        r[e] = (float)((double)R[e] - lam * (double)dW[e] - acc[u][w]);
+        if (MODE == 0)
+          R64[e] = acc[u][w];
+        else
+          r[e] = (float)(R64[e] - (double)sc->lambda * (double)B[e] - acc[u][w]);
       }
     }
 }
@@ -394,6 +399,7 @@ struct WsLayout {
   float* T;    // NB x NB
   Scalars* sc;
   double* part;
+  double* R64; // d x d, C W accumulated in fp64 (refinement only)
 };
 
 WsLayout carve(void* ws, int d) {
@@ -407,7 +413,8 @@ WsLayout carve(void* ws, int d) {
   w.P = (float*)p; p += dd;
   w.T = (float*)p; p += NB * NB * sizeof(float);
   w.sc = (Scalars*)p; p += 256;
-  w.part = (double*)p;
+  w.part = (double*)p; p += DOT_BLOCKS * 5 * sizeof(double);
+  w.R64 = (double*)p;
   return w;
 }
 
@@ -420,7 +427,8 @@ WsLayout carve(void* ws, int d) {
 }  // namespace
 
 size_t solve_workspace_bytes(int d) {
-  return (size_t)d * d * sizeof(float) * 6 + NB * NB * sizeof(float) + 256 + DOT_BLOCKS * 5 * sizeof(double) + 256;
+  return (size_t)d * d * sizeof(float) * 6 + NB * NB * sizeof(float) + 256 + DOT_BLOCKS * 5 * sizeof(double) +
+         (size_t)d * d * sizeof(double) + 256;
 }
 
 hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
@@ -482,15 +490,21 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
     Gemm g = mk(w.Bx + d, ldb, 1, w.Bx, ldb, 0, L.delta_w, d, d, d, d, 1.f, 0.f, 1);
     ISPA_TRY(run_gemms(&g, 1, s));
   }
-  if (L.refine) {
+  if (L.refine > 0) {
+    // iterative refinement: r = C W - (G + lambda I) dW with fp64 accumulation (C W formed once in
+    // fp64), then dW += (L^-1)^T (L^-1 r) with the fp32 factor
     const int tpd = (d + 63) / 64;
-    hipLaunchKernelGGL(resid64_kernel, dim3(tpd * tpd), dim3(NT), 0, s, L.G, L.delta_w, w.Rc, d, w.sc, w.P);
+    hipLaunchKernelGGL(gemm64_kernel<0>, dim3(tpd * tpd), dim3(NT), 0, s, L.C, w.Wf, d, w.sc, w.R64, nullptr);
     ISPA_TRY(hipGetLastError());
-    // t = L^-1 r (into Mx, no longer needed), dW += (L^-1)^T t
-    Gemm g1 = mk(w.Bx + d, ldb, 0, w.P, d, 0, w.Mx, d, d, d, d, 1.f, 0.f, 2);
-    ISPA_TRY(run_gemms(&g1, 1, s));
-    Gemm g2 = mk(w.Bx + d, ldb, 1, w.Mx, d, 0, L.delta_w, d, d, d, d, 1.f, 1.f, 1);
-    ISPA_TRY(run_gemms(&g2, 1, s));
+    for (int it = 0; it < L.refine; ++it) {
+      hipLaunchKernelGGL(gemm64_kernel<1>, dim3(tpd * tpd), dim3(NT), 0, s, L.G, L.delta_w, d, w.sc, w.R64, w.P);
+      ISPA_TRY(hipGetLastError());
+      // t = L^-1 r (into Mx, no longer needed), dW += (L^-1)^T t
+      Gemm g1 = mk(w.Bx + d, ldb, 0, w.P, d, 0, w.Mx, d, d, d, d, 1.f, 0.f, 2);
+      ISPA_TRY(run_gemms(&g1, 1, s));
+      Gemm g2 = mk(w.Bx + d, ldb, 1, w.Mx, d, 0, L.delta_w, d, d, d, d, 1.f, 1.f, 1);
+      ISPA_TRY(run_gemms(&g2, 1, s));
+    }
   }
   if (L.eps) {
     Gemm g = mk(w.Wf, d, 0, w.Wf, d, 1, w.P, d, d, d, d, 1.f, 0.f);
