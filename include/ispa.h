@@ -100,11 +100,16 @@ typedef struct ispa_attn_shape {
  * dtypes: io_dtype BF16 or F16 (MFMA path; stat_dtype F16, BF16 or F32) or
  * F32 (stat_dtype F32).  Requires n_q >= 1, n_sink + n_cur >= 1 (an empty local
  * set is EINVAL), n_hist >= 0.
+ * Workspace: BF16/F16 inputs need ispa_workspace_bytes(ISPA_CALL_DUAL_ATTN,
+ * shape, 0) bytes (16-byte aligned; EWORKSPACE otherwise): the call first writes
+ * a transposed copy of V there, which the attention kernel streams, and the dual
+ * stream parks the local-branch outputs there while the history branch runs.
+ * Calls that share a workspace must not overlap in time.  F32 inputs
+ * need none (workspace may be NULL).  The 16-bit path addresses K and the copy
+ * with 32-bit byte offsets: n_k * d * 2 must stay below 2^31 (EUNSUPPORTED).
  * Precision: QK^T and PV run on MFMA with fp32 accumulation.  With BF16 inputs
- * and F16 statistics the PV product uses fp16 probabilities and an fp16 copy of
- * V made in the workspace (exact for |v| < 65504; larger values become inf);
- * this needs ispa_workspace_bytes(ISPA_CALL_DUAL_ATTN, shape, 0) bytes of
- * workspace.  Every other combination needs none (workspace may be NULL).
+ * and F16 statistics the PV product uses fp16 probabilities and the V copy is
+ * converted to fp16 (exact for |v| < 65504; larger values become inf).
  */
 int ispa_dual_attn(const ispa_attn_shape* shape, int io_dtype,
                    const void* q, const void* k, const void* v,
@@ -171,7 +176,8 @@ int ispa_absorb_solve(int d, const float* G, const float* C, const float* D,
  *   q [n_q, d], k/v [n_k, d] with the layout of ispa_attn_shape (history rows,
  *   if any, are skipped), w_new [d, d], out [n_q, d]; all io_dtype BF16 or F16.
  *   workspace: at least ispa_workspace_bytes(ISPA_CALL_LOCAL_ATTN_PROJ, shape, d)
- *   bytes (the local attention output between the two kernels).
+ *   bytes, 16-byte aligned (the local attention output between the two kernels
+ *   and the transposed copy of V); n_k * d * 2 below 2^31 as for ispa_dual_attn.
  */
 int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype,
                                const void* q, const void* k, const void* v, const void* w_new,

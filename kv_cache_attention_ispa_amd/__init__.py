@@ -109,8 +109,7 @@ def workspace_bytes(call_id: int, shape: Optional[AttnShape] = None, d: int = 0)
 def dual_attn(shape: AttnShape, q, k, v, a_full=None, a_loc_t=None, delta_a_t=None, ld_stat: Optional[int] = None,
               lse_loc=None, lse_hist=None, workspace=None, stream=None) -> None:
     """ispa_dual_attn: see include/ispa.h.  Stat outputs are feature-major [d, ld_stat] views;
-    workspace (bytes from workspace_bytes(CALL_DUAL_ATTN, shape)) is needed for bf16 inputs with
-    fp16 statistics."""
+    workspace (bytes from workspace_bytes(CALL_DUAL_ATTN, shape)) is needed for bf16/fp16 inputs."""
     for n, t in (("q", q), ("k", k), ("v", v), ("a_full", a_full), ("lse_loc", lse_loc), ("lse_hist", lse_hist)):
         _dense(t, n)
     stat = a_loc_t if a_loc_t is not None else delta_a_t

@@ -28,6 +28,25 @@ float eff_scale(const ispa_attn_shape* s) { return s->scale > 0.f ? s->scale : 1
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ISPA_OK : ISPA_EHIP; }
 
+// The local attention output between the two kernels of ispa_local_attn_fused_proj, rounded up to
+// 256 bytes; the V^T copy follows it in the workspace.
+size_t local_a_bytes(const ispa_attn_shape* s) {
+  return ((size_t)s->n_q * s->n_heads * s->head_dim * 2 + 255) / 256 * 256;
+}
+
+// ispa_dual_attn's workspace (16-bit inputs): the V^T copy, then the parked local outputs.
+size_t dual_ws_bytes(const ispa_attn_shape* s) {
+  return attn_vt_bytes_aligned((int64_t)s->n_sink + s->n_hist + s->n_cur, (int64_t)s->n_heads * s->head_dim) +
+         attn_stash_bytes(s->n_q, s->n_heads);
+}
+
+// Buffer addressing of the 16-bit path uses 32-bit byte offsets into K and V^T.
+bool fits_buffer(const ispa_attn_shape* s) {
+  const int64_t n_k = (int64_t)s->n_sink + s->n_hist + s->n_cur;
+  const int64_t d = (int64_t)s->n_heads * s->head_dim;
+  return n_k * d * 2 < INT32_MAX && (int64_t)attn_vt_bytes(n_k, d) < INT32_MAX;
+}
+
 }  // namespace
 
 extern "C" {
@@ -49,12 +68,12 @@ size_t ispa_workspace_bytes(int call_id, const ispa_attn_shape* shape, int d) {
   switch (call_id) {
     case ISPA_CALL_DUAL_ATTN:
       if (!shape || shape->n_heads < 1) return 0;
-      return attn_f16_values_bytes((int64_t)shape->n_sink + shape->n_hist + shape->n_cur,
-                                   (int64_t)shape->n_heads * shape->head_dim) + 256;
+      return dual_ws_bytes(shape);
     case ISPA_CALL_ABSORB_SOLVE: return d > 0 ? solve_workspace_bytes(d) : 0;
     case ISPA_CALL_LOCAL_ATTN_PROJ:
       if (!shape || shape->n_q < 1 || shape->n_heads < 1) return 0;
-      return (size_t)shape->n_q * shape->n_heads * shape->head_dim * 2 + 256;
+      return local_a_bytes(shape) + attn_vt_bytes_aligned((int64_t)shape->n_sink + shape->n_hist + shape->n_cur,
+                                                          (int64_t)shape->n_heads * shape->head_dim);
     default: return (size_t)-1;
   }
 }
@@ -78,7 +97,7 @@ int ispa_dual_attn(const ispa_attn_shape* shape, int io_dtype, const void* q, co
   if (io_dtype == ISPA_F32) {
     if ((a_loc_t || delta_a_t) && stat_dtype != ISPA_F32) return ISPA_EUNSUPPORTED;
   } else {
-    if (shape->head_dim != 128) return ISPA_EUNSUPPORTED;
+    if (shape->head_dim != 128 || !fits_buffer(shape)) return ISPA_EUNSUPPORTED;
   }
   AttnLaunch L;
   L.mode = dual ? 0 : 1;
@@ -102,10 +121,8 @@ int ispa_dual_attn(const ispa_attn_shape* shape, int io_dtype, const void* q, co
   L.scale = eff_scale(shape);
   L.ws = workspace;
   L.ws_bytes = workspace_bytes;
-  if (attn_needs_f16_values(L)) {
-    const size_t need = attn_f16_values_bytes((int64_t)shape->n_sink + shape->n_hist + shape->n_cur,
-                                              (int64_t)shape->n_heads * shape->head_dim);
-    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return ISPA_EWORKSPACE;
+  if (io_dtype != ISPA_F32) {
+    if (!workspace || workspace_bytes < dual_ws_bytes(shape) || !aligned16(workspace)) return ISPA_EWORKSPACE;
   }
   return hip_status(launch_attention(L, (hipStream_t)stream));
 }
@@ -171,7 +188,7 @@ int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype, const
   int st = check_shape(shape);
   if (st) return st;
   if (io_dtype != ISPA_BF16 && io_dtype != ISPA_F16) return ISPA_EUNSUPPORTED;
-  if (shape->head_dim != 128) return ISPA_EUNSUPPORTED;
+  if (shape->head_dim != 128 || !fits_buffer(shape)) return ISPA_EUNSUPPORTED;
   if (!q || !k || !v || !w_new || !out) return ISPA_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(w_new) || !aligned16(out)) return ISPA_EINVAL;
   const size_t need = ispa_workspace_bytes(ISPA_CALL_LOCAL_ATTN_PROJ, shape, 0);
@@ -197,8 +214,8 @@ int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype, const
   L.n_heads = shape->n_heads;
   L.head_dim = shape->head_dim;
   L.scale = eff_scale(shape);
-  L.ws = nullptr;
-  L.ws_bytes = 0;
+  L.ws = (char*)workspace + local_a_bytes(shape);
+  L.ws_bytes = workspace_bytes - local_a_bytes(shape);
   hipError_t e = launch_attention(L, s);
   if (e != hipSuccess) return ISPA_EHIP;
   const int d = shape->n_heads * shape->head_dim;

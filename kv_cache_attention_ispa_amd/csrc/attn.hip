@@ -9,99 +9,91 @@
 // and w = e^(LSE_H - LSE_F), A_full = A_loc + w (O_H - A_loc).
 //
 // Kernel design (bf16 / fp16, head_dim 128):
-//  * one work-group = 128 queries of one head, 4 waves x 32 queries;
-//  * keys stream through LDS in tiles of 64 rows (K and V, double-buffered,
-//    padded row pitches) with direct global-to-LDS loads issued one tile ahead;
-//    a branch is a virtual row range made of
-//    up to two physical segments, so the sink + current-chunk local set is
-//    one contiguous loop and only its last tile needs a mask;
-//  * S^T = K Q^T with 32x32x16 MFMA: every lane owns one query, so the softmax
-//    max/sum are in-lane plus one cross-lane step (lanes l and l^32);
-//  * O^T = V^T P^T with 32x32x16 MFMA: P^T stays in registers (a lane's
-//    accumulator registers are exactly its B operand, with the reduction index
-//    ordered as two groups of 4 consecutive keys), V^T comes from the row-major
-//    V tile through transposing LDS reads;
-//  * exp2 with the softmax scale folded into log2(e); fp32 accumulation;
-//  * when the statistics are requested in fp16 from bf16 inputs, V is copied to
-//    fp16 first and the probabilities are rounded to fp16 (11-bit mantissa) for
-//    the PV product, which keeps dA accurate enough for ill-conditioned
-//    absorption problems; QK^T stays in bf16;
-//  * blockIdx -> (head, query block) is XCD-aware so the work-groups of one head
-//    share an L2.
+//  * one work-group = 256 queries of one head: 8 waves x 32 queries, one work-group per CU,
+//    two waves per SIMD;
+//  * the two groups of four waves ping-pong: while one group runs its matrix phase
+//    (S^T = K Q^T of the next key tile and O^T += V^T P^T of the current one) the other
+//    runs its softmax phase (VALU), and every phase ends in a work-group barrier, so the
+//    matrix cores and the vector ALUs of a SIMD are busy at the same time;
+//  * keys stream through three-deep LDS rings of K tiles (64 keys x 128 dims) and V^T tiles
+//    (128 dims x 64 keys, read from a transposed copy of V that the call writes first), padded
+//    row pitches, filled with direct global-to-LDS loads two tiles ahead; every ring slot is its
+//    own LDS array, so the compiler can tell a slot being filled from a slot being read and only
+//    the explicit waits below order them;
+//  * a branch is a virtual row range made of up to two physical segments; the local branch
+//    (sink + current chunk) and the history branch form one tile sequence, the local state is
+//    closed when the first history tile is reached;
+//  * S^T = K Q^T with 32x32x16 MFMA: every lane owns one query, so the softmax max/sum are
+//    in-lane plus one exchange between lanes l and l^32 (v_permlane32_swap);
+//  * O^T = V^T P^T with 32x32x16 MFMA: P^T stays in registers -- the K rows of the QK operand
+//    are loaded in a permuted order so that a lane's accumulator registers are exactly its PV
+//    B operand over 8 consecutive keys -- and V^T is one plain 16-byte LDS read per MFMA (the
+//    transposing LDS read delivers a third of the bandwidth of plain reads on gfx950);
+//  * exp2 with the softmax scale folded into log2(e); the reference max only moves when a
+//    tile's max exceeds it by more than 2^8; the row sum adds the rounded 16-bit
+//    probabilities with packed dot products, so it matches what the PV product consumed;
+//  * when the statistics are requested in fp16 from bf16 inputs, V is copied to fp16 first and
+//    the probabilities are rounded to fp16 (11-bit mantissa) for the PV product, which keeps dA
+//    accurate enough for ill-conditioned absorption problems; QK^T stays in bf16;
+//  * blockIdx -> (head, query block) is XCD-aware so the work-groups of one head share an L2.
 #include "common.hpp"
 #include "kernels.hpp"
+
+#include <type_traits>
 
 namespace ispa {
 
 namespace {
 
 constexpr int HD = 128;          // head dim of the MFMA path
-constexpr int BM = 128;          // queries per work-group
 constexpr int BN = 64;           // keys per tile
-constexpr int NTHREADS = 256;
+constexpr int WAVES = 8;
+constexpr int MFMA_THREADS = WAVES * 64;
+constexpr int BM = WAVES * 32;   // queries per work-group of the MFMA path
+constexpr int NTHREADS = 256;    // fp32 path
 constexpr float kRescaleSlack = 8.f;   // log2 units: probabilities stay below 2^8 between rescales
-// LDS tiles are row-major with padded pitches: every MFMA operand read is a per-lane base
-// address plus an immediate offset, and the read patterns below hit distinct banks.
+// LDS tiles are row-major with padded pitches: every MFMA operand read is a per-lane base address
+// plus an immediate offset, and 16 consecutive lanes of a 16-byte read hit 16 distinct 4-bank groups.
+// K tiles are 64 key rows x 128 head dims; V tiles are transposed: 128 head-dim rows x 64 keys.
 constexpr int K_PITCH = HD * 2 + 16;              // 272 bytes per key row
-constexpr int V_PITCH = HD * 2 + 64;              // 320 bytes per value row
+constexpr int VT_PITCH = BN * 2 + 16;             // 144 bytes per head-dim row
+constexpr int K_SLOTS = K_PITCH / 16;             // 16-byte slots per row (the last one padding)
+constexpr int VT_SLOTS = VT_PITCH / 16;
 constexpr int K_TILE = BN * K_PITCH;
-constexpr int V_TILE = BN * V_PITCH;
-constexpr int STAGE_BYTES = K_TILE + V_TILE;
-constexpr int LDS_BYTES = 2 * STAGE_BYTES;        // double-buffered: 74 KiB
+constexpr int V_TILE = HD * VT_PITCH;
+constexpr int K_INST = BN * K_SLOTS / 64;         // wave-wide 16-byte loads per K tile (17)
+constexpr int V_INST = HD * VT_SLOTS / 64;        // per V^T tile (18)
+constexpr int LOADS_PER_WAVE = (K_INST + V_INST + WAVES - 1) / WAVES;   // 5: every wave issues the same count
+static_assert(K_SLOTS * BN % 64 == 0 && VT_SLOTS * HD % 64 == 0, "tile must be whole wave loads");
 
-// A branch: virtual rows [0, len) mapped onto up to two physical row segments.
-struct Branch {
-  int start0, len0, start1, len;
-  __device__ __forceinline__ int row(int v) const { return v < len0 ? start0 + v : start1 + (v - len0); }
-};
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 
-// Global -> LDS staging of one 64-row tile of K or V for one head with direct-to-LDS loads
-// (global_load_lds_dwordx4: lane l of a wave instruction writes 16 bytes at base + 16 l).  A padded
-// row of PITCH bytes is PITCH/16 slots, 16 of them data; the tile is a run of 64 * PITCH/16 slots
-// filled 64 at a time by every lane.  A lane that falls on a padding slot loads its row's last
-// chunk again (padding is never read).  Rows past the end of the branch are filled with the
-// branch's last row, so the values stay finite (their probabilities are zero).
-template <int PITCH>
-struct DmaTile {
-  static constexpr int SLOTS = PITCH / 16;                   // slots per row
-  static constexpr int NINST = SLOTS;                        // 64 rows x SLOTS slots / 64 lanes
-  static constexpr int PER_WAVE = (NINST + 3) / 4;
-  uint32_t off[PER_WAVE];   // byte offset of this lane's chunk from the tile's first row
-  __device__ __forceinline__ void init(int wave, int lane, int d) {
-#pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const int p = 64 * (wave + 4 * j) + lane;
-      const int r = p / SLOTS, c = min(p % SLOTS, 15);
-      off[j] = (uint32_t)(r * d + c * 8) * 2u;
-    }
+// The key tiles of one launch: up to three segments of consecutive cache rows, each cut into 64-row
+// tiles (the last one partial).  Dual stream: sink rows, current-chunk rows (together the local
+// branch) and history rows (the history branch, starting at tile t_hist); single stream: one
+// segment of all rows, or the sink and current-chunk segments.  A tile never crosses a segment
+// boundary, so every tile is 64 consecutive rows; rows past the segment's end are loaded too (the
+// next segment, or zeros past the end of the buffer) and masked.
+struct Sched {
+  // segment g: first cache row r_g, row count l_g, one past its last tile index e_g (scalars, no
+  // arrays: everything here stays in SGPRs)
+  int r0, r1, r2, l0, l1, l2, e0, e1, e2;
+  int n, t_hist;
+  __device__ __forceinline__ void set(int ra, int la, int rb, int lb, int rc, int lc) {
+    r0 = ra; l0 = la; r1 = rb; l1 = lb; r2 = rc; l2 = lc;
+    e0 = (la + BN - 1) / BN;
+    e1 = e0 + (lb + BN - 1) / BN;
+    e2 = e1 + (lc + BN - 1) / BN;
+    n = e2;
   }
-  // Issue the loads of tile rows [tile_start, tile_start + 64) of branch br (column block col0).
-  __device__ __forceinline__ void issue(const uint16_t* __restrict__ src, int d, int col0, const Branch& br,
-                                        int tile_start, char* tile, int wave, int lane) const {
-    const bool contiguous = tile_start + 64 <= br.len &&
-                            (tile_start + 64 <= br.len0 || tile_start >= br.len0);
-    if (contiguous) {
-      const char* base = (const char*)(src + (int64_t)br.row(tile_start) * d + col0);
-#pragma unroll
-      for (int j = 0; j < PER_WAVE; ++j) {
-        const int inst = wave + 4 * j;
-        if (inst < NINST)
-          __builtin_amdgcn_global_load_lds((const void*)(base + off[j]), (lds_void*)(tile + 1024 * inst), 16, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < PER_WAVE; ++j) {
-        const int inst = wave + 4 * j;
-        if (inst < NINST) {
-          const int p = 64 * inst + lane;
-          const int r = p / SLOTS, c = min(p % SLOTS, 15);
-          int vi = tile_start + r;
-          vi = vi < br.len ? vi : br.len - 1;
-          const uint16_t* g = src + (int64_t)br.row(vi) * d + col0 + c * 8;
-          __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(tile + 1024 * inst), 16, 0, 0);
-        }
-      }
-    }
+  // first cache row of tile t and its number of valid rows
+  __device__ __forceinline__ int row(int t) const {
+    return t < e0 ? r0 + BN * t : t < e1 ? r1 + BN * (t - e0) : r2 + BN * (t - e1);
+  }
+  __device__ __forceinline__ int valid(int t) const {
+    return t < e0 ? l0 - BN * t : t < e1 ? l1 - BN * (t - e0) : l2 - BN * (t - e1);
   }
 };
 
@@ -109,6 +101,9 @@ struct AttnParams {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
+  const uint16_t* vt;   // 16-bit path: V^T [d, ldv]
+  int ldv;
+  void* stash;          // dual stream: parked local outputs, kAttnStashBytesPerBlock per work-group
   void* a_full;       // token-major, io dtype
   void* a_loc_t;      // feature-major, stat dtype
   void* delta_a_t;    // feature-major, stat dtype
@@ -119,146 +114,231 @@ struct AttnParams {
   float scale_log2;
 };
 
+// Load group k = {K tile k, V^T tile k-1}: K_INST + V_INST wave-wide direct-to-LDS loads (16 bytes
+// per lane, buffer addressing), dealt round-robin to the 8 waves, LOADS_PER_WAVE each (the few left
+// over repeat the last V^T load, identical data).  Load `inst` of a tile with PITCH-byte rows puts
+// lane l on slot 64 inst + l of the tile: row (64 inst + l) / SLOTS, 16-byte chunk (64 inst + l) % SLOTS;
+// a lane on a padding slot loads its row's last chunk again (padding is never read).  A lane's byte
+// offset within the tile is fixed; the tile's first key is the scalar offset.
+struct Loader {
+  __amdgpu_buffer_rsrc_t rk, rv;
+  uint32_t off[LOADS_PER_WAVE];
+  __device__ __forceinline__ void init(const AttnParams& p, int n_k, int wave, int lane) {
+    // raw buffers over K [n_k, d] and V^T [d, ldv]; reads past the end return zeros.  Word 3
+    // (0x00020000) is the untyped-access descriptor of gfx9.
+    rk = __builtin_amdgcn_make_buffer_rsrc((void*)p.k, (short)0, (int)((int64_t)n_k * p.d * 2), 0x00020000);
+    rv = __builtin_amdgcn_make_buffer_rsrc((void*)p.vt, (short)0, (int)((int64_t)p.d * p.ldv * 2), 0x00020000);
+#pragma unroll
+    for (int j = 0; j < LOADS_PER_WAVE; ++j) {
+      const int idx = wave + WAVES * j;
+      if (idx < K_INST) {
+        const int slot = 64 * idx + lane;
+        off[j] = (uint32_t)((slot / K_SLOTS) * p.d + min(slot % K_SLOTS, 15) * 8) * 2u;
+      } else {
+        const int slot = 64 * min(idx - K_INST, V_INST - 1) + lane;
+        off[j] = (uint32_t)((slot / VT_SLOTS) * p.ldv + min(slot % VT_SLOTS, 7) * 8) * 2u;
+      }
+    }
+  }
+  // Every wave issues exactly LOADS_PER_WAVE loads per group, also past the ends of the tile
+  // sequence (then a valid tile is loaded again into a ring slot nobody reads), so the number of
+  // loads in flight is the same on every path and one wait count fits all iterations.
+  __device__ __forceinline__ void issue(const Sched& sc, int k, const AttnParams& p, int head, char* kt, char* vt,
+                                        int wave) const {
+    const int tk = min(k, sc.n - 1);
+    const int tv = min(max(k - 1, 0), sc.n - 1);
+    const uint32_t sk = (uint32_t)(sc.row(tk) * p.d + head * HD) * 2u;
+    const uint32_t sv = (uint32_t)(head * HD * p.ldv + sc.row(tv)) * 2u;
+#pragma unroll
+    for (int j = 0; j < LOADS_PER_WAVE; ++j) {
+      const int idx = wave + WAVES * j;
+      if (idx < K_INST) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kt + 1024 * idx), 16, off[j], sk, 0, 0);
+      } else {
+        const int vi = min(idx - K_INST, V_INST - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vt + 1024 * vi), 16, off[j], sv, 0, 0);
+      }
+    }
+  }
+};
+
 // Online-softmax state of one branch for the 32 queries of a wave.
 struct BranchState {
   f32x16 o[4];     // O^T accumulators: d tile t, lane l, reg r -> d = 32t + 8(r/4) + 4(l/32) + r%4
-  float m;         // running max (log2 units), identical in lanes l and l^32
+  float m;         // running reference max (log2 units), identical in lanes l and l^32
   float lsum;      // partial row sum over this lane's keys
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+    m = -INFINITY;
+    lsum = 0.f;
+  }
 };
 
-// T: element type of Q and K (QK^T MFMA); TP: element type of P and V (PV MFMA).
+// value of x in lane l ^ 32, combined with x: v_permlane32_swap exchanges the two wave halves.
+__device__ __forceinline__ float max_xor32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// acc + lo + hi of two packed fp16 values (one v_dot2c with (1, 1)).  With fp16 probabilities the
+// row sum adds the rounded values the PV product consumed (relative rounding 2^-12 each, well inside
+// the LSE tolerance); bf16 rounding (2^-9) would show in the LSE, so there the fp32 values are added.
+template <typename TP> constexpr bool kSumRounded = false;
+template <> constexpr bool kSumRounded<F16> = true;
+__device__ __forceinline__ float add_pair_f16(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), f16x2{(_Float16)1.f, (_Float16)1.f}, acc, false);
+}
+template <typename TP> __device__ __forceinline__ float add_pair(uint32_t w, float acc) { return add_pair_f16(w, acc); }
+
+// Matrix phase of one wave: S^T = K Q^T for the next tile and O^T += V^T P^T for the current one.
+// kt/vt are the ring slots holding that K and V tile.  The phase is 8 steps of 2 QK and 2 PV MFMAs;
+// the LDS operands of steps i+1 and i+2 are in flight while step i runs, and scheduling barriers keep
+// the compiler from hoisting more reads than that.
+struct MatrixOps {
+  u32x4 a0, a1;   // K rows of the two 32-key halves, 16 head dims
+  u32x4 b[2];     // V^T operands of the two PV MFMAs
+};
+
+// K rows are read in the order key(m) = m with bits 2 and 3 swapped (lane m of the A operand loads
+// key row key(m)).  Then accumulator register r of S^T holds key 32 kt + 16 (r/8) + 8 (l/32) + r%8,
+// so the 8 probabilities a lane packs for PV step (kt, u) are the consecutive keys
+// 32 kt + 16 u + 8 (l/32) + 0..7 -- exactly the reduction index of its B operand -- and the matching
+// V^T operand is one 16-byte read of 8 consecutive keys.
+__device__ __forceinline__ int key_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+__device__ __forceinline__ MatrixOps matrix_ops(const char* kb, const char* vb, int i) {
+  MatrixOps m;
+  m.a0 = *(const u32x4*)(kb + 32 * i);
+  m.a1 = *(const u32x4*)(kb + 32 * K_PITCH + 32 * i);
+  // PV step c = (kt, u, tt): A[d = 32 tt + l%32][k = 8 (l/32) + j] = V^T[d][32 kt + 16 u + 8 (l/32) + j]
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = 2 * i + h;
+    const int kt = c >> 3, u = (c >> 2) & 1, tt = c & 3;
+    m.b[h] = *(const u32x4*)(vb + 32 * tt * VT_PITCH + (32 * kt + 16 * u) * 2);
+  }
+  return m;
+}
+
 template <typename T, typename TP>
-__device__ __forceinline__ void run_branch(const AttnParams& p, const Branch& br, const u32x4 (&qf)[8], int col0,
-                                           char* lds, BranchState& st) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int hi = lane >> 5;
+__device__ __forceinline__ void matrix_phase(const char* kt, const char* vt, int kbase, int vbase,
+                                             const u32x4 (&qf)[8], const u32x4 (&pf)[2][2], f32x16 (&s)[2],
+                                             f32x16 (&o)[4]) {
+  const char* kb = kt + kbase;
+  const char* vb = vt + vbase;
+  MatrixOps cur = matrix_ops(kb, vb, 0);
+  MatrixOps nx1 = matrix_ops(kb, vb, 1);
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int i = 0; i < 8; ++i) {
+    MatrixOps nx2;
+    if (i < 6) nx2 = matrix_ops(kb, vb, i + 2);
+    // accumulator register r of lane l: key 32 kt + 8 (r/4) + 4 (l/32) + r%4 of the rows read (see key_row)
+    s[0] = mfma32x32x16<T>(cur.a0, qf[i], i == 0 ? f32x16{} : s[0]);
+    s[1] = mfma32x32x16<T>(cur.a1, qf[i], i == 0 ? f32x16{} : s[1]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st.o[t][r] = 0.f;
-  st.m = -INFINITY;
-  st.lsum = 0.f;
-  const int n_tiles = (br.len + BN - 1) / BN;
-  if (n_tiles == 0) return;
-
-  const int wave = tid >> 6;
-  DmaTile<K_PITCH> kd;
-  DmaTile<V_PITCH> vd;
-  kd.init(wave, lane, p.d);
-  vd.init(wave, lane, p.d);
-  __syncthreads();  // previous users of the LDS stages are done
-  kd.issue(p.k, p.d, col0, br, 0, lds, wave, lane);
-  vd.issue(p.v, p.d, col0, br, 0, lds + K_TILE, wave, lane);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  // per-lane LDS bases; every read below adds a compile-time offset
-  const int kbase = (lane & 31) * K_PITCH + hi * 16;
-  const int g = lane >> 4, i16 = lane & 15;
-  const int vbase = (4 * (g >> 1) + (i16 >> 2)) * V_PITCH + (16 * (g & 1) + 4 * (i16 & 3)) * 2;
-  for (int t = 0; t < n_tiles; ++t) {
-    char* stage = lds + (t & 1) * STAGE_BYTES;
-    const bool has_next = t + 1 < n_tiles;
-    // the next tile streams into the other stage while this one is computed
-    if (has_next) {
-      char* next = lds + ((t + 1) & 1) * STAGE_BYTES;
-      kd.issue(p.k, p.d, col0, br, (t + 1) * BN, next, wave, lane);
-      vd.issue(p.v, p.d, col0, br, (t + 1) * BN, next + K_TILE, wave, lane);
+    for (int h = 0; h < 2; ++h) {
+      const int c = 2 * i + h;
+      o[c & 3] = mfma32x32x16<TP>(cur.b[h], pf[c >> 3][(c >> 2) & 1], o[c & 3]);
     }
-
-    // ---- S^T = K Q^T for two 32-key sub-tiles.  Accumulator register r of lane l holds
-    // key 32 kt + 8 (r/4) + 4 (l/32) + r%4 of this tile for query l%32.
-    f32x16 s[2];
-    const char* kb = stage + kbase;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      f32x16 acc = {};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const u32x4 a = *(const u32x4*)(kb + 32 * kt * K_PITCH + 32 * ks);
-        acc = mfma32x32x16<T>(a, qf[ks], acc);
-      }
-      s[kt] = acc;
-    }
-    // ---- mask keys past the end of the branch (last tile only)
-    const int valid = br.len - t * BN;
-    if (valid < BN) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key >= valid) s[kt][r] = -INFINITY;
-        }
-    }
-    // ---- online softmax (log2 domain).  The reference max m only moves when this tile's max
-    // exceeds it by more than kRescaleSlack (then O and the row sum are rescaled, for the whole
-    // wave at once); otherwise the probabilities are taken against the stale reference and stay
-    // below 2^kRescaleSlack.  The final normalisation uses the same reference, so this is exact.
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    mx = wave_max_xor32(mx) * p.scale_log2;
-    if (__builtin_amdgcn_ballot_w64(mx > st.m + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(st.m, mx);
-      const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-      st.m = m_new;
-      st.lsum *= alpha;
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st.o[tt][r] *= alpha;
-    }
-    const float m_ref = st.m;
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
-    u32x4 pf[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          e[j] = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * u + j], p.scale_log2, -m_ref));
-          rs[j & 3] += e[j];
-        }
-        pf[kt][u] = u32x4{pack2<TP>(e[0], e[1]), pack2<TP>(e[2], e[3]), pack2<TP>(e[4], e[5]), pack2<TP>(e[6], e[7])};
-      }
-    st.lsum += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-
-    // ---- O^T += V^T P^T.  MFMA step (kt, u) of lane half h uses the probabilities of keys
-    // 32 kt + 16 u + 4 h + 0..3 and 32 kt + 16 u + 8 + 4 h + 0..3 (registers 8u..8u+7); the
-    // matching V^T operand is two transposing reads of 4 keys x 16 columns per 16-lane group.
-    const char* vb = stage + K_TILE + vbase;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const u32x2 h0 = lds_read_tr16((const lds_void*)(vb + (32 * kt + 16 * u) * V_PITCH + 64 * tt));
-          const u32x2 h1 = lds_read_tr16((const lds_void*)(vb + (32 * kt + 16 * u + 8) * V_PITCH + 64 * tt));
-          const u32x4 a = u32x4{h0.x, h0.y, h1.x, h1.y};
-          st.o[tt] = mfma32x32x16<TP>(a, pf[kt][u], st.o[tt]);
-        }
-      }
-
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    if (i < 7) cur = nx1;
+    if (i < 6) nx1 = nx2;
   }
 }
 
+// Softmax phase of one wave for a tile whose scores are in s: mask, running max, probabilities
+// (rounded to TP and packed as the PV B operand), row sum.
+template <typename TP>
+__device__ __forceinline__ void softmax_phase(f32x16 (&s)[2], int valid, float scale_log2, int hi, BranchState& st,
+                                              u32x4 (&pf)[2][2]) {
+  if (valid < BN) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kt + 16 * (r >> 3) + 8 * hi + (r & 7);   // see key_row
+        if (key >= valid) s[kt][r] = -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+  mx = max_xor32(mx) * scale_log2;
+  // The reference max only moves when this tile's max exceeds it by more than kRescaleSlack (then O
+  // and the row sum are rescaled, for the whole wave at once); otherwise the probabilities are taken
+  // against the stale reference and stay below 2^kRescaleSlack.  The final normalisation uses the
+  // same reference, so this is exact.
+  if (__builtin_amdgcn_ballot_w64(mx > st.m + kRescaleSlack) != 0) {
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.m = m_new;
+    st.lsum *= alpha;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[tt][r] *= alpha;
+  }
+  const float m_ref = st.m;
+  float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * u + j], scale_log2, -m_ref));
+      const u32x4 w = u32x4{pack2<TP>(e[0], e[1]), pack2<TP>(e[2], e[3]), pack2<TP>(e[4], e[5]), pack2<TP>(e[6], e[7])};
+      pf[kt][u] = w;
+      if (kSumRounded<TP>) {
+        rs0 = add_pair<TP>(w[0], rs0);
+        rs1 = add_pair<TP>(w[1], rs1);
+        rs0 = add_pair<TP>(w[2], rs0);
+        rs1 = add_pair<TP>(w[3], rs1);
+      } else {
+        rs0 += (e[0] + e[1]) + (e[2] + e[3]);
+        rs1 += (e[4] + e[5]) + (e[6] + e[7]);
+      }
+    }
+  st.lsum += rs0 + rs1;
+}
+
+// The local-branch output O_L of a wave, parked in the workspace while the history branch runs
+// (registers are the scarce resource there): fp16 pairs, or fp32 when the statistics are fp32.  A
+// wave's slot holds NREG dwords per lane, register-major, so every store and load moves 256
+// contiguous bytes per wave.  After fetch() the values are in registers again.
 template <typename ST>
 struct OlStash {
+  static constexpr int NREG = 32;
+  uint32_t* slot;
   uint32_t h[4][8];
-  __device__ __forceinline__ void save(const f32x16 (&o)[4]) {
+  __device__ __forceinline__ void keep(const f32x16 (&o)[4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int j = 0; j < 8; ++j) h[t][j] = pack2<F16>(o[t][2 * j], o[t][2 * j + 1]);
+  }
+  __device__ __forceinline__ void save(const f32x16 (&o)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) slot[(8 * t + j) * 64] = pack2<F16>(o[t][2 * j], o[t][2 * j + 1]);
+  }
+  __device__ __forceinline__ void fetch() {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h[t][j] = slot[(8 * t + j) * 64];
   }
   __device__ __forceinline__ float get(int t, int r) const {
     return f16_bits_to_float((uint16_t)(h[t][r >> 1] >> (16 * (r & 1))));
@@ -266,13 +346,29 @@ struct OlStash {
 };
 template <>
 struct OlStash<F32> {
+  static constexpr int NREG = 64;
+  uint32_t* slot;
   f32x16 o[4];
-  __device__ __forceinline__ void save(const f32x16 (&x)[4]) {
+  __device__ __forceinline__ void keep(const f32x16 (&x)[4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) o[t] = x[t];
   }
+  __device__ __forceinline__ void save(const f32x16 (&x)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) slot[(16 * t + r) * 64] = __float_as_uint(x[t][r]);
+  }
+  __device__ __forceinline__ void fetch() {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[t][r] = __uint_as_float(slot[(16 * t + r) * 64]);
+  }
   __device__ __forceinline__ float get(int t, int r) const { return o[t][r]; }
 };
+static_assert(OlStash<F32>::NREG * 64 * 4 * WAVES == kAttnStashBytesPerBlock && BM == kAttnQueriesPerBlock,
+              "stash slot size");
 
 template <typename ST>
 __device__ __forceinline__ void store_stat(void* base, int64_t idx, float v) {
@@ -295,18 +391,35 @@ __device__ __forceinline__ void store_token_major(void* out, int d, int col0, in
     }
 }
 
+// Closes a branch: O <- O / l; returns the full row sum l (both lane halves).
+__device__ __forceinline__ float close_branch(BranchState& st) {
+  const float L = sum_xor32(st.lsum);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.o[t][r] *= inv;
+  return L;
+}
+
 // MODE 0: dual stream; MODE 1: single stream over all rows; MODE 2: single stream over the local rows.
 // T: type of Q, K and of the token-major output; TP: type of P and V in the PV product; ST: statistics.
 template <typename T, typename TP, typename ST, int MODE>
-__global__ __launch_bounds__(NTHREADS, 2) void attn_mfma_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+__global__ __launch_bounds__(MFMA_THREADS, 2) void attn_mfma_kernel(AttnParams p) {
+  // three-deep K and V rings, one LDS array per slot
+  __shared__ __attribute__((aligned(16))) char k0[K_TILE];
+  __shared__ __attribute__((aligned(16))) char k1[K_TILE];
+  __shared__ __attribute__((aligned(16))) char k2[K_TILE];
+  __shared__ __attribute__((aligned(16))) char v0[V_TILE];
+  __shared__ __attribute__((aligned(16))) char v1[V_TILE];
+  __shared__ __attribute__((aligned(16))) char v2[V_TILE];
   const int n_blocks = p.n_qblk * p.n_heads;
   const int logical = xcd_remap(blockIdx.x, n_blocks);
   const int head = logical / p.n_qblk;
   const int qblk = logical % p.n_qblk;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int grp = wave >> 2;   // waves 0-3 and 4-7 alternate between matrix and softmax phases
   const int hi = lane >> 5;
   const int qrow = qblk * BM + wave * 32 + (lane & 31);
   const bool qok = qrow < p.n_q;
@@ -319,62 +432,161 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_mfma_kernel(AttnParams p) {
     qf[ks] = qok ? *(const u32x4*)(p.q + (int64_t)qrow * p.d + col0 + 16 * ks + 8 * hi) : u32x4{0, 0, 0, 0};
 
   const int n_k = p.n_sink + p.n_hist + p.n_cur;
-  BranchState st;
+  Sched sc;
   if (MODE == 1) {
-    Branch all{0, n_k, 0, n_k};
-    run_branch<T, TP>(p, all, qf, col0, lds, st);
+    sc.set(0, n_k, 0, 0, 0, 0);
+    sc.t_hist = sc.n;
   } else {
-    Branch loc{0, p.n_sink, p.n_sink + p.n_hist, p.n_sink + p.n_cur};
-    run_branch<T, TP>(p, loc, qf, col0, lds, st);
+    sc.set(0, p.n_sink, p.n_sink + p.n_hist, p.n_cur, p.n_sink, MODE == 0 ? p.n_hist : 0);
+    sc.t_hist = sc.e1;
   }
-  float L = st.lsum + __shfl_xor(st.lsum, 32);
-  float inv = 1.f / L;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st.o[t][r] *= inv;
+
+  Loader ld;
+  ld.init(p, n_k, wave, lane);
+  // Ring slots are chosen at compile time (the iteration loop below is unrolled by the ring depth),
+  // so the compiler's memory-dependency analysis sees which slot each in-flight load writes.
+  auto kslot = [&](auto J) -> char* {
+    if constexpr (decltype(J)::value == 0) return k0;
+    else if constexpr (decltype(J)::value == 1) return k1;
+    else return k2;
+  };
+  auto vslot = [&](auto J) -> char* {
+    if constexpr (decltype(J)::value == 0) return v0;
+    else if constexpr (decltype(J)::value == 1) return v1;
+    else return v2;
+  };
+  // load group k: K tile k into K slot k % 3, V^T tile k-1 into V slot (k-1) % 3
+  ld.issue(sc, 0, p, head, k0, v2, wave);
+  ld.issue(sc, 1, p, head, k1, v0, wave);
+  ld.issue(sc, 2, p, head, k2, v1, wave);
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+  __builtin_amdgcn_s_barrier();
+
+  const int kbase = key_row(lane & 31) * K_PITCH + hi * 16;
+  const int vbase = (lane & 31) * VT_PITCH + hi * 16;
+
+  BranchState st;
+  f32x16 s[2];
+  u32x4 pf[2][2];
+  OlStash<ST> ol;
+  ol.slot = (uint32_t*)p.stash + (size_t)(blockIdx.x * WAVES + wave) * OlStash<ST>::NREG * 64 + lane;
+  float m_loc = -INFINITY, l_loc = 0.f;
+
+  // Matrix phase M(t) = QK(t+1) + PV(t) reads K slot (t+1) % 3 and V slot t % 3.  M(-1) only needs
+  // QK(0): its PV runs on whatever the registers and V slot 2 hold and O is cleared afterwards;
+  // M(n-1) only needs PV(n-1): its QK result is never used.
+  auto matrix = [&](auto J, int t) {   // J = (t + 1) % 3
+    constexpr int j = decltype(J)::value;
+    matrix_phase<T, TP>(kslot(J), vslot(std::integral_constant<int, (j + 2) % 3>{}), kbase, vbase, qf, pf, s, st.o);
+    if (t < 0) st.reset();
+  };
+  auto softmax = [&](int t) {
+    if (t < 0 || t >= sc.n) return;
+    if (MODE == 0 && t == sc.t_hist) {
+      // first history tile: the local branch is complete
+      m_loc = st.m;
+      l_loc = close_branch(st);
+      ol.save(st.o);
+      st.reset();
+    }
+    softmax_phase<TP>(s, sc.valid(t), p.scale_log2, hi, st, pf);
+  };
+  auto phase_end = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Iteration i covers two phases.  Waves 0-3 run M(i-1) and then the softmax of tile i; waves 4-7,
+  // one phase behind, run the softmax of tile i-1 and then M(i-1).  Load group k (K tile k, V^T tile
+  // k-1) is issued at the start of iteration k-2 (groups 0-2 before the loop; iteration 0 loads
+  // group 2 again) and waited for at the end of iteration k-1, when only group k+1 may stay in
+  // flight; the ring slots it overwrites were last read in the second phase of iteration k-3.
+  // J = i % 3.
+  auto issue_ahead = [&](auto J, int i) {
+    constexpr int j = decltype(J)::value;
+    ld.issue(sc, i + 2, p, head, kslot(std::integral_constant<int, (j + 2) % 3>{}),
+             vslot(std::integral_constant<int, (j + 1) % 3>{}), wave);
+  };
+  auto wait_loads = [&](int) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(LOADS_PER_WAVE)); };
+  // the two wave groups run separate copies of the loop (one branch per group, outside the loop)
+  auto iteration0 = [&](auto J, int i) {
+    issue_ahead(J, i);
+    matrix(J, i - 1);
+    phase_end();
+    softmax(i);
+    wait_loads(i);
+    phase_end();
+  };
+  auto iteration1 = [&](auto J, int i) {
+    issue_ahead(J, i);
+    softmax(i - 1);
+    phase_end();
+    matrix(J, i - 1);
+    wait_loads(i);
+    phase_end();
+  };
+  const std::integral_constant<int, 0> J0;
+  const std::integral_constant<int, 1> J1;
+  const std::integral_constant<int, 2> J2;
+  if (grp == 0) {
+    for (int i = 0; i <= sc.n; i += 3) {
+      iteration0(J0, i);
+      if (i + 1 > sc.n) break;
+      iteration0(J1, i + 1);
+      if (i + 2 > sc.n) break;
+      iteration0(J2, i + 2);
+    }
+  } else {
+    for (int i = 0; i <= sc.n; i += 3) {
+      iteration1(J0, i);
+      if (i + 1 > sc.n) break;
+      iteration1(J1, i + 1);
+      if (i + 2 > sc.n) break;
+      iteration1(J2, i + 2);
+    }
+  }
 
   if (MODE != 0) {
+    close_branch(st);
     store_token_major<T>(p.a_full, p.d, col0, qrow, qok, st.o);
     return;
   }
 
-  // ---- dual stream: local branch done
-  const float m_loc = st.m, l_loc = L;
+  // ---- dual stream: merge the local and history states through their log-sum-exp
+  float m_h = -INFINITY, l_h = 0.f;
+  if (sc.n > sc.t_hist) {
+    m_h = st.m;
+    l_h = close_branch(st);
+  } else {
+    m_loc = st.m;
+    l_loc = close_branch(st);
+    ol.keep(st.o);
+  }
+  if (sc.n > sc.t_hist) {
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));   // this wave's stash stores have completed
+    ol.fetch();
+  }
   if (p.lse_loc && qok && hi == 0) p.lse_loc[(int64_t)head * p.n_q + qrow] = (m_loc + __log2f(l_loc)) * kLn2;
+  if (p.lse_hist && qok && hi == 0)
+    p.lse_hist[(int64_t)head * p.n_q + qrow] = l_h > 0.f ? (m_h + __log2f(l_h)) * kLn2 : -INFINITY;
   if (p.a_loc_t && qok) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int c = col0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
-        store_stat<ST>(p.a_loc_t, (int64_t)c * p.ld_stat + qrow, st.o[t][r]);
+        store_stat<ST>(p.a_loc_t, (int64_t)c * p.ld_stat + qrow, ol.get(t, r));
       }
   }
-  // Keep A_loc for the merge while the history branch runs: fp32 when the statistics are fp32,
-  // otherwise packed fp16 (the statistics are rounded to 16 bits anyway).
-  OlStash<ST> ol;
-  ol.save(st.o);
-
-  Branch hist{p.n_sink, p.n_hist, 0, p.n_hist};
-  run_branch<T, TP>(p, hist, qf, col0, lds, st);
-  const float l_h = st.lsum + __shfl_xor(st.lsum, 32);
-  const float m_h = st.m;
-  // merge through the log-sum-exp states
   const float mm = fmaxf(m_loc, m_h);
   const float a = l_loc * __builtin_amdgcn_exp2f(m_loc - mm);
   const float b = l_h > 0.f ? l_h * __builtin_amdgcn_exp2f(m_h - mm) : 0.f;
   const float w = b / (a + b);
-  const float inv_h = l_h > 0.f ? 1.f / l_h : 0.f;
-  if (p.lse_hist && qok && hi == 0)
-    p.lse_hist[(int64_t)head * p.n_q + qrow] = l_h > 0.f ? (m_h + __log2f(l_h)) * kLn2 : -INFINITY;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float da = w * (st.o[t][r] * inv_h - ol.get(t, r));
-      st.o[t][r] = da;  // reuse as dA
-    }
+    for (int r = 0; r < 16; ++r) st.o[t][r] = l_h > 0.f ? w * (st.o[t][r] - ol.get(t, r)) : 0.f;  // dA
   if (p.delta_a_t && qok) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -397,6 +609,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_mfma_kernel(AttnParams p) {
 // fp32 path (any head_dim in {64, 128}): plain VALU online softmax, keys staged through LDS.
 // HD/32 threads share one query; each owns 32 dimensions of q and of the outputs.
 // ---------------------------------------------------------------------------------------------
+// A branch of the fp32 path: virtual rows [0, len) mapped onto up to two physical row segments.
+struct Branch {
+  int start0, len0, start1, len;
+  __device__ __forceinline__ int row(int v) const { return v < len0 ? start0 + v : start1 + (v - len0); }
+};
+
 template <int HDF>
 struct F32Cfg {
   static constexpr int TPQ = HDF / 32;          // threads per query
@@ -523,6 +741,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_f32_kernel(AttnParams p) {
   }
 }
 
+
 AttnParams make_params(const AttnLaunch& L) {
   AttnParams p;
   p.q = (const uint16_t*)L.q;
@@ -544,23 +763,44 @@ AttnParams make_params(const AttnLaunch& L) {
   return p;
 }
 
-// bf16 -> fp16 copy of V (exact for |v| < 65504), so the PV product of the statistics path can run
-// with fp16 probabilities.
-__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
-                                                          int64_t n8) {
-  for (int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
-    const u32x4 x = ((const u32x4*)in)[i];
+// V^T copy for the 16-bit path: vt[c, key] = v[key, c] for c < d, key < n_k; keys [n_k, ldv) are
+// zero, so every V^T tile the attention kernel streams is finite.  With CONVERT the values go from
+// bf16 to fp16 (exact for |v| < 65504), for the fp16 PV product of the statistics path.  One
+// work-group transposes a 64-key x 64-column block through LDS; global reads and writes are
+// 16 bytes per lane along rows.
+template <bool CONVERT>
+__global__ __launch_bounds__(256) void vt_kernel(const uint16_t* __restrict__ v, uint16_t* __restrict__ vt, int n_k,
+                                                 int d, int ldv) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];   // [key][column]
+  const int key0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int r = threadIdx.x >> 3, ch = threadIdx.x & 7;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int key = key0 + r + 32 * pass;
+    u32x4 x = u32x4{0, 0, 0, 0};
+    if (key < n_k) x = *(const u32x4*)(v + (int64_t)key * d + c0 + 8 * ch);
+    if (CONVERT) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        x[j] = pack2<F16>(bf16_bits_to_float((uint16_t)(x[j] & 0xFFFFu)), bf16_bits_to_float((uint16_t)(x[j] >> 16)));
+    }
+    *(u32x4*)&tile[r + 32 * pass][8 * ch] = x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int c = r + 32 * pass;
     u32x4 y;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      y[j] = pack2<F16>(bf16_bits_to_float((uint16_t)(x[j] & 0xFFFFu)), bf16_bits_to_float((uint16_t)(x[j] >> 16)));
-    ((u32x4*)out)[i] = y;
+      y[j] = (uint32_t)tile[8 * ch + 2 * j][c] | ((uint32_t)tile[8 * ch + 2 * j + 1][c] << 16);
+    *(u32x4*)(vt + (int64_t)(c0 + c) * ldv + key0 + 8 * ch) = y;
   }
 }
 
 template <typename T, typename TP, int MODE>
 hipError_t launch_mfma_stat(AttnParams p, int stat, hipStream_t s) {
-  dim3 grid(p.n_qblk * p.n_heads), block(NTHREADS);
+  dim3 grid(p.n_qblk * p.n_heads), block(MFMA_THREADS);
   if (MODE != 0 || stat == DT_F16)
     hipLaunchKernelGGL((attn_mfma_kernel<T, TP, F16, MODE>), grid, block, 0, s, p);
   else if (stat == DT_BF16)
@@ -573,18 +813,21 @@ hipError_t launch_mfma_stat(AttnParams p, int stat, hipStream_t s) {
 template <typename T, int MODE>
 hipError_t launch_mfma_mode(AttnParams p, const AttnLaunch& L, hipStream_t s) {
   p.n_qblk = (p.n_q + BM - 1) / BM;
-  if (attn_needs_f16_values(L)) {
-    // statistics requested in fp16 from bf16 inputs: P and V in fp16 for the PV product
-    const int64_t n = (int64_t)(L.n_sink + L.n_hist + L.n_cur) * L.n_heads * L.head_dim;
-    const int64_t n8 = n / 8;
-    const int blocks = (int)((n8 + 255) / 256 < 2048 ? (n8 + 255) / 256 : 2048);
-    hipLaunchKernelGGL(bf16_to_f16_kernel, dim3(blocks), dim3(256), 0, s, (const uint16_t*)L.v, (uint16_t*)L.ws, n8);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    p.v = (const uint16_t*)L.ws;
-    return launch_mfma_stat<T, F16, MODE>(p, L.stat, s);
-  }
-  return launch_mfma_stat<T, T, MODE>(p, L.stat, s);
+  const int n_k = L.n_sink + L.n_hist + L.n_cur;
+  p.ldv = (int)attn_vt_ld(n_k);
+  p.vt = (const uint16_t*)L.ws;
+  p.stash = (char*)L.ws + attn_vt_bytes_aligned(n_k, p.d);
+  const dim3 tgrid(p.ldv / 64, p.d / 64);
+  // statistics requested in fp16 from bf16 inputs: P and V in fp16 for the PV product
+  const bool f16_values = attn_needs_f16_values(L);
+  if (f16_values)
+    hipLaunchKernelGGL(vt_kernel<true>, tgrid, dim3(256), 0, s, (const uint16_t*)L.v, (uint16_t*)L.ws, n_k, p.d, p.ldv);
+  else
+    hipLaunchKernelGGL(vt_kernel<false>, tgrid, dim3(256), 0, s, (const uint16_t*)L.v, (uint16_t*)L.ws, n_k, p.d,
+                       p.ldv);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return f16_values ? launch_mfma_stat<T, F16, MODE>(p, L.stat, s) : launch_mfma_stat<T, T, MODE>(p, L.stat, s);
 }
 
 template <int HDF, int MODE>

@@ -23,14 +23,26 @@ struct AttnLaunch {
   float* lse_hist;
   int n_q, n_sink, n_hist, n_cur, n_heads, head_dim;
   float scale;
-  void* ws;          // device workspace (fp16 copy of V when attn_needs_f16_values)
+  void* ws;          // device workspace (16-bit inputs: the transposed copy of V, see attn_vt_bytes)
   size_t ws_bytes;
 };
-// Dual stream from bf16 inputs with fp16 statistics: the PV product runs on an fp16 copy of V.
+// The 16-bit (MFMA) path streams V from a transposed copy V^T [d, ldv] (ldv = n_k rounded up to
+// 64 keys, pad keys zero) that the call writes into the workspace first.
+inline int64_t attn_vt_ld(int64_t n_k) { return (n_k + 63) / 64 * 64; }
+inline size_t attn_vt_bytes(int64_t n_k, int64_t d) { return (size_t)(d * attn_vt_ld(n_k) * 2); }
+// The dual stream parks each work-group's local outputs (256 queries x 128 dims, up to fp32) in the
+// workspace after the V^T copy while the history branch runs.
+constexpr int64_t kAttnQueriesPerBlock = 256;
+constexpr size_t kAttnStashBytesPerBlock = 256 * 128 * 4;
+inline size_t attn_vt_bytes_aligned(int64_t n_k, int64_t d) { return (attn_vt_bytes(n_k, d) + 255) / 256 * 256; }
+inline size_t attn_stash_bytes(int64_t n_q, int64_t n_heads) {
+  return (size_t)((n_q + kAttnQueriesPerBlock - 1) / kAttnQueriesPerBlock * n_heads) * kAttnStashBytesPerBlock;
+}
+// Dual stream from bf16 inputs with fp16 statistics: the PV product runs on fp16 probabilities and
+// the V^T copy is converted to fp16.
 inline bool attn_needs_f16_values(const AttnLaunch& L) {
   return L.mode == 0 && L.io == DT_BF16 && L.stat == DT_F16 && (L.a_loc_t || L.delta_a_t);
 }
-inline size_t attn_f16_values_bytes(int64_t n_k, int64_t d) { return (size_t)(n_k * d * 2); }
 hipError_t launch_attention(const AttnLaunch& L, hipStream_t s);
 
 // Gram statistics: out_z (+)= X_z Y_z^T for z in {G: (A, A), C: (A, dA), D: (dA, dA)}.

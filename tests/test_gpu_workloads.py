@@ -200,7 +200,8 @@ def test_rollout_layers(chunk):
     qd, kd, vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
     # F-layer: full-only mode
     a_full = t.empty((sh.n_q, sh.d), dtype=t.bfloat16, device="cuda")
-    ispa.dual_attn(ispa.AttnShape.of(sh), qd, kd, vd, a_full=a_full)
+    ws = t.empty(ispa.workspace_bytes(ispa.CALL_DUAL_ATTN, ispa.AttnShape.of(sh)), dtype=t.uint8, device="cuda")
+    ispa.dual_attn(ispa.AttnShape.of(sh), qd, kd, vd, a_full=a_full, workspace=ws)
     t.cuda.synchronize()
     ref, _ = oracle.softmax_attention(q[rows], k, v, np.arange(n_rows), sh.n_heads, threads=8)
     assert maxrel(host(a_full)[rows], ref) <= 2e-2
