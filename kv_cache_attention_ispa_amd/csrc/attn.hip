@@ -30,8 +30,12 @@
 //    B operand over 8 consecutive keys -- and V^T is one plain 16-byte LDS read per MFMA (the
 //    transposing LDS read delivers a third of the bandwidth of plain reads on gfx950);
 //  * exp2 with the softmax scale folded into log2(e); the reference max only moves when a
-//    tile's max exceeds it by more than 2^8; the row sum adds the rounded 16-bit
-//    probabilities with packed dot products, so it matches what the PV product consumed;
+//    tile's max exceeds it by more than 2^8; with fp16 probabilities the row sum adds the
+//    rounded values with packed dot products (fewer instructions than fp32 adds, although
+//    v_dot2 shares the matrix pipeline);
+//  * each group issues the direct-to-LDS loads of the tile two ahead at the start of its
+//    softmax phase: the memory pipeline accepts a burst only at its own pace, which stalls the
+//    issuing wave, and the softmax phase is the shorter one;
 //  * when the statistics are requested in fp16 from bf16 inputs, V is copied to fp16 first and
 //    the probabilities are rounded to fp16 (11-bit mantissa) for the PV product, which keeps dA
 //    accurate enough for ill-conditioned absorption problems; QK^T stays in bf16;
@@ -143,22 +147,30 @@ struct Loader {
   // Every wave issues exactly LOADS_PER_WAVE loads per group, also past the ends of the tile
   // sequence (then a valid tile is loaded again into a ring slot nobody reads), so the number of
   // loads in flight is the same on every path and one wait count fits all iterations.
-  __device__ __forceinline__ void issue(const Sched& sc, int k, const AttnParams& p, int head, char* kt, char* vt,
-                                        int wave) const {
+  struct Group {
+    uint32_t sk, sv;   // byte offsets of the K tile and the V^T tile
+    char* kt;
+    char* vt;
+  };
+  __device__ __forceinline__ Group group(const Sched& sc, int k, const AttnParams& p, int head, char* kt,
+                                         char* vt) const {
     const int tk = min(k, sc.n - 1);
     const int tv = min(max(k - 1, 0), sc.n - 1);
-    const uint32_t sk = (uint32_t)(sc.row(tk) * p.d + head * HD) * 2u;
-    const uint32_t sv = (uint32_t)(head * HD * p.ldv + sc.row(tv)) * 2u;
-#pragma unroll
-    for (int j = 0; j < LOADS_PER_WAVE; ++j) {
-      const int idx = wave + WAVES * j;
-      if (idx < K_INST) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kt + 1024 * idx), 16, off[j], sk, 0, 0);
-      } else {
-        const int vi = min(idx - K_INST, V_INST - 1);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vt + 1024 * vi), 16, off[j], sv, 0, 0);
-      }
+    return Group{(uint32_t)(sc.row(tk) * p.d + head * HD) * 2u, (uint32_t)(head * HD * p.ldv + sc.row(tv)) * 2u,
+                 kt, vt};
+  }
+  __device__ __forceinline__ void issue_one(const Group& g, int j, int wave) const {
+    const int idx = wave + WAVES * j;
+    if (idx < K_INST) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(g.kt + 1024 * idx), 16, off[j], g.sk, 0, 0);
+    } else {
+      const int vi = min(idx - K_INST, V_INST - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(g.vt + 1024 * vi), 16, off[j], g.sv, 0, 0);
     }
+  }
+  __device__ __forceinline__ void issue(const Group& g, int wave) const {
+#pragma unroll
+    for (int j = 0; j < LOADS_PER_WAVE; ++j) issue_one(g, j, wave);
   }
 };
 
@@ -189,20 +201,15 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// acc + lo + hi of two packed fp16 values (one v_dot2c with (1, 1)).  With fp16 probabilities the
-// row sum adds the rounded values the PV product consumed (relative rounding 2^-12 each, well inside
-// the LSE tolerance); bf16 rounding (2^-9) would show in the LSE, so there the fp32 values are added.
-template <typename TP> constexpr bool kSumRounded = false;
-template <> constexpr bool kSumRounded<F16> = true;
-__device__ __forceinline__ float add_pair_f16(uint32_t w, float acc) {
+// acc + lo + hi of two packed fp16 values (one v_dot2c_f32_f16).
+__device__ __forceinline__ float add_f16_pair(uint32_t w, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), f16x2{(_Float16)1.f, (_Float16)1.f}, acc, false);
 }
-template <typename TP> __device__ __forceinline__ float add_pair(uint32_t w, float acc) { return add_pair_f16(w, acc); }
 
 // Matrix phase of one wave: S^T = K Q^T for the next tile and O^T += V^T P^T for the current one.
 // kt/vt are the ring slots holding that K and V tile.  The phase is 8 steps of 2 QK and 2 PV MFMAs;
-// the LDS operands of steps i+1 and i+2 are in flight while step i runs, and scheduling barriers keep
-// the compiler from hoisting more reads than that.
+// the LDS operands of step i+1 are read while step i runs, and scheduling barriers keep the compiler
+// from hoisting more reads than that (registers are at their limit).
 struct MatrixOps {
   u32x4 a0, a1;   // K rows of the two 32-key halves, 16 head dims
   u32x4 b[2];     // V^T operands of the two PV MFMAs
@@ -236,11 +243,10 @@ __device__ __forceinline__ void matrix_phase(const char* kt, const char* vt, int
   const char* kb = kt + kbase;
   const char* vb = vt + vbase;
   MatrixOps cur = matrix_ops(kb, vb, 0);
-  MatrixOps nx1 = matrix_ops(kb, vb, 1);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    MatrixOps nx2;
-    if (i < 6) nx2 = matrix_ops(kb, vb, i + 2);
+    MatrixOps nxt;
+    if (i < 7) nxt = matrix_ops(kb, vb, i + 1);
     // accumulator register r of lane l: key 32 kt + 8 (r/4) + 4 (l/32) + r%4 of the rows read (see key_row)
     s[0] = mfma32x32x16<T>(cur.a0, qf[i], i == 0 ? f32x16{} : s[0]);
     s[1] = mfma32x32x16<T>(cur.a1, qf[i], i == 0 ? f32x16{} : s[1]);
@@ -250,8 +256,7 @@ __device__ __forceinline__ void matrix_phase(const char* kt, const char* vt, int
       o[c & 3] = mfma32x32x16<TP>(cur.b[h], pf[c >> 3][(c >> 2) & 1], o[c & 3]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (i < 7) cur = nx1;
-    if (i < 6) nx1 = nx2;
+    if (i < 7) cur = nxt;
   }
 }
 
@@ -300,12 +305,15 @@ __device__ __forceinline__ void softmax_phase(f32x16 (&s)[2], int valid, float s
       for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * u + j], scale_log2, -m_ref));
       const u32x4 w = u32x4{pack2<TP>(e[0], e[1]), pack2<TP>(e[2], e[3]), pack2<TP>(e[4], e[5]), pack2<TP>(e[6], e[7])};
       pf[kt][u] = w;
-      if (kSumRounded<TP>) {
-        rs0 = add_pair<TP>(w[0], rs0);
-        rs1 = add_pair<TP>(w[1], rs1);
-        rs0 = add_pair<TP>(w[2], rs0);
-        rs1 = add_pair<TP>(w[3], rs1);
+      if (std::is_same<TP, F16>::value) {
+        // fp16 probabilities: add the rounded values the PV product consumes (relative rounding
+        // 2^-12 each, well inside the LSE tolerance), four packed dot products with (1, 1)
+        rs0 = add_f16_pair(w[0], rs0);
+        rs1 = add_f16_pair(w[1], rs1);
+        rs0 = add_f16_pair(w[2], rs0);
+        rs1 = add_f16_pair(w[3], rs1);
       } else {
+        // bf16 rounding (2^-9) would show in the LSE: add the fp32 values
         rs0 += (e[0] + e[1]) + (e[2] + e[3]);
         rs1 += (e[4] + e[5]) + (e[6] + e[7]);
       }
@@ -456,9 +464,9 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void attn_mfma_kernel(AttnParams p
     else return v2;
   };
   // load group k: K tile k into K slot k % 3, V^T tile k-1 into V slot (k-1) % 3
-  ld.issue(sc, 0, p, head, k0, v2, wave);
-  ld.issue(sc, 1, p, head, k1, v0, wave);
-  ld.issue(sc, 2, p, head, k2, v1, wave);
+  ld.issue(ld.group(sc, 0, p, head, k0, v2), wave);
+  ld.issue(ld.group(sc, 1, p, head, k1, v0), wave);
+  ld.issue(ld.group(sc, 2, p, head, k2, v1), wave);
   __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
   __builtin_amdgcn_s_barrier();
 
@@ -480,6 +488,12 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void attn_mfma_kernel(AttnParams p
     matrix_phase<T, TP>(kslot(J), vslot(std::integral_constant<int, (j + 2) % 3>{}), kbase, vbase, qf, pf, s, st.o);
     if (t < 0) st.reset();
   };
+  // load group i+2 (J = i % 3)
+  auto issue_ahead = [&](auto J, int i) {
+    constexpr int j = decltype(J)::value;
+    ld.issue(ld.group(sc, i + 2, p, head, kslot(std::integral_constant<int, (j + 2) % 3>{}),
+                      vslot(std::integral_constant<int, (j + 1) % 3>{})), wave);
+  };
   auto softmax = [&](int t) {
     if (t < 0 || t >= sc.n) return;
     if (MODE == 0 && t == sc.t_hist) {
@@ -499,21 +513,16 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void attn_mfma_kernel(AttnParams p
   };
   // Iteration i covers two phases.  Waves 0-3 run M(i-1) and then the softmax of tile i; waves 4-7,
   // one phase behind, run the softmax of tile i-1 and then M(i-1).  Load group k (K tile k, V^T tile
-  // k-1) is issued at the start of iteration k-2 (groups 0-2 before the loop; iteration 0 loads
-  // group 2 again) and waited for at the end of iteration k-1, when only group k+1 may stay in
+  // k-1) is issued during the softmax phases of iteration k-2 (groups 0-2 before the loop; iteration 0
+  // loads group 2 again) and waited for at the end of iteration k-1, when only group k+1 may stay in
   // flight; the ring slots it overwrites were last read in the second phase of iteration k-3.
   // J = i % 3.
-  auto issue_ahead = [&](auto J, int i) {
-    constexpr int j = decltype(J)::value;
-    ld.issue(sc, i + 2, p, head, kslot(std::integral_constant<int, (j + 2) % 3>{}),
-             vslot(std::integral_constant<int, (j + 1) % 3>{}), wave);
-  };
   auto wait_loads = [&](int) { __builtin_amdgcn_s_waitcnt(wait_vmcnt(LOADS_PER_WAVE)); };
   // the two wave groups run separate copies of the loop (one branch per group, outside the loop)
   auto iteration0 = [&](auto J, int i) {
-    issue_ahead(J, i);
     matrix(J, i - 1);
     phase_end();
+    issue_ahead(J, i);
     softmax(i);
     wait_loads(i);
     phase_end();
