@@ -6,9 +6,8 @@
 // computed once, without iteration.  With G = A_loc^T A_loc and C = A_loc^T dA:
 //
 //   R = C W;   G + lambda I = L L^T (blocked right-looking Cholesky, fp32);
-//   the forward solve runs inside the same sweep on the augmented right-hand
-//   side [R | I], which leaves Y = L^-1 R and L^-1 when the sweep ends, so the
-//   backward solve is one triangular GEMM: dW = (L^-1)^T Y.
+//   the sweep also carries the identity, which leaves L^-1 when it ends; then
+//   Z = L^-1 R and dW = (L^-1)^T Z are two triangular GEMMs.
 //   Optional iterative refinement (a given number of steps): r = C W - (G + lambda I) dW
 //   accumulated in fp64 (C W formed once in fp64), then dW += (L^-1)^T (L^-1 r).
 //
@@ -207,7 +206,7 @@ __global__ __launch_bounds__(NT) void lambda_kernel(const float* G, int d, float
   }
 }
 
-// Mx = G + lambda I; Rc, Bx[:, :d] hold R (filled later), Bx[:, d:] = I; Wf = W as fp32.
+// Mx = G + lambda I; Bx = I (becomes L^-1); Wf = W as fp32.
 template <typename WT>
 __global__ __launch_bounds__(NT) void setup_kernel(const float* G, const typename WT::storage* W, int d,
                                                    const Scalars* sc, float* Mx, float* Bx, float* Wf) {
@@ -216,30 +215,36 @@ __global__ __launch_bounds__(NT) void setup_kernel(const float* G, const typenam
   for (int64_t e = blockIdx.x * (int64_t)NT + threadIdx.x; e < n; e += (int64_t)gridDim.x * NT) {
     const int i = (int)(e / d), j = (int)(e % d);
     Mx[e] = G[e] + (i == j ? lam : 0.f);
-    Bx[(int64_t)i * 2 * d + d + j] = (i == j) ? 1.f : 0.f;
+    Bx[e] = (i == j) ? 1.f : 0.f;
     Wf[e] = Cvt<WT>::to_f(W[e]);
   }
 }
 
-// Factor the diagonal block Mx[k0:k0+nb, k0:k0+nb] = L L^T in place (lower) and write T = L^-1.
-// 256 threads: thread t owns row i = t/4, columns 16 (t%4) .. +15 of the block A (kept symmetric,
-// so row j also holds column j) and of the augmented block U that starts as I.  Step j broadcasts
-// row j through LDS (one barrier) and records it; then every row i > j applies
-//   a_ik -= (a_ij / p_j) a_jk,      u_i -= (a_ij / p_j) u_j,      p_j = a_jj,
-// i.e. right-looking Cholesky and forward substitution with the divisions by l_jj = sqrt(p_j)
-// deferred.  Entries a_ik with k <= j are finished after step j and may take garbage afterwards:
-// the factor is read back from the recorded rows, L_ij = rec_j[i] / sqrt(p_j) for i > j.
-// U's row j is final at step j and rows i <= j are never updated again; (L^-1)_i = u_i / sqrt(p_i).
+// Factor the diagonal block Mx[k0:k0+nb, k0:k0+nb] = L L^T in place (lower) and write T = L^-1,
+// two columns per barrier.  1024 threads (the step is latency bound; more waves per SIMD hide it):
+// thread t owns row i = t/16, columns 4 (t%16) .. +3 of the block A (kept symmetric: row j also
+// holds column j) and of the augmented block U that starts as I.  Step s handles columns j = 2s and
+// j+1.  Rows j and j+1 (all earlier steps applied) are published in LDS (double-buffered, so one
+// barrier per step); then every thread forms, on its columns,
+//   row'_{j+1} = row_{j+1} - (a01 / p0) row_j          (p0 = a_jj, a01 = a_{j,j+1}),
+// i.e. row j+1 after elimination with row j (pivot p1 = a_{j+1,j+1} - a01^2 / p0), and every row
+// i > j+1 applies both eliminations,
+//   a_i -= f0 row_j + f1 row'_{j+1},  f0 = x0 / p0,  f1 = (x1 - f0 a01) / p1,
+// where x0, x1 are row i's entries in columns j, j+1 (by symmetry, rows j and j+1's entries in
+// column i).  The same combination updates u_i: right-looking Cholesky and forward substitution in
+// one sweep, with the divisions by l_jj = sqrt(p_j) deferred.  The final rows (row j as published,
+// row'_{j+1}) are recorded: L_ij = rec_j[i] / sqrt(p_j) for i > j, (L^-1)_i = u_i / sqrt(p_i).
 // Rows past nb (last panel) are padded with the identity.
-__global__ __launch_bounds__(256) void diag_kernel(float* Mx, int d, int k0, int nb, float* T, int* info) {
-  __shared__ __attribute__((aligned(16))) float rec[NB][NB + 4];   // row j as broadcast at step j
-  __shared__ __attribute__((aligned(16))) float rowu[2][NB];
+constexpr int DIAG_THREADS = 1024;
+__global__ __launch_bounds__(DIAG_THREADS) void diag_kernel(float* Mx, int d, int k0, int nb, float* T, int* info) {
+  __shared__ __attribute__((aligned(16))) float curb[2][2][2][NB];   // [step parity][A or U][row j or j+1][col]
+  __shared__ __attribute__((aligned(16))) float rec[NB][NB + 4];     // final A rows
   __shared__ float pivs[NB];
   const int t = threadIdx.x;
-  const int i = t >> 2, c0 = (t & 3) * 16;
-  float ar[16], ur[16];
+  const int i = t >> 4, c0 = (t & 15) * 4;
+  float ar[4], ur[4];
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
+  for (int m = 0; m < 4; ++m) {
     const int k = c0 + m;
     float v;
     if (i < nb && k < nb)
@@ -249,46 +254,66 @@ __global__ __launch_bounds__(256) void diag_kernel(float* Mx, int d, int k0, int
     ar[m] = v;
     ur[m] = (i == k) ? 1.f : 0.f;
   }
-  for (int j = 0; j < NB; ++j) {
-    const int b = j & 1;
-    if (i == j) {
-#pragma unroll
-      for (int m = 0; m < 16; m += 4) {
-        *(f32x4*)&rec[j][c0 + m] = f32x4{ar[m], ar[m + 1], ar[m + 2], ar[m + 3]};
-        *(f32x4*)&rowu[b][c0 + m] = f32x4{ur[m], ur[m + 1], ur[m + 2], ur[m + 3]};
-      }
+  auto piv = [](float p) { return p > 0.f ? p : 1.f; };
+  for (int j = 0; j < NB; j += 2) {
+    float(*cur)[2][NB] = curb[(j >> 1) & 1];
+    const int q = i - j;   // 0: row j, 1: row j+1
+    if (q == 0 || q == 1) {
+      *(f32x4*)&cur[0][q][c0] = f32x4{ar[0], ar[1], ar[2], ar[3]};
+      *(f32x4*)&cur[1][q][c0] = f32x4{ur[0], ur[1], ur[2], ur[3]};
+      if (q == 0) *(f32x4*)&rec[j][c0] = f32x4{ar[0], ar[1], ar[2], ar[3]};
     }
     __syncthreads();
-    float piv = rec[j][j];
-    if (!(piv > 0.f)) {
-      if (t == 0 && j < nb && *info == 0) *info = k0 + j + 1;
-      piv = 1.f;
-    }
     if (i > j) {
-      const float f = rec[j][i] * __builtin_amdgcn_rcpf(piv);
-#pragma unroll
-      for (int m = 0; m < 16; m += 4) {
-        const f32x4 ra = *(const f32x4*)&rec[j][c0 + m];
-        const f32x4 ru = *(const f32x4*)&rowu[b][c0 + m];
+      const float p0 = piv(cur[0][0][j]);
+      const float a01 = cur[0][0][j + 1];
+      const float r0 = __builtin_amdgcn_rcpf(p0);
+      const float g = a01 * r0;   // row'_{j+1} = row_{j+1} - g row_j
+      const float p1raw = cur[0][1][j + 1] - g * a01;
+      const f32x4 a0 = *(const f32x4*)&cur[0][0][c0];
+      const f32x4 u0 = *(const f32x4*)&cur[1][0][c0];
+      if (q == 1) {
+        // row j+1 itself: its final value is row'_{j+1}
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          ar[m + e] = fmaf(-f, ra[e], ar[m + e]);
-          ur[m + e] = fmaf(-f, ru[e], ur[m + e]);
+          ar[e] = fmaf(-g, a0[e], ar[e]);
+          ur[e] = fmaf(-g, u0[e], ur[e]);
+        }
+        *(f32x4*)&rec[j + 1][c0] = f32x4{ar[0], ar[1], ar[2], ar[3]};
+        if ((t & 15) == 0) {
+          pivs[j] = cur[0][0][j];
+          pivs[j + 1] = p1raw;
+        }
+      } else {
+        const float f0 = cur[0][0][i] * r0;
+        const float f1 = (cur[0][1][i] - f0 * a01) * __builtin_amdgcn_rcpf(piv(p1raw));
+        const f32x4 a1 = *(const f32x4*)&cur[0][1][c0];
+        const f32x4 u1 = *(const f32x4*)&cur[1][1][c0];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ar[e] = fmaf(-f1, fmaf(-g, a0[e], a1[e]), fmaf(-f0, a0[e], ar[e]));
+          ur[e] = fmaf(-f1, fmaf(-g, u0[e], u1[e]), fmaf(-f0, u0[e], ur[e]));
         }
       }
     }
-    if (t == 0) pivs[j] = piv;
   }
   __syncthreads();
+  if (t == 0) {
+    for (int j = 0; j < nb; ++j)
+      if (!(pivs[j] > 0.f)) {
+        if (*info == 0) *info = k0 + j + 1;
+        break;
+      }
+  }
   if (i < nb) {
-    const float inv_i = 1.f / sqrtf(pivs[i]);
+    const float inv_i = 1.f / sqrtf(piv(pivs[i]));
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    for (int m = 0; m < 4; ++m) {
       const int k = c0 + m;
       if (k >= nb) continue;
       float l = 0.f;
-      if (k < i) l = rec[k][i] / sqrtf(pivs[k]);
-      else if (k == i) l = sqrtf(pivs[i]);
+      if (k < i) l = rec[k][i] / sqrtf(piv(pivs[k]));
+      else if (k == i) l = sqrtf(piv(pivs[i]));
       Mx[(int64_t)(k0 + i) * d + k0 + k] = l;
       T[i * NB + k] = ur[m] * inv_i;
     }
@@ -392,7 +417,7 @@ constexpr int DOT_BLOCKS = 512;
 
 struct WsLayout {
   float* Mx;   // d x d
-  float* Bx;   // d x 2d
+  float* Bx;   // d x d: I, then L^-1
   float* Rc;   // d x d
   float* Wf;   // d x d
   float* P;    // d x d (W W^T, also the refinement residual)
@@ -450,44 +475,46 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
     hipLaunchKernelGGL(setup_kernel<F32>, dim3(eb), dim3(NT), 0, s, L.G, (const float*)L.W, d, w.sc, w.Mx, w.Bx, w.Wf);
   ISPA_TRY(hipGetLastError());
 
-  // R = C W into the left half of the augmented right-hand side, and a copy kept in Rc
+  // R = C W
   {
-    Gemm g = mk(L.C, d, 0, w.Wf, d, 0, w.Bx, 2 * d, d, d, d, 1.f, 0.f);
+    Gemm g = mk(L.C, d, 0, w.Wf, d, 0, w.Rc, d, d, d, d, 1.f, 0.f);
     ISPA_TRY(run_gemms(&g, 1, s));
-    ISPA_TRY(hipMemcpy2DAsync(w.Rc, (size_t)d * sizeof(float), w.Bx, (size_t)2 * d * sizeof(float),
-                              (size_t)d * sizeof(float), (size_t)d, hipMemcpyDeviceToDevice, s));
   }
-  const int64_t ldb = 2 * (int64_t)d;
+  // Cholesky sweep; the identity part becomes L^-1 (only its columns < k0 + nb are nonzero in row
+  // block k, and rows above the panel are final)
+  const int64_t ldb = d;
   for (int k0 = 0; k0 < d; k0 += NB) {
     const int nb = d - k0 < NB ? d - k0 : NB;
     const int below = d - k0 - nb;
-    hipLaunchKernelGGL(diag_kernel, dim3(1), dim3(256), 0, s, w.Mx, d, k0, nb, w.T, L.info);
+    hipLaunchKernelGGL(diag_kernel, dim3(1), dim3(DIAG_THREADS), 0, s, w.Mx, d, k0, nb, w.T, L.info);
     ISPA_TRY(hipGetLastError());
-    // panel: L21 = A21 T^T; Y_k = T B_k (R part, and the nonzero columns of the identity part)
+    // panel: L21 = A21 T^T; Y_k = T B_k over the nonzero columns of the identity part
     {
-      Gemm g[3];
+      Gemm g[2];
       int c = 0;
       if (below > 0) g[c++] = mk(w.Mx + (int64_t)(k0 + nb) * d + k0, d, 0, w.T, NB, 1, w.Mx + (int64_t)(k0 + nb) * d + k0, d,
                                  below, nb, nb, 1.f, 0.f);
-      g[c++] = mk(w.T, NB, 0, w.Bx + (int64_t)k0 * ldb, ldb, 0, w.Bx + (int64_t)k0 * ldb, ldb, nb, d, nb, 1.f, 0.f);
-      g[c++] = mk(w.T, NB, 0, w.Bx + (int64_t)k0 * ldb + d, ldb, 0, w.Bx + (int64_t)k0 * ldb + d, ldb, nb, k0 + nb, nb,
-                  1.f, 0.f);
+      g[c++] = mk(w.T, NB, 0, w.Bx + (int64_t)k0 * ldb, ldb, 0, w.Bx + (int64_t)k0 * ldb, ldb, nb, k0 + nb, nb, 1.f, 0.f);
       ISPA_TRY(run_gemms(g, c, s));
     }
     if (below > 0) {
       // trailing update: A22 -= L21 L21^T (lower tiles); B_below -= L21 Y_k
       const float* L21 = w.Mx + (int64_t)(k0 + nb) * d + k0;
-      Gemm g[3] = {
+      Gemm g[2] = {
           mk(L21, d, 0, L21, d, 1, w.Mx + (int64_t)(k0 + nb) * d + k0 + nb, d, below, below, nb, -1.f, 1.f, 0, 1),
-          mk(L21, d, 0, w.Bx + (int64_t)k0 * ldb, ldb, 0, w.Bx + (int64_t)(k0 + nb) * ldb, ldb, below, d, nb, -1.f, 1.f),
-          mk(L21, d, 0, w.Bx + (int64_t)k0 * ldb + d, ldb, 0, w.Bx + (int64_t)(k0 + nb) * ldb + d, ldb, below, k0 + nb,
-             nb, -1.f, 1.f)};
-      ISPA_TRY(run_gemms(g, 3, s));
+          mk(L21, d, 0, w.Bx + (int64_t)k0 * ldb, ldb, 0, w.Bx + (int64_t)(k0 + nb) * ldb, ldb, below, k0 + nb, nb, -1.f,
+             1.f)};
+      ISPA_TRY(run_gemms(g, 2, s));
     }
   }
-  // dW = (L^-1)^T Y   (L^-1 lower triangular: only k >= m contributes)
+  // Z = L^-1 R (L^-1 lower triangular: only k < m0 + 64 contributes), into Mx (no longer needed)
   {
-    Gemm g = mk(w.Bx + d, ldb, 1, w.Bx, ldb, 0, L.delta_w, d, d, d, d, 1.f, 0.f, 1);
+    Gemm g = mk(w.Bx, ldb, 0, w.Rc, d, 0, w.Mx, d, d, d, d, 1.f, 0.f, 2);
+    ISPA_TRY(run_gemms(&g, 1, s));
+  }
+  // dW = (L^-1)^T Z   (op(A) upper triangular: only k >= m0 contributes)
+  {
+    Gemm g = mk(w.Bx, ldb, 1, w.Mx, d, 0, L.delta_w, d, d, d, d, 1.f, 0.f, 1);
     ISPA_TRY(run_gemms(&g, 1, s));
   }
   if (L.refine > 0) {
@@ -500,9 +527,9 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
       hipLaunchKernelGGL(gemm64_kernel<1>, dim3(tpd * tpd), dim3(NT), 0, s, L.G, L.delta_w, d, w.sc, w.R64, w.P);
       ISPA_TRY(hipGetLastError());
       // t = L^-1 r (into Mx, no longer needed), dW += (L^-1)^T t
-      Gemm g1 = mk(w.Bx + d, ldb, 0, w.P, d, 0, w.Mx, d, d, d, d, 1.f, 0.f, 2);
+      Gemm g1 = mk(w.Bx, ldb, 0, w.P, d, 0, w.Mx, d, d, d, d, 1.f, 0.f, 2);
       ISPA_TRY(run_gemms(&g1, 1, s));
-      Gemm g2 = mk(w.Bx + d, ldb, 1, w.Mx, d, 0, L.delta_w, d, d, d, d, 1.f, 1.f, 1);
+      Gemm g2 = mk(w.Bx, ldb, 1, w.Mx, d, 0, L.delta_w, d, d, d, d, 1.f, 1.f, 1);
       ISPA_TRY(run_gemms(&g2, 1, s));
     }
   }
