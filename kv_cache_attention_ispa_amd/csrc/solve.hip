@@ -220,38 +220,102 @@ __global__ __launch_bounds__(NT) void setup_kernel(const float* G, const typenam
   }
 }
 
-// Factor the diagonal block Mx[k0:k0+nb, k0:k0+nb] = L L^T in place (lower) and write T = L^-1,
-// two columns per barrier.  1024 threads (the step is latency bound; more waves per SIMD hide it):
-// thread t owns row i = t/16, columns 4 (t%16) .. +3 of the block A (kept symmetric: row j also
-// holds column j) and of the augmented block U that starts as I.  Step s handles columns j = 2s and
-// j+1.  Rows j and j+1 (all earlier steps applied) are published in LDS (double-buffered, so one
-// barrier per step); then every thread forms, on its columns,
-//   row'_{j+1} = row_{j+1} - (a01 / p0) row_j          (p0 = a_jj, a01 = a_{j,j+1}),
-// i.e. row j+1 after elimination with row j (pivot p1 = a_{j+1,j+1} - a01^2 / p0), and every row
-// i > j+1 applies both eliminations,
-//   a_i -= f0 row_j + f1 row'_{j+1},  f0 = x0 / p0,  f1 = (x1 - f0 a01) / p1,
-// where x0, x1 are row i's entries in columns j, j+1 (by symmetry, rows j and j+1's entries in
-// column i).  The same combination updates u_i: right-looking Cholesky and forward substitution in
-// one sweep, with the divisions by l_jj = sqrt(p_j) deferred.  The final rows (row j as published,
-// row'_{j+1}) are recorded: L_ij = rec_j[i] / sqrt(p_j) for i > j, (L^-1)_i = u_i / sqrt(p_i).
-// Rows past nb (last panel) are padded with the identity.
-constexpr int DIAG_THREADS = 1024;
-__global__ __launch_bounds__(DIAG_THREADS) void diag_kernel(float* Mx, int d, int k0, int nb, float* T, int* info) {
-  __shared__ __attribute__((aligned(16))) float curb[2][2][2][NB];   // [step parity][A or U][row j or j+1][col]
-  __shared__ __attribute__((aligned(16))) float rec[NB][NB + 4];     // final A rows
-  __shared__ float pivs[NB];
+// ------------------------------------------------------------------------------------------
+// Cholesky sweep, one launch per panel (64-wide block columns, nP of them).  With T_k = L_kk^-1:
+//   L_ik = A_ik T_k^T for the blocks below the diagonal, so the trailing update of panel k is
+//   A_ij -= X_i X_j^T with X_i = A_ik T_k^T, and the identity part (which becomes L^-1) is
+//   B_ic -= X_i (T_k B_kc) for the blocks below, while its block row k ends as T_k B_kc.
+// Launch k runs, side by side:
+//   * the factorization of diagonal block k (work-group 0): D = A_kk - X_k X_k^T (panel k-1's
+//     update of that block), D = L_kk L_kk^T, T_k = L_kk^-1  -> T slot k % 3;
+//   * panel k-1's trailing update of every other lower block of A and of the identity part;
+//   * the final product T_{k-2} B_{k-2,c} of block row k-2 (no launch reads that row any more).
+// The factors L are never needed again: the solve uses L^-1 only.  Launch nP finishes block rows
+// nP-2 and nP-1.  Every work-group has 1024 threads (16 waves); the 64 x 64 x 64 products run on
+// MFMA 16x16x4 (fp32), one 16 x 16 quadrant per wave.
+// ------------------------------------------------------------------------------------------
+constexpr int SW_THREADS = 1024;
+constexpr int BP = NB + 4;   // LDS pitch of a 64 x 64 block: 16 rows of a wave hit 16 distinct 4-bank groups
+
+struct SweepArgs {
+  float* Mx;   // d x d, G + lambda I, lower blocks updated in place
+  float* Bx;   // d x d, identity part, becomes L^-1
+  float* Tb;   // three 64 x 64 slots: T_k in slot k % 3
+  int* info;
+  int d, nP, k;
+  int n_a, n_i, f_row0, f_rows;   // work items: A blocks, identity blocks, final rows [f_row0, +f_rows)
+};
+
+// 64 x 64 block (row block rb, column block cb) of a d x d row-major matrix into LDS, zeros outside.
+__device__ __forceinline__ void sw_load(float (*dst)[BP], const float* src, int d, int rb, int cb) {
+  const int t = threadIdx.x;
+  const int r = t >> 4, c = (t & 15) * 4;
+  const int gr = rb * NB + r, gc = cb * NB + c;
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  if (gr < d && gc < d) v = *(const f32x4*)(src + (int64_t)gr * d + gc);
+  *(f32x4*)&dst[r][c] = v;
+}
+__device__ __forceinline__ void sw_load_t(float (*dst)[BP], const float* Tk) {
+  const int t = threadIdx.x;
+  const int r = t >> 4, c = (t & 15) * 4;
+  *(f32x4*)&dst[r][c] = *(const f32x4*)(Tk + r * NB + c);
+}
+
+// Quadrant (wave / 4, wave % 4) of X op(Y) over k < 64 (op(Y) = Y^T when ty): 16x16x4 MFMA,
+// register r of lane l holds row 4 (l / 16) + r, column l % 16 of the quadrant.
+__device__ __forceinline__ f32x4 sw_mm(const float (*X)[BP], const float (*Y)[BP], bool ty) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m0 = (wave >> 2) * 16, n0 = (wave & 3) * 16;
+  const int a = lane & 15, kk = lane >> 4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s4 = 0; s4 < NB; s4 += 4) {
+    const float x = X[m0 + a][s4 + kk];
+    const float y = ty ? Y[n0 + a][s4 + kk] : Y[s4 + kk][n0 + a];
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, acc, 0, 0, 0);
+  }
+  return acc;
+}
+__device__ __forceinline__ void sw_put(float (*dst)[BP], f32x4 v) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m0 = (wave >> 2) * 16 + 4 * (lane >> 4), n = (wave & 3) * 16 + (lane & 15);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dst[m0 + r][n] = v[r];
+}
+// global block (rb, cb) of a d x d matrix: C = beta C + v (beta 0 or 1)
+__device__ __forceinline__ void sw_store(float* C, int d, int rb, int cb, f32x4 v, bool accumulate) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m0 = rb * NB + (wave >> 2) * 16 + 4 * (lane >> 4), n = cb * NB + (wave & 3) * 16 + (lane & 15);
+  if (n >= d) return;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (m0 + r >= d) continue;
+    float* c = C + (int64_t)(m0 + r) * d + n;
+    *c = accumulate ? *c + v[r] : v[r];
+  }
+}
+
+// Factorization of the symmetric 64 x 64 block D (in LDS) = L L^T and T = L^-1, two columns per
+// barrier.  Thread t owns row i = t/16, columns 4 (t%16) .. +3 of D (symmetric: row j also holds
+// column j) and of U, which starts as I.  Step s handles columns j = 2s and j+1: rows j and j+1
+// (all earlier steps applied) are published (double-buffered, one barrier per step); every thread
+// forms, on its columns, row'_{j+1} = row_{j+1} - (a01 / p0) row_j (row j+1 after elimination with
+// row j; p0 = a_jj, a01 = a_{j,j+1}, pivot p1 = a_{j+1,j+1} - a01^2 / p0), and every row i > j+1
+// applies both eliminations, a_i -= f0 row_j + f1 row'_{j+1} with f0 = x0 / p0, f1 = (x1 - f0 a01) / p1,
+// x0, x1 = row i's entries in columns j, j+1 (by symmetry, rows j and j+1's entries in column i).
+// The same combination updates u_i: right-looking Cholesky and forward substitution in one sweep,
+// with the divisions by l_jj = sqrt(p_j) deferred: (L^-1)_i = u_i / sqrt(p_i).  Rows past nb (last
+// panel) hold the identity.  A non-positive pivot sets *info to its 1-based index (k0 + j + 1) and is
+// replaced by 1.
+__device__ __forceinline__ void sw_factor(const float (*D)[BP], float (*curb)[2][2][NB], float* pivs, int nb, int k0,
+                                          float* Tk, int* info) {
   const int t = threadIdx.x;
   const int i = t >> 4, c0 = (t & 15) * 4;
   float ar[4], ur[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int k = c0 + m;
-    float v;
-    if (i < nb && k < nb)
-      v = (k <= i) ? Mx[(int64_t)(k0 + i) * d + k0 + k] : Mx[(int64_t)(k0 + k) * d + k0 + i];
-    else
-      v = (i == k) ? 1.f : 0.f;
-    ar[m] = v;
+    ar[m] = (i < nb && k < nb) ? D[i][k] : (i == k ? 1.f : 0.f);
     ur[m] = (i == k) ? 1.f : 0.f;
   }
   auto piv = [](float p) { return p > 0.f ? p : 1.f; };
@@ -261,7 +325,6 @@ __global__ __launch_bounds__(DIAG_THREADS) void diag_kernel(float* Mx, int d, in
     if (q == 0 || q == 1) {
       *(f32x4*)&cur[0][q][c0] = f32x4{ar[0], ar[1], ar[2], ar[3]};
       *(f32x4*)&cur[1][q][c0] = f32x4{ur[0], ur[1], ur[2], ur[3]};
-      if (q == 0) *(f32x4*)&rec[j][c0] = f32x4{ar[0], ar[1], ar[2], ar[3]};
     }
     __syncthreads();
     if (i > j) {
@@ -273,13 +336,11 @@ __global__ __launch_bounds__(DIAG_THREADS) void diag_kernel(float* Mx, int d, in
       const f32x4 a0 = *(const f32x4*)&cur[0][0][c0];
       const f32x4 u0 = *(const f32x4*)&cur[1][0][c0];
       if (q == 1) {
-        // row j+1 itself: its final value is row'_{j+1}
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           ar[e] = fmaf(-g, a0[e], ar[e]);
           ur[e] = fmaf(-g, u0[e], ur[e]);
         }
-        *(f32x4*)&rec[j + 1][c0] = f32x4{ar[0], ar[1], ar[2], ar[3]};
         if ((t & 15) == 0) {
           pivs[j] = cur[0][0][j];
           pivs[j + 1] = p1raw;
@@ -305,19 +366,86 @@ __global__ __launch_bounds__(DIAG_THREADS) void diag_kernel(float* Mx, int d, in
         break;
       }
   }
-  if (i < nb) {
-    const float inv_i = 1.f / sqrtf(piv(pivs[i]));
+  const float inv_i = 1.f / sqrtf(i < nb ? piv(pivs[i]) : 1.f);
+  *(f32x4*)(Tk + i * NB + c0) = f32x4{ur[0] * inv_i, ur[1] * inv_i, ur[2] * inv_i, ur[3] * inv_i};
+}
+
+__global__ __launch_bounds__(SW_THREADS) void sweep_kernel(SweepArgs a) {
+  __shared__ __attribute__((aligned(16))) float L0[NB][BP], L1[NB][BP], L2[NB][BP], L3[NB][BP], L4[NB][BP];
+  __shared__ __attribute__((aligned(16))) float curb[2][2][2][NB];
+  __shared__ float pivs[NB];
+  const int k = a.k, d = a.d;
+  int q = blockIdx.x;
+  float* Tprev = a.Tb + ((k + 2) % 3) * NB * NB;   // T_{k-1}
+  if (k < a.nP) {
+    if (q == 0) {
+      // diagonal block k: D = A_kk - X_k X_k^T, then factor
+      sw_load(L1, a.Mx, d, k, k);
+      if (k > 0) {
+        sw_load(L0, a.Mx, d, k, k - 1);
+        sw_load_t(L2, Tprev);
+        __syncthreads();
+        sw_put(L3, sw_mm(L0, L2, true));                    // X_k = A_k,k-1 T_{k-1}^T
+        __syncthreads();
+        const f32x4 xx = sw_mm(L3, L3, true);               // X_k X_k^T
+        __syncthreads();
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int m0 = (wave >> 2) * 16 + 4 * (lane >> 4), n = (wave & 3) * 16 + (lane & 15);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int k = c0 + m;
-      if (k >= nb) continue;
-      float l = 0.f;
-      if (k < i) l = rec[k][i] / sqrtf(piv(pivs[k]));
-      else if (k == i) l = sqrtf(piv(pivs[i]));
-      Mx[(int64_t)(k0 + i) * d + k0 + k] = l;
-      T[i * NB + k] = ur[m] * inv_i;
+        for (int r = 0; r < 4; ++r) L1[m0 + r][n] -= xx[r];
+      }
+      __syncthreads();
+      const int nb = min(NB, d - k * NB);
+      sw_factor(L1, curb, pivs, nb, k * NB, a.Tb + (k % 3) * NB * NB, a.info);
+      return;
     }
+    --q;
   }
+  if (q < a.n_a) {
+    // trailing block (i, j) of A, k <= j <= i < nP, other than (k, k): A_ij -= X_i X_j^T
+    int p = q + 1;
+    int ii = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+    while ((ii + 1) * (ii + 2) / 2 <= p) ++ii;
+    while (ii * (ii + 1) / 2 > p) --ii;
+    const int i = k + ii, j = k + (p - ii * (ii + 1) / 2);
+    sw_load(L0, a.Mx, d, i, k - 1);
+    sw_load_t(L2, Tprev);
+    if (i != j) sw_load(L1, a.Mx, d, j, k - 1);
+    __syncthreads();
+    sw_put(L3, sw_mm(L0, L2, true));                        // X_i
+    if (i != j) sw_put(L4, sw_mm(L1, L2, true));            // X_j
+    __syncthreads();
+    const f32x4 v = sw_mm(L3, i != j ? L4 : L3, true);
+    sw_store(a.Mx, d, i, j, -v, true);
+    return;
+  }
+  q -= a.n_a;
+  if (q < a.n_i) {
+    // identity part below panel k-1: B_ic -= X_i (T_{k-1} B_{k-1,c}), c < k
+    const int i = k + q / k, c = q % k;
+    sw_load(L0, a.Mx, d, i, k - 1);
+    sw_load(L1, a.Bx, d, k - 1, c);
+    sw_load_t(L2, Tprev);
+    __syncthreads();
+    sw_put(L3, sw_mm(L0, L2, true));                        // X_i
+    sw_put(L4, sw_mm(L2, L1, false));                       // T_{k-1} B_{k-1,c}
+    __syncthreads();
+    const f32x4 v = sw_mm(L3, L4, false);
+    sw_store(a.Bx, d, i, c, -v, true);
+    return;
+  }
+  q -= a.n_i;
+  // final block rows: B_rc = T_r B_rc, c <= r
+  int r = a.f_row0, n = r + 1;
+  if (q >= n) {
+    q -= n;
+    r += 1;
+  }
+  sw_load(L1, a.Bx, d, r, q);
+  sw_load_t(L2, a.Tb + (r % 3) * NB * NB);
+  __syncthreads();
+  const f32x4 v = sw_mm(L2, L1, false);
+  sw_store(a.Bx, d, r, q, v, false);
 }
 
 // out = A B accumulated in fp64 (A, B fp32 [d, d] row-major); 64 x 64 tile per work-group,
@@ -421,7 +549,7 @@ struct WsLayout {
   float* Rc;   // d x d
   float* Wf;   // d x d
   float* P;    // d x d (W W^T, also the refinement residual)
-  float* T;    // NB x NB
+  float* T;    // three NB x NB slots
   Scalars* sc;
   double* part;
   double* R64; // d x d, C W accumulated in fp64 (refinement only)
@@ -436,7 +564,7 @@ WsLayout carve(void* ws, int d) {
   w.Rc = (float*)p; p += dd;
   w.Wf = (float*)p; p += dd;
   w.P = (float*)p; p += dd;
-  w.T = (float*)p; p += NB * NB * sizeof(float);
+  w.T = (float*)p; p += 3 * NB * NB * sizeof(float);
   w.sc = (Scalars*)p; p += 256;
   w.part = (double*)p; p += DOT_BLOCKS * 5 * sizeof(double);
   w.R64 = (double*)p;
@@ -452,7 +580,7 @@ WsLayout carve(void* ws, int d) {
 }  // namespace
 
 size_t solve_workspace_bytes(int d) {
-  return (size_t)d * d * sizeof(float) * 6 + NB * NB * sizeof(float) + 256 + DOT_BLOCKS * 5 * sizeof(double) +
+  return (size_t)d * d * sizeof(float) * 6 + 3 * NB * NB * sizeof(float) + 256 + DOT_BLOCKS * 5 * sizeof(double) +
          (size_t)d * d * sizeof(double) + 256;
 }
 
@@ -480,31 +608,35 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
     Gemm g = mk(L.C, d, 0, w.Wf, d, 0, w.Rc, d, d, d, d, 1.f, 0.f);
     ISPA_TRY(run_gemms(&g, 1, s));
   }
-  // Cholesky sweep; the identity part becomes L^-1 (only its columns < k0 + nb are nonzero in row
-  // block k, and rows above the panel are final)
+  // Cholesky sweep (one launch per panel, plus one that finishes the last two block rows of L^-1)
   const int64_t ldb = d;
-  for (int k0 = 0; k0 < d; k0 += NB) {
-    const int nb = d - k0 < NB ? d - k0 : NB;
-    const int below = d - k0 - nb;
-    hipLaunchKernelGGL(diag_kernel, dim3(1), dim3(DIAG_THREADS), 0, s, w.Mx, d, k0, nb, w.T, L.info);
-    ISPA_TRY(hipGetLastError());
-    // panel: L21 = A21 T^T; Y_k = T B_k over the nonzero columns of the identity part
-    {
-      Gemm g[2];
-      int c = 0;
-      if (below > 0) g[c++] = mk(w.Mx + (int64_t)(k0 + nb) * d + k0, d, 0, w.T, NB, 1, w.Mx + (int64_t)(k0 + nb) * d + k0, d,
-                                 below, nb, nb, 1.f, 0.f);
-      g[c++] = mk(w.T, NB, 0, w.Bx + (int64_t)k0 * ldb, ldb, 0, w.Bx + (int64_t)k0 * ldb, ldb, nb, k0 + nb, nb, 1.f, 0.f);
-      ISPA_TRY(run_gemms(g, c, s));
-    }
-    if (below > 0) {
-      // trailing update: A22 -= L21 L21^T (lower tiles); B_below -= L21 Y_k
-      const float* L21 = w.Mx + (int64_t)(k0 + nb) * d + k0;
-      Gemm g[2] = {
-          mk(L21, d, 0, L21, d, 1, w.Mx + (int64_t)(k0 + nb) * d + k0 + nb, d, below, below, nb, -1.f, 1.f, 0, 1),
-          mk(L21, d, 0, w.Bx + (int64_t)k0 * ldb, ldb, 0, w.Bx + (int64_t)(k0 + nb) * ldb, ldb, below, k0 + nb, nb, -1.f,
-             1.f)};
-      ISPA_TRY(run_gemms(g, 2, s));
+  {
+    const int nP = (d + NB - 1) / NB;
+    for (int k = 0; k <= nP; ++k) {
+      SweepArgs a;
+      a.Mx = w.Mx;
+      a.Bx = w.Bx;
+      a.Tb = w.T;
+      a.info = L.info;
+      a.d = d;
+      a.nP = nP;
+      a.k = k;
+      const int m = nP - k;   // block rows at or below panel k
+      a.n_a = (k >= 1 && m >= 1) ? m * (m + 1) / 2 - 1 : 0;
+      a.n_i = (k >= 1 && m >= 1) ? m * k : 0;
+      int n_f = 0;
+      if (k == nP) {
+        a.f_row0 = nP >= 2 ? nP - 2 : nP - 1;
+        a.f_rows = nP >= 2 ? 2 : 1;
+        n_f = nP >= 2 ? (nP - 1) + nP : nP;
+      } else {
+        a.f_row0 = k - 2;
+        a.f_rows = k >= 2 ? 1 : 0;
+        n_f = k >= 2 ? k - 1 : 0;
+      }
+      const int grid = (k < nP ? 1 : 0) + a.n_a + a.n_i + n_f;
+      hipLaunchKernelGGL(sweep_kernel, dim3(grid), dim3(SW_THREADS), 0, s, a);
+      ISPA_TRY(hipGetLastError());
     }
   }
   // Z = L^-1 R (L^-1 lower triangular: only k < m0 + 64 contributes), into Mx (no longer needed)
