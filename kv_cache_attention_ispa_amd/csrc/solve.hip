@@ -244,6 +244,14 @@ struct SweepArgs {
   int* info;
   int d, nP, k;
   int n_a, n_i, f_row0, f_rows;   // work items: A blocks, identity blocks, final rows [f_row0, +f_rows)
+  // products that do not depend on the sweep ride along in its launches, one K range at a time:
+  // R = C W (always) and P = W W^T (for epsilon); this launch computes output blocks
+  // [fill0, fill0 + n_fill) of K range [kb0, kb1) (in 64-blocks), added to earlier ranges when kb0 > 0
+  const float* C;
+  const float* Wf;
+  float* R;
+  float* P;
+  int n_fill, fill0, kb0, kb1;
 };
 
 // 64 x 64 block (row block rb, column block cb) of a d x d row-major matrix into LDS, zeros outside.
@@ -401,6 +409,35 @@ __global__ __launch_bounds__(SW_THREADS) void sweep_kernel(SweepArgs a) {
     }
     --q;
   }
+  if (q < a.n_fill) {
+    // block (i, j) of R = C W or P = W W^T over K blocks [kb0, kb1), double-buffered through LDS
+    const int nT = a.nP;
+    const int g = a.fill0 + q;
+    const bool is_p = g >= nT * nT;
+    const int tt = g % (nT * nT), i = tt / nT, j = tt % nT;
+    const float* X = is_p ? a.Wf : a.C;
+    auto bx = [&](int b) { return b ? L3 : L0; };
+    auto by = [&](int b) { return b ? L4 : L1; };
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    sw_load(bx(0), X, d, i, a.kb0);
+    if (is_p) sw_load(by(0), a.Wf, d, j, a.kb0);
+    else sw_load(by(0), a.Wf, d, a.kb0, j);
+    for (int kb = a.kb0; kb < a.kb1; ++kb) {
+      const int b = (kb - a.kb0) & 1;
+      __syncthreads();
+      if (kb + 1 < a.kb1) {
+        sw_load(bx(b ^ 1), X, d, i, kb + 1);
+        if (is_p) sw_load(by(b ^ 1), a.Wf, d, j, kb + 1);
+        else sw_load(by(b ^ 1), a.Wf, d, kb + 1, j);
+      }
+      const f32x4 v = sw_mm(bx(b), by(b), is_p);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] += v[r];
+    }
+    sw_store(is_p ? a.P : a.R, d, i, j, acc, a.kb0 > 0);
+    return;
+  }
+  q -= a.n_fill;
   if (q < a.n_a) {
     // trailing block (i, j) of A, k <= j <= i < nP, other than (k, k): A_ij -= X_i X_j^T
     int p = q + 1;
@@ -546,9 +583,10 @@ constexpr int DOT_BLOCKS = 512;
 struct WsLayout {
   float* Mx;   // d x d
   float* Bx;   // d x d: I, then L^-1
+  float* Rs;   // d x d: refinement residual
   float* Rc;   // d x d
   float* Wf;   // d x d
-  float* P;    // d x d (W W^T, also the refinement residual)
+  float* P;    // d x d (W W^T)
   float* T;    // three NB x NB slots
   Scalars* sc;
   double* part;
@@ -560,7 +598,8 @@ WsLayout carve(void* ws, int d) {
   const size_t dd = (size_t)d * d * sizeof(float);
   WsLayout w;
   w.Mx = (float*)p; p += dd;
-  w.Bx = (float*)p; p += 2 * dd;
+  w.Bx = (float*)p; p += dd;
+  w.Rs = (float*)p; p += dd;
   w.Rc = (float*)p; p += dd;
   w.Wf = (float*)p; p += dd;
   w.P = (float*)p; p += dd;
@@ -603,15 +642,15 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
     hipLaunchKernelGGL(setup_kernel<F32>, dim3(eb), dim3(NT), 0, s, L.G, (const float*)L.W, d, w.sc, w.Mx, w.Bx, w.Wf);
   ISPA_TRY(hipGetLastError());
 
-  // R = C W
-  {
-    Gemm g = mk(L.C, d, 0, w.Wf, d, 0, w.Rc, d, d, d, d, 1.f, 0.f);
-    ISPA_TRY(run_gemms(&g, 1, s));
-  }
   // Cholesky sweep (one launch per panel, plus one that finishes the last two block rows of L^-1)
   const int64_t ldb = d;
   {
     const int nP = (d + NB - 1) / NB;
+    // R = C W and (for epsilon) P = W W^T ride along, split into three K ranges spread over the
+    // launches in order, so a range is added only after the one before it is complete
+    const int n_launch = nP + 1;
+    const int n_out = nP * nP * (L.eps ? 2 : 1);
+    const int n_range = n_launch < 3 ? n_launch : 3;   // launch k works on range k * n_range / n_launch
     for (int k = 0; k <= nP; ++k) {
       SweepArgs a;
       a.Mx = w.Mx;
@@ -634,7 +673,19 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
         a.f_rows = k >= 2 ? 1 : 0;
         n_f = k >= 2 ? k - 1 : 0;
       }
-      const int grid = (k < nP ? 1 : 0) + a.n_a + a.n_i + n_f;
+      const int range = k * n_range / n_launch;
+      const int first = (range * n_launch + n_range - 1) / n_range;   // first launch of this range
+      const int next = ((range + 1) * n_launch + n_range - 1) / n_range;
+      const int slot = k - first, n_slots = next - first;
+      a.C = L.C;
+      a.Wf = w.Wf;
+      a.R = w.Rc;
+      a.P = w.P;
+      a.kb0 = range * nP / n_range;
+      a.kb1 = (range + 1) * nP / n_range;
+      a.fill0 = (int)((int64_t)n_out * slot / n_slots);
+      a.n_fill = a.kb0 < a.kb1 ? (int)((int64_t)n_out * (slot + 1) / n_slots) - a.fill0 : 0;
+      const int grid = (k < nP ? 1 : 0) + a.n_fill + a.n_a + a.n_i + n_f;
       hipLaunchKernelGGL(sweep_kernel, dim3(grid), dim3(SW_THREADS), 0, s, a);
       ISPA_TRY(hipGetLastError());
     }
@@ -656,18 +707,16 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
     hipLaunchKernelGGL(gemm64_kernel<0>, dim3(tpd * tpd), dim3(NT), 0, s, L.C, w.Wf, d, w.sc, w.R64, nullptr);
     ISPA_TRY(hipGetLastError());
     for (int it = 0; it < L.refine; ++it) {
-      hipLaunchKernelGGL(gemm64_kernel<1>, dim3(tpd * tpd), dim3(NT), 0, s, L.G, L.delta_w, d, w.sc, w.R64, w.P);
+      hipLaunchKernelGGL(gemm64_kernel<1>, dim3(tpd * tpd), dim3(NT), 0, s, L.G, L.delta_w, d, w.sc, w.R64, w.Rs);
       ISPA_TRY(hipGetLastError());
       // t = L^-1 r (into Mx, no longer needed), dW += (L^-1)^T t
-      Gemm g1 = mk(w.Bx, ldb, 0, w.P, d, 0, w.Mx, d, d, d, d, 1.f, 0.f, 2);
+      Gemm g1 = mk(w.Bx, ldb, 0, w.Rs, d, 0, w.Mx, d, d, d, d, 1.f, 0.f, 2);
       ISPA_TRY(run_gemms(&g1, 1, s));
       Gemm g2 = mk(w.Bx, ldb, 1, w.Mx, d, 0, L.delta_w, d, d, d, d, 1.f, 1.f, 1);
       ISPA_TRY(run_gemms(&g2, 1, s));
     }
   }
   if (L.eps) {
-    Gemm g = mk(w.Wf, d, 0, w.Wf, d, 1, w.P, d, d, d, d, 1.f, 0.f);
-    ISPA_TRY(run_gemms(&g, 1, s));
     hipLaunchKernelGGL(dots_kernel, dim3(DOT_BLOCKS), dim3(NT), 0, s, L.D, L.G, w.P, w.Wf, w.Rc, L.delta_w, dd, w.part);
     ISPA_TRY(hipGetLastError());
     hipLaunchKernelGGL(eps_kernel, dim3(1), dim3(NT), 0, s, w.part, DOT_BLOCKS, w.sc, L.eps);
