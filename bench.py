@@ -191,7 +191,7 @@ def main():
         "local_layer_step_ms": round(local_ms, 4),
         "step_tflops": round(step_flops / (total_ms / args.steps * 1e-3) / 1e12, 2),
         "eps": round(float(eps.item()), 6),
-        "roofline": {"bound": "mfma", "kernel": "ispa_dual_attn call: bf16_to_f16_kernel (V copy) + attn_mfma_kernel",
+        "roofline": {"bound": "mfma", "kernel": "ispa_dual_attn call: vt_kernel (V^T copy) + attn_mfma_kernel",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "flops_per_launch": attn_flops, "avg_launch_ms": round(attn_ms, 4)},

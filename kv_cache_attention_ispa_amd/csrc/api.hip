@@ -133,6 +133,8 @@ int ispa_gram_accum(int d, int n, int stat_dtype, const void* a_loc_t, const voi
   if (!valid_dtype(stat_dtype)) return ISPA_EUNSUPPORTED;
   if (!a_loc_t || !delta_a_t || !G || !C) return ISPA_EINVAL;
   if (ld < n || ld % 8 != 0) return ISPA_EINVAL;
+  // the 16-bit kernel addresses a 128-row slice of a statistic with 32-bit byte offsets
+  if (stat_dtype != ISPA_F32 && ld * 2 * 128 >= INT32_MAX) return ISPA_EUNSUPPORTED;
   if (!aligned16(a_loc_t) || !aligned16(delta_a_t) || !aligned16(G) || !aligned16(C) || !aligned16(D))
     return ISPA_EINVAL;
   if (accumulate != 0 && accumulate != 1) return ISPA_EINVAL;

@@ -70,9 +70,6 @@ constexpr int V_INST = HD * VT_SLOTS / 64;        // per V^T tile (18)
 constexpr int LOADS_PER_WAVE = (K_INST + V_INST + WAVES - 1) / WAVES;   // 5: every wave issues the same count
 static_assert(K_SLOTS * BN % 64 == 0 && VT_SLOTS * HD % 64 == 0, "tile must be whole wave loads");
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 
 // The key tiles of one launch: up to three segments of consecutive cache rows, each cut into 64-row
 // tiles (the last one partial).  Dual stream: sink rows, current-chunk rows (together the local

@@ -99,6 +99,10 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return xcd * per + (xcd < rem ? xcd : rem) + local;
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+
 __device__ __forceinline__ float wave_max_xor32(float x) {
   return fmaxf(x, __shfl_xor(x, 32));
 }

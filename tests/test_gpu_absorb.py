@@ -50,6 +50,17 @@ def test_gram_matches_float64_of_same_inputs(dtype, d, ns):
     assert maxrel(G, Gr) <= 1e-4 and maxrel(C, Cr) <= 1e-4 and maxrel(D, Dr) <= 1e-4
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d,n", [(384, 517), (640, 64), (96, 33)])
+def test_gram_without_d(dtype, d, n):
+    """D = NULL: only G (lower tiles, mirrored) and C are computed."""
+    rng = np.random.default_rng(d + n)
+    chunks = [(wl.round_to(rng.standard_normal((n, d)) * 0.05, dtype), wl.round_to(rng.standard_normal((n, d)) * 0.03, dtype))]
+    G, C, _ = _gram_gpu(chunks, dtype, d, with_d=False)
+    Gr, Cr, _ = oracle.gram_stats(chunks)
+    assert maxrel(G, Gr) <= 1e-4 and maxrel(C, Cr) <= 1e-4
+
+
 def _spd_problem(d, n, seed, w_dtype="f32"):
     rng = np.random.default_rng(seed)
     a = rng.standard_normal((n, d)) * 0.05
