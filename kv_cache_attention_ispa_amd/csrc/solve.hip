@@ -26,155 +26,170 @@ namespace ispa {
 namespace {
 
 constexpr int NB = 64;          // Cholesky panel width
-constexpr int TB = 64;          // GEMM output tile
-constexpr int TK = 32;          // GEMM k-step
 constexpr int NT = 256;
 
 // ------------------------------------------------------------------------------------------
-// fp32 GEMM on MFMA (32x32x2): C = alpha * op(A) op(B) + beta * C, 64 x 64 tiles, 4 waves.
-// op(A)[m][k] = transA ? A[k*lda + m] : A[m*lda + k];  op(B)[k][n] = transB ? B[n*ldb + k] : B[k*ldb + n].
-// kmode: 0 full k range; 1 k >= m0 (op(A) upper triangular); 2 k < m0 + 64 (op(A) lower triangular).
-// lower_only: skip output tiles strictly above the diagonal.
+// Triangular fp32 GEMM on MFMA (32x32x2): C = alpha * op(A) B + beta * C for d x d row-major
+// matrices, op(A) = A lower triangular (TA = false: only k < m0 + 64 contributes to a row block at
+// m0) or op(A) = A^T with A lower triangular (TA = true: only k >= m0).  64 x 64 output tiles, 4
+// waves of 32 x 32; k streams through a 4-deep LDS ring of 32-wide stages filled by direct-to-LDS
+// buffer loads issued three stages ahead; two work-groups per CU.  Tiles are dispatched longest
+// k range first.
+// A stage holds op(A) rows m0 .. m0+63 x k0 .. k0+31 and B rows k0 .. k0+31 x n0 .. n0+63.
+//   TA = false: A[m][k] rows of 128 bytes, 16-byte chunk c of row m at 16 (c ^ (m % 8)); the MFMA
+//     k order is permuted so one 16-byte read of A[m][4c .. 4c+3] feeds four MFMAs (the k index of
+//     A and B only has to agree within the sum).
+//   TA = true: A[k][m] rows of 256 bytes (the stage is a row slice of A itself).
+//   B: B[k][n] rows of 256 bytes.
 // ------------------------------------------------------------------------------------------
-struct Gemm {
+constexpr int TG_TILE = 64, TG_K = 32, TG_RING = 4;
+constexpr int TG_STAGE = TG_TILE * TG_K * 4;   // bytes of one operand stage (8 KiB)
+
+struct TrGemm {
   const float* A;
   const float* B;
   float* C;
-  int64_t lda, ldb, ldc;
-  int M, N, K;
-  int transA, transB, kmode, lower_only;
+  int d, tiles;   // tiles per dimension
   float alpha, beta;
 };
-struct GemmBatch {
-  Gemm g[3];
-  int tiles_n[3];
-  int tile_start[4];
-  int count;
-};
 
-__global__ __launch_bounds__(NT) void gemm_f32_kernel(GemmBatch b) {
-  __shared__ float As[2][TK][TB + 4];
-  __shared__ float Bs[2][TK][TB + 4];
-  int pid = 0;
-  while (pid + 1 < b.count && (int)blockIdx.x >= b.tile_start[pid + 1]) ++pid;
-  const Gemm g = b.g[pid];
-  const int t = blockIdx.x - b.tile_start[pid];
-  const int bm = t / b.tiles_n[pid], bn = t % b.tiles_n[pid];
-  if (g.lower_only && bn > bm) return;
-  const int m0 = bm * TB, n0 = bn * TB;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <bool TA>
+__global__ __launch_bounds__(NT, 2) void trgemm_kernel(TrGemm g) {
+  __shared__ __attribute__((aligned(16))) char a0[TG_STAGE], a1[TG_STAGE], a2[TG_STAGE], a3[TG_STAGE];
+  __shared__ __attribute__((aligned(16))) char b0[TG_STAGE], b1[TG_STAGE], b2[TG_STAGE], b3[TG_STAGE];
+  const int T = g.tiles, d = g.d;
+  const int q = blockIdx.x;
+  const int bm = TA ? q / T : (T - 1) - q / T, bn = q % T;   // longest k range first
+  const int m0 = bm * TG_TILE, n0 = bn * TG_TILE;
+  const int k_begin = TA ? m0 : 0, k_end = TA ? d : min(d, m0 + TG_TILE);
+  const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  int k_begin = 0, k_end = g.K;
-  if (g.kmode == 1) k_begin = (m0 / TK) * TK;
-  if (g.kmode == 2) k_end = min(g.K, m0 + TB);
-  f32x16 acc = {};
-  // Each thread moves two 16-byte vectors of op(A) and two of op(B) per k-step (all sizes are
-  // multiples of 4, so a vector is either fully inside or fully outside the matrix).
-  f32x4 ra[2], rb[2];
-  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-  auto gload = [&](int k0) {
+
+  // raw buffers over A and B (reads past the end return zeros)
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, (int)((int64_t)d * d * 4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)g.B, (short)0, (int)((int64_t)d * d * 4), 0x00020000);
+  // Wave w issues A instructions 2w, 2w + 1 and B instructions 2w, 2w + 1 of a stage (8 each, 1 KiB).
+  uint32_t aoff[2], boff[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int e = tid + NT * h;                // 512 vectors per operand tile
-      if (!g.transA) {                           // A[m][k]: vector along k
-        const int m = e >> 3, kk = (e & 7) * 4;
-        const int gm = m0 + m, gk = k0 + kk;
-        ra[h] = (gm < g.M && gk < k_end) ? *(const f32x4*)(g.A + (int64_t)gm * g.lda + gk) : z4;
-      } else {                                   // A[k][m]: vector along m
-        const int kk = e >> 4, m = (e & 15) * 4;
-        const int gm = m0 + m, gk = k0 + kk;
-        ra[h] = (gm < g.M && gk < k_end) ? *(const f32x4*)(g.A + (int64_t)gk * g.lda + gm) : z4;
+  for (int j = 0; j < 2; ++j) {
+    const int i = 2 * wave + j;
+    if (TA) {   // A rows k: 4 rows x 256 bytes per instruction, lane -> row i*4 + l/16, chunk l%16
+      aoff[j] = (uint32_t)(((4 * i + (lane >> 4)) * d + m0 + 4 * (lane & 15)) * 4);
+    } else {    // A rows m: 8 rows x 128 bytes, lane -> row 8i + l/8, physical chunk l%8 = logical ^ (row % 8)
+      const int row = 8 * i + (lane >> 3), c = (lane & 7) ^ (row & 7);
+      aoff[j] = (uint32_t)(((m0 + row) * d + 4 * c) * 4);
+    }
+    boff[j] = (uint32_t)(((4 * i + (lane >> 4)) * d + n0 + 4 * (lane & 15)) * 4);
+  }
+  const int n_st = (k_end - k_begin + TG_K - 1) / TG_K;
+  auto issue = [&](char* as, char* bs, int st) {
+    const int k0 = k_begin + st * TG_K;
+    const bool ok = k0 < k_end;
+    // A: TA moves down rows (k0 rows of d floats), else along the row (k0 floats)
+    const uint32_t ask = TA ? (uint32_t)k0 * d * 4 : (uint32_t)k0 * 4;
+    const uint32_t bsk = (uint32_t)k0 * d * 4;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(as + 1024 * (2 * wave + j)), 16,
+                                               ok ? aoff[j] + ask : 0x80000000u, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(bs + 1024 * (2 * wave + j)), 16,
+                                               ok ? boff[j] + bsk : 0x80000000u, 0, 0, 0);
+    }
+  };
+  auto aslot = [&](auto J) -> char* {
+    constexpr int j = decltype(J)::value;
+    if constexpr (j == 0) return a0;
+    else if constexpr (j == 1) return a1;
+    else if constexpr (j == 2) return a2;
+    else return a3;
+  };
+  auto bslot = [&](auto J) -> char* {
+    constexpr int j = decltype(J)::value;
+    if constexpr (j == 0) return b0;
+    else if constexpr (j == 1) return b1;
+    else if constexpr (j == 2) return b2;
+    else return b3;
+  };
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const int am = 32 * wm + l32, bnn = 32 * wn + l32;
+  issue(a0, b0, 0);
+  issue(a1, b1, 1);
+  issue(a2, b2, 2);
+  // Stage s (slot J = s % 4): wait for its loads, barrier, refill slot (s - 1) % 4 with stage s + 3,
+  // then 16 MFMAs.  Sub-stage u (k0 + 8u .. + 7): lane half h takes k = k0 + 8u + 4h + v, v = 0..3.
+  auto step = [&](auto J, int s) {
+    constexpr int j = decltype(J)::value;
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(8));
+    barrier();
+    issue(aslot(std::integral_constant<int, (j + 3) % 4>{}), bslot(std::integral_constant<int, (j + 3) % 4>{}), s + 3);
+    const char* as = aslot(J);
+    const char* bs = bslot(J);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float av[4];
+      if (TA) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) av[v] = *(const float*)(as + (8 * u + 4 * hi + v) * 256 + 4 * am);
+      } else {
+        const int c = 2 * u + hi;
+        const f32x4 x = *(const f32x4*)(as + am * 128 + 16 * (c ^ (am & 7)));
+        av[0] = x[0]; av[1] = x[1]; av[2] = x[2]; av[3] = x[3];
       }
-      if (!g.transB) {                           // B[k][n]: vector along n
-        const int kk = e >> 4, n = (e & 15) * 4;
-        const int gn = n0 + n, gk = k0 + kk;
-        rb[h] = (gn < g.N && gk < k_end) ? *(const f32x4*)(g.B + (int64_t)gk * g.ldb + gn) : z4;
-      } else {                                   // B[n][k]: vector along k
-        const int n = e >> 3, kk = (e & 7) * 4;
-        const int gn = n0 + n, gk = k0 + kk;
-        rb[h] = (gn < g.N && gk < k_end) ? *(const f32x4*)(g.B + (int64_t)gn * g.ldb + gk) : z4;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float bv = *(const float*)(bs + (8 * u + 4 * hi + v) * 256 + 4 * bnn);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[v], bv, acc, 0, 0, 0);
       }
     }
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int e = tid + NT * h;
-      if (!g.transA) {
-        const int m = e >> 3, kk = (e & 7) * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) As[buf][kk + j][m] = ra[h][j];
-      } else {
-        const int kk = e >> 4, m = (e & 15) * 4;
-        *(f32x4*)&As[buf][kk][m] = ra[h];
-      }
-      if (!g.transB) {
-        const int kk = e >> 4, n = (e & 15) * 4;
-        *(f32x4*)&Bs[buf][kk][n] = rb[h];
-      } else {
-        const int n = e >> 3, kk = (e & 7) * 4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Bs[buf][kk + j][n] = rb[h][j];
-      }
-    }
-  };
-  if (k_begin < k_end) {
-    gload(k_begin);
-    sstore(0);
-    __syncthreads();
-    int buf = 0;
-    for (int k0 = k_begin; k0 < k_end; k0 += TK) {
-      const bool nxt = k0 + TK < k_end;
-      if (nxt) gload(k0 + TK);
-#pragma unroll
-      for (int s = 0; s < TK / 2; ++s) {
-        const float a = As[buf][2 * s + (lane >> 5)][32 * wm + (lane & 31)];
-        const float bb = Bs[buf][2 * s + (lane >> 5)][32 * wn + (lane & 31)];
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bb, acc, 0, 0, 0);
-      }
-      if (nxt) sstore(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
-    }
+  for (int s = 0; s < n_st; s += TG_RING) {
+    step(std::integral_constant<int, 0>{}, s);
+    step(std::integral_constant<int, 1>{}, s + 1);
+    step(std::integral_constant<int, 2>{}, s + 2);
+    step(std::integral_constant<int, 3>{}, s + 3);
   }
-  const int col = n0 + 32 * wn + (lane & 31);
-  if (col >= g.N) return;
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));   // loads past the last stage (zeros) have landed
+  const int col = n0 + 32 * wn + l32;
+  if (col >= d) return;
+  float* cb = g.C + (int64_t)(m0 + 32 * wm + 4 * hi) * d + col;
+  const int rows = d - (m0 + 32 * wm + 4 * hi);
+  if (g.beta == 0.f) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = m0 + 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    if (row >= g.M) continue;
-    float* c = g.C + (int64_t)row * g.ldc + col;
-    *c = g.beta == 0.f ? g.alpha * acc[r] : fmaf(g.alpha, acc[r], g.beta * *c);
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + (r & 3);
+      if (row < rows) cb[(int64_t)row * d] = g.alpha * acc[r];
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + (r & 3);
+      if (row < rows) cb[(int64_t)row * d] = fmaf(g.alpha, acc[r], g.beta * cb[(int64_t)row * d]);
+    }
   }
 }
 
-hipError_t run_gemms(const Gemm* gs, int count, hipStream_t s) {
-  GemmBatch b;
-  b.count = count;
-  int total = 0;
-  for (int i = 0; i < count; ++i) {
-    b.g[i] = gs[i];
-    const int tm = (gs[i].M + TB - 1) / TB, tn = (gs[i].N + TB - 1) / TB;
-    b.tiles_n[i] = tn;
-    b.tile_start[i] = total;
-    total += (gs[i].M > 0 && gs[i].N > 0) ? tm * tn : 0;
-  }
-  b.tile_start[count] = total;
-  if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_f32_kernel, dim3(total), dim3(NT), 0, s, b);
-  return hipGetLastError();
-}
-
-Gemm mk(const float* A, int64_t lda, int transA, const float* B, int64_t ldb, int transB, float* C, int64_t ldc, int M,
-        int N, int K, float alpha, float beta, int kmode = 0, int lower_only = 0) {
-  Gemm g;
+// C = alpha op(L) B + beta C with L = A lower triangular (op = identity or transpose)
+hipError_t run_trgemm(bool transA, const float* A, const float* B, float* C, int d, float alpha, float beta,
+                      hipStream_t s) {
+  TrGemm g;
   g.A = A; g.B = B; g.C = C;
-  g.lda = lda; g.ldb = ldb; g.ldc = ldc;
-  g.M = M; g.N = N; g.K = K;
-  g.transA = transA; g.transB = transB;
-  g.kmode = kmode; g.lower_only = lower_only;
+  g.d = d;
+  g.tiles = (d + TG_TILE - 1) / TG_TILE;
   g.alpha = alpha; g.beta = beta;
-  return g;
+  const dim3 grid(g.tiles * g.tiles);
+  if (transA) hipLaunchKernelGGL(trgemm_kernel<true>, grid, dim3(NT), 0, s, g);
+  else hipLaunchKernelGGL(trgemm_kernel<false>, grid, dim3(NT), 0, s, g);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------------------
@@ -643,7 +658,6 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
   ISPA_TRY(hipGetLastError());
 
   // Cholesky sweep (one launch per panel, plus one that finishes the last two block rows of L^-1)
-  const int64_t ldb = d;
   {
     const int nP = (d + NB - 1) / NB;
     // R = C W and (for epsilon) P = W W^T ride along, split into three K ranges spread over the
@@ -691,15 +705,9 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
     }
   }
   // Z = L^-1 R (L^-1 lower triangular: only k < m0 + 64 contributes), into Mx (no longer needed)
-  {
-    Gemm g = mk(w.Bx, ldb, 0, w.Rc, d, 0, w.Mx, d, d, d, d, 1.f, 0.f, 2);
-    ISPA_TRY(run_gemms(&g, 1, s));
-  }
+  ISPA_TRY(run_trgemm(false, w.Bx, w.Rc, w.Mx, d, 1.f, 0.f, s));
   // dW = (L^-1)^T Z   (op(A) upper triangular: only k >= m0 contributes)
-  {
-    Gemm g = mk(w.Bx, ldb, 1, w.Mx, d, 0, L.delta_w, d, d, d, d, 1.f, 0.f, 1);
-    ISPA_TRY(run_gemms(&g, 1, s));
-  }
+  ISPA_TRY(run_trgemm(true, w.Bx, w.Mx, L.delta_w, d, 1.f, 0.f, s));
   if (L.refine > 0) {
     // iterative refinement: r = C W - (G + lambda I) dW with fp64 accumulation (C W formed once in
     // fp64), then dW += (L^-1)^T (L^-1 r) with the fp32 factor
@@ -710,10 +718,8 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
       hipLaunchKernelGGL(gemm64_kernel<1>, dim3(tpd * tpd), dim3(NT), 0, s, L.G, L.delta_w, d, w.sc, w.R64, w.Rs);
       ISPA_TRY(hipGetLastError());
       // t = L^-1 r (into Mx, no longer needed), dW += (L^-1)^T t
-      Gemm g1 = mk(w.Bx, ldb, 0, w.Rs, d, 0, w.Mx, d, d, d, d, 1.f, 0.f, 2);
-      ISPA_TRY(run_gemms(&g1, 1, s));
-      Gemm g2 = mk(w.Bx, ldb, 1, w.Mx, d, 0, L.delta_w, d, d, d, d, 1.f, 1.f, 1);
-      ISPA_TRY(run_gemms(&g2, 1, s));
+      ISPA_TRY(run_trgemm(false, w.Bx, w.Rs, w.Mx, d, 1.f, 0.f, s));
+      ISPA_TRY(run_trgemm(true, w.Bx, w.Mx, L.delta_w, d, 1.f, 1.f, s));
     }
   }
   if (L.eps) {
