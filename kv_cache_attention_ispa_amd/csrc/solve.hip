@@ -51,7 +51,20 @@ struct TrGemm {
   float* C;
   int d, tiles;   // tiles per dimension
   float alpha, beta;
+  const void* W;  // optional fold: Wn = W + C (final value), in dtype wdt
+  void* Wn;
+  int wdt;
 };
+
+// Wn[e] = W[e] + v, rounded to nearest in W's dtype
+__device__ __forceinline__ void fold_store(const TrGemm& g, int64_t e, float v) {
+  if (g.wdt == DT_BF16)
+    ((uint16_t*)g.Wn)[e] = Cvt<BF16>::from_f(Cvt<BF16>::to_f(((const uint16_t*)g.W)[e]) + v);
+  else if (g.wdt == DT_F16)
+    ((uint16_t*)g.Wn)[e] = Cvt<F16>::from_f(Cvt<F16>::to_f(((const uint16_t*)g.W)[e]) + v);
+  else
+    ((float*)g.Wn)[e] = ((const float*)g.W)[e] + v;
+}
 
 template <bool TA>
 __global__ __launch_bounds__(NT, 2) void trgemm_kernel(TrGemm g) {
@@ -161,27 +174,25 @@ __global__ __launch_bounds__(NT, 2) void trgemm_kernel(TrGemm g) {
   __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));   // loads past the last stage (zeros) have landed
   const int col = n0 + 32 * wn + l32;
   if (col >= d) return;
-  float* cb = g.C + (int64_t)(m0 + 32 * wm + 4 * hi) * d + col;
+  const int64_t e0 = (int64_t)(m0 + 32 * wm + 4 * hi) * d + col;
+  float* cb = g.C + e0;
   const int rows = d - (m0 + 32 * wm + 4 * hi);
-  if (g.beta == 0.f) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 8 * (r >> 2) + (r & 3);
-      if (row < rows) cb[(int64_t)row * d] = g.alpha * acc[r];
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 8 * (r >> 2) + (r & 3);
-      if (row < rows) cb[(int64_t)row * d] = fmaf(g.alpha, acc[r], g.beta * cb[(int64_t)row * d]);
+  for (int r = 0; r < 16; ++r) {
+    const int row = 8 * (r >> 2) + (r & 3);
+    if (row < rows) {
+      const float v = g.beta == 0.f ? g.alpha * acc[r] : fmaf(g.alpha, acc[r], g.beta * cb[(int64_t)row * d]);
+      cb[(int64_t)row * d] = v;
+      if (g.Wn) fold_store(g, e0 + (int64_t)row * d, v);
     }
   }
 }
 
 // C = alpha op(L) B + beta C with L = A lower triangular (op = identity or transpose)
 hipError_t run_trgemm(bool transA, const float* A, const float* B, float* C, int d, float alpha, float beta,
-                      hipStream_t s) {
+                      hipStream_t s, const void* W = nullptr, void* Wn = nullptr, int wdt = 0) {
   TrGemm g;
+  g.W = W; g.Wn = Wn; g.wdt = wdt;
   g.A = A; g.B = B; g.C = C;
   g.d = d;
   g.tiles = (d + TG_TILE - 1) / TG_TILE;
@@ -201,35 +212,15 @@ struct Scalars {
   double dots[8];
 };
 
-// lambda (absolute or lambda * tr(G) / d), info = 0.
-__global__ __launch_bounds__(NT) void lambda_kernel(const float* G, int d, float lam, int relative, Scalars* sc,
-                                                    float* lambda_out, int* info) {
-  __shared__ double part[NT];
-  double s = 0.0;
-  for (int i = threadIdx.x; i < d; i += NT) s += (double)G[(int64_t)i * d + i];
-  part[threadIdx.x] = s;
-  __syncthreads();
-  for (int o = NT / 2; o > 0; o >>= 1) {
-    if ((int)threadIdx.x < o) part[threadIdx.x] += part[threadIdx.x + o];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    const float l = relative ? (float)((double)lam * part[0] / (double)d) : lam;
-    sc->lambda = l;
-    if (lambda_out) *lambda_out = l;
-    *info = 0;
-  }
-}
-
-// Mx = G + lambda I; Bx = I (becomes L^-1); Wf = W as fp32.
+// Mx = G (lambda joins the diagonal blocks as the sweep factors them); Bx = I (becomes L^-1);
+// Wf = W as fp32.
 template <typename WT>
-__global__ __launch_bounds__(NT) void setup_kernel(const float* G, const typename WT::storage* W, int d,
-                                                   const Scalars* sc, float* Mx, float* Bx, float* Wf) {
+__global__ __launch_bounds__(NT) void setup_kernel(const float* G, const typename WT::storage* W, int d, float* Mx,
+                                                   float* Bx, float* Wf) {
   const int64_t n = (int64_t)d * d;
-  const float lam = sc->lambda;
   for (int64_t e = blockIdx.x * (int64_t)NT + threadIdx.x; e < n; e += (int64_t)gridDim.x * NT) {
     const int i = (int)(e / d), j = (int)(e % d);
-    Mx[e] = G[e] + (i == j ? lam : 0.f);
+    Mx[e] = G[e];
     Bx[e] = (i == j) ? 1.f : 0.f;
     Wf[e] = Cvt<WT>::to_f(W[e]);
   }
@@ -267,6 +258,13 @@ struct SweepArgs {
   float* R;
   float* P;
   int n_fill, fill0, kb0, kb1;
+  // lambda (absolute, or lam * tr(G) / d): set by the first launch's diagonal work-group (which
+  // also clears *info) in sc, and added to each diagonal block as it is factored
+  Scalars* sc;
+  const float* G;
+  float lam;
+  int relative;
+  float* lambda_out;
 };
 
 // 64 x 64 block (row block rb, column block cb) of a d x d row-major matrix into LDS, zeros outside.
@@ -419,6 +417,29 @@ __global__ __launch_bounds__(SW_THREADS) void sweep_kernel(SweepArgs a) {
       }
       __syncthreads();
       const int nb = min(NB, d - k * NB);
+      if (k == 0) {
+        // tr(G) in fp64 over the 16 waves, then lambda; info starts at 0
+        double t = 0.0;
+        for (int i = threadIdx.x; i < d; i += SW_THREADS) t += (double)a.G[(int64_t)i * d + i];
+        for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
+        double* red = (double*)&L4[0][0];
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = t;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          double tr = 0.0;
+          for (int w2 = 0; w2 < SW_THREADS / 64; ++w2) tr += red[w2];
+          const float l = a.relative ? (float)((double)a.lam * tr / (double)d) : a.lam;
+          a.sc->lambda = l;
+          if (a.lambda_out) *a.lambda_out = l;
+          *a.info = 0;
+          red[0] = l;
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < nb) L1[threadIdx.x][threadIdx.x] += (float)red[0];   // G + lambda I
+      } else {
+        if ((int)threadIdx.x < nb) L1[threadIdx.x][threadIdx.x] += a.sc->lambda;  // G + lambda I
+      }
+      __syncthreads();
       sw_factor(L1, curb, pivs, nb, k * NB, a.Tb + (k % 3) * NB * NB, a.info);
       return;
     }
@@ -543,7 +564,7 @@ __global__ __launch_bounds__(NT) void gemm64_kernel(const float* A, const float*
     }
 }
 
-// Partial dot products for epsilon: <D,P>, <G,P>, <W,R>, <dW,R>, <dW,dW>.
+// Partial dot products for epsilon: <D,P>, <G,P>, <W,R>, <dW,R>, <dW,dW> (fp64 per block).
 __global__ __launch_bounds__(NT) void dots_kernel(const float* D, const float* G, const float* P, const float* Wf,
                                                   const float* R, const float* dW, int64_t n, double* part) {
   double s[5] = {0, 0, 0, 0, 0};
@@ -566,6 +587,8 @@ __global__ __launch_bounds__(NT) void dots_kernel(const float* D, const float* G
   if (threadIdx.x < 5) part[blockIdx.x * 5 + threadIdx.x] = red[threadIdx.x][0];
 }
 
+// eps = sqrt(max(<D,P> - <dW,R> - lambda <dW,dW>, 0) / (<G,P> + 2 <W,R> + <D,P>)), partials added
+// in block order
 __global__ __launch_bounds__(NT) void eps_kernel(const double* part, int nblk, const Scalars* sc, float* eps) {
   __shared__ double red[5][NT];
   double t[5] = {0, 0, 0, 0, 0};
@@ -584,13 +607,6 @@ __global__ __launch_bounds__(NT) void eps_kernel(const double* part, int nblk, c
     const double den2 = red[1][0] + 2.0 * red[2][0] + red[0][0];
     *eps = (float)sqrt((num2 > 0.0 ? num2 : 0.0) / den2);
   }
-}
-
-template <typename WT>
-__global__ __launch_bounds__(NT) void fold_kernel(const typename WT::storage* W, const float* dW, int64_t n,
-                                                  typename WT::storage* out) {
-  for (int64_t e = blockIdx.x * (int64_t)NT + threadIdx.x; e < n; e += (int64_t)gridDim.x * NT)
-    out[e] = Cvt<WT>::from_f(Cvt<WT>::to_f(W[e]) + dW[e]);
 }
 
 constexpr int DOT_BLOCKS = 512;
@@ -644,17 +660,12 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
   const int64_t dd = (int64_t)d * d;
   const int eb = (int)((dd + NT - 1) / NT > 2048 ? 2048 : (dd + NT - 1) / NT);
 
-  hipLaunchKernelGGL(lambda_kernel, dim3(1), dim3(NT), 0, s, L.G, d, L.lambda, L.lambda_relative, w.sc, L.lambda_out,
-                     L.info);
-  ISPA_TRY(hipGetLastError());
   if (L.w_dtype == DT_BF16)
-    hipLaunchKernelGGL(setup_kernel<BF16>, dim3(eb), dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, w.sc, w.Mx, w.Bx,
-                       w.Wf);
+    hipLaunchKernelGGL(setup_kernel<BF16>, dim3(eb), dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, w.Mx, w.Bx, w.Wf);
   else if (L.w_dtype == DT_F16)
-    hipLaunchKernelGGL(setup_kernel<F16>, dim3(eb), dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, w.sc, w.Mx, w.Bx,
-                       w.Wf);
+    hipLaunchKernelGGL(setup_kernel<F16>, dim3(eb), dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, w.Mx, w.Bx, w.Wf);
   else
-    hipLaunchKernelGGL(setup_kernel<F32>, dim3(eb), dim3(NT), 0, s, L.G, (const float*)L.W, d, w.sc, w.Mx, w.Bx, w.Wf);
+    hipLaunchKernelGGL(setup_kernel<F32>, dim3(eb), dim3(NT), 0, s, L.G, (const float*)L.W, d, w.Mx, w.Bx, w.Wf);
   ISPA_TRY(hipGetLastError());
 
   // Cholesky sweep (one launch per panel, plus one that finishes the last two block rows of L^-1)
@@ -691,6 +702,11 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
       const int first = (range * n_launch + n_range - 1) / n_range;   // first launch of this range
       const int next = ((range + 1) * n_launch + n_range - 1) / n_range;
       const int slot = k - first, n_slots = next - first;
+      a.sc = w.sc;
+      a.G = L.G;
+      a.lam = L.lambda;
+      a.relative = L.lambda_relative;
+      a.lambda_out = L.lambda_out;
       a.C = L.C;
       a.Wf = w.Wf;
       a.R = w.Rc;
@@ -707,7 +723,8 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
   // Z = L^-1 R (L^-1 lower triangular: only k < m0 + 64 contributes), into Mx (no longer needed)
   ISPA_TRY(run_trgemm(false, w.Bx, w.Rc, w.Mx, d, 1.f, 0.f, s));
   // dW = (L^-1)^T Z   (op(A) upper triangular: only k >= m0 contributes)
-  ISPA_TRY(run_trgemm(true, w.Bx, w.Mx, L.delta_w, d, 1.f, 0.f, s));
+  // (W_new = W + dW is written by the last product that updates dW)
+  ISPA_TRY(run_trgemm(true, w.Bx, w.Mx, L.delta_w, d, 1.f, 0.f, s, L.W, L.refine > 0 ? nullptr : L.w_new, L.w_dtype));
   if (L.refine > 0) {
     // iterative refinement: r = C W - (G + lambda I) dW with fp64 accumulation (C W formed once in
     // fp64), then dW += (L^-1)^T (L^-1 r) with the fp32 factor
@@ -719,24 +736,14 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
       ISPA_TRY(hipGetLastError());
       // t = L^-1 r (into Mx, no longer needed), dW += (L^-1)^T t
       ISPA_TRY(run_trgemm(false, w.Bx, w.Rs, w.Mx, d, 1.f, 0.f, s));
-      ISPA_TRY(run_trgemm(true, w.Bx, w.Mx, L.delta_w, d, 1.f, 1.f, s));
+      ISPA_TRY(run_trgemm(true, w.Bx, w.Mx, L.delta_w, d, 1.f, 1.f, s, L.W, it + 1 == L.refine ? L.w_new : nullptr,
+                          L.w_dtype));
     }
   }
   if (L.eps) {
     hipLaunchKernelGGL(dots_kernel, dim3(DOT_BLOCKS), dim3(NT), 0, s, L.D, L.G, w.P, w.Wf, w.Rc, L.delta_w, dd, w.part);
     ISPA_TRY(hipGetLastError());
     hipLaunchKernelGGL(eps_kernel, dim3(1), dim3(NT), 0, s, w.part, DOT_BLOCKS, w.sc, L.eps);
-    ISPA_TRY(hipGetLastError());
-  }
-  if (L.w_new) {
-    if (L.w_dtype == DT_BF16)
-      hipLaunchKernelGGL(fold_kernel<BF16>, dim3(eb), dim3(NT), 0, s, (const uint16_t*)L.W, L.delta_w, dd,
-                         (uint16_t*)L.w_new);
-    else if (L.w_dtype == DT_F16)
-      hipLaunchKernelGGL(fold_kernel<F16>, dim3(eb), dim3(NT), 0, s, (const uint16_t*)L.W, L.delta_w, dd,
-                         (uint16_t*)L.w_new);
-    else
-      hipLaunchKernelGGL(fold_kernel<F32>, dim3(eb), dim3(NT), 0, s, (const float*)L.W, L.delta_w, dd, (float*)L.w_new);
     ISPA_TRY(hipGetLastError());
   }
   return hipSuccess;
