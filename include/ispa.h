@@ -129,7 +129,9 @@ int ispa_dual_attn(const ispa_attn_shape* shape, int io_dtype,
  *                        columns [0, n) are the tokens; ld >= n, ld % 8 == 0.
  *   G, C, D            : [d, d] fp32 row-major.  accumulate = 0 overwrites,
  *                        1 adds.  G and D are symmetric and written in full.
- *   D may be NULL.  d % 32 == 0 and d <= 16384; n >= 1.
+ *   D may be NULL.  d % 32 == 0 and d <= 16384; n >= 1.  16-bit statistics are
+ *   read in 128-row slices with 32-bit byte offsets: 256 * ld must stay below
+ *   2^31 (EUNSUPPORTED).
  */
 int ispa_gram_accum(int d, int n, int stat_dtype, const void* a_loc_t, const void* delta_a_t, int64_t ld,
                     int accumulate, float* G, float* C, float* D, void* stream);
