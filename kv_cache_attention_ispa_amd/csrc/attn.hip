@@ -55,7 +55,7 @@ constexpr int WAVES = 8;
 constexpr int MFMA_THREADS = WAVES * 64;
 constexpr int BM = WAVES * 32;   // queries per work-group of the MFMA path
 constexpr int NTHREADS = 256;    // fp32 path
-constexpr float kRescaleSlack = 8.f;   // log2 units: probabilities stay below 2^8 between rescales
+constexpr float kLazyLimit = 8192.f;   // 2^13: a lane's partial row sum that triggers a rescale
 // LDS tiles are row-major with padded pitches: every MFMA operand read is a per-lane base address
 // plus an immediate offset, and 16 consecutive lanes of a 16-byte read hit 16 distinct 4-bank groups.
 // K tiles are 64 key rows x 128 head dims; V tiles are transposed: 128 head-dim rows x 64 keys.
@@ -271,17 +271,47 @@ __device__ __forceinline__ void softmax_phase(f32x16 (&s)[2], int valid, float s
         if (key >= valid) s[kt][r] = -INFINITY;
       }
   }
-  float mx = -INFINITY;
+  // probabilities against a reference max (packed as the PV operand) and this lane's partial row sum
+  auto probs = [&](float m_ref) -> float {
+    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-  mx = max_xor32(mx) * scale_log2;
-  // The reference max only moves when this tile's max exceeds it by more than kRescaleSlack (then O
-  // and the row sum are rescaled, for the whole wave at once); otherwise the probabilities are taken
-  // against the stale reference and stay below 2^kRescaleSlack.  The final normalisation uses the
-  // same reference, so this is exact.
-  if (__builtin_amdgcn_ballot_w64(mx > st.m + kRescaleSlack) != 0) {
+      for (int u = 0; u < 2; ++u) {
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * u + j], scale_log2, -m_ref));
+        const u32x4 w = u32x4{pack2<TP>(e[0], e[1]), pack2<TP>(e[2], e[3]), pack2<TP>(e[4], e[5]), pack2<TP>(e[6], e[7])};
+        pf[kt][u] = w;
+        if (std::is_same<TP, F16>::value) {
+          // fp16 probabilities: add the rounded values the PV product consumes (relative rounding
+          // 2^-12 each, well inside the LSE tolerance), four packed dot products with (1, 1)
+          rs0 = add_f16_pair(w[0], rs0);
+          rs1 = add_f16_pair(w[1], rs1);
+          rs0 = add_f16_pair(w[2], rs0);
+          rs1 = add_f16_pair(w[3], rs1);
+        } else {
+          // bf16 rounding (2^-9) would show in the LSE: add the fp32 values
+          rs0 += (e[0] + e[1]) + (e[2] + e[3]);
+          rs1 += (e[4] + e[5]) + (e[6] + e[7]);
+        }
+      }
+    return rs0 + rs1;
+  };
+  // The reference max is not recomputed per tile: the probabilities are taken against the running
+  // reference, and only when a lane's partial sum exceeds 2^kLazyLog2 (some probability would, or
+  // overflowed, or the reference is still -inf) does the tile compute its max, move the reference
+  // (O and the row sum rescaled, for the whole wave at once) and redo its probabilities.  Between
+  // rescales every probability stays below 2^kLazyLog2, well inside fp16.  The final normalisation
+  // uses the same reference, so this is exact.
+  float rs = probs(st.m);
+  if (__builtin_amdgcn_ballot_w64(!(rs <= kLazyLimit)) != 0) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+    mx = max_xor32(mx) * scale_log2;
     const float m_new = fmaxf(st.m, mx);
     const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
     st.m = m_new;
@@ -290,32 +320,9 @@ __device__ __forceinline__ void softmax_phase(f32x16 (&s)[2], int valid, float s
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.o[tt][r] *= alpha;
+    rs = probs(m_new);
   }
-  const float m_ref = st.m;
-  float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      float e[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * u + j], scale_log2, -m_ref));
-      const u32x4 w = u32x4{pack2<TP>(e[0], e[1]), pack2<TP>(e[2], e[3]), pack2<TP>(e[4], e[5]), pack2<TP>(e[6], e[7])};
-      pf[kt][u] = w;
-      if (std::is_same<TP, F16>::value) {
-        // fp16 probabilities: add the rounded values the PV product consumes (relative rounding
-        // 2^-12 each, well inside the LSE tolerance), four packed dot products with (1, 1)
-        rs0 = add_f16_pair(w[0], rs0);
-        rs1 = add_f16_pair(w[1], rs1);
-        rs0 = add_f16_pair(w[2], rs0);
-        rs1 = add_f16_pair(w[3], rs1);
-      } else {
-        // bf16 rounding (2^-9) would show in the LSE: add the fp32 values
-        rs0 += (e[0] + e[1]) + (e[2] + e[3]);
-        rs1 += (e[4] + e[5]) + (e[6] + e[7]);
-      }
-    }
-  st.lsum += rs0 + rs1;
+  st.lsum += rs;
 }
 
 // The local-branch output O_L of a wave, parked in the workspace while the history branch runs
