@@ -24,14 +24,14 @@ constexpr int NT = 256;
 
 // ------------------------------------------------------------------------------------------
 // 16-bit Gram: out (+)= X Y^T, X/Y [d, ld] (rows = features), tokens [0, n).
-// A work item is a 256 x 128 output tile (256 rows of X against 128 rows of Y), 4 waves as 2 x 2
-// of 128 x 64.  G and D are symmetric: only tiles that meet the lower triangle run, each 128 x 128
-// block strictly below the diagonal is also stored transposed, and blocks above it are dropped.
-// Tokens stream through a 3-deep LDS ring of 64-token stages (128 bytes of every row: a load
-// instruction fetches whole 128-byte lines of 8 rows, which is what lets L2 feed a CU at ~45-60
-// B/clk; 64-byte pieces of 16 rows get half that), filled by direct-to-LDS buffer loads issued two
-// stages ahead.  At the full MFMA rate a CU takes 48 B/clk of operands from L2 and reads 96 B/clk
-// of LDS.
+// A work item is a 256 x 128 output tile (256 rows of X against 128 rows of Y): 8 multiplying
+// waves as 4 x 2 of 64 x 64 and 4 loading waves.  G and D are symmetric: only tiles that meet the
+// lower triangle run, each 128 x 128 block strictly below the diagonal is also stored transposed,
+// and blocks above it are dropped.  Tokens stream through a 3-deep LDS ring of 64-token stages
+// (128 bytes of every row: a load instruction fetches whole 128-byte lines of 8 rows, which is what
+// lets L2 feed a CU at ~45-60 B/clk; 64-byte pieces of 16 rows get half that), filled by
+// direct-to-LDS buffer loads issued two stages ahead.  At the full MFMA rate a CU takes 48 B/clk of
+// operands from L2 and reads 128 B/clk of LDS.
 // ------------------------------------------------------------------------------------------
 constexpr int GB = 128;
 constexpr int GK = 32;                      // (projection below)
@@ -79,7 +79,7 @@ __device__ __forceinline__ void gram_item(const GramArgs& a, int q, int& z, int&
 }
 
 template <typename T>
-__global__ __launch_bounds__(2 * NT) void gram16_kernel(GramArgs a) {
+__global__ __launch_bounds__(3 * NT) void gram16_kernel(GramArgs a) {
   __shared__ __attribute__((aligned(16))) char x0[R_XTILE], x1[R_XTILE], x2[R_XTILE];
   __shared__ __attribute__((aligned(16))) char y0[R_YTILE], y1[R_YTILE], y2[R_YTILE];
   int z, bi, bj;
@@ -108,13 +108,13 @@ __global__ __launch_bounds__(2 * NT) void gram16_kernel(GramArgs a) {
   const int n_steps = (a.n + RK - 1) / RK;
   const int tail_step = (a.n & 7) ? (a.n - 1) / RK : -1;   // stage holding a partly valid chunk
 
-  // Waves 4-7 load, waves 0-3 multiply.  A wave that issues a burst of direct-to-LDS loads waits at
+  // Waves 8-11 load, waves 0-7 multiply.  A wave that issues a burst of direct-to-LDS loads waits at
   // issue until the CU's load path has taken them, so loads and MFMAs belong to different waves.
   // One barrier per stage: at barrier s, stage s is in LDS and the multipliers are done with stage
   // s - 1; then the multipliers run stage s while the loaders refill slot (s - 1) % 3 with stage
   // s + 2 and wait for stage s + 1.
-  if (wave >= 4) {
-    const int w = wave - 4;
+  if (wave >= 8) {
+    const int w = wave - 8;
     // raw buffers over the tile's rows of X and of Y (rows past d fall outside: zeros)
     const int64_t row_bytes = a.ld * 2;
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(2 * NT) void gram16_kernel(GramArgs a) {
     };
     // zero tokens n .. of the chunk that straddles n (X rows: loader threads 0-255, Y rows: 0-127)
     auto fix_tail = [&](char* xs, char* ys, int step) {
-      const int t = tid - 2 * GB, t0 = step * RK, c = (a.n - t0) >> 3, e0 = (a.n - t0) & 7;
+      const int t = tid - 4 * GB, t0 = step * RK, c = (a.n - t0) >> 3, e0 = (a.n - t0) & 7;
       char* bx = xs + r_off(t, c);
       char* by = ys + r_off(t & (GB - 1), c);
       for (int e = e0; e < 8; ++e) {
@@ -186,28 +186,28 @@ __global__ __launch_bounds__(2 * NT) void gram16_kernel(GramArgs a) {
   }
 
   const int wm = wave >> 1, wn = wave & 1;
-  f32x16 acc[4][2];
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-  // per-lane read offsets: A fragment m = X rows 128 wm + 32 m + l % 32, B fragment m = Y rows
+  // per-lane read offsets: A fragment m = X rows 64 wm + 32 m + l % 32, B fragment m = Y rows
   // 64 wn + 32 m + l % 32, chunk 2 kk + l / 32.  The swizzle term depends on the row only through
   // bits 1-3, the same for rows r and r + 32 m, and chunk 2 kk + h = h ^ 2 kk: offset(kk) = offset(0) ^ 32 kk.
-  const int aoff = r_off(128 * wm + (lane & 31), hi);
+  const int aoff = r_off(64 * wm + (lane & 31), hi);
   const int boff = r_off(64 * wn + (lane & 31), hi);
   barrier();
   // fragments of k-step kk + 1 are read while the MFMAs of k-step kk run
   auto mstep = [&](auto J) {   // between barriers s and s + 1 (J = s % 3)
     const char* xs = xslot(J);
     const char* ys = yslot(J);
-    u32x4 af[2][4], bf[2][2];
+    u32x4 af[2][2], bf[2][2];
     auto frags = [&](int kk, u32x4* fa, u32x4* fb) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) fa[m] = *(const u32x4*)(xs + (aoff ^ (kk << 5)) + 32 * m * R_ROW);
+      for (int m = 0; m < 2; ++m) fa[m] = *(const u32x4*)(xs + (aoff ^ (kk << 5)) + 32 * m * R_ROW);
 #pragma unroll
       for (int m = 0; m < 2; ++m) fb[m] = *(const u32x4*)(ys + (boff ^ (kk << 5)) + 32 * m * R_ROW);
     };
@@ -216,16 +216,16 @@ __global__ __launch_bounds__(2 * NT) void gram16_kernel(GramArgs a) {
     for (int kk = 0; kk < RK / 16; ++kk) {
       if (kk + 1 < RK / 16) frags(kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = mfma32x32x16<T>(af[kk & 1][mi], bf[kk & 1][ni], acc[mi][ni]);
     }
     // order for the scheduler: reads(0) reads(1) mfma(0) reads(2) mfma(1) reads(3) mfma(2) mfma(3)
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int kk = 0; kk < RK / 16; ++kk) {
-      if (kk + 1 < RK / 16) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      if (kk + 1 < RK / 16) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
     barrier();
   };
@@ -237,19 +237,19 @@ __global__ __launch_bounds__(2 * NT) void gram16_kernel(GramArgs a) {
   }
   barrier();                                   // the ring is idle
 
-  // this wave's 128 x 64 block lies in the 128 x 128 block (rb, bj), rb = 2 bi + wm
-  const int rb = 2 * bi + wm;
+  // this wave's 64 x 64 block lies in the 128 x 128 block (rb, bj), rb = 2 bi + wm / 2
+  const int rb = 2 * bi + (wm >> 1);
   if (z != 1 && rb < bj) return;                // above the diagonal of G or D
   const bool mirror = z != 1 && rb > bj;
   float* out = a.out[z];
   // transposed copies go through this wave's 4.5 KiB of the (now idle) ring
-  float* tb = (float*)(x0 + wave * (G_TPITCH * 32 * 4));
+  float* tb = (float*)((wave < 4 ? x0 : x1) + (wave & 3) * (G_TPITCH * 32 * 4));
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
       const int col = j0 + 64 * wn + 32 * ni + (lane & 31);
-      const int rowb = i0 + 128 * wm + 32 * mi;
+      const int rowb = i0 + 64 * wm + 32 * mi;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = rowb + 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -450,9 +450,9 @@ hipError_t launch_gram(const GramLaunch& L, hipStream_t s) {
     int items = 0;
     for (int b = 0; b < a.rb; ++b) items += a.cb + a.n_sym * std::min(2 * b + 2, a.cb);
     if (L.stat == DT_BF16)
-      hipLaunchKernelGGL(gram16_kernel<BF16>, dim3(items), dim3(2 * NT), 0, s, a);
+      hipLaunchKernelGGL(gram16_kernel<BF16>, dim3(items), dim3(3 * NT), 0, s, a);
     else
-      hipLaunchKernelGGL(gram16_kernel<F16>, dim3(items), dim3(2 * NT), 0, s, a);
+      hipLaunchKernelGGL(gram16_kernel<F16>, dim3(items), dim3(3 * NT), 0, s, a);
   }
   return hipGetLastError();
 }
