@@ -241,6 +241,8 @@ __global__ __launch_bounds__(NT) void setup_kernel(const float* G, const typenam
 // MFMA 16x16x4 (fp32), one 16 x 16 quadrant per wave.
 // ------------------------------------------------------------------------------------------
 constexpr int SW_THREADS = 1024;
+constexpr int SW_FILL_RANGES = 6;   // K ranges of the R / P products (4 blocks each at d = 1536)
+static_assert(SW_THREADS >= 512, "the diagonal factorization uses 512 threads");
 constexpr int BP = NB + 4;   // LDS pitch of a 64 x 64 block: 16 rows of a wave hit 16 distinct 4-bank groups
 
 struct SweepArgs {
@@ -251,7 +253,7 @@ struct SweepArgs {
   int d, nP, k;
   int n_a, n_i, f_row0, f_rows;   // work items: A blocks, identity blocks, final rows [f_row0, +f_rows)
   // products that do not depend on the sweep ride along in its launches, one K range at a time:
-  // R = C W (always) and P = W W^T (for epsilon); this launch computes output blocks
+  // R = C W (always) and the lower block triangle of P = W W^T (for epsilon); this launch computes output blocks
   // [fill0, fill0 + n_fill) of K range [kb0, kb1) (in 64-blocks), added to earlier ranges when kb0 > 0
   const float* C;
   const float* Wf;
@@ -276,10 +278,31 @@ __device__ __forceinline__ void sw_load(float (*dst)[BP], const float* src, int 
   if (gr < d && gc < d) v = *(const f32x4*)(src + (int64_t)gr * d + gc);
   *(f32x4*)&dst[r][c] = v;
 }
+// The same block in two halves: this thread's 16 bytes from global memory, then into LDS.
+__device__ __forceinline__ f32x4 sw_gload(const float* src, int d, int rb, int cb) {
+  const int t = threadIdx.x;
+  const int gr = rb * NB + (t >> 4), gc = cb * NB + (t & 15) * 4;
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  if (gr < d && gc < d) v = *(const f32x4*)(src + (int64_t)gr * d + gc);
+  return v;
+}
+__device__ __forceinline__ void sw_lput(float (*dst)[BP], f32x4 v) {
+  const int t = threadIdx.x;
+  *(f32x4*)&dst[t >> 4][(t & 15) * 4] = v;
+}
 __device__ __forceinline__ void sw_load_t(float (*dst)[BP], const float* Tk) {
   const int t = threadIdx.x;
   const int r = t >> 4, c = (t & 15) * 4;
   *(f32x4*)&dst[r][c] = *(const f32x4*)(Tk + r * NB + c);
+}
+
+// p-th entry (row-major) of a lower triangle: row ii, column jj <= ii.
+__device__ __forceinline__ void tri_decode(int p, int& ii, int& jj) {
+  int r = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
+  while ((r + 1) * (r + 2) / 2 <= p) ++r;
+  while (r * (r + 1) / 2 > p) --r;
+  ii = r;
+  jj = p - r * (r + 1) / 2;
 }
 
 // Quadrant (wave / 4, wave % 4) of X op(Y) over k < 64 (op(Y) = Y^T when ty): 16x16x4 MFMA,
@@ -316,83 +339,117 @@ __device__ __forceinline__ void sw_store(float* C, int d, int rb, int cb, f32x4 
   }
 }
 
-// Factorization of the symmetric 64 x 64 block D (in LDS) = L L^T and T = L^-1, two columns per
-// barrier.  Thread t owns row i = t/16, columns 4 (t%16) .. +3 of D (symmetric: row j also holds
-// column j) and of U, which starts as I.  Step s handles columns j = 2s and j+1: rows j and j+1
-// (all earlier steps applied) are published (double-buffered, one barrier per step); every thread
-// forms, on its columns, row'_{j+1} = row_{j+1} - (a01 / p0) row_j (row j+1 after elimination with
-// row j; p0 = a_jj, a01 = a_{j,j+1}, pivot p1 = a_{j+1,j+1} - a01^2 / p0), and every row i > j+1
-// applies both eliminations, a_i -= f0 row_j + f1 row'_{j+1} with f0 = x0 / p0, f1 = (x1 - f0 a01) / p1,
-// x0, x1 = row i's entries in columns j, j+1 (by symmetry, rows j and j+1's entries in column i).
-// The same combination updates u_i: right-looking Cholesky and forward substitution in one sweep,
-// with the divisions by l_jj = sqrt(p_j) deferred: (L^-1)_i = u_i / sqrt(p_i).  Rows past nb (last
-// panel) hold the identity.  A non-positive pivot sets *info to its 1-based index (k0 + j + 1) and is
-// replaced by 1.
+// Factorization of the symmetric 64 x 64 block D (in LDS) = L L^T and T = L^-1 with 2 x 2 pivot
+// blocks, one barrier per pivot pair.  512 threads work: pair p = t/16 holds rows 2p and 2p+1 at
+// columns 4 (t%16) .. +3 of one combined row per matrix row (columns left of the current pivot hold
+// u_i, the row of U that accumulates the eliminations and starts as e_i; the others hold the Schur
+// complement), and in all 16 lanes its own diagonal block B_p = [[d00, d01], [d01, d11]].  Step s
+// publishes rows 2s, 2s+1 as they stand and B_s^-1; every row i of a later pair then takes
+// w_i -= [x0 x1] B_s^-1 [w_2s; w_2s+1] with x0, x1 the row's Schur entries in the pivot columns (read,
+// by symmetry, from the published rows), which zeroes those entries; they are set to the u values
+// -[x0 x1] B_s^-1 instead, and the pair's own block gets the same update.  At the end U D U^T is
+// block diagonal with blocks B_p, so T = C^-1 U with C = chol(B_p) per pair: row 2p is u_2p / sqrt(p0),
+// row 2p+1 is (u_2p+1 - g u_2p) / sqrt(p1) with p0 = d00, g = d01 / p0, p1 = d11 - g d01.  The
+// pivots p0, p1 are the scalar Cholesky pivots; a non-positive one sets *info to its 1-based index
+// (k0 + j + 1) and the block is then replaced by I (the results are undefined).  Rows past nb (last
+// panel) hold the identity.
 __device__ __forceinline__ void sw_factor(const float (*D)[BP], float (*curb)[2][2][NB], float* pivs, int nb, int k0,
                                           float* Tk, int* info) {
+  __shared__ __attribute__((aligned(16))) float binv[2][4];
   const int t = threadIdx.x;
-  const int i = t >> 4, c0 = (t & 15) * 4;
-  float ar[4], ur[4];
+  const bool act = t < 512;
+  const int p = (t >> 4) & 31, cg = t & 15, c0 = 4 * cg;
+  auto dv = [&](int i, int k) { return (i < nb && k < nb) ? D[i][k] : (i == k ? 1.f : 0.f); };
+  float w[2][4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int k = c0 + m;
-    ar[m] = (i < nb && k < nb) ? D[i][k] : (i == k ? 1.f : 0.f);
-    ur[m] = (i == k) ? 1.f : 0.f;
-  }
-  auto piv = [](float p) { return p > 0.f ? p : 1.f; };
-  for (int j = 0; j < NB; j += 2) {
-    float(*cur)[2][NB] = curb[(j >> 1) & 1];
-    const int q = i - j;   // 0: row j, 1: row j+1
-    if (q == 0 || q == 1) {
-      *(f32x4*)&cur[0][q][c0] = f32x4{ar[0], ar[1], ar[2], ar[3]};
-      *(f32x4*)&cur[1][q][c0] = f32x4{ur[0], ur[1], ur[2], ur[3]};
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[h][e] = dv(2 * p + h, c0 + e);
+  float d00 = dv(2 * p, 2 * p), d01 = dv(2 * p, 2 * p + 1), d11 = dv(2 * p + 1, 2 * p + 1);
+  float b00 = 0.f, b01 = 0.f, b11 = 0.f;
+  auto invert = [&]() {
+    const float det = fmaf(d00, d11, -d01 * d01);
+    const bool ok = d00 > 0.f && det > 0.f;
+    const float rd = __builtin_amdgcn_rcpf(ok ? det : 1.f);
+    b00 = ok ? d11 * rd : 1.f;
+    b01 = ok ? -d01 * rd : 0.f;
+    b11 = ok ? d00 * rd : 1.f;
+  };
+  if (act && p == 0) invert();
+  // step s; the pivot columns 2s, 2s+1 sit at positions m, m+1 of column group s/2
+  auto step = [&](auto parc, int s) {
+    constexpr int par = decltype(parc)::value, m = 2 * par;
+    float(*cur)[NB] = curb[par][0];
+    if (act && p == s) {
+      *(f32x4*)&cur[0][c0] = f32x4{w[0][0], w[0][1], w[0][2], w[0][3]};
+      *(f32x4*)&cur[1][c0] = f32x4{w[1][0], w[1][1], w[1][2], w[1][3]};
+      if (cg == 0) *(f32x4*)&binv[par][0] = f32x4{b00, b01, b11, 0.f};
     }
     __syncthreads();
-    if (i > j) {
-      const float p0 = piv(cur[0][0][j]);
-      const float a01 = cur[0][0][j + 1];
-      const float r0 = __builtin_amdgcn_rcpf(p0);
-      const float g = a01 * r0;   // row'_{j+1} = row_{j+1} - g row_j
-      const float p1raw = cur[0][1][j + 1] - g * a01;
-      const f32x4 a0 = *(const f32x4*)&cur[0][0][c0];
-      const f32x4 u0 = *(const f32x4*)&cur[1][0][c0];
-      if (q == 1) {
+    if (act && p > s) {
+      const f32x4 bv = *(const f32x4*)&binv[par][0];
+      const f32x4 P0 = *(const f32x4*)&cur[0][c0];
+      const f32x4 P1 = *(const f32x4*)&cur[1][c0];
+      const f32x2 X0 = *(const f32x2*)&cur[0][2 * p];
+      const f32x2 X1 = *(const f32x2*)&cur[1][2 * p];
+      float f0[2], f1[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ar[e] = fmaf(-g, a0[e], ar[e]);
-          ur[e] = fmaf(-g, u0[e], ur[e]);
-        }
-        if ((t & 15) == 0) {
-          pivs[j] = cur[0][0][j];
-          pivs[j + 1] = p1raw;
-        }
-      } else {
-        const float f0 = cur[0][0][i] * r0;
-        const float f1 = (cur[0][1][i] - f0 * a01) * __builtin_amdgcn_rcpf(piv(p1raw));
-        const f32x4 a1 = *(const f32x4*)&cur[0][1][c0];
-        const f32x4 u1 = *(const f32x4*)&cur[1][1][c0];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ar[e] = fmaf(-f1, fmaf(-g, a0[e], a1[e]), fmaf(-f0, a0[e], ar[e]));
-          ur[e] = fmaf(-f1, fmaf(-g, u0[e], u1[e]), fmaf(-f0, u0[e], ur[e]));
-        }
+      for (int h = 0; h < 2; ++h) {
+        f0[h] = fmaf(X1[h], bv[1], X0[h] * bv[0]);
+        f1[h] = fmaf(X1[h], bv[2], X0[h] * bv[1]);
       }
+      d00 = fmaf(-f1[0], X1[0], fmaf(-f0[0], X0[0], d00));
+      d01 = fmaf(-f1[0], X1[1], fmaf(-f0[0], X0[1], d01));
+      d11 = fmaf(-f1[1], X1[1], fmaf(-f0[1], X0[1], d11));
+      const bool own = cg == (s >> 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[h][e] = fmaf(-f1[h], P1[e], fmaf(-f0[h], P0[e], w[h][e]));
+        w[h][m] = own ? -f0[h] : w[h][m];
+        w[h][m + 1] = own ? -f1[h] : w[h][m + 1];
+      }
+      if (p == s + 1) invert();
     }
+  };
+  for (int s = 0; s < NB / 2; s += 2) {
+    step(std::integral_constant<int, 0>{}, s);
+    step(std::integral_constant<int, 1>{}, s + 1);
+  }
+  const int j = 2 * p;
+  const float p0 = d00 > 0.f ? d00 : 1.f;
+  const float g = d01 / p0;
+  const float p1raw = fmaf(-g, d01, d11);
+  const float p1 = p1raw > 0.f ? p1raw : 1.f;
+  if (act && cg == 0) {
+    pivs[j] = d00;
+    pivs[j + 1] = p1raw;
   }
   __syncthreads();
-  if (t == 0) {
-    for (int j = 0; j < nb; ++j)
-      if (!(pivs[j] > 0.f)) {
-        if (*info == 0) *info = k0 + j + 1;
-        break;
-      }
+  if (t < 64) {
+    // first non-positive (or NaN) pivot of the block, if any
+    const uint64_t bad = __ballot(t < nb && !(pivs[t] > 0.f));
+    if (t == 0 && bad != 0 && *info == 0) *info = k0 + __builtin_ctzll(bad) + 1;
   }
-  const float inv_i = 1.f / sqrtf(i < nb ? piv(pivs[i]) : 1.f);
-  *(f32x4*)(Tk + i * NB + c0) = f32x4{ur[0] * inv_i, ur[1] * inv_i, ur[2] * inv_i, ur[3] * inv_i};
+  if (act) {
+    const float s0 = 1.f / sqrtf(p0), s1 = 1.f / sqrtf(p1);
+    float o0[4], o1[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = c0 + e;
+      const float u0 = k < j ? w[0][e] : (k == j ? 1.f : 0.f);
+      const float u1 = k < j ? w[1][e] : (k == j + 1 ? 1.f : 0.f);
+      o0[e] = u0 * s0;
+      o1[e] = fmaf(-g, u0, u1) * s1;
+    }
+    *(f32x4*)(Tk + j * NB + c0) = f32x4{o0[0], o0[1], o0[2], o0[3]};
+    *(f32x4*)(Tk + (j + 1) * NB + c0) = f32x4{o1[0], o1[1], o1[2], o1[3]};
+  }
 }
 
 __global__ __launch_bounds__(SW_THREADS) void sweep_kernel(SweepArgs a) {
-  __shared__ __attribute__((aligned(16))) float L0[NB][BP], L1[NB][BP], L2[NB][BP], L3[NB][BP], L4[NB][BP];
+  // four blocks (plus the factorization's few hundred bytes) keep two work-groups on a CU
+  __shared__ __attribute__((aligned(16))) float L0[NB][BP], L1[NB][BP], L2[NB][BP], L3[NB][BP];
   __shared__ __attribute__((aligned(16))) float curb[2][2][2][NB];
   __shared__ float pivs[NB];
   const int k = a.k, d = a.d;
@@ -406,9 +463,11 @@ __global__ __launch_bounds__(SW_THREADS) void sweep_kernel(SweepArgs a) {
         sw_load(L0, a.Mx, d, k, k - 1);
         sw_load_t(L2, Tprev);
         __syncthreads();
-        sw_put(L3, sw_mm(L0, L2, true));                    // X_k = A_k,k-1 T_{k-1}^T
+        const f32x4 x = sw_mm(L0, L2, true);                // X_k = A_k,k-1 T_{k-1}^T
         __syncthreads();
-        const f32x4 xx = sw_mm(L3, L3, true);               // X_k X_k^T
+        sw_put(L0, x);
+        __syncthreads();
+        const f32x4 xx = sw_mm(L0, L0, true);               // X_k X_k^T
         __syncthreads();
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int m0 = (wave >> 2) * 16 + 4 * (lane >> 4), n = (wave & 3) * 16 + (lane & 15);
@@ -422,7 +481,7 @@ __global__ __launch_bounds__(SW_THREADS) void sweep_kernel(SweepArgs a) {
         double t = 0.0;
         for (int i = threadIdx.x; i < d; i += SW_THREADS) t += (double)a.G[(int64_t)i * d + i];
         for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
-        double* red = (double*)&L4[0][0];
+        double* red = (double*)&L2[0][0];
         if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = t;
         __syncthreads();
         if (threadIdx.x == 0) {
@@ -446,29 +505,48 @@ __global__ __launch_bounds__(SW_THREADS) void sweep_kernel(SweepArgs a) {
     --q;
   }
   if (q < a.n_fill) {
-    // block (i, j) of R = C W or P = W W^T over K blocks [kb0, kb1), double-buffered through LDS
+    // block (i, j) of R = C W (all blocks) or P = W W^T (j <= i: P is symmetric) over K blocks
+    // [kb0, kb1)
     const int nT = a.nP;
     const int g = a.fill0 + q;
     const bool is_p = g >= nT * nT;
-    const int tt = g % (nT * nT), i = tt / nT, j = tt % nT;
+    int i = g / nT, j = g % nT;
+    if (is_p) tri_decode(g - nT * nT, i, j);
     const float* X = is_p ? a.Wf : a.C;
-    auto bx = [&](int b) { return b ? L3 : L0; };
-    auto by = [&](int b) { return b ? L4 : L1; };
+    // K block kb0 + t passes through registers (loaded two steps ahead) into LDS slot t % 2
+    const int n = a.kb1 - a.kb0;
+    auto gx = [&](int t) { return sw_gload(X, d, i, a.kb0 + t); };
+    auto gy = [&](int t) { return is_p ? sw_gload(a.Wf, d, j, a.kb0 + t) : sw_gload(a.Wf, d, a.kb0 + t, j); };
+    f32x4 rx[2], ry[2];
+    sw_lput(L0, gx(0));
+    sw_lput(L1, gy(0));
+    if (n > 1) {
+      rx[1] = gx(1);
+      ry[1] = gy(1);
+    }
+    if (n > 2) {
+      rx[0] = gx(2);
+      ry[0] = gy(2);
+    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    sw_load(bx(0), X, d, i, a.kb0);
-    if (is_p) sw_load(by(0), a.Wf, d, j, a.kb0);
-    else sw_load(by(0), a.Wf, d, a.kb0, j);
-    for (int kb = a.kb0; kb < a.kb1; ++kb) {
-      const int b = (kb - a.kb0) & 1;
+    auto step = [&](auto bc, int t) {
+      constexpr int b = decltype(bc)::value;
       __syncthreads();
-      if (kb + 1 < a.kb1) {
-        sw_load(bx(b ^ 1), X, d, i, kb + 1);
-        if (is_p) sw_load(by(b ^ 1), a.Wf, d, j, kb + 1);
-        else sw_load(by(b ^ 1), a.Wf, d, kb + 1, j);
-      }
-      const f32x4 v = sw_mm(bx(b), by(b), is_p);
+      const f32x4 v = b ? sw_mm(L2, L3, is_p) : sw_mm(L0, L1, is_p);
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] += v[r];
+      if (t + 1 < n) {
+        sw_lput(b ? L0 : L2, rx[b ^ 1]);
+        sw_lput(b ? L1 : L3, ry[b ^ 1]);
+      }
+      if (t + 3 < n) {
+        rx[b ^ 1] = gx(t + 3);
+        ry[b ^ 1] = gy(t + 3);
+      }
+    };
+    for (int t = 0; t < n; t += 2) {
+      step(std::integral_constant<int, 0>{}, t);
+      if (t + 1 < n) step(std::integral_constant<int, 1>{}, t + 1);
     }
     sw_store(is_p ? a.P : a.R, d, i, j, acc, a.kb0 > 0);
     return;
@@ -476,19 +554,20 @@ __global__ __launch_bounds__(SW_THREADS) void sweep_kernel(SweepArgs a) {
   q -= a.n_fill;
   if (q < a.n_a) {
     // trailing block (i, j) of A, k <= j <= i < nP, other than (k, k): A_ij -= X_i X_j^T
-    int p = q + 1;
-    int ii = (int)((sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);
-    while ((ii + 1) * (ii + 2) / 2 <= p) ++ii;
-    while (ii * (ii + 1) / 2 > p) --ii;
-    const int i = k + ii, j = k + (p - ii * (ii + 1) / 2);
+    int ii, jj;
+    tri_decode(q + 1, ii, jj);
+    const int i = k + ii, j = k + jj;
     sw_load(L0, a.Mx, d, i, k - 1);
     sw_load_t(L2, Tprev);
     if (i != j) sw_load(L1, a.Mx, d, j, k - 1);
     __syncthreads();
-    sw_put(L3, sw_mm(L0, L2, true));                        // X_i
-    if (i != j) sw_put(L4, sw_mm(L1, L2, true));            // X_j
+    const f32x4 xi = sw_mm(L0, L2, true);                   // X_i
+    const f32x4 xj = i != j ? sw_mm(L1, L2, true) : xi;     // X_j
     __syncthreads();
-    const f32x4 v = sw_mm(L3, i != j ? L4 : L3, true);
+    sw_put(L0, xi);
+    sw_put(L1, xj);
+    __syncthreads();
+    const f32x4 v = sw_mm(L0, L1, true);
     sw_store(a.Mx, d, i, j, -v, true);
     return;
   }
@@ -500,10 +579,13 @@ __global__ __launch_bounds__(SW_THREADS) void sweep_kernel(SweepArgs a) {
     sw_load(L1, a.Bx, d, k - 1, c);
     sw_load_t(L2, Tprev);
     __syncthreads();
-    sw_put(L3, sw_mm(L0, L2, true));                        // X_i
-    sw_put(L4, sw_mm(L2, L1, false));                       // T_{k-1} B_{k-1,c}
+    const f32x4 xi = sw_mm(L0, L2, true);                   // X_i
+    const f32x4 tb = sw_mm(L2, L1, false);                  // T_{k-1} B_{k-1,c}
     __syncthreads();
-    const f32x4 v = sw_mm(L3, L4, false);
+    sw_put(L0, xi);
+    sw_put(L1, tb);
+    __syncthreads();
+    const f32x4 v = sw_mm(L0, L1, false);
     sw_store(a.Bx, d, i, c, -v, true);
     return;
   }
@@ -564,18 +646,33 @@ __global__ __launch_bounds__(NT) void gemm64_kernel(const float* A, const float*
     }
 }
 
-// Partial dot products for epsilon: <D,P>, <G,P>, <W,R>, <dW,R>, <dW,dW> (fp64 per block).
+// Partial dot products for epsilon: <D,P>, <G,P>, <W,R>, <dW,R>, <dW,dW> (fp64 per block), row by row.
+// Only the lower 64-block triangle of P is formed; D and G are symmetric, so blocks below the
+// diagonal count twice and the upper ones are skipped.
 __global__ __launch_bounds__(NT) void dots_kernel(const float* D, const float* G, const float* P, const float* Wf,
-                                                  const float* R, const float* dW, int64_t n, double* part) {
+                                                  const float* R, const float* dW, int d, double* part) {
   double s[5] = {0, 0, 0, 0, 0};
-  for (int64_t e = blockIdx.x * (int64_t)NT + threadIdx.x; e < n; e += (int64_t)gridDim.x * NT) {
-    const double p = P[e], r = R[e], dw = dW[e];
-    s[0] += (double)D[e] * p;
-    s[1] += (double)G[e] * p;
-    s[2] += (double)Wf[e] * r;
-    s[3] += dw * r;
-    s[4] += dw * dw;
-  }
+  for (int r = blockIdx.x; r < d; r += gridDim.x)
+    for (int c = 4 * (int)threadIdx.x; c < d; c += 4 * NT) {
+      const int64_t e = (int64_t)r * d + c;
+      const f32x4 rv = *(const f32x4*)(R + e), dv = *(const f32x4*)(dW + e), wv = *(const f32x4*)(Wf + e);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s[2] += (double)wv[u] * rv[u];
+        s[3] += (double)dv[u] * rv[u];
+        s[4] += (double)dv[u] * dv[u];
+      }
+      const int rb = r / NB, cb = c / NB;
+      if (rb >= cb) {
+        const double wt = rb > cb ? 2.0 : 1.0;
+        const f32x4 pv = *(const f32x4*)(P + e), Dv = *(const f32x4*)(D + e), gv = *(const f32x4*)(G + e);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          s[0] += wt * ((double)Dv[u] * pv[u]);
+          s[1] += wt * ((double)gv[u] * pv[u]);
+        }
+      }
+    }
   __shared__ double red[5][NT];
   for (int q = 0; q < 5; ++q) red[q][threadIdx.x] = s[q];
   __syncthreads();
@@ -587,8 +684,6 @@ __global__ __launch_bounds__(NT) void dots_kernel(const float* D, const float* G
   if (threadIdx.x < 5) part[blockIdx.x * 5 + threadIdx.x] = red[threadIdx.x][0];
 }
 
-// eps = sqrt(max(<D,P> - <dW,R> - lambda <dW,dW>, 0) / (<G,P> + 2 <W,R> + <D,P>)), partials added
-// in block order
 __global__ __launch_bounds__(NT) void eps_kernel(const double* part, int nblk, const Scalars* sc, float* eps) {
   __shared__ double red[5][NT];
   double t[5] = {0, 0, 0, 0, 0};
@@ -671,11 +766,12 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
   // Cholesky sweep (one launch per panel, plus one that finishes the last two block rows of L^-1)
   {
     const int nP = (d + NB - 1) / NB;
-    // R = C W and (for epsilon) P = W W^T ride along, split into three K ranges spread over the
-    // launches in order, so a range is added only after the one before it is complete
+    // R = C W and (for epsilon) the lower block triangle of P = W W^T ride along, split into
+    // SW_FILL_RANGES K ranges spread over the launches in order, so a range is added only after the
+    // one before it is complete
     const int n_launch = nP + 1;
-    const int n_out = nP * nP * (L.eps ? 2 : 1);
-    const int n_range = n_launch < 3 ? n_launch : 3;   // launch k works on range k * n_range / n_launch
+    const int n_out = nP * nP + (L.eps ? nP * (nP + 1) / 2 : 0);
+    const int n_range = n_launch < SW_FILL_RANGES ? n_launch : SW_FILL_RANGES;   // launch k works on range k * n_range / n_launch
     for (int k = 0; k <= nP; ++k) {
       SweepArgs a;
       a.Mx = w.Mx;
@@ -741,7 +837,7 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
     }
   }
   if (L.eps) {
-    hipLaunchKernelGGL(dots_kernel, dim3(DOT_BLOCKS), dim3(NT), 0, s, L.D, L.G, w.P, w.Wf, w.Rc, L.delta_w, dd, w.part);
+    hipLaunchKernelGGL(dots_kernel, dim3(DOT_BLOCKS), dim3(NT), 0, s, L.D, L.G, w.P, w.Wf, w.Rc, L.delta_w, d, w.part);
     ISPA_TRY(hipGetLastError());
     hipLaunchKernelGGL(eps_kernel, dim3(1), dim3(NT), 0, s, w.part, DOT_BLOCKS, w.sc, L.eps);
     ISPA_TRY(hipGetLastError());
