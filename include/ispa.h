@@ -51,7 +51,7 @@ enum {
   ISPA_EINVAL = 1,        /* NULL required pointer, bad size, misaligned pointer */
   ISPA_EUNSUPPORTED = 2,  /* head_dim or dtype combination not implemented      */
   ISPA_EWORKSPACE = 3,    /* workspace missing or smaller than required         */
-  ISPA_EHIP = 4           /* a kernel launch failed                             */
+  ISPA_EHIP = 4           /* a kernel launch or HIP runtime call failed         */
 };
 
 /* call ids for ispa_workspace_bytes */
@@ -184,6 +184,59 @@ int ispa_absorb_solve(int d, const float* G, const float* C, const float* D,
 int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype,
                                const void* q, const void* k, const void* v, const void* w_new,
                                void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * KV-cache manager -- the K/V storage on either side of the hot path.
+ * Technical summary section 2, stage 3 "Memory-Efficient Inference": after the
+ * warmup the F-layers keep attending to the whole growing cache while the
+ * converted L-layers keep only the sink tokens and the current chunk; their
+ * history rows are what the method frees.  A cache object holds, per layer,
+ * K and V rows in the order of ispa_attn_shape (sink | history | current),
+ * ready to pass to ispa_dual_attn / ispa_local_attn_fused_proj.
+ *
+ * Unlike the calls above, a cache OWNS device memory: ispa_kv_create
+ * allocates it (hipMalloc), ispa_kv_release_history reallocates one layer and
+ * ispa_kv_destroy frees everything (hipMalloc/hipFree, so these three may
+ * synchronise the device).  A handle is not thread-safe: calls on one handle
+ * must come from one host thread at a time.  Row data is copied with
+ * hipMemcpyAsync on `stream`; the caller's source rows must stay valid until
+ * the stream reaches the copy.  HIP allocation or copy failures return
+ * ISPA_EHIP.
+ *
+ *   ispa_kv_create: n_layers >= 1 layers of rows of width d (d % 8 == 0) in
+ *     dtype (F32, BF16 or F16); sink_rows >= 0 sink rows, chunks of
+ *     chunk_rows >= 1 rows; every layer reserves sink_rows +
+ *     max_chunks * chunk_rows rows of K and of V (max_chunks >= 1, total
+ *     below 2^31 rows).  *out receives the handle (NULL on error).
+ *   ispa_kv_destroy: frees the handle and its memory (NULL is a no-op).
+ *   ispa_kv_write_sink: copies sink_rows rows of k and v ([sink_rows, d]
+ *     each) into the sink rows of `layer`.
+ *   ispa_kv_append_chunk: copies one chunk (chunk_rows rows of k and v).  A
+ *     full layer appends it after its rows (the previous current chunk becomes
+ *     history; EINVAL once max_chunks chunks are held); a converted layer
+ *     overwrites its current chunk.
+ *   ispa_kv_release_history: converts a full layer: a new allocation of
+ *     sink_rows + chunk_rows rows receives the sink and the current chunk, the
+ *     stream is synchronised and the old allocation freed.  EINVAL if the layer
+ *     is already converted.
+ *   ispa_kv_layer: the layer's K and V base pointers (valid until the next
+ *     ispa_kv_release_history of that layer or ispa_kv_destroy) and
+ *     rows[0..2] = n_sink, n_hist, n_cur for ispa_attn_shape.
+ *   ispa_kv_bytes: *held_bytes = bytes of K and V rows the layers hold
+ *     (sink + history + current of full layers, sink + current of converted
+ *     ones: the quantity the method reduces); *reserved_bytes = bytes of device
+ *     memory the cache has allocated.
+ */
+typedef struct ispa_kv_cache ispa_kv_cache;
+
+int ispa_kv_create(int n_layers, int d, int dtype, int32_t sink_rows, int32_t chunk_rows, int32_t max_chunks,
+                   ispa_kv_cache** out);
+int ispa_kv_destroy(ispa_kv_cache* kv);
+int ispa_kv_write_sink(ispa_kv_cache* kv, int layer, const void* k, const void* v, void* stream);
+int ispa_kv_append_chunk(ispa_kv_cache* kv, int layer, const void* k, const void* v, void* stream);
+int ispa_kv_release_history(ispa_kv_cache* kv, int layer, void* stream);
+int ispa_kv_layer(const ispa_kv_cache* kv, int layer, void** k, void** v, int32_t* rows);
+int ispa_kv_bytes(const ispa_kv_cache* kv, int64_t* held_bytes, int64_t* reserved_bytes);
 
 /* Workspace bytes a call needs (0 if none).  `shape` is used by the attention
  * calls, `d` by ISPA_CALL_ABSORB_SOLVE.  Returns (size_t)-1 for an unknown call. */

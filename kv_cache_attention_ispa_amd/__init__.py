@@ -13,7 +13,7 @@ from typing import Optional
 
 __all__ = ["IspaError", "AttnShape", "lib", "dual_attn", "gram_accum", "absorb_solve",
            "local_attn_fused_proj", "workspace_bytes", "CALL_DUAL_ATTN", "CALL_ABSORB_SOLVE",
-           "CALL_LOCAL_ATTN_PROJ", "library_path"]
+           "CALL_LOCAL_ATTN_PROJ", "library_path", "KVCache"]
 
 F32, BF16, F16 = 0, 1, 2
 CALL_DUAL_ATTN, CALL_ABSORB_SOLVE, CALL_LOCAL_ATTN_PROJ = 0, 1, 2
@@ -66,7 +66,16 @@ def lib() -> ctypes.CDLL:
         L.ispa_status_string.argtypes = [_i32]
         L.ispa_status_string.restype = ctypes.c_char_p
         L.ispa_version.restype = ctypes.c_int
-        for f in ("ispa_dual_attn", "ispa_gram_accum", "ispa_absorb_solve", "ispa_local_attn_fused_proj"):
+        L.ispa_kv_create.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_vp)]
+        L.ispa_kv_destroy.argtypes = [_vp]
+        L.ispa_kv_write_sink.argtypes = [_vp, _i32, _vp, _vp, _vp]
+        L.ispa_kv_append_chunk.argtypes = [_vp, _i32, _vp, _vp, _vp]
+        L.ispa_kv_release_history.argtypes = [_vp, _i32, _vp]
+        L.ispa_kv_layer.argtypes = [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_i32)]
+        L.ispa_kv_bytes.argtypes = [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
+        for f in ("ispa_dual_attn", "ispa_gram_accum", "ispa_absorb_solve", "ispa_local_attn_fused_proj",
+                  "ispa_kv_create", "ispa_kv_destroy", "ispa_kv_write_sink", "ispa_kv_append_chunk",
+                  "ispa_kv_release_history", "ispa_kv_layer", "ispa_kv_bytes"):
             getattr(L, f).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -156,3 +165,74 @@ def local_attn_fused_proj(shape: AttnShape, q, k, v, w_new, out, workspace, stre
                                             _ptr(w_new), _ptr(out), _ptr(workspace),
                                             workspace.numel() * workspace.element_size(), _stream(stream)),
            "ispa_local_attn_fused_proj")
+
+
+class _DeviceRows:
+    """A [rows, d] view of device memory the library owns, for torch.as_tensor (no copy)."""
+
+    def __init__(self, ptr: int, rows: int, d: int, dtype: int):
+        self.__cuda_array_interface__ = {"shape": (rows, d), "typestr": {F32: "<f4", F16: "<f2", BF16: "<i2"}[dtype],
+                                         "data": (ptr, False), "version": 3}
+
+
+class KVCache:
+    """ispa_kv_*: per-layer K/V rows (sink | history | current) on the device, owned by the library.
+
+    A full layer grows by one chunk per append_chunk; release_history converts a layer to sink +
+    current chunk only.  See include/ispa.h for the contract."""
+
+    def __init__(self, n_layers: int, d: int, dtype, sink_rows: int, chunk_rows: int, max_chunks: int):
+        import torch
+        self.dtype = dtype
+        self.d = d
+        self._code = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}[dtype]
+        h = _vp()
+        _check(lib().ispa_kv_create(n_layers, d, self._code, sink_rows, chunk_rows, max_chunks, ctypes.byref(h)),
+               "ispa_kv_create")
+        self._h = h
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            _check(lib().ispa_kv_destroy(self._h), "ispa_kv_destroy")
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _rows(self, t, name):
+        if not t.is_contiguous() or t.dtype != self.dtype or t.shape[-1] != self.d:
+            raise ValueError(f"{name} must be contiguous [rows, {self.d}] {self.dtype}")
+        return _ptr(t)
+
+    def write_sink(self, layer: int, k, v, stream=None) -> None:
+        _check(lib().ispa_kv_write_sink(self._h, layer, self._rows(k, "k"), self._rows(v, "v"), _stream(stream)),
+               "ispa_kv_write_sink")
+
+    def append_chunk(self, layer: int, k, v, stream=None) -> None:
+        _check(lib().ispa_kv_append_chunk(self._h, layer, self._rows(k, "k"), self._rows(v, "v"), _stream(stream)),
+               "ispa_kv_append_chunk")
+
+    def release_history(self, layer: int, stream=None) -> None:
+        _check(lib().ispa_kv_release_history(self._h, layer, _stream(stream)), "ispa_kv_release_history")
+
+    def layer(self, layer: int):
+        """(k, v, (n_sink, n_hist, n_cur)): k and v are torch views of the layer's rows (no copy),
+        valid until release_history of that layer or close()."""
+        import torch
+        kp, vp, rows = _vp(), _vp(), (_i32 * 3)()
+        _check(lib().ispa_kv_layer(self._h, layer, ctypes.byref(kp), ctypes.byref(vp), rows), "ispa_kv_layer")
+        n = rows[0] + rows[1] + rows[2]
+        views = []
+        for p in (kp.value, vp.value):
+            t = torch.as_tensor(_DeviceRows(p, n, self.d, self._code), device="cuda")
+            views.append(t.view(self.dtype) if self._code == BF16 else t)
+        return views[0], views[1], (rows[0], rows[1], rows[2])
+
+    def bytes(self):
+        """(held, reserved): bytes of K and V rows held, bytes of device memory allocated."""
+        held, reserved = _i64(), _i64()
+        _check(lib().ispa_kv_bytes(self._h, ctypes.byref(held), ctypes.byref(reserved)), "ispa_kv_bytes")
+        return held.value, reserved.value

@@ -59,7 +59,7 @@ const char* ispa_status_string(int status) {
     case ISPA_EINVAL: return "invalid argument";
     case ISPA_EUNSUPPORTED: return "unsupported head_dim or dtype combination";
     case ISPA_EWORKSPACE: return "workspace missing or too small";
-    case ISPA_EHIP: return "HIP launch error";
+    case ISPA_EHIP: return "HIP launch or runtime error";
     default: return "unknown status";
   }
 }

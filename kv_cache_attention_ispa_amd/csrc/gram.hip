@@ -36,8 +36,6 @@ constexpr int NT = 256;
 constexpr int GB = 128;
 constexpr int GK = 32;                      // (projection below)
 constexpr int G_ROW = GK * 2;               // (projection below)
-constexpr int G_TILE = GB * G_ROW;          // (projection below)
-constexpr int G_STAGE = 2 * G_TILE;         // (projection below)
 constexpr int RK = 64;                      // tokens per Gram stage
 constexpr int R_ROW = RK * 2;               // 128 bytes per staged row
 constexpr int R_XTILE = 2 * GB * R_ROW;     // 256 rows of X: 32 KiB

@@ -129,3 +129,21 @@ def test_local_proj_rejects_bad_arguments(L):
     assert f(w=0) == EINVAL
     assert f(ws=0) == EWORKSPACE
     assert f(wsb=need - 1) == EWORKSPACE
+
+
+def test_kv_cache_rejects_bad_arguments_without_allocating(L):
+    """ispa_kv_*: invalid sizes, dtypes and NULL handles fail on the host before any HIP call."""
+    h = ctypes.c_void_p(FAKE)
+    for args in ((0, 64, 1, 8, 16, 2), (2, 60, 1, 8, 16, 2), (2, 64, 7, 8, 16, 2), (2, 64, 1, -1, 16, 2),
+                 (2, 64, 1, 8, 0, 2), (2, 64, 1, 8, 16, 0), (2, 64, 1, 8, 1 << 30, 4)):
+        assert L.ispa_kv_create(*args, ctypes.byref(h)) == EINVAL, args
+        assert h.value is None
+    assert L.ispa_kv_create(2, 64, 1, 8, 16, 2, None) == EINVAL
+    assert L.ispa_kv_destroy(None) == OK
+    p, r = ctypes.c_void_p(), (ctypes.c_int32 * 3)()
+    assert L.ispa_kv_layer(None, 0, ctypes.byref(p), ctypes.byref(p), r) == EINVAL
+    held, res = ctypes.c_int64(), ctypes.c_int64()
+    assert L.ispa_kv_bytes(None, ctypes.byref(held), ctypes.byref(res)) == EINVAL
+    assert L.ispa_kv_append_chunk(None, 0, FAKE, FAKE, None) == EINVAL
+    assert L.ispa_kv_write_sink(None, 0, FAKE, FAKE, None) == EINVAL
+    assert L.ispa_kv_release_history(None, 0, None) == EINVAL

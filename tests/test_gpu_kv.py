@@ -1,0 +1,185 @@
+"""KV-cache manager (ispa_kv_*): row contents, segment sizes and bytes against the closed form.
+
+The pages' inference stage keeps the whole growing cache in F-layers and only sink + current chunk
+in converted L-layers (technical summary, section 2, stage 3 "Memory-Efficient Inference"); the
+held bytes are compared with oracle.kv_cache_bytes, which writes that statement out.  Row contents
+are bit-exact copies (compared with torch.equal on the device), and an attention call over a
+cache view must give exactly what it gives over the same rows assembled by hand.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gpu_util import torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _chunk(t, rows, d, seed):
+    g = t.Generator(device="cpu").manual_seed(seed)
+    return t.randn((rows, d), generator=g).to(t.bfloat16).cuda()
+
+
+def test_kv_cache_rows_segments_and_bytes():
+    """30-layer-style schedule at a small shape: sink = 1 frame, chunk = 3 frames, 15 of 30 layers
+    converted after a 4-chunk warmup; every layer's rows and the held bytes are checked each chunk."""
+    import kv_cache_attention_ispa_amd as ispa
+    t = torch()
+    frame, chunk_frames, d, n_layers, n_chunks, t_warm = 16, 3, 64, 6, 7, 4
+    local = [1, 2, 4]
+    sink, chunk = frame, frame * chunk_frames
+    kv = ispa.KVCache(n_layers, d, t.bfloat16, sink, chunk, n_chunks)
+    exp_k, exp_v = [], []
+    for layer in range(n_layers):
+        ks, vs = _chunk(t, sink, d, 1000 + layer), _chunk(t, sink, d, 2000 + layer)
+        kv.write_sink(layer, ks, vs)
+        exp_k.append([ks]), exp_v.append([vs])
+    for c in range(n_chunks):
+        if c == t_warm:
+            for layer in local:
+                kv.release_history(layer)
+                exp_k[layer] = [exp_k[layer][0], exp_k[layer][-1]]
+                exp_v[layer] = [exp_v[layer][0], exp_v[layer][-1]]
+        for layer in range(n_layers):
+            kc, vc = _chunk(t, chunk, d, 10000 * c + layer), _chunk(t, chunk, d, 10000 * c + 100 + layer)
+            kv.append_chunk(layer, kc, vc)
+            if c >= t_warm and layer in local:
+                exp_k[layer][-1], exp_v[layer][-1] = kc, vc
+            else:
+                exp_k[layer].append(kc), exp_v[layer].append(vc)
+        t.cuda.synchronize()
+        n_local = len(local) if c >= t_warm else 0
+        for layer in range(n_layers):
+            k, v, rows = kv.layer(layer)
+            conv = c >= t_warm and layer in local
+            assert rows == (sink, 0 if conv else c * chunk, chunk)
+            assert t.equal(k, t.cat(exp_k[layer])) and t.equal(v, t.cat(exp_v[layer]))
+        held, reserved = kv.bytes()
+        assert held == oracle.kv_cache_bytes(c, n_layers, n_local, frame, chunk_frames, d)
+        full_cap = 2 * (sink + n_chunks * chunk) * d * 2
+        assert reserved == (n_layers - n_local) * full_cap + n_local * 2 * (sink + chunk) * d * 2
+    kv.close()
+
+
+def test_kv_cache_errors():
+    import kv_cache_attention_ispa_amd as ispa
+    t = torch()
+    kv = ispa.KVCache(2, 64, t.bfloat16, 8, 16, 2)
+    x = _chunk(t, 16, 64, 0)
+    kv.append_chunk(0, x, x)
+    kv.append_chunk(0, x, x)
+    with pytest.raises(ispa.IspaError):
+        kv.append_chunk(0, x, x)          # capacity: max_chunks chunks
+    kv.release_history(0)
+    with pytest.raises(ispa.IspaError):
+        kv.release_history(0)             # already converted
+    kv.append_chunk(0, x, x)              # a converted layer overwrites its current chunk
+    with pytest.raises(ispa.IspaError):
+        kv.layer(2)
+    kv.release_history(1)                 # no chunk yet: sink only
+    k, v, rows = kv.layer(1)
+    assert rows == (8, 0, 0) and k.shape == (8, 64)
+    kv.close()
+
+
+def test_attention_on_cache_views():
+    """The dual attention over a cache view (after a conversion elsewhere in the cache) equals the
+    call on the same rows assembled by hand, bit for bit."""
+    import kv_cache_attention_ispa_amd as ispa
+    t = torch()
+    n_heads, hd = 2, 128
+    d, sink, chunk, n_q = n_heads * hd, 64, 192, 192
+    kv = ispa.KVCache(2, d, t.bfloat16, sink, chunk, 4)
+    ks, vs = _chunk(t, sink, d, 1), _chunk(t, sink, d, 2)
+    rows_k, rows_v = [ks], [vs]
+    for layer in range(2):
+        kv.write_sink(layer, ks, vs)
+    for c in range(3):
+        kc, vc = _chunk(t, chunk, d, 10 + c), _chunk(t, chunk, d, 20 + c)
+        for layer in range(2):
+            kv.append_chunk(layer, kc, vc)
+        rows_k.append(kc), rows_v.append(vc)
+    kv.release_history(1)
+    q = _chunk(t, n_q, d, 99)
+    k, v, (n_s, n_h, n_c) = kv.layer(0)
+    shape = ispa.AttnShape(n_q, n_s, n_h, n_c, n_heads, hd, 0.0)
+    ws = t.empty(ispa.workspace_bytes(ispa.CALL_DUAL_ATTN, shape), dtype=t.uint8, device="cuda")
+    outs = []
+    for kk, vv in ((k, v), (t.cat(rows_k), t.cat(rows_v))):
+        a_full = t.empty((n_q, d), dtype=t.bfloat16, device="cuda")
+        lse_l = t.empty((n_heads, n_q), device="cuda")
+        lse_h = t.empty((n_heads, n_q), device="cuda")
+        ispa.dual_attn(shape, q, kk, vv, a_full=a_full, lse_loc=lse_l, lse_hist=lse_h, workspace=ws)
+        t.cuda.synchronize()
+        outs.append((a_full.clone(), lse_l.clone(), lse_h.clone()))
+    for a, b in zip(*outs):
+        assert t.equal(a, b)
+    # the converted layer: sink + current chunk, as an L-layer's local attention sees it
+    k1, v1, rows1 = kv.layer(1)
+    assert rows1 == (sink, 0, chunk)
+    assert t.equal(k1, t.cat([ks, rows_k[-1]])) and t.equal(v1, t.cat([vs, rows_v[-1]]))
+    kv.close()
+
+
+def test_kv_cache_rollout_memory():
+    """The 1.3B rollout shape (30 layers, d = 1536, sink 1560 rows, chunks of 4680 rows, 40 chunks):
+    reserve the whole rollout, run the 4-chunk warmup, convert 15 layers and run to chunk 39.  Device
+    memory (hipMemGetInfo through torch) drops by what the converted layers released; held bytes
+    equal the closed form (48.3% of a full cache at chunk 39); appends run at copy speed."""
+    import time
+    import kv_cache_attention_ispa_amd as ispa
+    t = torch()
+    w = wl.ROLLOUT_1P3B
+    sh = wl.chunk_shape(w, 0)
+    d, frame, cf = sh.d, w.frame, w.chunk_frames
+    sink, chunk, n_chunks, n_layers, n_local, t_warm = frame, frame * cf, 40, 30, 15, 4
+    src_k, src_v = _chunk(t, chunk, d, 5), _chunk(t, chunk, d, 6)
+    t.cuda.synchronize()
+    free0, _ = t.cuda.mem_get_info()
+    kv = ispa.KVCache(n_layers, d, t.bfloat16, sink, chunk, n_chunks)
+    held, reserved = kv.bytes()
+    free1, _ = t.cuda.mem_get_info()
+    assert abs((free0 - free1) - reserved) <= 256 << 20, (free0 - free1, reserved)
+    for layer in range(n_layers):
+        kv.write_sink(layer, src_k[:sink], src_v[:sink])
+    local = list(range(0, n_layers, 2))   # any 15 layers
+    copy_s = 0.0
+    for c in range(n_chunks):
+        if c == t_warm:
+            for layer in local:
+                kv.release_history(layer)
+            freed = n_local * 2 * (n_chunks - 1) * chunk * d * 2
+            t.cuda.synchronize()
+            for _ in range(30):   # the runtime may report a freed allocation a little later
+                free2, _ = t.cuda.mem_get_info()
+                if abs((free2 - free1) - freed) <= 256 << 20:
+                    break
+                time.sleep(0.1)
+            assert abs((free2 - free1) - freed) <= 256 << 20, (free2 - free1, freed)
+        t.cuda.synchronize()
+        t0 = time.perf_counter()
+        for layer in range(n_layers):
+            kv.append_chunk(layer, src_k, src_v)
+        t.cuda.synchronize()
+        copy_s += time.perf_counter() - t0
+    held, reserved = kv.bytes()
+    assert held == oracle.kv_cache_bytes(n_chunks - 1, n_layers, n_local, frame, cf, d)
+    frac = 1.0 - held / oracle.kv_cache_bytes(n_chunks - 1, n_layers, 0, frame, cf, d)
+    assert abs(frac - oracle.kv_removed_fraction(n_chunks - 1, n_layers, n_local, frame, cf, d)) < 1e-12
+    # spot check: a full layer's last chunk and a converted layer's current chunk
+    k, v, rows = kv.layer(1)
+    assert rows == (sink, (n_chunks - 1) * chunk, chunk) and t.equal(k[-chunk:], src_k)
+    k, v, rows = kv.layer(0)
+    assert rows == (sink, 0, chunk) and t.equal(v[sink:], src_v)
+    moved = n_chunks * n_layers * 2 * chunk * d * 2
+    print(f"\nkv rollout: held {held / 1e9:.2f} GB at chunk 39 ({frac:.1%} of a full cache removed), "
+          f"reserved {reserved / 1e9:.2f} GB, appends {moved / copy_s / 1e9:.0f} GB/s of rows")
+    kv.close()
+    t.cuda.synchronize()
+    for _ in range(30):
+        free3, _ = t.cuda.mem_get_info()
+        if abs(free3 - free0) <= 256 << 20:
+            break
+        time.sleep(0.1)
+    assert abs(free3 - free0) <= 256 << 20
