@@ -18,7 +18,10 @@ that definition written out:
 * the absorption -> the ridge normal equations solved by a float64 Cholesky
   factorisation (``absorb``);
 * layer selection -> a stable sort of the reconstruction errors (``absorb``);
-* KV-cache accounting -> closed-form byte counts (``accounting``).
+* KV-cache accounting -> closed-form byte counts (``accounting``);
+* the W8A8 variant of the L-layer projection -> per-channel absmax E4M3 codes
+  taken from the format definition, then a float64 product of the decoded
+  values (``fp8``).
 
 Every function is pinned by ``tests/test_oracle_*.py`` against things other
 than itself: brute force on tiny inputs, hand-computed fixtures under
