@@ -55,7 +55,8 @@ enum {
 };
 
 /* call ids for ispa_workspace_bytes */
-enum { ISPA_CALL_DUAL_ATTN = 0, ISPA_CALL_ABSORB_SOLVE = 1, ISPA_CALL_LOCAL_ATTN_PROJ = 2 };
+enum { ISPA_CALL_DUAL_ATTN = 0, ISPA_CALL_ABSORB_SOLVE = 1, ISPA_CALL_LOCAL_ATTN_PROJ = 2,
+       ISPA_CALL_LOCAL_ATTN_PROJ_W8A8 = 3 };
 
 /*
  * One layer's KV cache, rows in this order:
@@ -184,6 +185,46 @@ int ispa_absorb_solve(int d, const float* G, const float* C, const float* D,
 int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype,
                                const void* q, const void* k, const void* v, const void* w_new,
                                void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * W8A8 variant of the L-layer step (FP8 weights and activations).
+ * Technical summary section 4 "Results": the method combined with W8A8
+ * post-training quantisation gives the largest overall speed-up; the pages
+ * name no scheme.  This library reads it as symmetric absmax scaling per
+ * channel into OCP FP8 E4M3 codes (1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits, largest finite value 448):
+ *   s = absmax / 448 in float32 (1 for an all-zero channel),
+ *   code = E4M3(clamp(x / s, -448, 448)), rounded to nearest even, x / s an
+ *   IEEE float32 division.
+ * Weights get one scale per output channel, activations one per token; the
+ * product is out[i, j] = s_a[i] s_w[j] sum_k dec(Aq[i, k]) dec(Wq[k, j]) with
+ * fp32 accumulation, rounded to the io dtype.
+ *
+ *   ispa_quantize_weight_fp8: W [d_in, d_out] (F32, BF16 or F16) ->
+ *     wq_t [d_out, d_in] E4M3 codes (one byte each; W TRANSPOSED, so both
+ *     operands of the product are contiguous along d_in) and w_scales [d_out]
+ *     fp32.  d_in % 64 == 0, d_out % 4 == 0, both <= 65536.  Run once per
+ *     converted layer on W_new.
+ *   ispa_local_attn_fused_proj_w8a8: as ispa_local_attn_fused_proj, but the
+ *     local attention output (rounded to io_dtype) is quantised per token and
+ *     multiplied by the quantised W_new: out = W8A8(LocalAttn(Q; sink +
+ *     current), W_new).  workspace: ispa_workspace_bytes(
+ *     ISPA_CALL_LOCAL_ATTN_PROJ_W8A8, shape, 0) bytes, 16-byte aligned.  The
+ *     attention itself stays in io_dtype (the pages do not say how attention
+ *     would be quantised).
+ */
+int ispa_quantize_weight_fp8(int d_in, int d_out, int w_dtype, const void* w, void* wq_t, float* w_scales,
+                             void* stream);
+/*   ispa_quantize_rows_fp8: the activation side on its own: x [rows, cols] (row
+ *     stride ldx elements; F32, BF16 or F16) -> q [rows, cols] E4M3 codes (row
+ *     stride ldq bytes) and scales [rows] fp32, one scale per row.  cols % 8
+ *     == 0, ldq % 8 == 0. */
+int ispa_quantize_rows_fp8(int rows, int cols, int dtype, const void* x, int64_t ldx, void* q, int64_t ldq,
+                           float* scales, void* stream);
+int ispa_local_attn_fused_proj_w8a8(const ispa_attn_shape* shape, int io_dtype,
+                                    const void* q, const void* k, const void* v,
+                                    const void* wq_t, const float* w_scales,
+                                    void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * KV-cache manager -- the K/V storage on either side of the hot path.

@@ -13,10 +13,11 @@ from typing import Optional
 
 __all__ = ["IspaError", "AttnShape", "lib", "dual_attn", "gram_accum", "absorb_solve",
            "local_attn_fused_proj", "workspace_bytes", "CALL_DUAL_ATTN", "CALL_ABSORB_SOLVE",
-           "CALL_LOCAL_ATTN_PROJ", "library_path", "KVCache"]
+           "CALL_LOCAL_ATTN_PROJ", "CALL_LOCAL_ATTN_PROJ_W8A8", "library_path", "KVCache",
+           "quantize_weight_fp8", "quantize_rows_fp8", "local_attn_fused_proj_w8a8"]
 
 F32, BF16, F16 = 0, 1, 2
-CALL_DUAL_ATTN, CALL_ABSORB_SOLVE, CALL_LOCAL_ATTN_PROJ = 0, 1, 2
+CALL_DUAL_ATTN, CALL_ABSORB_SOLVE, CALL_LOCAL_ATTN_PROJ, CALL_LOCAL_ATTN_PROJ_W8A8 = 0, 1, 2, 3
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -66,6 +67,10 @@ def lib() -> ctypes.CDLL:
         L.ispa_status_string.argtypes = [_i32]
         L.ispa_status_string.restype = ctypes.c_char_p
         L.ispa_version.restype = ctypes.c_int
+        L.ispa_quantize_weight_fp8.argtypes = [_i32, _i32, _i32, _vp, _vp, _vp, _vp]
+        L.ispa_quantize_rows_fp8.argtypes = [_i32, _i32, _i32, _vp, _i64, _vp, _i64, _vp, _vp]
+        L.ispa_local_attn_fused_proj_w8a8.argtypes = [ctypes.POINTER(AttnShape), _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                      _vp, _sz, _vp]
         L.ispa_kv_create.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_vp)]
         L.ispa_kv_destroy.argtypes = [_vp]
         L.ispa_kv_write_sink.argtypes = [_vp, _i32, _vp, _vp, _vp]
@@ -74,6 +79,7 @@ def lib() -> ctypes.CDLL:
         L.ispa_kv_layer.argtypes = [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_i32)]
         L.ispa_kv_bytes.argtypes = [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
         for f in ("ispa_dual_attn", "ispa_gram_accum", "ispa_absorb_solve", "ispa_local_attn_fused_proj",
+                  "ispa_quantize_weight_fp8", "ispa_quantize_rows_fp8", "ispa_local_attn_fused_proj_w8a8",
                   "ispa_kv_create", "ispa_kv_destroy", "ispa_kv_write_sink", "ispa_kv_append_chunk",
                   "ispa_kv_release_history", "ispa_kv_layer", "ispa_kv_bytes"):
             getattr(L, f).restype = ctypes.c_int
@@ -165,6 +171,37 @@ def local_attn_fused_proj(shape: AttnShape, q, k, v, w_new, out, workspace, stre
                                             _ptr(w_new), _ptr(out), _ptr(workspace),
                                             workspace.numel() * workspace.element_size(), _stream(stream)),
            "ispa_local_attn_fused_proj")
+
+
+def quantize_weight_fp8(w, wq_t, w_scales, stream=None) -> None:
+    """ispa_quantize_weight_fp8: w [d_in, d_out] -> wq_t [d_out, d_in] E4M3 codes (uint8), w_scales [d_out]."""
+    for n_, t in (("w", w), ("wq_t", wq_t), ("w_scales", w_scales)):
+        _dense(t, n_)
+    d_in, d_out = w.shape
+    _check(lib().ispa_quantize_weight_fp8(d_in, d_out, _dtype_code(w), _ptr(w), _ptr(wq_t), _ptr(w_scales),
+                                          _stream(stream)), "ispa_quantize_weight_fp8")
+
+
+def quantize_rows_fp8(x, q, scales, stream=None) -> None:
+    """ispa_quantize_rows_fp8: x [rows, cols] -> q [rows, cols] E4M3 codes (uint8), scales [rows]."""
+    for n_, t in (("q", q), ("scales", scales)):
+        _dense(t, n_)
+    if x.stride(1) != 1 or q.stride(1) != 1:
+        raise ValueError("rows must be contiguous")
+    rows, cols = x.shape
+    _check(lib().ispa_quantize_rows_fp8(rows, cols, _dtype_code(x), _ptr(x), x.stride(0), _ptr(q), q.stride(0),
+                                        _ptr(scales), _stream(stream)), "ispa_quantize_rows_fp8")
+
+
+def local_attn_fused_proj_w8a8(shape: AttnShape, q, k, v, wq_t, w_scales, out, workspace, stream=None) -> None:
+    """ispa_local_attn_fused_proj_w8a8: out = W8A8(LocalAttn(q; sink + current), W_new) with W_new given as
+    the codes and scales of quantize_weight_fp8."""
+    for n_, t in (("q", q), ("k", k), ("v", v), ("wq_t", wq_t), ("w_scales", w_scales), ("out", out)):
+        _dense(t, n_)
+    _check(lib().ispa_local_attn_fused_proj_w8a8(ctypes.byref(shape), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
+                                                 _ptr(wq_t), _ptr(w_scales), _ptr(out), _ptr(workspace),
+                                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+           "ispa_local_attn_fused_proj_w8a8")
 
 
 class _DeviceRows:

@@ -34,6 +34,14 @@ size_t local_a_bytes(const ispa_attn_shape* s) {
   return ((size_t)s->n_q * s->n_heads * s->head_dim * 2 + 255) / 256 * 256;
 }
 
+// The E4M3 codes of the local attention output and their per-token scales (W8A8 projection).
+size_t w8a8_codes_bytes(const ispa_attn_shape* s) {
+  return ((size_t)s->n_q * s->n_heads * s->head_dim + 255) / 256 * 256;
+}
+size_t w8a8_act_bytes(const ispa_attn_shape* s) {
+  return w8a8_codes_bytes(s) + ((size_t)s->n_q * 4 + 255) / 256 * 256;
+}
+
 // ispa_dual_attn's workspace (16-bit inputs): the V^T copy, then the parked local outputs.
 size_t dual_ws_bytes(const ispa_attn_shape* s) {
   return attn_vt_bytes_aligned((int64_t)s->n_sink + s->n_hist + s->n_cur, (int64_t)s->n_heads * s->head_dim) +
@@ -74,6 +82,11 @@ size_t ispa_workspace_bytes(int call_id, const ispa_attn_shape* shape, int d) {
       if (!shape || shape->n_q < 1 || shape->n_heads < 1) return 0;
       return local_a_bytes(shape) + attn_vt_bytes_aligned((int64_t)shape->n_sink + shape->n_hist + shape->n_cur,
                                                           (int64_t)shape->n_heads * shape->head_dim);
+    case ISPA_CALL_LOCAL_ATTN_PROJ_W8A8:
+      if (!shape || shape->n_q < 1 || shape->n_heads < 1) return 0;
+      return local_a_bytes(shape) + attn_vt_bytes_aligned((int64_t)shape->n_sink + shape->n_hist + shape->n_cur,
+                                                          (int64_t)shape->n_heads * shape->head_dim) +
+             w8a8_act_bytes(shape);
     default: return (size_t)-1;
   }
 }
@@ -230,6 +243,70 @@ int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype, const
   P.b = w_new;
   P.out = out;
   return hip_status(launch_proj(P, s));
+}
+
+int ispa_quantize_weight_fp8(int d_in, int d_out, int w_dtype, const void* w, void* wq_t, float* w_scales,
+                             void* stream) {
+  if (d_in < 1 || d_out < 1 || d_in % 64 != 0 || d_out % 4 != 0 || d_in > 65536 || d_out > 65536)
+    return ISPA_EINVAL;
+  if (!valid_dtype(w_dtype)) return ISPA_EINVAL;
+  if (!w || !wq_t || !w_scales) return ISPA_EINVAL;
+  if (!aligned16(w) || !aligned16(wq_t) || !aligned4(w_scales)) return ISPA_EINVAL;
+  return hip_status(launch_quant_weight(w_dtype, w, d_in, d_out, (uint8_t*)wq_t, w_scales, (hipStream_t)stream));
+}
+
+int ispa_quantize_rows_fp8(int rows, int cols, int dtype, const void* x, int64_t ldx, void* q, int64_t ldq,
+                           float* scales, void* stream) {
+  if (rows < 1 || cols < 1 || cols % 8 != 0 || ldx < cols || ldq < cols || ldq % 8 != 0) return ISPA_EINVAL;
+  if (!valid_dtype(dtype)) return ISPA_EINVAL;
+  if (!x || !q || !scales) return ISPA_EINVAL;
+  if (!aligned16(x) || !aligned16(q) || !aligned4(scales)) return ISPA_EINVAL;
+  return hip_status(launch_quant_rows(dtype, x, ldx, rows, cols, (uint8_t*)q, ldq, scales, (hipStream_t)stream));
+}
+
+int ispa_local_attn_fused_proj_w8a8(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k,
+                                    const void* v, const void* wq_t, const float* w_scales, void* out,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if (io_dtype != ISPA_BF16 && io_dtype != ISPA_F16) return ISPA_EUNSUPPORTED;
+  if (shape->head_dim != 128 || !fits_buffer(shape)) return ISPA_EUNSUPPORTED;
+  if (!q || !k || !v || !wq_t || !w_scales || !out) return ISPA_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(wq_t) || !aligned4(w_scales) || !aligned16(out))
+    return ISPA_EINVAL;
+  const size_t need = ispa_workspace_bytes(ISPA_CALL_LOCAL_ATTN_PROJ_W8A8, shape, 0);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return ISPA_EWORKSPACE;
+  const hipStream_t s = (hipStream_t)stream;
+  const int d = shape->n_heads * shape->head_dim;
+  const size_t a_bytes = local_a_bytes(shape);
+  const size_t vt_bytes = attn_vt_bytes_aligned((int64_t)shape->n_sink + shape->n_hist + shape->n_cur, d);
+  uint8_t* aq = (uint8_t*)workspace + a_bytes + vt_bytes;
+  float* sa = (float*)(aq + w8a8_codes_bytes(shape));
+  AttnLaunch L;
+  L.mode = 2;
+  L.io = io_dtype;
+  L.stat = ISPA_F16;
+  L.q = q;
+  L.k = k;
+  L.v = v;
+  L.a_full = workspace;
+  L.a_loc_t = nullptr;
+  L.delta_a_t = nullptr;
+  L.ld_stat = 0;
+  L.lse_loc = nullptr;
+  L.lse_hist = nullptr;
+  L.n_q = shape->n_q;
+  L.n_sink = shape->n_sink;
+  L.n_hist = shape->n_hist;
+  L.n_cur = shape->n_cur;
+  L.n_heads = shape->n_heads;
+  L.head_dim = shape->head_dim;
+  L.scale = eff_scale(shape);
+  L.ws = (char*)workspace + a_bytes;
+  L.ws_bytes = vt_bytes;
+  if (launch_attention(L, s) != hipSuccess) return ISPA_EHIP;
+  if (launch_quant_rows(io_dtype, workspace, d, shape->n_q, d, aq, d, sa, s) != hipSuccess) return ISPA_EHIP;
+  return hip_status(launch_proj8(io_dtype, aq, sa, (const uint8_t*)wq_t, w_scales, out, shape->n_q, d, d, s));
 }
 
 }  // extern "C"

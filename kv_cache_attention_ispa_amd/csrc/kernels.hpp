@@ -68,6 +68,15 @@ struct ProjLaunch {
 };
 hipError_t launch_proj(const ProjLaunch& L, hipStream_t s);
 
+// W8A8 projection (fp8.hip): per-row E4M3 codes + scales of a [rows, cols] matrix; the weights per
+// output channel, written transposed; out[m, n] = (Aq Wq) s_a s_w^T (k % 64 == 0).
+hipError_t launch_quant_rows(int dtype, const void* x, int64_t ldx, int rows, int cols, uint8_t* q, int64_t ldq,
+                             float* scales, hipStream_t s);
+hipError_t launch_quant_weight(int dtype, const void* w, int d_in, int d_out, uint8_t* wq_t, float* scales,
+                               hipStream_t s);
+hipError_t launch_proj8(int out_dtype, const uint8_t* aq, const float* sa, const uint8_t* wq_t, const float* sw,
+                        void* out, int m, int n, int k, hipStream_t s);
+
 struct SolveLaunch {
   int d;
   const float* G;

@@ -1,0 +1,135 @@
+"""GPU parity of the W8A8 variant (ispa_quantize_weight_fp8, ispa_quantize_rows_fp8,
+ispa_local_attn_fused_proj_w8a8) against oracle/fp8.py.
+
+Codes and scales are decisions taken in float32 on both sides, so they must agree bit for bit.
+The L-layer output is compared with the oracle's W8A8 L-layer, whose attention output is the exact
+one rounded to bf16; the GPU's own attention output differs from it by rounding, which can move a
+few activation codes by one step, so that comparison uses the 16-bit attention tolerance.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import fp8
+import workloads as wl
+from gpu_util import dev, host, maxrel, torch, tdtype
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("w_dtype", ["f32", "bf16", "f16"])
+def test_weight_codes_and_scales_bit_exact(w_dtype):
+    import kv_cache_attention_ispa_amd as ispa
+    t = torch()
+    d_in, d_out = 256, 196
+    rng = np.random.default_rng(11)
+    W = rng.standard_normal((d_in, d_out)) * rng.uniform(0.001, 3, (1, d_out))
+    W[:, 5] = 0.0                                   # an all-zero channel: scale 1, codes 0
+    W[7, 9] = 3e4 if w_dtype != "f16" else 6e4      # one large entry dominates its channel
+    W = wl.round_to(W, w_dtype)
+    wq = t.empty((d_out, d_in), dtype=t.uint8, device="cuda")
+    sw = t.empty((d_out,), device="cuda")
+    ispa.quantize_weight_fp8(dev(W, w_dtype), wq, sw)
+    t.cuda.synchronize()
+    codes, scales = fp8.quantize_weight(W)
+    assert np.array_equal(sw.cpu().numpy(), scales)
+    assert np.array_equal(wq.cpu().numpy(), codes)
+
+
+@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
+def test_row_codes_and_scales_bit_exact(x_dtype):
+    import kv_cache_attention_ispa_amd as ispa
+    t = torch()
+    rows, cols, ld = 70, 1536, 1536 + 16
+    rng = np.random.default_rng(12)
+    X = wl.round_to(rng.standard_normal((rows, cols)) * rng.uniform(1e-4, 50, (rows, 1)), x_dtype)
+    X[3] = 0.0
+    Xp = np.zeros((rows, ld))
+    Xp[:, :cols] = X
+    xd = dev(Xp, x_dtype)[:, :cols]
+    q = t.empty((rows, cols), dtype=t.uint8, device="cuda")
+    s = t.empty((rows,), device="cuda")
+    ispa.quantize_rows_fp8(xd, q, s)
+    t.cuda.synchronize()
+    codes, scales = fp8.quantize_rows(X)
+    assert np.array_equal(s.cpu().numpy(), scales)
+    assert np.array_equal(q.cpu().numpy(), codes)
+
+
+def _l_layer_w8a8(shape, q, k, v, W, io):
+    import kv_cache_attention_ispa_amd as ispa
+    t = torch()
+    d = shape.d
+    wq = t.empty((d, d), dtype=t.uint8, device="cuda")
+    sw = t.empty((d,), device="cuda")
+    ispa.quantize_weight_fp8(dev(W, io), wq, sw)
+    s = ispa.AttnShape.of(shape)
+    ws = t.empty(ispa.workspace_bytes(ispa.CALL_LOCAL_ATTN_PROJ_W8A8, s), dtype=t.uint8, device="cuda")
+    out = t.empty((shape.n_q, d), dtype=tdtype(io), device="cuda")
+    ispa.local_attn_fused_proj_w8a8(s, dev(q, io), dev(k, io), dev(v, io), wq, sw, out, ws)
+    t.cuda.synchronize()
+    return host(out)
+
+
+@pytest.mark.parametrize("io,shape", [
+    ("bf16", wl.AttnShape(200, 70, 0, 130, 2, 128)),      # ragged: 2 row tiles, 2 column tiles
+    ("bf16", wl.AttnShape(129, 64, 90, 65, 3, 128)),      # history rows present and skipped
+    ("f16", wl.AttnShape(64, 0, 0, 96, 1, 128)),          # no sink, one head
+])
+def test_w8a8_l_layer_matches_oracle(io, shape):
+    rng = np.random.default_rng(13)
+    d = shape.d
+    q = wl.round_to(rng.standard_normal((shape.n_q, d)), io)
+    k = wl.round_to(rng.standard_normal((shape.n_k, d)), io)
+    v = wl.round_to(rng.standard_normal((shape.n_k, d)), io)
+    W = wl.round_to(rng.standard_normal((d, d)) / math.sqrt(d), io)
+    got = _l_layer_w8a8(shape, q, k, v, W, io)
+    loc = oracle.branch_rows(shape.n_sink, shape.n_hist, shape.n_cur)["local"]
+    ref = fp8.local_layer_output_w8a8(q, k[loc], v[loc], shape.n_sink, shape.n_cur, shape.n_heads, W)
+    assert maxrel(got, ref) <= 2e-2
+    # and the quantisation error itself is visible against the unquantised L-layer
+    exact = oracle.local_layer_output(q, k[loc], v[loc], shape.n_sink, shape.n_cur, shape.n_heads, W)
+    assert maxrel(ref, exact) > 1e-3
+
+
+def test_w8a8_l_layer_1p3b_sampled_rows_and_timing():
+    """The 1.3B L-layer shape (4680 queries, sink 1560 + current 4680 rows, 12 heads): sampled rows
+    against the oracle, and the step timed against the 16-bit projection."""
+    import kv_cache_attention_ispa_amd as ispa
+    t = torch()
+    w = wl.LAYER_1P3B
+    s = w.shape
+    x = wl.layer_inputs(w)
+    loc = oracle.branch_rows(s.n_sink, s.n_hist, s.n_cur)["local"]
+    k_loc, v_loc = x["k"][loc], x["v"][loc]
+    lsh = wl.AttnShape(s.n_q, s.n_sink, 0, s.n_cur, s.n_heads, s.head_dim)
+    got = _l_layer_w8a8(lsh, x["q"], k_loc, v_loc, x["w"], "bf16")
+    rows = np.arange(0, s.n_q, 311)
+    ref = fp8.local_layer_output_w8a8(x["q"][rows], k_loc, v_loc, s.n_sink, s.n_cur, s.n_heads, x["w"], threads=8)
+    assert maxrel(got[rows], ref) <= 2e-2
+    # timing: both L-layer variants on the same inputs
+    d = s.d
+    sh = ispa.AttnShape.of(lsh)
+    qd, kd, vd, Wd = dev(x["q"], "bf16"), dev(k_loc, "bf16"), dev(v_loc, "bf16"), dev(x["w"], "bf16")
+    wq = t.empty((d, d), dtype=t.uint8, device="cuda")
+    sw = t.empty((d,), device="cuda")
+    ispa.quantize_weight_fp8(Wd, wq, sw)
+    out = t.empty((s.n_q, d), dtype=t.bfloat16, device="cuda")
+    ws8 = t.empty(ispa.workspace_bytes(ispa.CALL_LOCAL_ATTN_PROJ_W8A8, sh), dtype=t.uint8, device="cuda")
+    ws16 = t.empty(ispa.workspace_bytes(ispa.CALL_LOCAL_ATTN_PROJ, sh), dtype=t.uint8, device="cuda")
+    runs = {"bf16": lambda: ispa.local_attn_fused_proj(sh, qd, kd, vd, Wd, out, ws16),
+            "w8a8": lambda: ispa.local_attn_fused_proj_w8a8(sh, qd, kd, vd, wq, sw, out, ws8)}
+    best = {}
+    e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        for name, f in runs.items():
+            f()
+            e0.record()
+            for _ in range(5):
+                f()
+            e1.record()
+            t.cuda.synchronize()
+            best[name] = min(best.get(name, 1e9), e0.elapsed_time(e1) / 5 * 1e3)
+    print(f"\nL-layer step at the 1.3B shape: bf16 projection {best['bf16']:.1f} us, W8A8 {best['w8a8']:.1f} us")
