@@ -211,7 +211,7 @@ int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype,
  *     current), W_new).  workspace: ispa_workspace_bytes(
  *     ISPA_CALL_LOCAL_ATTN_PROJ_W8A8, shape, 0) bytes, 16-byte aligned.  The
  *     attention itself stays in io_dtype (the pages do not say how attention
- *     would be quantised).
+ *     would be quantised).  n_q * d must stay below 2^31 (EUNSUPPORTED).
  */
 int ispa_quantize_weight_fp8(int d_in, int d_out, int w_dtype, const void* w, void* wq_t, float* w_scales,
                              void* stream);

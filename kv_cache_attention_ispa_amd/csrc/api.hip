@@ -278,6 +278,7 @@ int ispa_local_attn_fused_proj_w8a8(const ispa_attn_shape* shape, int io_dtype, 
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return ISPA_EWORKSPACE;
   const hipStream_t s = (hipStream_t)stream;
   const int d = shape->n_heads * shape->head_dim;
+  if ((int64_t)shape->n_q * d >= INT32_MAX) return ISPA_EUNSUPPORTED;   // 32-bit buffer offsets of the product
   const size_t a_bytes = local_a_bytes(shape);
   const size_t vt_bytes = attn_vt_bytes_aligned((int64_t)shape->n_sink + shape->n_hist + shape->n_cur, d);
   uint8_t* aq = (uint8_t*)workspace + a_bytes + vt_bytes;

@@ -103,6 +103,36 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 
+// Epilogue of a wave's 64 x 64 part of a 128 x 128 output tile (wave (wm, wn) owns rows 64 wm ..,
+// columns 64 wn ..; accumulator register r of lane l of block (mi, ni) is element (64 wm + 32 mi +
+// 8 (r/4) + 4 (l/32) + r%4, 64 wn + 32 ni + l%32), the 32x32 MFMA layout): each value times
+// scale(row, col) (tile coordinates) is rounded to T into the wave's own 8 KiB of LDS, which is then
+// written out as 16-byte row pieces, 8 lanes per 128-byte row.  The caller makes sure no wave still
+// reads `lds` (a barrier after the last use); n % 8 == 0.
+template <typename T, typename F>
+__device__ __forceinline__ void store_wave_tile_64(const f32x16 (&acc)[2][2], char* lds, typename T::storage* out,
+                                                   int64_t ld, int m0, int n0, int m, int n, F scale) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hi = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int c = 32 * ni + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rr = 32 * mi + 8 * (r >> 2) + 4 * hi + (r & 3);
+        *(typename T::storage*)(lds + rr * 128 + 2 * c) = Cvt<T>::from_f(acc[mi][ni][r] * scale(64 * wm + rr, 64 * wn + c));
+      }
+    }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = lane + 64 * i, rr = q >> 3, ch = q & 7;
+    const int row = m0 + 64 * wm + rr, col = n0 + 64 * wn + 8 * ch;
+    if (row < m && col < n) *(u32x4*)(out + (int64_t)row * ld + col) = *(const u32x4*)(lds + rr * 128 + 16 * ch);
+  }
+}
+
 __device__ __forceinline__ float wave_max_xor32(float x) {
   return fmaxf(x, __shfl_xor(x, 32));
 }

@@ -412,18 +412,9 @@ __global__ __launch_bounds__(NT, 2) void proj16_kernel(ProjArgs p) {
     if (nxt) sstore(lds + ((s + 1) & 1) * P_STAGE);
     __syncthreads();
   }
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int col = n0 + 64 * wn + 32 * ni + (lane & 31);
-      if (col >= p.n) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + 64 * wm + 32 * mi + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (row < p.m) p.out[(int64_t)row * p.n + col] = Cvt<T>::from_f(acc[mi][ni][r]);
-      }
-    }
+  // each wave's 64 x 64 part through its own 8 KiB of the (now idle) stage buffers
+  store_wave_tile_64<T>(acc, lds + 8192 * wave, (typename T::storage*)p.out, p.n, m0, n0, p.m, p.n,
+                        [](int, int) { return 1.f; });
 }
 
 }  // namespace
