@@ -179,8 +179,9 @@ int ispa_absorb_solve(int d, const float* G, const float* C, const float* D,
  *   q [n_q, d], k/v [n_k, d] with the layout of ispa_attn_shape (history rows,
  *   if any, are skipped), w_new [d, d], out [n_q, d]; all io_dtype BF16 or F16.
  *   workspace: at least ispa_workspace_bytes(ISPA_CALL_LOCAL_ATTN_PROJ, shape, d)
- *   bytes, 16-byte aligned (the local attention output between the two kernels
- *   and the transposed copy of V); n_k * d * 2 below 2^31 as for ispa_dual_attn.
+ *   bytes, 16-byte aligned (the local attention output between the two kernels,
+ *   the transposed copy of V and a transposed copy of w_new); n_k * d * 2 and
+ *   n_q * d * 2 below 2^31 (ISPA_EUNSUPPORTED otherwise).
  */
 int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype,
                                const void* q, const void* k, const void* v, const void* w_new,

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libispa.so")
-SOURCES = ["api.hip", "attn.hip", "gram.hip", "solve.hip", "kv.hip", "fp8.hip"]
+SOURCES = ["api.hip", "attn.hip", "gram.hip", "solve.hip", "kv.hip", "fp8.hip", "proj.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled for all device code.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",

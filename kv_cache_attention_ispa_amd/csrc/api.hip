@@ -34,6 +34,12 @@ size_t local_a_bytes(const ispa_attn_shape* s) {
   return ((size_t)s->n_q * s->n_heads * s->head_dim * 2 + 255) / 256 * 256;
 }
 
+// The transposed copy of W_new the 16-bit projection reads ([d, d] 16-bit).
+size_t w_t_bytes(const ispa_attn_shape* s) {
+  const size_t d = (size_t)s->n_heads * s->head_dim;
+  return (d * d * 2 + 255) / 256 * 256;
+}
+
 // The E4M3 codes of the local attention output and their per-token scales (W8A8 projection).
 size_t w8a8_codes_bytes(const ispa_attn_shape* s) {
   return ((size_t)s->n_q * s->n_heads * s->head_dim + 255) / 256 * 256;
@@ -81,7 +87,8 @@ size_t ispa_workspace_bytes(int call_id, const ispa_attn_shape* shape, int d) {
     case ISPA_CALL_LOCAL_ATTN_PROJ:
       if (!shape || shape->n_q < 1 || shape->n_heads < 1) return 0;
       return local_a_bytes(shape) + attn_vt_bytes_aligned((int64_t)shape->n_sink + shape->n_hist + shape->n_cur,
-                                                          (int64_t)shape->n_heads * shape->head_dim);
+                                                          (int64_t)shape->n_heads * shape->head_dim) +
+             w_t_bytes(shape);
     case ISPA_CALL_LOCAL_ATTN_PROJ_W8A8:
       if (!shape || shape->n_q < 1 || shape->n_heads < 1) return 0;
       return local_a_bytes(shape) + attn_vt_bytes_aligned((int64_t)shape->n_sink + shape->n_hist + shape->n_cur,
@@ -204,6 +211,7 @@ int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype, const
   if (st) return st;
   if (io_dtype != ISPA_BF16 && io_dtype != ISPA_F16) return ISPA_EUNSUPPORTED;
   if (shape->head_dim != 128 || !fits_buffer(shape)) return ISPA_EUNSUPPORTED;
+  if ((int64_t)shape->n_q * shape->n_heads * shape->head_dim * 2 >= INT32_MAX) return ISPA_EUNSUPPORTED;
   if (!q || !k || !v || !w_new || !out) return ISPA_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(w_new) || !aligned16(out)) return ISPA_EINVAL;
   const size_t need = ispa_workspace_bytes(ISPA_CALL_LOCAL_ATTN_PROJ, shape, 0);
@@ -229,12 +237,15 @@ int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype, const
   L.n_heads = shape->n_heads;
   L.head_dim = shape->head_dim;
   L.scale = eff_scale(shape);
+  const size_t vt_bytes = attn_vt_bytes_aligned((int64_t)shape->n_sink + shape->n_hist + shape->n_cur,
+                                                (int64_t)shape->n_heads * shape->head_dim);
   L.ws = (char*)workspace + local_a_bytes(shape);
-  L.ws_bytes = workspace_bytes - local_a_bytes(shape);
+  L.ws_bytes = vt_bytes;
   hipError_t e = launch_attention(L, s);
   if (e != hipSuccess) return ISPA_EHIP;
   const int d = shape->n_heads * shape->head_dim;
   ProjLaunch P;
+  P.bt = (char*)workspace + local_a_bytes(shape) + vt_bytes;
   P.io = io_dtype;
   P.m = shape->n_q;
   P.n = d;

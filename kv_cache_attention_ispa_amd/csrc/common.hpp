@@ -103,7 +103,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 
-// Epilogue of a wave's 64 x 64 part of a 128 x 128 output tile (wave (wm, wn) owns rows 64 wm ..,
+// Epilogue of a wave's 64 x 64 part of a 128-column output tile (wave w = (wm, wn) = (w / 2, w % 2) owns rows 64 wm ..
 // columns 64 wn ..; accumulator register r of lane l of block (mi, ni) is element (64 wm + 32 mi +
 // 8 (r/4) + 4 (l/32) + r%4, 64 wn + 32 ni + l%32), the 32x32 MFMA layout): each value times
 // scale(row, col) (tile coordinates) is rounded to T into the wave's own 8 KiB of LDS, which is then

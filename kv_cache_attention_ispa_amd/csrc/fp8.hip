@@ -16,9 +16,7 @@
 //  * wq_colmax_kernel, wq_scale_kernel, wq_quant_kernel: the weights per output channel (block maxima,
 //    scales, codes), written transposed
 //    (Wq^T [d_out, d_in]) so that both operands of the product are contiguous along k;
-//  * proj8_kernel: out = (Aq Wq) * s_a s_w^T on v_mfma_scale_f32_32x32x64_f8f6f4 (block scales set
-//    to 1), 128 x 128 tiles of 4 waves, k in 64-deep stages through a four-deep ring of direct-to-LDS
-//    loads issued three stages ahead.
+//  * the product out = (Aq Wq) s_a s_w^T runs on the shared projection kernel (proj.hip).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -27,7 +25,6 @@
 namespace ispa {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) int i32x8;
 constexpr float kE4M3Max = 448.f;
 
 template <typename T> __device__ __forceinline__ float ld_elem(const void* p, int64_t i) {
@@ -127,130 +124,6 @@ __global__ __launch_bounds__(256) void wq_quant_kernel(const void* w, int d_in, 
   }
 }
 
-// ---- out = (Aq Wq) s_a s_w^T ----
-// A operand: lane l holds Aq[m0 + l%32][k0 + 32 (l/32) + 0..31] (32 codes, 8 dwords); B operand:
-// lane l holds Wq^T[n0 + l%32][k0 + 32 (l/32) + 0..31]; accumulator register r of lane l is
-// out[8 (r/4) + 4 (l/32) + r%4][l%32] of the 32 x 32 block.  A stage is k0 .. k0 + 63 of 128 rows of
-// each operand, 64-byte LDS rows; 16-byte chunk c of row r sits at r*64 + 16 (c ^ ((r >> 2) & 3)), so
-// the 16 rows a quarter-wave reads at one chunk hit 16 distinct 16-byte bank groups.  Stages stream
-// through a four-deep ring with direct-to-LDS buffer loads issued three stages ahead (a 1 KiB load
-// instruction covers 16 rows; lane l fills byte 16 l, i.e. row 16 i + l/4 at swizzled position l%4,
-// so it loads logical chunk (l%4) ^ ((row >> 2) & 3)).  Every ring slot is its own LDS array and the
-// stage loop is unrolled by the ring depth, so each wait covers exactly the stage it needs.
-constexpr int P8_BK = 64;                        // k per stage (one MFMA)
-constexpr int P8_TILE = 128 * P8_BK;             // bytes of one operand stage
-__device__ __forceinline__ int p8_off(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
-
-template <typename T>
-__global__ __launch_bounds__(256, 2) void proj8_kernel(const uint8_t* aq, const float* sa, const uint8_t* wq_t,
-                                                        const float* sw, void* out, int m, int n, int k, int tiles_m,
-                                                        int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t a0[P8_TILE], a1[P8_TILE], a2[P8_TILE], a3[P8_TILE];
-  __shared__ __attribute__((aligned(16))) uint8_t b0[P8_TILE], b1[P8_TILE], b2[P8_TILE], b3[P8_TILE];
-  const int logical = xcd_remap(blockIdx.x, tiles_m * tiles_n);
-  const int bn = logical / tiles_m, bm = logical % tiles_m;
-  const int m0 = bm * 128, n0 = bn * 128;
-  const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-
-  // rows past m (n) read past the end of the buffer: zeros
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)aq, (short)0, m * k, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)wq_t, (short)0, n * k, 0x00020000);
-  // wave w issues A instructions 2w, 2w + 1 and B instructions 2w, 2w + 1 of a stage
-  uint32_t aoff[2], boff[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = 16 * (2 * wave + j) + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 2) & 3);
-    aoff[j] = (m0 + row < m) ? (uint32_t)((m0 + row) * k + 16 * c) : 0x80000000u;
-    boff[j] = (n0 + row < n) ? (uint32_t)((n0 + row) * k + 16 * c) : 0x80000000u;
-  }
-  const int n_st = k / P8_BK;
-  auto issue = [&](uint8_t* as, uint8_t* bs, int st) {
-    const bool ok = st < n_st;
-    const uint32_t k0 = (uint32_t)st * P8_BK;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(as + 1024 * (2 * wave + j)), 16,
-                                               ok && aoff[j] != 0x80000000u ? aoff[j] + k0 : 0x80000000u, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(bs + 1024 * (2 * wave + j)), 16,
-                                               ok && boff[j] != 0x80000000u ? boff[j] + k0 : 0x80000000u, 0, 0, 0);
-    }
-  };
-  auto aslot = [&](auto J) -> uint8_t* {
-    constexpr int j = decltype(J)::value;
-    if constexpr (j == 0) return a0;
-    else if constexpr (j == 1) return a1;
-    else if constexpr (j == 2) return a2;
-    else return a3;
-  };
-  auto bslot = [&](auto J) -> uint8_t* {
-    constexpr int j = decltype(J)::value;
-    if constexpr (j == 0) return b0;
-    else if constexpr (j == 1) return b1;
-    else if constexpr (j == 2) return b2;
-    else return b3;
-  };
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-
-  issue(a0, b0, 0);
-  issue(a1, b1, 1);
-  issue(a2, b2, 2);
-  // stage s (slot J = s % 4): wait for its loads, barrier, refill slot (s + 3) % 4, then 4 MFMAs
-  auto step = [&](auto J, int st) {
-    constexpr int j = decltype(J)::value;
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(8));
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    issue(aslot(std::integral_constant<int, (j + 3) % 4>{}), bslot(std::integral_constant<int, (j + 3) % 4>{}), st + 3);
-    const uint8_t* as = aslot(J);
-    const uint8_t* bs = bslot(J);
-    i32x8 af[2], bf[2];
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      const int row = 64 * wm + 32 * mi + (lane & 31);
-      const u32x4 lo = *(const u32x4*)(as + p8_off(row, 2 * hi)), h4 = *(const u32x4*)(as + p8_off(row, 2 * hi + 1));
-      af[mi] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)h4[0], (int)h4[1], (int)h4[2], (int)h4[3]};
-    }
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int row = 64 * wn + 32 * ni + (lane & 31);
-      const u32x4 lo = *(const u32x4*)(bs + p8_off(row, 2 * hi)), h4 = *(const u32x4*)(bs + p8_off(row, 2 * hi + 1));
-      bf[ni] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)h4[0], (int)h4[1], (int)h4[2], (int)h4[3]};
-    }
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mi], bf[ni], acc[mi][ni], 0, 0, 0, 127, 0, 127);
-  };
-  for (int st = 0; st < n_st; st += 4) {
-    step(std::integral_constant<int, 0>{}, st);
-    step(std::integral_constant<int, 1>{}, st + 1);
-    step(std::integral_constant<int, 2>{}, st + 2);
-    step(std::integral_constant<int, 3>{}, st + 3);
-  }
-  __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));   // loads past the last stage (zeros) have landed
-  // per-row and per-column scales of the tile; then each wave's part through its own ring slot
-  __shared__ float sa_t[128], sw_t[128];
-  if (tid < 128) sa_t[tid] = m0 + tid < m ? sa[m0 + tid] : 0.f;
-  else sw_t[tid - 128] = n0 + tid - 128 < n ? sw[n0 + tid - 128] : 0.f;
-  __syncthreads();
-  uint8_t* mine = wave == 0 ? a0 : wave == 1 ? a1 : wave == 2 ? a2 : a3;
-  store_wave_tile_64<T>(acc, (char*)mine, (typename T::storage*)out, n, m0, n0, m, n,
-                        [&](int row, int col) { return sa_t[row] * sw_t[col]; });
-}
-
 }  // namespace
 
 hipError_t launch_quant_rows(int dtype, const void* x, int64_t ldx, int rows, int cols, uint8_t* q, int64_t ldq,
@@ -288,14 +161,5 @@ hipError_t launch_quant_weight(int dtype, const void* w, int d_in, int d_out, ui
   return hipGetLastError();
 }
 
-hipError_t launch_proj8(int out_dtype, const uint8_t* aq, const float* sa, const uint8_t* wq_t, const float* sw,
-                        void* out, int m, int n, int k, hipStream_t s) {
-  const int tm = (m + 127) / 128, tn = (n + 127) / 128;
-  if (out_dtype == DT_BF16)
-    hipLaunchKernelGGL(proj8_kernel<BF16>, dim3(tm * tn), dim3(256), 0, s, aq, sa, wq_t, sw, out, m, n, k, tm, tn);
-  else
-    hipLaunchKernelGGL(proj8_kernel<F16>, dim3(tm * tn), dim3(256), 0, s, aq, sa, wq_t, sw, out, m, n, k, tm, tn);
-  return hipGetLastError();
-}
 
 }  // namespace ispa

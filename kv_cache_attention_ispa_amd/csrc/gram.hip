@@ -1,4 +1,4 @@
-// Absorption statistics and the local-layer projection (gfx950).
+// Absorption statistics (gfx950).
 //
 // The closed-form absorption of the ISPA technical summary (gist.science,
 // nl/pt), section 2, stage 2 "Layer Absorb", needs G = A_loc^T A_loc and
@@ -7,10 +7,6 @@
 // dual-stream kernel writes A_loc and dA feature-major ([d, tokens]), so every
 // statistic is a product X Y^T in which both operands are contiguous along the
 // reduction (token) dimension: the MFMA operands are read as 16-byte rows.
-//
-// Stage 3 "Memory-Efficient Inference" projects the local attention output by
-// W_new = W + dW: a plain row-major GEMM whose B operand is read through the
-// transposing LDS load.
 #include <algorithm>
 
 #include "common.hpp"
@@ -34,8 +30,6 @@ constexpr int NT = 256;
 // operands from L2 and reads 128 B/clk of LDS.
 // ------------------------------------------------------------------------------------------
 constexpr int GB = 128;
-constexpr int GK = 32;                      // (projection below)
-constexpr int G_ROW = GK * 2;               // (projection below)
 constexpr int RK = 64;                      // tokens per Gram stage
 constexpr int R_ROW = RK * 2;               // 128 bytes per staged row
 constexpr int R_XTILE = 2 * GB * R_ROW;     // 256 rows of X: 32 KiB
@@ -44,7 +38,6 @@ constexpr int R_XLOADS = R_XTILE / 1024 / 4, R_YLOADS = R_YTILE / 1024 / 4;   //
 constexpr int R_LOADS = R_XLOADS + R_YLOADS;
 constexpr int G_TPITCH = 36;                // floats per row of a transposed 32 x 32 block in LDS
 
-__device__ __forceinline__ int g_off(int row, int chunk) { return row * G_ROW + ((chunk ^ ((row >> 1) & 3)) << 4); }
 // Gram ring layout: 16-byte chunk c (tokens 8 c .. 8 c + 7) of row r at r * 128 + 16 (c ^ ((r / 2) % 8)):
 // the 16 rows read by one quarter-wave of a ds_read_b128 (same logical chunk) cover all 16 chunk
 // positions of 256 bytes.
@@ -322,101 +315,6 @@ __global__ __launch_bounds__(NT) void gram32_kernel(GramArgs a) {
     }
 }
 
-// ------------------------------------------------------------------------------------------
-// 16-bit projection out[m, n] = A[m, :] @ B[:, n], A [M, K], B [K, N] row-major, fp32 accumulate.
-// 128 x 128 tile, k-step 32; the B operand comes from the row-major tile via transposing reads.
-// ------------------------------------------------------------------------------------------
-constexpr int P_BROW = 128 * 2;            // B tile row: 128 columns, 256 bytes
-constexpr int P_ATILE = 128 * G_ROW;       // A tile: 128 rows x 32 k
-constexpr int P_BTILE = GK * P_BROW;       // B tile: 32 rows x 128 n
-constexpr int P_STAGE = P_ATILE + P_BTILE;
-
-__device__ __forceinline__ int b_swz(int row) { return ((row & 3) << 2) | (((row >> 3) & 1) << 1); }
-__device__ __forceinline__ int b_off(int row, int chunk) { return row * P_BROW + ((chunk ^ b_swz(row)) << 4); }
-
-struct ProjArgs {
-  const uint16_t* a;
-  const uint16_t* b;
-  uint16_t* out;
-  int m, n, k, tiles_m, tiles_n;
-};
-
-template <typename T>
-__global__ __launch_bounds__(NT, 2) void proj16_kernel(ProjArgs p) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * P_STAGE];
-  const int logical = xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n);
-  const int bn = logical / p.tiles_m, bm = logical % p.tiles_m;   // column-block major: B tile reuse per XCD
-  const int m0 = bm * 128, n0 = bn * 128;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hi = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int g = lane >> 4, i16 = lane & 15;
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-
-  u32x4 ar[2], br[2];
-  auto gload = [&](int step) {
-    const int k0 = step * GK;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = (tid >> 2) + 64 * i;            // A: 128 rows x 4 chunks
-      ar[i] = (m0 + row < p.m) ? *(const u32x4*)(p.a + (int64_t)(m0 + row) * p.k + k0 + (tid & 3) * 8)
-                               : u32x4{0, 0, 0, 0};
-      const int brow = (tid >> 4) + 16 * i;           // B: 32 rows x 16 chunks
-      const int bcol = n0 + (tid & 15) * 8;
-      br[i] = (bcol < p.n) ? *(const u32x4*)(p.b + (int64_t)(k0 + brow) * p.n + bcol) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto sstore = [&](char* st) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *(u32x4*)(st + g_off((tid >> 2) + 64 * i, tid & 3)) = ar[i];
-      *(u32x4*)(st + P_ATILE + b_off((tid >> 4) + 16 * i, tid & 15)) = br[i];
-    }
-  };
-  const int n_steps = p.k / GK;
-  gload(0);
-  sstore(lds);
-  __syncthreads();
-  for (int s = 0; s < n_steps; ++s) {
-    char* st = lds + (s & 1) * P_STAGE;
-    const bool nxt = s + 1 < n_steps;
-    if (nxt) gload(s + 1);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      u32x4 af[2], bf[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi) af[mi] = *(const u32x4*)(st + g_off(64 * wm + 32 * mi + (lane & 31), 2 * kk + hi));
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        u32x2 h[2];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int row = 16 * kk + 8 * (g >> 1) + 4 * half + (i16 >> 2);
-          const int col = 64 * wn + 32 * ni + 16 * (g & 1) + 4 * (i16 & 3);
-          const int off = row * P_BROW + (((col >> 3) ^ b_swz(row)) << 4) + 2 * (col & 7);
-          h[half] = lds_read_tr16((const lds_void*)(st + P_ATILE + off));
-        }
-        bf[ni] = u32x4{h[0].x, h[0].y, h[1].x, h[1].y};
-      }
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = mfma32x32x16<T>(af[mi], bf[ni], acc[mi][ni]);
-    }
-    if (nxt) sstore(lds + ((s + 1) & 1) * P_STAGE);
-    __syncthreads();
-  }
-  // each wave's 64 x 64 part through its own 8 KiB of the (now idle) stage buffers
-  store_wave_tile_64<T>(acc, lds + 8192 * wave, (typename T::storage*)p.out, p.n, m0, n0, p.m, p.n,
-                        [](int, int) { return 1.f; });
-}
-
 }  // namespace
 
 hipError_t launch_gram(const GramLaunch& L, hipStream_t s) {
@@ -443,24 +341,6 @@ hipError_t launch_gram(const GramLaunch& L, hipStream_t s) {
     else
       hipLaunchKernelGGL(gram16_kernel<F16>, dim3(items), dim3(3 * NT), 0, s, a);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_proj(const ProjLaunch& L, hipStream_t s) {
-  ProjArgs p;
-  p.a = (const uint16_t*)L.a;
-  p.b = (const uint16_t*)L.b;
-  p.out = (uint16_t*)L.out;
-  p.m = L.m;
-  p.n = L.n;
-  p.k = L.k;
-  p.tiles_m = (L.m + 127) / 128;
-  p.tiles_n = (L.n + 127) / 128;
-  dim3 grid(p.tiles_m * p.tiles_n);
-  if (L.io == DT_BF16)
-    hipLaunchKernelGGL(proj16_kernel<BF16>, grid, dim3(NT), 0, s, p);
-  else
-    hipLaunchKernelGGL(proj16_kernel<F16>, grid, dim3(NT), 0, s, p);
   return hipGetLastError();
 }
 

@@ -58,12 +58,14 @@ struct GramLaunch {
 };
 hipError_t launch_gram(const GramLaunch& L, hipStream_t s);
 
-// out[m, n] = in0 @ in1 for 16-bit row-major operands (local-layer projection), fp32 accumulate.
+// out[m, n] = a @ b for 16-bit row-major operands (local-layer projection), fp32 accumulate; b is
+// first transposed into bt ([n, k], caller-provided scratch).
 struct ProjLaunch {
   int io;
   int m, n, k;
   const void* a;   // [m, k]
   const void* b;   // [k, n]
+  void* bt;        // [n, k] scratch
   void* out;       // [m, n]
 };
 hipError_t launch_proj(const ProjLaunch& L, hipStream_t s);
