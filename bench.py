@@ -44,7 +44,139 @@ def parse():
     p.add_argument("--cpu-queries", type=int, default=1800, help="query rows in the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also launch one plain 1 GiB device copy (for HBM counter calibration)")
+    p.add_argument("--no-secondary", action="store_true",
+                   help="skip the secondary measurements (14B layer, warmup per layer, rollout chunks, cold cache)")
     return p.parse_args()
+
+
+def timed(torch, fn, reps: int, warm: int, stream, before=None) -> dict:
+    """Median / min / max milliseconds of fn() over reps calls, HIP events on the call's stream around
+    each call (before() runs outside the timed span)."""
+    for _ in range(warm):
+        fn()
+    spans = []
+    for _ in range(reps):
+        if before is not None:
+            before()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        spans.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in spans)
+    return {"median": round(ms[len(ms) // 2], 4), "min": round(ms[0], 4), "max": round(ms[-1], 4)}
+
+
+def secondary(torch, ispa, wl, stream, run_attn_1p3b) -> dict:
+    """The secondary figures at the other workload shapes.  Inputs are drawn on the device (seeded
+    N(0,1) bf16, W ~ N(0, 1/d)); times are medians (min, max) of HIP-event spans per call."""
+    out = {}
+    # cold cache: 512 MiB written between calls (the MALL holds 256 MiB)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = timed(torch, run_attn_1p3b, 10, 1, stream, before=lambda: scratch.fill_(1))
+    s2 = wl.LAYER_1P3B.shape
+    out["attn_1p3b_cold"] = {"ms": cold, "tflops_median": round(s2.attn_flops() / cold["median"] / 1e9, 2)}
+    del scratch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20260701)
+    rnd = lambda *sz: torch.randn(sz, generator=g, device="cuda").to(torch.bfloat16)
+
+    def layer_buffers(sh, d):
+        ld = ((sh.n_q + 7) // 8) * 8
+        b = {"ld": ld, "a_full": torch.empty((sh.n_q, d), dtype=torch.bfloat16, device="cuda"),
+             "a_t": torch.empty((d, ld), dtype=torch.float16, device="cuda"),
+             "da_t": torch.empty((d, ld), dtype=torch.float16, device="cuda"),
+             "lse_l": torch.empty((sh.n_heads, sh.n_q), device="cuda"),
+             "lse_h": torch.empty((sh.n_heads, sh.n_q), device="cuda"),
+             "ws": torch.empty(ispa.workspace_bytes(ispa.CALL_DUAL_ATTN, sh), dtype=torch.uint8, device="cuda")}
+        for n in ("G", "C", "D", "dW"):
+            b[n] = torch.empty((d, d), device="cuda")
+        b["ws_solve"] = torch.empty(ispa.workspace_bytes(ispa.CALL_ABSORB_SOLVE, None, d), dtype=torch.uint8,
+                                    device="cuda")
+        b["w_new"] = torch.empty((d, d), dtype=torch.bfloat16, device="cuda")
+        b["eps"] = torch.empty((1,), device="cuda")
+        b["info"] = torch.zeros((1,), dtype=torch.int32, device="cuda")
+        return b
+
+    def dual(sh, q, k, v, b):
+        ispa.dual_attn(sh, q, k, v, a_full=b["a_full"], a_loc_t=b["a_t"], delta_a_t=b["da_t"], ld_stat=b["ld"],
+                       lse_loc=b["lse_l"], lse_hist=b["lse_h"], workspace=b["ws"], stream=stream)
+
+    def solve(W, b, refine):
+        ispa.absorb_solve(b["G"], b["C"], W, 1e-3, True, b["dW"], b["info"], b["ws_solve"], D=b["D"],
+                          w_new=b["w_new"], eps=b["eps"], refine=refine, stream=stream)
+
+    # 14B layer (40 heads x 128, 4680 queries, 1560 + 31200 + 4680 cached rows): one refinement step
+    w = wl.LAYER_14B
+    s4 = w.shape
+    d = s4.d
+    q, k, v = rnd(s4.n_q, d), rnd(s4.n_k, d), rnd(s4.n_k, d)
+    W = (torch.randn((d, d), generator=g, device="cuda") / math.sqrt(d)).to(torch.bfloat16)
+    sh = ispa.AttnShape.of(s4)
+    b = layer_buffers(sh, d)
+    t_attn = timed(torch, lambda: dual(sh, q, k, v, b), 5, 2, stream)
+    t_gram = timed(torch, lambda: ispa.gram_accum(b["a_t"], b["da_t"], s4.n_q, b["G"], b["C"], b["D"], stream=stream),
+                   5, 1, stream)
+    t_solve = timed(torch, lambda: solve(W, b, 1), 3, 1, stream)
+    if int(b["info"].item()) != 0:
+        raise RuntimeError(f"14B-layer solve reported info={int(b['info'].item())}")
+    loc = torch.cat([torch.arange(s4.n_sink), torch.arange(s4.n_sink + s4.n_hist, s4.n_k)]).cuda()
+    k_loc, v_loc = k[loc].contiguous(), v[loc].contiguous()
+    sh_l = ispa.AttnShape(s4.n_q, s4.n_sink, 0, s4.n_cur, s4.n_heads, s4.head_dim, 0.0)
+    ws_l = torch.empty(ispa.workspace_bytes(ispa.CALL_LOCAL_ATTN_PROJ, sh_l), dtype=torch.uint8, device="cuda")
+    y = torch.empty((s4.n_q, d), dtype=torch.bfloat16, device="cuda")
+    t_loc = timed(torch, lambda: ispa.local_attn_fused_proj(sh_l, q, k_loc, v_loc, b["w_new"], y, ws_l,
+                                                             stream=stream), 5, 1, stream)
+    out["layer_14b"] = {
+        "attn_ms": t_attn, "attn_tflops_median": round(s4.attn_flops() / t_attn["median"] / 1e9, 2),
+        "gram_ms": t_gram, "solve_refine1_ms": t_solve,
+        "absorb_ms_per_layer_median": round(t_gram["median"] + t_solve["median"], 4),
+        "local_layer_step_ms": t_loc,
+        "local_layer_tflops_median": round((s4.local_flops() + 2.0 * s4.n_q * d * d) / t_loc["median"] / 1e9, 2)}
+    del q, k, v, W, b, k_loc, v_loc, ws_l, y
+
+    # warmup of one 1.3B layer: 4 chunks (history 0, 4680, 9360, 14040 rows), statistics accumulated
+    # over the 18720 warmup tokens, then the solve with epsilon
+    s2 = wl.LAYER_1P3B.shape
+    d = s2.d
+    n_max = s2.n_sink + 3 * 4680 + s2.n_cur
+    q, k, v = rnd(s2.n_q, d), rnd(n_max, d), rnd(n_max, d)
+    W = (torch.randn((d, d), generator=g, device="cuda") / math.sqrt(d)).to(torch.bfloat16)
+    shapes = [ispa.AttnShape(s2.n_q, s2.n_sink, 4680 * c, s2.n_cur, s2.n_heads, s2.head_dim, 0.0) for c in range(4)]
+    b = layer_buffers(shapes[-1], d)
+
+    def warmup_layer():
+        for c, shc in enumerate(shapes):
+            n_k = shc.n_sink + shc.n_hist + shc.n_cur
+            dual(shc, q, k[:n_k], v[:n_k], b)
+            ispa.gram_accum(b["a_t"], b["da_t"], s2.n_q, b["G"], b["C"], b["D"], accumulate=c > 0, stream=stream)
+        solve(W, b, 0)
+
+    t_warm = timed(torch, warmup_layer, 5, 1, stream)
+    flops = sum(4.0 * s2.n_q * (sh_.n_sink + sh_.n_hist + sh_.n_cur) * d for sh_ in shapes)
+    out["warmup_1p3b_per_layer"] = {"chunks": 4, "tokens": 4 * s2.n_q, "ms": t_warm,
+                                    "attn_gflop": round(flops / 1e9, 2)}
+    del q, k, v, W, b
+
+    # rollout of the 1.3B model: F-layer (full attention over 1560 (3c + 4) rows) at chunks 4, 20, 39
+    n_max = 1560 * (3 * 39 + 4)
+    q, k, v = rnd(s2.n_q, d), rnd(n_max, d), rnd(n_max, d)
+    a_full = torch.empty((s2.n_q, d), dtype=torch.bfloat16, device="cuda")
+    f_layer = {}
+    for c in (4, 20, 39):
+        n_k = 1560 * (3 * c + 4)
+        shc = ispa.AttnShape(s2.n_q, s2.n_sink, n_k - s2.n_sink - s2.n_cur, s2.n_cur, s2.n_heads, s2.head_dim, 0.0)
+        ws = torch.empty(ispa.workspace_bytes(ispa.CALL_DUAL_ATTN, shc), dtype=torch.uint8, device="cuda")
+        t = timed(torch, lambda: ispa.dual_attn(shc, q, k[:n_k], v[:n_k], a_full=a_full, workspace=ws, stream=stream),
+                  5, 1, stream)
+        f_layer[f"chunk_{c}"] = {"n_k": n_k, "ms": t,
+                                 "tflops_median": round(4.0 * s2.n_q * n_k * d / t["median"] / 1e9, 2)}
+        del ws
+    out["rollout_1p3b_f_layer"] = f_layer
+    del q, k, v, a_full
+    torch.cuda.synchronize()
+    return out
 
 
 def attn_source_hash() -> str:
@@ -196,6 +328,13 @@ def main():
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "flops_per_launch": attn_flops, "avg_launch_ms": round(attn_ms, 4)},
     }
+    if not args.no_secondary:
+        attn_ms_all = np.sort(seg[:, 0])
+        result["attn_ms_stats"] = {"median": round(float(np.median(attn_ms_all)), 4),
+                                   "min": round(float(attn_ms_all[0]), 4), "max": round(float(attn_ms_all[-1]), 4)}
+        run_attn = lambda: ispa.dual_attn(shape, q, k, v, a_full=a_full, a_loc_t=a_loc_t, delta_a_t=da_t, ld_stat=ld,
+                                          lse_loc=lse_l, lse_hist=lse_h, workspace=ws_attn, stream=stream)
+        result["secondary"] = secondary(torch, ispa, wl, stream, run_attn)
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

@@ -603,47 +603,97 @@ __global__ __launch_bounds__(SW_THREADS) void sweep_kernel(SweepArgs a) {
   sw_store(a.Bx, d, r, q, v, false);
 }
 
-// out = A B accumulated in fp64 (A, B fp32 [d, d] row-major); 64 x 64 tile per work-group,
-// 4 x 4 outputs per thread.  MODE 0: R64 = A B (fp64 store).  MODE 1: the refinement residual
-// r = R64 - lambda dW - A B with A = G and B = dW (fp32 store).
+// out = A B accumulated in fp64 (A, B fp32 [d, d] row-major; products of fp32 values are exact in
+// fp64) on v_mfma_f64_16x16x4f64.  128 x 128 tiles of 4 waves (2 x 2 of 64 x 64, each 4 x 4 blocks of
+// 16 x 16); k in stages of 16 staged through LDS as fp64 (A row-major with an odd pitch, so the 16
+// rows a quarter-wave reads at one k fall in distinct banks; B row-major), the next stage's global
+// loads held in registers while the current one multiplies; one barrier per stage.
+// MFMA operands: lane l holds A[16 i + l%16][4 s + l/16] and B[4 s + l/16][16 j + l%16]; result
+// register r of lane l is element (16 i + l/16 + 4 r, 16 j + l%16) (rows interleaved; a probe of the
+// instruction on the device fixed this).
+// MODE 0: R64 = A B (fp64 store).  MODE 1: the refinement residual r = R64 - lambda dW - A B with
+// A = G and B = dW (fp32 store).  d is a multiple of 32.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+constexpr int G64_AP = 17, G64_BP = 130;   // LDS pitches in doubles
+
 template <int MODE>
-__global__ __launch_bounds__(NT) void gemm64_kernel(const float* A, const float* B, int d, const Scalars* sc,
-                                                    double* R64, float* r) {
-  __shared__ float as[16][65];
-  __shared__ float bs[16][65];
-  const int tpd = (d + 63) / 64;
-  const int i0 = (blockIdx.x / tpd) * 64, j0 = (blockIdx.x % tpd) * 64;
-  const int tid = threadIdx.x, ti = tid / 16, tj = tid % 16;
-  double acc[4][4] = {};
-  for (int k0 = 0; k0 < d; k0 += 16) {
-    __syncthreads();
-    for (int e = tid; e < 64 * 16; e += NT) {
-      const int a = e / 16, kk = e % 16;
-      as[kk][a] = (i0 + a < d && k0 + kk < d) ? A[(int64_t)(i0 + a) * d + k0 + kk] : 0.f;
-      const int kk2 = e / 64, b = e % 64;
-      bs[kk2][b] = (j0 + b < d && k0 + kk2 < d) ? B[(int64_t)(k0 + kk2) * d + j0 + b] : 0.f;
+__global__ __launch_bounds__(NT, 2) void gemm64_kernel(const float* A, const float* B, int d, const Scalars* sc,
+                                                       double* R64, float* r) {
+  __shared__ double as[2][128 * G64_AP];
+  __shared__ __attribute__((aligned(16))) double bs[2][16 * G64_BP];
+  const int tpd = (d + 127) / 128;
+  const int i0 = (blockIdx.x / tpd) * 128, j0 = (blockIdx.x % tpd) * 128;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, lr = lane & 15, lk = lane >> 4;
+  f64x4 acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f64x4{0.0, 0.0, 0.0, 0.0};
+  // stage loads: A rows i0 + q/4, columns k0 + 4 (q%4) .. +3; B row k0 + q/32, columns j0 + 4 (q%32) .. +3
+  f32x4 ra[2], rb[2];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int q = tid + NT * h;
+      const int ar = q >> 2, ac = 4 * (q & 3), br = q >> 5, bc = 4 * (q & 31);
+      ra[h] = i0 + ar < d ? *(const f32x4*)(A + (int64_t)(i0 + ar) * d + k0 + ac) : f32x4{0.f, 0.f, 0.f, 0.f};
+      rb[h] = j0 + bc < d ? *(const f32x4*)(B + (int64_t)(k0 + br) * d + j0 + bc) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int q = tid + NT * h;
+      const int ar = q >> 2, ac = 4 * (q & 3), br = q >> 5, bc = 4 * (q & 31);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) as[buf][ar * G64_AP + ac + e] = (double)ra[h][e];
+      double* bp = &bs[buf][br * G64_BP + bc];
+      *(f64x2*)bp = f64x2{(double)rb[h][0], (double)rb[h][1]};
+      *(f64x2*)(bp + 2) = f64x2{(double)rb[h][2], (double)rb[h][3]};
+    }
+  };
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int n_st = d / 16;
+  for (int st = 0; st < n_st; ++st) {
+    const int cur = st & 1;
+    if (st + 1 < n_st) gload(16 * (st + 1));
+    const double* ap = &as[cur][(64 * wm + lr) * G64_AP + lk];
+    const double* bp = &bs[cur][lk * G64_BP + 64 * wn + lr];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      double af[4], bf[4];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) af[mi] = ap[16 * mi * G64_AP + 4 * kk];
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) bf[ni] = bp[4 * kk * G64_BP + 16 * ni];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+    }
+    if (st + 1 < n_st) sstore(cur ^ 1);
     __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk)
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) acc[u][w] = fma((double)as[kk][ti * 4 + u], (double)bs[kk][tj * 4 + w], acc[u][w]);
   }
+  const double lam = MODE == 1 ? (double)sc->lambda : 0.0;
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int i = i0 + ti * 4 + u, j = j0 + tj * 4 + w;
-      if (i < d && j < d) {
-        const int64_t e = (int64_t)i * d + j;
-        if (MODE == 0)
-          R64[e] = acc[u][w];
-        else
-          r[e] = (float)(R64[e] - (double)sc->lambda * (double)B[e] - acc[u][w]);
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = i0 + 64 * wm + 16 * mi + lk + 4 * q, j = j0 + 64 * wn + 16 * ni + lr;
+        if (i < d && j < d) {
+          const int64_t e = (int64_t)i * d + j;
+          if (MODE == 0)
+            R64[e] = acc[mi][ni][q];
+          else
+            r[e] = (float)(R64[e] - lam * (double)B[e] - acc[mi][ni][q]);
+        }
       }
-    }
 }
 
 // Partial dot products for epsilon: <D,P>, <G,P>, <W,R>, <dW,R>, <dW,dW> (fp64 per block), row by row.
@@ -824,7 +874,7 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
   if (L.refine > 0) {
     // iterative refinement: r = C W - (G + lambda I) dW with fp64 accumulation (C W formed once in
     // fp64), then dW += (L^-1)^T (L^-1 r) with the fp32 factor
-    const int tpd = (d + 63) / 64;
+    const int tpd = (d + 127) / 128;
     hipLaunchKernelGGL(gemm64_kernel<0>, dim3(tpd * tpd), dim3(NT), 0, s, L.C, w.Wf, d, w.sc, w.R64, nullptr);
     ISPA_TRY(hipGetLastError());
     for (int it = 0; it < L.refine; ++it) {
