@@ -133,3 +133,44 @@ def test_w8a8_l_layer_1p3b_sampled_rows_and_timing():
             t.cuda.synchronize()
             best[name] = min(best.get(name, 1e9), e0.elapsed_time(e1) / 5 * 1e3)
     print(f"\nL-layer step at the 1.3B shape: bf16 projection {best['bf16']:.1f} us, W8A8 {best['w8a8']:.1f} us")
+
+
+def test_l_layer_14b_sampled_rows():
+    """Both L-layer variants at the 14B shape (d = 5120 = 40 heads x 128; 4680 queries over sink
+    1560 + current 4680 rows), on sampled rows (the first and the last, ragged, output tiles
+    included) against the oracle.
+
+    16-bit: random inputs, the attention tolerance.  W8A8: the activation codes are decisions on the
+    attention output, whose bf16 rounding on the GPU differs from the exact one in many elements;
+    about 1/32 of those differences move an E4M3 code by one step (1/8 of the value), and over 5120
+    terms such flips can reach the 2e-2 bar (1.3B-shaped random inputs stay below it, see above).  So
+    the full-size product is pinned on inputs whose attention output is exact: Q = 0 makes every
+    probability 1 and every local V row is the same bf16 vector c, so the output is c (6240 c is
+    exact in fp32) on both sides, the codes agree, and each output may differ from the oracle's only
+    by its own bf16 rounding (half a unit, 2^-9 relative; one unit where the fp32 sums sit at a tie)."""
+    import kv_cache_attention_ispa_amd as ispa
+    t = torch()
+    n_q, n_s, n_c, H = 4680, 1560, 4680, 40
+    sh = wl.AttnShape(n_q, n_s, 0, n_c, H, 128)
+    d = sh.d
+    rng = np.random.default_rng(5120)
+    q = wl.round_to(rng.standard_normal((n_q, d)), "bf16")
+    k = wl.round_to(rng.standard_normal((sh.n_k, d)), "bf16")
+    v = wl.round_to(rng.standard_normal((sh.n_k, d)), "bf16")
+    W = wl.round_to(rng.standard_normal((d, d)) / math.sqrt(d), "bf16")
+    s = ispa.AttnShape.of(sh)
+    out16 = t.empty((n_q, d), dtype=t.bfloat16, device="cuda")
+    ws16 = t.empty(ispa.workspace_bytes(ispa.CALL_LOCAL_ATTN_PROJ, s), dtype=t.uint8, device="cuda")
+    ispa.local_attn_fused_proj(s, dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(W, "bf16"), out16, ws16)
+    t.cuda.synchronize()
+    got16 = host(out16)
+    rows = np.unique(np.concatenate([np.arange(0, n_q, 331), [255, 256, 4607, 4608, n_q - 1]]))
+    ref16 = oracle.local_layer_output(q[rows], k, v, n_s, n_c, H, W, threads=8)
+    assert maxrel(got16[rows], ref16) <= 2e-2
+    q0 = np.zeros_like(q)
+    v_c = np.repeat(wl.round_to(rng.standard_normal((1, d)), "bf16"), sh.n_k, axis=0)
+    got8 = _l_layer_w8a8(sh, q0, k, v_c, W, "bf16")[rows]
+    ref8 = fp8.local_layer_output_w8a8(q0[rows], k, v_c, n_s, n_c, H, W, threads=8)
+    assert np.all(np.abs(got8 - ref8) <= 2.0 ** -8 * np.abs(ref8) + 1e-5 * np.abs(ref8).max())
+    print(f"\n14B L-layer: 16-bit max-rel {maxrel(got16[rows], ref16):.2e}, W8A8 (exact attention) max-rel "
+          f"{maxrel(got8, ref8):.2e}")
