@@ -219,7 +219,7 @@ int ispa_quantize_weight_fp8(int d_in, int d_out, int w_dtype, const void* w, vo
 /*   ispa_quantize_rows_fp8: the activation side on its own: x [rows, cols] (row
  *     stride ldx elements; F32, BF16 or F16) -> q [rows, cols] E4M3 codes (row
  *     stride ldq bytes) and scales [rows] fp32, one scale per row.  cols % 8
- *     == 0, ldq % 8 == 0. */
+ *     == 0, ldx % 8 == 0, ldq % 8 == 0 (EINVAL otherwise). */
 int ispa_quantize_rows_fp8(int rows, int cols, int dtype, const void* x, int64_t ldx, void* q, int64_t ldq,
                            float* scales, void* stream);
 int ispa_local_attn_fused_proj_w8a8(const ispa_attn_shape* shape, int io_dtype,

@@ -268,7 +268,8 @@ int ispa_quantize_weight_fp8(int d_in, int d_out, int w_dtype, const void* w, vo
 
 int ispa_quantize_rows_fp8(int rows, int cols, int dtype, const void* x, int64_t ldx, void* q, int64_t ldq,
                            float* scales, void* stream) {
-  if (rows < 1 || cols < 1 || cols % 8 != 0 || ldx < cols || ldq < cols || ldq % 8 != 0) return ISPA_EINVAL;
+  if (rows < 1 || cols < 1 || cols % 8 != 0 || ldx < cols || ldx % 8 != 0 || ldq < cols || ldq % 8 != 0)
+    return ISPA_EINVAL;
   if (!valid_dtype(dtype)) return ISPA_EINVAL;
   if (!x || !q || !scales) return ISPA_EINVAL;
   if (!aligned16(x) || !aligned16(q) || !aligned4(scales)) return ISPA_EINVAL;

@@ -11,8 +11,9 @@
 // hence the explicit clamp.
 //
 // Kernels:
-//  * quant_rows_kernel: one wave per row of a [rows, cols] matrix (16-bit or fp32): absmax, scale,
-//    codes written row-major -- the activations, token by token;
+//  * quant_rows_kernel: one wave per row of a [rows, cols] matrix (16-bit or fp32), read once with
+//    16-byte loads and kept in registers (rows up to 5120 values): absmax, scale, codes written
+//    row-major -- the activations, token by token;
 //  * wq_colmax_kernel, wq_scale_kernel, wq_quant_kernel: the weights per output channel (block maxima,
 //    scales, codes), written transposed
 //    (Wq^T [d_out, d_in]) so that both operands of the product are contiguous along k;
@@ -42,26 +43,75 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
 __device__ __forceinline__ float e4m3_scale(float amax) { return amax > 0.f ? amax / kE4M3Max : 1.f; }
 
 // ---- activations: one wave per row, 8 consecutive values per lane and step ----
-template <typename T>
+// eight consecutive values of a row as floats (one 16-byte load for 16-bit types, two for fp32)
+template <typename T> __device__ __forceinline__ void ld8(const void* p, int64_t i, float (&v)[8]) {
+  if constexpr (sizeof(typename T::storage) == 2) {
+    const u32x4 r = *(const u32x4*)((const typename T::storage*)p + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = Cvt<T>::to_f((typename T::storage)(r[e] & 0xFFFFu));
+      v[2 * e + 1] = Cvt<T>::to_f((typename T::storage)(r[e] >> 16));
+    }
+  } else {
+    const f32x4 a = *(const f32x4*)((const float*)p + i), b = *(const f32x4*)((const float*)p + i + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = a[e];
+      v[4 + e] = b[e];
+    }
+  }
+}
+
+// The row stays in registers between the maximum and the codes when it has at most 512 NREG values
+// per 64 lanes (NREG > 0); NREG = 0 reads it twice.
+template <typename T, int NREG>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* x, int64_t ldx, int rows, int cols, uint8_t* q,
                                                          int64_t ldq, float* scales) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int64_t base = (int64_t)row * ldx;
+  uint8_t* qr = q + (int64_t)row * ldq;
   float amax = 0.f;
-  for (int c = 8 * lane; c < cols; c += 512)
+  if constexpr (NREG > 0) {
+    float v[NREG][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(ld_elem<T>(x, base + c + e)));
+    for (int j = 0; j < NREG; ++j) {
+      const int c = 8 * lane + 512 * j;
+      if (c < cols) ld8<T>(x, base + c, v[j]);
+      else
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-  const float s = e4m3_scale(amax);
-  if (lane == 0) scales[row] = s;
-  for (int c = 8 * lane; c < cols; c += 512) {
+        for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const float s = e4m3_scale(amax);
+    if (lane == 0) scales[row] = s;
+#pragma unroll
+    for (int j = 0; j < NREG; ++j) {
+      const int c = 8 * lane + 512 * j;
+      if (c < cols)
+        *(u32x2*)(qr + c) = u32x2{e4m3_pack4(v[j][0] / s, v[j][1] / s, v[j][2] / s, v[j][3] / s),
+                                  e4m3_pack4(v[j][4] / s, v[j][5] / s, v[j][6] / s, v[j][7] / s)};
+    }
+  } else {
     float v[8];
+    for (int c = 8 * lane; c < cols; c += 512) {
+      ld8<T>(x, base + c, v);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = ld_elem<T>(x, base + c + e) / s;
-    *(u32x2*)(q + (int64_t)row * ldq + c) = u32x2{e4m3_pack4(v[0], v[1], v[2], v[3]), e4m3_pack4(v[4], v[5], v[6], v[7])};
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const float s = e4m3_scale(amax);
+    if (lane == 0) scales[row] = s;
+    for (int c = 8 * lane; c < cols; c += 512) {
+      ld8<T>(x, base + c, v);
+      *(u32x2*)(qr + c) = u32x2{e4m3_pack4(v[0] / s, v[1] / s, v[2] / s, v[3] / s),
+                                e4m3_pack4(v[4] / s, v[5] / s, v[6] / s, v[7] / s)};
+    }
   }
 }
 
@@ -124,17 +174,25 @@ __global__ __launch_bounds__(256) void wq_quant_kernel(const void* w, int d_in, 
   }
 }
 
+template <typename T>
+void quant_rows_t(const void* x, int64_t ldx, int rows, int cols, uint8_t* q, int64_t ldq, float* scales,
+                  hipStream_t s) {
+  const dim3 grid((rows + 3) / 4);
+  if (cols <= 512 * 4)
+    hipLaunchKernelGGL((quant_rows_kernel<T, 4>), grid, dim3(256), 0, s, x, ldx, rows, cols, q, ldq, scales);
+  else if (cols <= 512 * 10)
+    hipLaunchKernelGGL((quant_rows_kernel<T, 10>), grid, dim3(256), 0, s, x, ldx, rows, cols, q, ldq, scales);
+  else
+    hipLaunchKernelGGL((quant_rows_kernel<T, 0>), grid, dim3(256), 0, s, x, ldx, rows, cols, q, ldq, scales);
+}
+
 }  // namespace
 
 hipError_t launch_quant_rows(int dtype, const void* x, int64_t ldx, int rows, int cols, uint8_t* q, int64_t ldq,
                              float* scales, hipStream_t s) {
-  const dim3 grid((rows + 3) / 4);
-  if (dtype == DT_BF16)
-    hipLaunchKernelGGL(quant_rows_kernel<BF16>, grid, dim3(256), 0, s, x, ldx, rows, cols, q, ldq, scales);
-  else if (dtype == DT_F16)
-    hipLaunchKernelGGL(quant_rows_kernel<F16>, grid, dim3(256), 0, s, x, ldx, rows, cols, q, ldq, scales);
-  else
-    hipLaunchKernelGGL(quant_rows_kernel<F32>, grid, dim3(256), 0, s, x, ldx, rows, cols, q, ldq, scales);
+  if (dtype == DT_BF16) quant_rows_t<BF16>(x, ldx, rows, cols, q, ldq, scales, s);
+  else if (dtype == DT_F16) quant_rows_t<F16>(x, ldx, rows, cols, q, ldq, scales, s);
+  else quant_rows_t<F32>(x, ldx, rows, cols, q, ldq, scales, s);
   return hipGetLastError();
 }
 

@@ -147,3 +147,31 @@ def test_kv_cache_rejects_bad_arguments_without_allocating(L):
     assert L.ispa_kv_append_chunk(None, 0, FAKE, FAKE, None) == EINVAL
     assert L.ispa_kv_write_sink(None, 0, FAKE, FAKE, None) == EINVAL
     assert L.ispa_kv_release_history(None, 0, None) == EINVAL
+
+
+def test_w8a8_calls_reject_bad_arguments(L):
+    """ispa_quantize_weight_fp8, ispa_quantize_rows_fp8 and ispa_local_attn_fused_proj_w8a8: sizes,
+    strides, dtypes, NULL pointers and short workspaces fail on the host."""
+    qw = lambda d_in=128, d_out=64, dt=1, w=FAKE, wq=FAKE, sc=FAKE: L.ispa_quantize_weight_fp8(d_in, d_out, dt, w, wq,
+                                                                                                  sc, None)
+    assert qw(d_in=96) == EINVAL                 # d_in % 64
+    assert qw(d_out=66) == EINVAL                # d_out % 4
+    assert qw(dt=7) == EINVAL
+    assert qw(wq=0) == EINVAL
+    assert qw(w=FAKE + 4) == EINVAL              # misaligned
+    qr = lambda rows=4, cols=64, dt=1, ldx=64, ldq=64, q=FAKE: L.ispa_quantize_rows_fp8(rows, cols, dt, FAKE, ldx, q,
+                                                                                       ldq, FAKE, None)
+    assert qr(cols=60) == EINVAL                 # cols % 8
+    assert qr(ldx=60) == EINVAL                  # ldx < cols
+    assert qr(ldx=68) == EINVAL                  # ldx % 8 (16-byte row loads)
+    assert qr(ldq=68) == EINVAL                  # ldq % 8
+    assert qr(rows=0) == EINVAL
+    assert qr(q=0) == EINVAL
+    sh = ispa.AttnShape(64, 8, 0, 64, 2, 128, 0.0)
+    need = ispa.workspace_bytes(ispa.CALL_LOCAL_ATTN_PROJ_W8A8, sh)
+    f = lambda io=1, wq=FAKE, ws=FAKE, wsb=need: L.ispa_local_attn_fused_proj_w8a8(
+        ctypes.byref(sh), io, FAKE, FAKE, FAKE, wq, FAKE, FAKE, ws, wsb, None)
+    assert f(io=0) == EUNSUPPORTED               # fp32 io
+    assert f(wq=0) == EINVAL
+    assert f(ws=0) == EWORKSPACE
+    assert f(wsb=need - 1) == EWORKSPACE

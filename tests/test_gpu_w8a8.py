@@ -38,13 +38,15 @@ def test_weight_codes_and_scales_bit_exact(w_dtype):
     assert np.array_equal(wq.cpu().numpy(), codes)
 
 
-@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
-def test_row_codes_and_scales_bit_exact(x_dtype):
+@pytest.mark.parametrize("x_dtype,cols", [("bf16", 1536), ("f32", 1536), ("f16", 5120), ("bf16", 6144)])
+def test_row_codes_and_scales_bit_exact(x_dtype, cols):
+    """Rows held in registers (up to 2048 and 5120 values) and rows read twice (6144 values)."""
     import kv_cache_attention_ispa_amd as ispa
     t = torch()
-    rows, cols, ld = 70, 1536, 1536 + 16
+    rows, ld = 70, cols + 16
     rng = np.random.default_rng(12)
-    X = wl.round_to(rng.standard_normal((rows, cols)) * rng.uniform(1e-4, 50, (rows, 1)), x_dtype)
+    X = wl.round_to(rng.standard_normal((rows, cols)) * rng.uniform(1e-3 if x_dtype == "f16" else 1e-4, 50, (rows, 1)),
+                    x_dtype)
     X[3] = 0.0
     Xp = np.zeros((rows, ld))
     Xp[:, :cols] = X
