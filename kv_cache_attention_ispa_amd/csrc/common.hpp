@@ -109,6 +109,11 @@ constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 // scale(row, col) (tile coordinates) is rounded to T into the wave's own 8 KiB of LDS, which is then
 // written out as 16-byte row pieces, 8 lanes per 128-byte row.  The caller makes sure no wave still
 // reads `lds` (a barrier after the last use); n % 8 == 0.
+// Lanes of one wave exchanging data through LDS: the hardware runs a wave's LDS instructions in
+// order, but the compiler, reasoning per lane, could move one lane's read above another lane's write.
+// A wavefront-scope fence keeps the program order and emits no instruction.
+__device__ __forceinline__ void wave_lds_order() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
+
 template <typename T, typename F>
 __device__ __forceinline__ void store_wave_tile_64(const f32x16 (&acc)[2][2], char* lds, typename T::storage* out,
                                                    int64_t ld, int m0, int n0, int m, int n, F scale) {
@@ -125,6 +130,7 @@ __device__ __forceinline__ void store_wave_tile_64(const f32x16 (&acc)[2][2], ch
         *(typename T::storage*)(lds + rr * 128 + 2 * c) = Cvt<T>::from_f(acc[mi][ni][r] * scale(64 * wm + rr, 64 * wn + c));
       }
     }
+  wave_lds_order();
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int q = lane + 64 * i, rr = q >> 3, ch = q & 7;

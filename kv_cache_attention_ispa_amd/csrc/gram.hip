@@ -258,6 +258,7 @@ __global__ __launch_bounds__(3 * NT) void gram16_kernel(GramArgs a) {
           *(f32x4*)(tb + (lane & 31) * G_TPITCH + 8 * q + 4 * hi) =
               f32x4{acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]};
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        wave_lds_order();
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int c = 8 * e + (lane >> 3), r4 = 4 * (lane & 7);
@@ -269,6 +270,7 @@ __global__ __launch_bounds__(3 * NT) void gram16_kernel(GramArgs a) {
           }
         }
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        wave_lds_order();   // these reads stay ahead of the next block's writes
       }
     }
 }
