@@ -472,7 +472,7 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void attn_mfma_kernel(AttnParams p
   ld.issue(ld.group(sc, 1, p, head, k1, v0), wave);
   ld.issue(ld.group(sc, 2, p, head, k2, v1), wave);
   __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
-  __builtin_amdgcn_s_barrier();
+  lds_barrier();
 
   const int kbase = key_row(lane & 31) * K_PITCH + hi * 16;
   const int vbase = (lane & 31) * VT_PITCH + hi * 16;
@@ -509,12 +509,7 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void attn_mfma_kernel(AttnParams p
     }
     softmax_phase<TP>(s, sc.valid(t), p.scale_log2, hi, st, pf);
   };
-  auto phase_end = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
+  auto phase_end = [&]() { lds_barrier(); };
   // Iteration i covers two phases.  Waves 0-3 run M(i-1) and then the softmax of tile i; waves 4-7,
   // one phase behind, run the softmax of tile i-1 and then M(i-1).  Load group k (K tile k, V^T tile
   // k-1) is issued during the softmax phases of iteration k-2 (groups 0-2 before the loop; iteration 0

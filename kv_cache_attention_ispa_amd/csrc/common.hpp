@@ -109,6 +109,18 @@ constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 // scale(row, col) (tile coordinates) is rounded to T into the wave's own 8 KiB of LDS, which is then
 // written out as 16-byte row pieces, 8 lanes per 128-byte row.  The caller makes sure no wave still
 // reads `lds` (a barrier after the last use); n % 8 == 0.
+// Work-group barrier of the pipelined kernels: this wave's LDS operations complete first, while loads
+// into LDS issued ahead stay in flight (no vmcnt wait, unlike __syncthreads); the wavefront-scope
+// fences keep the compiler from moving memory operations across the barrier and emit no instruction.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Lanes of one wave exchanging data through LDS: the hardware runs a wave's LDS instructions in
 // order, but the compiler, reasoning per lane, could move one lane's read above another lane's write.
 // A wavefront-scope fence keeps the program order and emits no instruction.

@@ -90,12 +90,7 @@ __global__ __launch_bounds__(3 * NT) void gram16_kernel(GramArgs a) {
     else if constexpr (j == 1) return y1;
     else return y2;
   };
-  auto barrier = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
+  auto barrier = [&]() { lds_barrier(); };
   const int n_steps = (a.n + RK - 1) / RK;
   const int tail_step = (a.n & 7) ? (a.n - 1) / RK : -1;   // stage holding a partly valid chunk
 

@@ -67,12 +67,7 @@ __global__ __launch_bounds__(768, 1) void gemm_nt_kernel(const uint8_t* a, const
     else if constexpr (j == 1) return b1;
     else return b2;
   };
-  auto barrier = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
+  auto barrier = [&]() { lds_barrier(); };
   const int n_st = row_bytes / NT_BK;
 
   // One barrier per stage: at barrier s, stage s is in LDS and the multipliers are done with stage

@@ -124,12 +124,7 @@ __global__ __launch_bounds__(NT, 2) void trgemm_kernel(TrGemm g) {
     else if constexpr (j == 2) return b2;
     else return b3;
   };
-  auto barrier = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
+  auto barrier = [&]() { lds_barrier(); };
 
   f32x16 acc;
 #pragma unroll
