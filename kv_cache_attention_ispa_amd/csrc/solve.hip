@@ -66,12 +66,20 @@ __device__ __forceinline__ void fold_store(const TrGemm& g, int64_t e, float v) 
     ((float*)g.Wn)[e] = ((const float*)g.W)[e] + v;
 }
 
+// Work-group b -> tile rank (ranks: longest k range first).  Two work-groups share a CU and the
+// dispatcher deals them out round-robin, so b and b + 256 tend to meet on one CU; the second 256
+// take the ranks in reverse, which pairs each long tile with a short one.
+__device__ __forceinline__ int tg_rank(int b, int n) {
+  const int hi = n < 512 ? n : 512;
+  return (b >= 256 && b < hi) ? 256 + (hi - 1 - b) : b;
+}
+
 template <bool TA>
 __global__ __launch_bounds__(NT, 2) void trgemm_kernel(TrGemm g) {
   __shared__ __attribute__((aligned(16))) char a0[TG_STAGE], a1[TG_STAGE], a2[TG_STAGE], a3[TG_STAGE];
   __shared__ __attribute__((aligned(16))) char b0[TG_STAGE], b1[TG_STAGE], b2[TG_STAGE], b3[TG_STAGE];
   const int T = g.tiles, d = g.d;
-  const int q = blockIdx.x;
+  const int q = tg_rank(blockIdx.x, gridDim.x);
   const int bm = TA ? q / T : (T - 1) - q / T, bn = q % T;   // longest k range first
   const int m0 = bm * TG_TILE, n0 = bn * TG_TILE;
   const int k_begin = TA ? m0 : 0, k_end = TA ? d : min(d, m0 + TG_TILE);
