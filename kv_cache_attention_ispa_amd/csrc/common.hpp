@@ -10,7 +10,6 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
@@ -79,14 +78,6 @@ template <> __device__ __forceinline__ f32x16 mfma32x32x16<BF16>(u32x4 a, u32x4 
 template <> __device__ __forceinline__ f32x16 mfma32x32x16<F16>(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
                                                 0, 0, 0);
-}
-
-// LDS transposing read of four 16-bit values.  Within each group of 16 lanes,
-// lane j receives element (j % 4) of the 8-byte chunk addressed by lane 4*e + j/4,
-// for e = 0..3.
-__device__ __forceinline__ u32x2 lds_read_tr16(const lds_void* p) {
-  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
-  return __builtin_bit_cast(u32x2, r);
 }
 
 // Work-group id -> logical tile id such that each XCD receives a contiguous range
