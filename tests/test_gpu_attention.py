@@ -159,6 +159,25 @@ def test_local_attn_fused_proj(io, n_hist):
     assert maxrel(host(out), ref) <= TOL[io]
 
 
+@pytest.mark.parametrize("io", ["bf16", "f16"])
+def test_local_attn_fused_proj_five_heads(io):
+    """d = 640: the projection's k loop has 10 (16-bit) stages for a ring of 3, so the last turn runs on
+    zero-filled stages; 530 queries give three row tiles, the last one ragged."""
+    import kv_cache_attention_ispa_amd as ispa
+    t = torch()
+    shape = wl.AttnShape(530, 40, 0, 260, 5, 128)
+    q, k, v = _inputs(shape, io, 57)
+    rng = np.random.default_rng(58)
+    w_new = wl.round_to(rng.standard_normal((shape.d, shape.d)) / math.sqrt(shape.d), io)
+    s = ispa.AttnShape.of(shape)
+    ws = t.empty(ispa.workspace_bytes(ispa.CALL_LOCAL_ATTN_PROJ, s), dtype=t.uint8, device="cuda")
+    out = t.empty((shape.n_q, shape.d), dtype=tdtype(io), device="cuda")
+    ispa.local_attn_fused_proj(s, dev(q, io), dev(k, io), dev(v, io), dev(w_new, io), out, ws)
+    t.cuda.synchronize()
+    ref = oracle.local_layer_output(q, k, v, shape.n_sink, shape.n_cur, shape.n_heads, w_new)
+    assert maxrel(host(out), ref) <= TOL[io]
+
+
 def test_layer_1p3b_sampled_rows():
     """The 1.3B-shaped layer at full size (4680 queries, 20280 cached rows, 12 heads), in the launch
     configuration the bench times; 64 sampled query rows checked against the oracle."""
