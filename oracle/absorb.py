@@ -19,7 +19,7 @@ definition: accumulate G = A_loc^T A_loc and C = A_loc^T (A_full - A_loc)
 (G + lambda I) dW = R with a float64 Cholesky factorisation (a library routine
 used as one step).
 
-Readings (listed in the design doc): the norm on matrices is Frobenius; A is
+Readings of points the pages leave open: the norm on matrices is Frobenius; A is
 [tokens, d] and the projection is A @ W with W [d_in, d_out]; lambda is either
 absolute or relative, lambda_rel * tr(G) / d; epsilon is the relative Frobenius
 residual of the data term on the warmup rows; selection is a stable ascending

@@ -12,7 +12,7 @@ log-sum-exp states.  That merge is exact, so this oracle does NOT use it to
 produce A_full: A_full comes from a separate plain pass over all rows, and the
 merge (``lse_merge``) exists only so the tests can pin the identity.
 
-Readings of points the pages leave open (each listed in the design doc):
+Readings of points the pages leave open:
   * cache rows are ordered [sink | history | current chunk]; the local set is
     sink + current chunk, the history set is the rows in between;
   * no mask: every query sees every row of its set (chunk-level causality comes
