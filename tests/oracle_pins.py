@@ -359,6 +359,34 @@ def check_selection(impl):
     assert list(impl.select_local_layers(eps, 0)) == []
 
 
+def check_golden_l_layer(impl):
+    """Hand-worked converted-layer step: local attention over sink + current rows, then A @ W_new."""
+    g = _golden("l_layer_hand.json")
+    q, k, v, w = (np.array(g[x], dtype=np.float64) for x in ("q", "k", "v", "w_new"))
+    out = impl.local_layer_output(q, k, v, g["n_sink"], g["n_cur"], g["n_heads"], w)
+    assert np.allclose(out, np.array(g["expect"]["out"]), rtol=0, atol=1e-13)
+    # the identity projection leaves the attention output itself
+    att = impl.local_layer_output(q, k, v, g["n_sink"], g["n_cur"], g["n_heads"], np.eye(w.shape[0]))
+    assert np.allclose(att, np.array(g["expect"]["attention"]), rtol=0, atol=1e-13)
+
+
+def check_golden_residual_and_fold(impl):
+    g = _golden("residual_fold_hand.json")
+    r = g["residual"]
+    got = impl.normal_equation_residual(*(np.array(r[x]) for x in ("G", "C", "w", "delta_w")), r["lambda"])
+    assert abs(got - r["expect"]) <= 1e-15
+    f = g["fold"]
+    assert np.array_equal(impl.fold_weights(np.array(f["w"]), np.array(f["delta_w"])), np.array(f["expect"]))
+
+
+def check_golden_w8a8_l_layer(impl):
+    """W8A8 converted-layer step where the bf16 storage of the attention output decides an E4M3 code."""
+    g = _golden("w8a8_l_layer_hand.json")
+    q, k, v, w = (np.array(g[x], dtype=np.float64) for x in ("q", "k", "v", "w"))
+    out = impl.local_layer_output_w8a8(q, k, v, g["n_sink"], g["n_cur"], g["n_heads"], w)
+    assert np.array_equal(out, np.array(g["expect"]["out"]))
+
+
 # ----------------------------------------------------------------------------
 # accounting
 # ----------------------------------------------------------------------------
@@ -394,6 +422,7 @@ ATTENTION_PINS = [check_brute_force, check_golden_attention, check_q_zero, check
                   check_split_invariance, check_permutations]
 ABSORB_PINS = [check_golden_ridge, check_residual, check_augmented_lstsq, check_lambda_limits,
                check_relative_lambda, check_linearity_in_w, check_optimality, check_rowspace,
-               check_eps_two_ways, check_zero_absorb, check_gram_associativity, check_selection]
+               check_eps_two_ways, check_zero_absorb, check_gram_associativity, check_selection,
+               check_golden_l_layer, check_golden_residual_and_fold, check_golden_w8a8_l_layer]
 ACCOUNTING_PINS = [check_kv_bytes, check_flops]
 ALL_PINS = ATTENTION_PINS + ABSORB_PINS + ACCOUNTING_PINS

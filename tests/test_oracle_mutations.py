@@ -11,12 +11,13 @@ import numpy as np
 import pytest
 
 import oracle
+from oracle import fp8
 from oracle_pins import ALL_PINS
 
 NAMES = ["branch_rows", "softmax_attention", "dual_stream", "lse_merge", "gram_stats", "ridge_lambda",
          "solve_delta_w", "normal_equation_residual", "recon_error_direct", "recon_error_traces",
          "select_local_layers", "fold_weights", "local_layer_output", "attn_flops", "kv_cache_bytes",
-         "kv_removed_fraction", "default_scale"]
+         "kv_removed_fraction", "default_scale", "local_layer_output_w8a8"]
 
 
 def _ns(**over):
@@ -141,6 +142,28 @@ def _flops_half(n_q, n_k, head_dim, n_heads):
     return 2 * n_q * n_k * head_dim * n_heads
 
 
+def _l_layer_w_transposed(q, k, v, n_sink, n_cur, n_heads, W_new, scale=None, threads=1):
+    return oracle.local_layer_output(q, k, v, n_sink, n_cur, n_heads, np.asarray(W_new).T, scale, threads)
+
+
+def _fold_subtracts(W, dW):
+    return np.asarray(W, dtype=np.float64) - np.asarray(dW, dtype=np.float64)
+
+
+def _residual_zero(G, C, W, dW, lam):
+    return 0.0
+
+
+def _residual_no_lambda(G, C, W, dW, lam):
+    return oracle.normal_equation_residual(G, C, W, dW, 0.0)
+
+
+def _w8a8_no_bf16_rounding(q, k, v, n_sink, n_cur, n_heads, W, scale=None, threads=1):
+    rows = oracle.branch_rows(n_sink, 0, n_cur)["local"]
+    a, _ = oracle.softmax_attention(q, k, v, rows, n_heads, scale, threads=threads)
+    return fp8.w8a8_matmul(a.astype(np.float32), W)
+
+
 MUTANTS = {
     "scale_1_over_d": dict(softmax_attention=_softmax_variant(scale_fn=lambda dh: 1.0 / dh),
                            dual_stream=_dual_with(_softmax_variant(scale_fn=lambda dh: 1.0 / dh))),
@@ -161,6 +184,11 @@ MUTANTS = {
     "select_highest": dict(select_local_layers=_select_highest),
     "kv_rows_drop_sink": dict(kv_cache_bytes=_kv_off_by_one),
     "flops_half": dict(attn_flops=_flops_half),
+    "l_layer_projects_by_w_transposed": dict(local_layer_output=_l_layer_w_transposed),
+    "fold_subtracts_delta_w": dict(fold_weights=_fold_subtracts),
+    "residual_returns_zero": dict(normal_equation_residual=_residual_zero),
+    "residual_drops_lambda": dict(normal_equation_residual=_residual_no_lambda),
+    "w8a8_skips_bf16_storage": dict(local_layer_output_w8a8=_w8a8_no_bf16_rounding),
 }
 
 
