@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16/fp16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dual_attn_layer_1p3b_traffic.json")
 ATTN_SOURCE = os.path.join(ROOT, "kv_cache_attention_ispa_amd", "csrc", "attn.hip")
@@ -196,21 +197,34 @@ def measured_traffic():
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(x, s, n_rows: int):
-    """The oracle, as it stands, on a bounded sample: dual-stream attention for n_rows queries
-    (all heads, all cached rows) plus the float64 ridge solve at full size."""
+def cpu_baseline(x, s, n_rows: int, lam: float):
+    """The oracle, as it stands, on a bounded sample: dual-stream attention for n_rows queries (all
+    heads, all cached rows), then the absorption at full size (float64 Gram over those rows' outputs
+    scaled to the 4680-token layer, and the float64 ridge solve at d = 1536)."""
     import numpy as np
     import oracle
-    threads = min(len(os.sched_getaffinity(0)), 16)
+    affinity = len(os.sched_getaffinity(0))
+    threads = min(affinity, 16)
     rows = np.linspace(0, s.n_q - 1, n_rows).astype(np.int64)
     t0 = time.perf_counter()
-    oracle.dual_stream(x["q"][rows], x["k"], x["v"], s.n_sink, s.n_hist, s.n_cur, s.n_heads, threads=threads)
+    r = oracle.dual_stream(x["q"][rows], x["k"], x["v"], s.n_sink, s.n_hist, s.n_cur, s.n_heads, threads=threads)
     t_attn = time.perf_counter() - t0
     flops = 4.0 * n_rows * s.n_k * s.head_dim * s.n_heads
-    return {"value": round(flops / t_attn / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    t0 = time.perf_counter()
+    G, C, D = oracle.gram_stats([(r["a_loc"], r["delta_a"])])
+    t_gram = (time.perf_counter() - t0) * s.n_q / n_rows
+    t0 = time.perf_counter()
+    oracle.solve_delta_w(G, C, x["w"], oracle.ridge_lambda(G, lam, True))
+    t_solve = time.perf_counter() - t0
+    return {"value": round(flops / t_attn / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "affinity_cores": affinity, "kind": "oracle",
+            "absorb_ms_per_layer": round(1e3 * (t_gram + t_solve), 1),
             "sample": f"float64 dual-stream attention (local, full and history passes) for {n_rows} of "
-                      f"{s.n_q} queries x {s.n_heads} heads x {s.n_k} cached rows, {t_attn:.2f} s; rate on the "
-                      f"same algorithmic FLOP count as the GPU value"}
+                      f"{s.n_q} queries x {s.n_heads} heads x {s.n_k} cached rows, {t_attn:.2f} s, rate on the "
+                      f"same algorithmic FLOP count as the GPU value; absorption: float64 G, C, D over those "
+                      f"{n_rows} rows ({t_gram * n_rows / s.n_q:.2f} s, scaled to {s.n_q} tokens) and the "
+                      f"float64 Cholesky solve at d = {G.shape[0]} ({t_solve:.2f} s); thread pool of {threads} "
+                      f"of the {affinity} host cores in this process's affinity"}
 
 
 def main():
@@ -293,8 +307,9 @@ def main():
     attn_ms, gram_ms, solve_ms, local_ms = seg.mean(axis=0)
     attn_flops = s.attn_flops()
     attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
-    gram_flops = 3 * 2.0 * s.n_q * d * d            # G, C, D computed as full d x d products
+    gram_flops = 4.0 * s.n_q * d * d                 # algorithmic: G n d^2 (symmetric), C 2 n d^2, D n d^2
     solve_flops = (13.0 / 3.0) * d ** 3              # R = CW, Cholesky, two triangular solves
+    absorb_roof_ms = 1e3 * (gram_flops / (PEAK_BF16_TFLOPS * 1e12) + solve_flops / (PEAK_FP32_TFLOPS * 1e12))
     local_flops = s.local_flops() + 2.0 * s.n_q * d * d
     step_flops = attn_flops + gram_flops + solve_flops + local_flops
 
@@ -327,6 +342,15 @@ def main():
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "flops_per_launch": attn_flops, "avg_launch_ms": round(attn_ms, 4)},
+        "roofline_absorb": {
+            "bound": "mfma", "unit": "ms",
+            "achieved_ms": round(gram_ms + solve_ms, 4), "roofline_ms": round(absorb_roof_ms, 4),
+            "frac": round(absorb_roof_ms / (gram_ms + solve_ms), 4),
+            "gram": {"flops": gram_flops, "ms": round(gram_ms, 4), "peak_tflops": PEAK_BF16_TFLOPS,
+                     "frac": round(gram_flops / (gram_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+            "solve": {"flops": solve_flops, "ms": round(solve_ms, 4), "peak_tflops": PEAK_FP32_TFLOPS,
+                      "frac": round(solve_flops / (solve_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)},
+            "note": "frac = (Gram FLOP / bf16 peak + solve FLOP / fp32 peak) / measured Gram + solve time"},
     }
     if not args.no_secondary:
         attn_ms_all = np.sort(seg[:, 0])
@@ -341,7 +365,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(x, s, args.cpu_queries)
+        result["cpu_baseline"] = cpu_baseline(x, s, args.cpu_queries, w.lam)
     print(json.dumps(result), flush=True)
 
 

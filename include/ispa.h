@@ -109,8 +109,12 @@ typedef struct ispa_attn_shape {
  * need none (workspace may be NULL).  The 16-bit path addresses K and the copy
  * with 32-bit byte offsets: n_k * d * 2 must stay below 2^31 (EUNSUPPORTED).
  * Precision: QK^T and PV run on MFMA with fp32 accumulation.  With BF16 inputs
- * and F16 statistics the PV product uses fp16 probabilities and the V copy is
- * converted to fp16 (exact for |v| < 65504; larger values become inf).
+ * and F16 or F32 statistics (dual mode) the PV product uses fp16 probabilities
+ * and the V copy is converted to fp16, for all outputs, A_full included.  That
+ * conversion is exact for bf16 values with 2^-17 <= |v| <= 65504 and for 0;
+ * smaller magnitudes become fp16 subnormals and lose low bits (below 2^-25 they
+ * become 0) and larger ones become inf.  BF16 statistics, the single-stream
+ * modes and F16 inputs use the input type for P and V.
  */
 int ispa_dual_attn(const ispa_attn_shape* shape, int io_dtype,
                    const void* q, const void* k, const void* v,
@@ -131,8 +135,9 @@ int ispa_dual_attn(const ispa_attn_shape* shape, int io_dtype,
  *   G, C, D            : [d, d] fp32 row-major.  accumulate = 0 overwrites,
  *                        1 adds.  G and D are symmetric and written in full.
  *   D may be NULL.  d % 32 == 0 and d <= 16384; n >= 1.  16-bit statistics are
- *   read in 128-row slices with 32-bit byte offsets: 256 * ld must stay below
- *   2^31 (EUNSUPPORTED).
+ *   read in 256-row slices with 32-bit byte offsets: 512 * ld must stay below
+ *   2^31 (EUNSUPPORTED).  Token columns [n, ld) are never read as data (they may
+ *   hold anything, NaN included).
  */
 int ispa_gram_accum(int d, int n, int stat_dtype, const void* a_loc_t, const void* delta_a_t, int64_t ld,
                     int accumulate, float* G, float* C, float* D, void* stream);
@@ -168,6 +173,26 @@ int ispa_absorb_solve(int d, const float* G, const float* C, const float* D,
                       float lambda, int lambda_relative, int refine,
                       float* delta_w, void* w_new, float* eps, float* lambda_out, int* info,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ispa_select_layers -- which layers become local-attention layers.
+ * Technical summary section 2, "Dynamic layer selection": after the warmup the
+ * layers are ranked by their reconstruction error epsilon (ispa_absorb_solve's
+ * eps output) and the lowest-error ones are converted.
+ *
+ *   eps   [n_layers] fp32, device: the per-layer errors.
+ *   info  [n_layers] int32, device (nullable): the solves' info words; a layer
+ *         with info != 0 (its factorisation failed, its eps is undefined) ranks
+ *         as if its eps were NaN.
+ *   k     how many layers to convert, 0 <= k <= n_layers.
+ *   role  [n_layers] int32, device, out: 1 for the k converted layers, 0 for the
+ *         layers that keep full attention.
+ *   order [n_layers] int32, device, out (nullable): the layer indices in rank order.
+ * Ranking: ascending eps; equal values rank the lower layer index first (a
+ * stable sort); NaN ranks after every number.  1 <= n_layers <= 4096.
+ */
+int ispa_select_layers(int n_layers, const float* eps, const int32_t* info, int k, int32_t* role, int32_t* order,
+                       void* stream);
 
 /*
  * ispa_local_attn_fused_proj -- one step of a converted L-layer.

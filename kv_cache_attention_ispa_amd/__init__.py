@@ -14,7 +14,7 @@ from typing import Optional
 __all__ = ["IspaError", "AttnShape", "lib", "dual_attn", "gram_accum", "absorb_solve",
            "local_attn_fused_proj", "workspace_bytes", "CALL_DUAL_ATTN", "CALL_ABSORB_SOLVE",
            "CALL_LOCAL_ATTN_PROJ", "CALL_LOCAL_ATTN_PROJ_W8A8", "library_path", "KVCache",
-           "quantize_weight_fp8", "quantize_rows_fp8", "local_attn_fused_proj_w8a8"]
+           "quantize_weight_fp8", "quantize_rows_fp8", "local_attn_fused_proj_w8a8", "select_layers"]
 
 F32, BF16, F16 = 0, 1, 2
 CALL_DUAL_ATTN, CALL_ABSORB_SOLVE, CALL_LOCAL_ATTN_PROJ, CALL_LOCAL_ATTN_PROJ_W8A8 = 0, 1, 2, 3
@@ -78,10 +78,11 @@ def lib() -> ctypes.CDLL:
         L.ispa_kv_release_history.argtypes = [_vp, _i32, _vp]
         L.ispa_kv_layer.argtypes = [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_i32)]
         L.ispa_kv_bytes.argtypes = [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
+        L.ispa_select_layers.argtypes = [_i32, _vp, _vp, _i32, _vp, _vp, _vp]
         for f in ("ispa_dual_attn", "ispa_gram_accum", "ispa_absorb_solve", "ispa_local_attn_fused_proj",
                   "ispa_quantize_weight_fp8", "ispa_quantize_rows_fp8", "ispa_local_attn_fused_proj_w8a8",
                   "ispa_kv_create", "ispa_kv_destroy", "ispa_kv_write_sink", "ispa_kv_append_chunk",
-                  "ispa_kv_release_history", "ispa_kv_layer", "ispa_kv_bytes"):
+                  "ispa_kv_release_history", "ispa_kv_layer", "ispa_kv_bytes", "ispa_select_layers"):
             getattr(L, f).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -89,7 +90,10 @@ def lib() -> ctypes.CDLL:
 
 def _dtype_code(t) -> int:
     import torch
-    return {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}[t.dtype]
+    codes = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+    if t.dtype not in codes:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
 
 
 def _ptr(t) -> Optional[int]:
@@ -105,6 +109,51 @@ def _dense(t, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _want(t, name, dtypes=None, shape=None, min_numel=None, contiguous=True):
+    """Check one tensor argument before anything reaches the C ABI: dtype, exact shape (None entries
+    are free), size and layout.  Raises ValueError; `t = None` passes (optional arguments)."""
+    if t is None:
+        return
+    if dtypes is not None:
+        import torch
+        ds = (dtypes,) if isinstance(dtypes, torch.dtype) else tuple(dtypes)
+        if t.dtype not in ds:
+            raise ValueError(f"{name} must have dtype {' or '.join(str(d) for d in ds)}, got {t.dtype}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and g != w for g, w in zip(t.shape, shape)):
+            raise ValueError(f"{name} must have shape {tuple('*' if w is None else w for w in shape)}, "
+                             f"got {tuple(t.shape)}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} needs at least {min_numel} elements, got {t.numel()}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"all tensors must be on one device, got {sorted(str(d) for d in devs)}")
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+
+
+def _io_dtypes():
+    import torch
+    return (torch.float32, torch.bfloat16, torch.float16)
+
+
+def _stat_view(t, name, d, n):
+    """A feature-major statistic: [d, >= n] with unit stride along tokens; returns its row stride."""
+    if t is None:
+        return None
+    if t.dim() != 2 or t.shape[0] != d or t.shape[1] < n:
+        raise ValueError(f"{name} must be a [{d}, >= {n}] feature-major view, got {tuple(t.shape)}")
+    if t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride along tokens")
+    return t.stride(0)
+
+
 def _stream(stream) -> int:
     import torch
     if stream is None:
@@ -117,6 +166,15 @@ def _check(status: int, where: str) -> None:
         raise IspaError(status, where)
 
 
+def _ws_bytes(workspace) -> int:
+    if workspace is None:
+        return 0
+    import torch
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    return workspace.numel()
+
+
 def workspace_bytes(call_id: int, shape: Optional[AttnShape] = None, d: int = 0) -> int:
     return int(lib().ispa_workspace_bytes(call_id, ctypes.byref(shape) if shape is not None else None, d))
 
@@ -125,28 +183,49 @@ def dual_attn(shape: AttnShape, q, k, v, a_full=None, a_loc_t=None, delta_a_t=No
               lse_loc=None, lse_hist=None, workspace=None, stream=None) -> None:
     """ispa_dual_attn: see include/ispa.h.  Stat outputs are feature-major [d, ld_stat] views;
     workspace (bytes from workspace_bytes(CALL_DUAL_ATTN, shape)) is needed for bf16/fp16 inputs."""
-    for n, t in (("q", q), ("k", k), ("v", v), ("a_full", a_full), ("lse_loc", lse_loc), ("lse_hist", lse_hist)):
-        _dense(t, n)
+    import torch
+    d = shape.n_heads * shape.head_dim
+    n_k = shape.n_sink + shape.n_hist + shape.n_cur
+    _want(q, "q", _io_dtypes(), (shape.n_q, d))
+    _want(k, "k", q.dtype, (n_k, d))
+    _want(v, "v", q.dtype, (n_k, d))
+    _want(a_full, "a_full", q.dtype, (shape.n_q, d))
+    for n_, t in (("lse_loc", lse_loc), ("lse_hist", lse_hist)):
+        _want(t, n_, torch.float32, (shape.n_heads, shape.n_q))
+    if a_loc_t is not None and delta_a_t is not None and a_loc_t.dtype != delta_a_t.dtype:
+        raise ValueError("a_loc_t and delta_a_t must share a dtype")
+    lds = [x for x in (_stat_view(a_loc_t, "a_loc_t", d, shape.n_q), _stat_view(delta_a_t, "delta_a_t", d, shape.n_q))
+           if x is not None]
+    if len(set(lds)) > 1:
+        raise ValueError("a_loc_t and delta_a_t must have the same leading dimension")
     stat = a_loc_t if a_loc_t is not None else delta_a_t
     if stat is not None:
-        if stat.stride(1) != 1:
-            raise ValueError("stat outputs must have unit stride along tokens")
+        _want(stat, "statistics", _io_dtypes(), contiguous=False)
         if ld_stat is None:
-            ld_stat = stat.stride(0)
+            ld_stat = lds[0]
+        elif ld_stat != lds[0]:
+            raise ValueError(f"ld_stat {ld_stat} differs from the statistics' row stride {lds[0]}")
     st = _dtype_code(stat) if stat is not None else F16
+    _same_device(q, k, v, a_full, a_loc_t, delta_a_t, lse_loc, lse_hist, workspace)
     _check(lib().ispa_dual_attn(ctypes.byref(shape), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(a_full), st,
                                 _ptr(a_loc_t), _ptr(delta_a_t), int(ld_stat or 0), _ptr(lse_loc), _ptr(lse_hist),
-                                _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
-                                _stream(stream)), "ispa_dual_attn")
+                                _ptr(workspace), _ws_bytes(workspace), _stream(stream)), "ispa_dual_attn")
 
 
 def gram_accum(a_loc_t, delta_a_t, n: int, G, C, D=None, accumulate: bool = False, stream=None) -> None:
     """ispa_gram_accum over tokens [0, n) of feature-major [d, ld] statistics."""
-    for n_, t in (("G", G), ("C", C), ("D", D)):
-        _dense(t, n_)
-    if a_loc_t.stride(1) != 1 or delta_a_t.stride(1) != 1 or a_loc_t.stride(0) != delta_a_t.stride(0):
-        raise ValueError("statistics must be feature-major views with one leading dimension")
+    import torch
+    if G.dim() != 2:
+        raise ValueError("G must be [d, d]")
     d = G.shape[0]
+    for n_, t in (("G", G), ("C", C), ("D", D)):
+        _want(t, n_, torch.float32, (d, d))
+    if a_loc_t.dtype != delta_a_t.dtype:
+        raise ValueError("a_loc_t and delta_a_t must share a dtype")
+    _want(a_loc_t, "a_loc_t", _io_dtypes(), contiguous=False)
+    if _stat_view(a_loc_t, "a_loc_t", d, n) != _stat_view(delta_a_t, "delta_a_t", d, n):
+        raise ValueError("statistics must be feature-major views with one leading dimension")
+    _same_device(a_loc_t, delta_a_t, G, C, D)
     _check(lib().ispa_gram_accum(d, int(n), _dtype_code(a_loc_t), _ptr(a_loc_t), _ptr(delta_a_t), a_loc_t.stride(0),
                                  int(bool(accumulate)), _ptr(G), _ptr(C), _ptr(D), _stream(stream)), "ispa_gram_accum")
 
@@ -154,41 +233,72 @@ def gram_accum(a_loc_t, delta_a_t, n: int, G, C, D=None, accumulate: bool = Fals
 def absorb_solve(G, C, W, lam: float, relative: bool, delta_w, info, workspace, D=None, w_new=None, eps=None,
                  lambda_out=None, refine: int = 0, stream=None) -> None:
     """ispa_absorb_solve: dW = (G + lambda I)^-1 C W (+ eps, W_new); refine = refinement steps."""
-    for n_, t in (("G", G), ("C", C), ("D", D), ("W", W), ("delta_w", delta_w), ("w_new", w_new)):
-        _dense(t, n_)
+    import torch
+    if G.dim() != 2:
+        raise ValueError("G must be [d, d]")
     d = G.shape[0]
+    for n_, t in (("G", G), ("C", C), ("D", D), ("delta_w", delta_w)):
+        _want(t, n_, torch.float32, (d, d))
+    _want(W, "W", _io_dtypes(), (d, d))
+    _want(w_new, "w_new", W.dtype, (d, d))
+    _want(info, "info", torch.int32, min_numel=1)
+    _want(eps, "eps", torch.float32, min_numel=1)
+    _want(lambda_out, "lambda_out", torch.float32, min_numel=1)
+    _same_device(G, C, D, W, delta_w, w_new, info, eps, lambda_out, workspace)
     _check(lib().ispa_absorb_solve(d, _ptr(G), _ptr(C), _ptr(D), _dtype_code(W), _ptr(W), float(lam), int(relative),
                                    int(refine), _ptr(delta_w), _ptr(w_new), _ptr(eps), _ptr(lambda_out), _ptr(info),
-                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+                                   _ptr(workspace), _ws_bytes(workspace), _stream(stream)),
            "ispa_absorb_solve")
+
+
+def _l_layer_args(shape, q, k, v, out):
+    import torch
+    d = shape.n_heads * shape.head_dim
+    n_k = shape.n_sink + shape.n_hist + shape.n_cur
+    _want(q, "q", (torch.bfloat16, torch.float16), (shape.n_q, d))
+    _want(k, "k", q.dtype, (n_k, d))
+    _want(v, "v", q.dtype, (n_k, d))
+    _want(out, "out", q.dtype, (shape.n_q, d))
+    return d
 
 
 def local_attn_fused_proj(shape: AttnShape, q, k, v, w_new, out, workspace, stream=None) -> None:
     """ispa_local_attn_fused_proj: out = LocalAttn(q; sink + current) @ w_new."""
-    for n_, t in (("q", q), ("k", k), ("v", v), ("w_new", w_new), ("out", out)):
-        _dense(t, n_)
+    d = _l_layer_args(shape, q, k, v, out)
+    _want(w_new, "w_new", q.dtype, (d, d))
+    _same_device(q, k, v, w_new, out, workspace)
     _check(lib().ispa_local_attn_fused_proj(ctypes.byref(shape), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
-                                            _ptr(w_new), _ptr(out), _ptr(workspace),
-                                            workspace.numel() * workspace.element_size(), _stream(stream)),
+                                            _ptr(w_new), _ptr(out), _ptr(workspace), _ws_bytes(workspace),
+                                            _stream(stream)),
            "ispa_local_attn_fused_proj")
 
 
 def quantize_weight_fp8(w, wq_t, w_scales, stream=None) -> None:
     """ispa_quantize_weight_fp8: w [d_in, d_out] -> wq_t [d_out, d_in] E4M3 codes (uint8), w_scales [d_out]."""
-    for n_, t in (("w", w), ("wq_t", wq_t), ("w_scales", w_scales)):
-        _dense(t, n_)
+    import torch
+    if w.dim() != 2:
+        raise ValueError("w must be [d_in, d_out]")
     d_in, d_out = w.shape
+    _want(w, "w", _io_dtypes())
+    _want(wq_t, "wq_t", torch.uint8, (d_out, d_in))
+    _want(w_scales, "w_scales", torch.float32, (d_out,))
+    _same_device(w, wq_t, w_scales)
     _check(lib().ispa_quantize_weight_fp8(d_in, d_out, _dtype_code(w), _ptr(w), _ptr(wq_t), _ptr(w_scales),
                                           _stream(stream)), "ispa_quantize_weight_fp8")
 
 
 def quantize_rows_fp8(x, q, scales, stream=None) -> None:
     """ispa_quantize_rows_fp8: x [rows, cols] -> q [rows, cols] E4M3 codes (uint8), scales [rows]."""
-    for n_, t in (("q", q), ("scales", scales)):
-        _dense(t, n_)
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, cols]")
+    rows, cols = x.shape
+    _want(x, "x", _io_dtypes(), contiguous=False)
+    _want(q, "q", torch.uint8, (rows, cols), contiguous=False)
+    _want(scales, "scales", torch.float32, (rows,))
     if x.stride(1) != 1 or q.stride(1) != 1:
         raise ValueError("rows must be contiguous")
-    rows, cols = x.shape
+    _same_device(x, q, scales)
     _check(lib().ispa_quantize_rows_fp8(rows, cols, _dtype_code(x), _ptr(x), x.stride(0), _ptr(q), q.stride(0),
                                         _ptr(scales), _stream(stream)), "ispa_quantize_rows_fp8")
 
@@ -196,12 +306,31 @@ def quantize_rows_fp8(x, q, scales, stream=None) -> None:
 def local_attn_fused_proj_w8a8(shape: AttnShape, q, k, v, wq_t, w_scales, out, workspace, stream=None) -> None:
     """ispa_local_attn_fused_proj_w8a8: out = W8A8(LocalAttn(q; sink + current), W_new) with W_new given as
     the codes and scales of quantize_weight_fp8."""
-    for n_, t in (("q", q), ("k", k), ("v", v), ("wq_t", wq_t), ("w_scales", w_scales), ("out", out)):
-        _dense(t, n_)
+    import torch
+    d = _l_layer_args(shape, q, k, v, out)
+    _want(wq_t, "wq_t", torch.uint8, (d, d))
+    _want(w_scales, "w_scales", torch.float32, (d,))
+    _same_device(q, k, v, wq_t, w_scales, out, workspace)
     _check(lib().ispa_local_attn_fused_proj_w8a8(ctypes.byref(shape), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
                                                  _ptr(wq_t), _ptr(w_scales), _ptr(out), _ptr(workspace),
-                                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+                                                 _ws_bytes(workspace), _stream(stream)),
            "ispa_local_attn_fused_proj_w8a8")
+
+
+def select_layers(eps, k: int, role, order=None, info=None, stream=None) -> None:
+    """ispa_select_layers: role[i] = 1 for the k layers with the lowest eps (stable; NaN, and layers whose
+    info is non-zero, last), else 0; order (optional) receives the layer indices in rank order."""
+    import torch
+    _want(eps, "eps", torch.float32)
+    if eps.dim() != 1:
+        raise ValueError("eps must be [n_layers]")
+    n = eps.shape[0]
+    _want(info, "info", torch.int32, (n,))
+    _want(role, "role", torch.int32, (n,))
+    _want(order, "order", torch.int32, (n,))
+    _same_device(eps, info, role, order)
+    _check(lib().ispa_select_layers(n, _ptr(eps), _ptr(info), int(k), _ptr(role), _ptr(order), _stream(stream)),
+           "ispa_select_layers")
 
 
 class _DeviceRows:

@@ -138,14 +138,17 @@ __global__ __launch_bounds__(3 * NT) void gram16_kernel(GramArgs a) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ry, (lds_void*)(ys + 1024 * (R_YLOADS * w + j)), 16,
                                                  ((j & 1) ? ok1 : ok0) ? yoff[j] + 2u * t0 : 0x80000000u, 0, 0, 0);
     };
-    // zero tokens n .. of the chunk that straddles n (X rows: loader threads 0-255, Y rows: 0-127)
+    // Zero tokens n .. of the chunk that straddles n, after this wave's own loads of that stage have
+    // landed.  Every row is zeroed by the wave that loaded it: X row r by loader r / 64 (thread r of
+    // the loader waves), Y row r by loader r / 32 (its lanes 0-31).
     auto fix_tail = [&](char* xs, char* ys, int step) {
       const int t = tid - 4 * GB, t0 = step * RK, c = (a.n - t0) >> 3, e0 = (a.n - t0) & 7;
       char* bx = xs + r_off(t, c);
-      char* by = ys + r_off(t & (GB - 1), c);
+      const bool ylane = lane < 32;
+      char* by = ys + r_off(32 * w + (lane & 31), c);
       for (int e = e0; e < 8; ++e) {
         *(uint16_t*)(bx + 2 * e) = 0;
-        if (t < GB) *(uint16_t*)(by + 2 * e) = 0;
+        if (ylane) *(uint16_t*)(by + 2 * e) = 0;
       }
     };
     issue(x0, y0, 0);

@@ -1,0 +1,160 @@
+"""The method's three stages for one generation instance, driven through the C ABI.
+
+Technical summary (gist.science, nl/pt), section 2 "Methodology":
+
+* stage 1 "Dual-Stream Warmup": for the first T_warm chunks every layer attends to its whole KV cache
+  with the dual stream, which yields A_full (what the model consumes) and A_loc (sink + current
+  chunk only); the absorption statistics G, C, D accumulate chunk by chunk;
+* stage 2 "Layer Absorb": at the transition each layer gets dW in closed form and its
+  reconstruction error epsilon;
+* "Dynamic layer selection": the k layers with the lowest epsilon are converted;
+* stage 3 "Memory-Efficient Inference": converted layers drop their cached history and run local
+  attention projected by W_new = W + dW; the other layers keep full attention over the growing cache.
+
+Every step runs in libispa's kernels (attention, statistics, solve, ranking, cache copies).  This
+class orders the calls, owns the buffers (PyTorch device memory, plus the library's KV cache) and
+reads the role map back to the host once, at the transition, to decide which caches to release.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence, Tuple
+
+from . import (AttnShape, CALL_ABSORB_SOLVE, CALL_DUAL_ATTN, CALL_LOCAL_ATTN_PROJ, IspaError, KVCache,
+               absorb_solve, dual_attn, gram_accum, local_attn_fused_proj, select_layers, workspace_bytes)
+
+WARMUP, STEADY = "warmup", "steady"
+
+
+class IspaRuntime:
+    """One instance of an n_layers attention stack under the method.
+
+    forward(layer, q, k, v) appends the chunk's K/V rows to the layer's cache and returns
+    (out, projected):
+      * during the warmup and for layers that keep full attention: out = A_full [n_q, d], the
+        attention output over the whole cache, projected = False (the caller applies its W);
+      * for converted layers after the transition: out = LocalAttn(q; sink + current) @ W_new,
+        projected = True.
+    transition(weights) runs the absorption for every layer, ranks the layers by epsilon, converts
+    the k_local lowest and releases their history rows.
+    """
+
+    def __init__(self, n_layers: int, n_heads: int, head_dim: int, sink_rows: int, chunk_rows: int,
+                 warmup_chunks: int, max_chunks: int, k_local: int, dtype=None, stat_dtype=None,
+                 lam: float = 1e-3, lam_relative: bool = True, refine: int = 0, keep_delta_w: bool = False,
+                 stream=None):
+        import torch
+        if not 0 <= k_local <= n_layers:
+            raise ValueError("k_local must be in [0, n_layers]")
+        if warmup_chunks < 1 or warmup_chunks > max_chunks:
+            raise ValueError("need 1 <= warmup_chunks <= max_chunks")
+        self.torch = torch
+        self.n_layers, self.n_heads, self.head_dim = n_layers, n_heads, head_dim
+        self.d = n_heads * head_dim
+        self.sink_rows, self.chunk_rows = sink_rows, chunk_rows
+        self.warmup_chunks, self.k_local = warmup_chunks, k_local
+        self.dtype = dtype or torch.bfloat16
+        self.stat_dtype = stat_dtype or torch.float16
+        self.lam, self.lam_relative, self.refine = lam, lam_relative, refine
+        self.keep_delta_w = keep_delta_w
+        self.stream = stream
+        dev = "cuda"
+        self.kv = KVCache(n_layers, self.d, self.dtype, sink_rows, chunk_rows, max_chunks)
+        self.chunks = [0] * n_layers
+        self.stage = WARMUP
+        d = self.d
+        self.ld = (chunk_rows + 7) // 8 * 8
+        self.a_t = torch.empty((d, self.ld), dtype=self.stat_dtype, device=dev)
+        self.da_t = torch.empty((d, self.ld), dtype=self.stat_dtype, device=dev)
+        self.stats: List[Optional[Tuple]] = [None] * n_layers       # (G, C, D) per layer, fp32 [d, d]
+        self.eps = torch.full((n_layers,), float("nan"), device=dev)
+        self.lambdas = torch.zeros((n_layers,), device=dev)
+        self.info = torch.zeros((n_layers,), dtype=torch.int32, device=dev)
+        self.role = torch.zeros((n_layers,), dtype=torch.int32, device=dev)
+        self.order = torch.zeros((n_layers,), dtype=torch.int32, device=dev)
+        self.roles: Optional[List[int]] = None
+        self.w_new = [None] * n_layers
+        self.delta_w = [None] * n_layers
+
+    # ------------------------------------------------------------------ helpers
+    def _shape(self, layer: int, n_q: int) -> Tuple[AttnShape, object, object]:
+        k, v, (n_s, n_h, n_c) = self.kv.layer(layer)
+        return AttnShape(n_q, n_s, n_h, n_c, self.n_heads, self.head_dim, 0.0), k, v
+
+    def _ws(self, call: int, shape: Optional[AttnShape], d: int = 0):
+        return self.torch.empty(workspace_bytes(call, shape, d), dtype=self.torch.uint8, device="cuda")
+
+    # ------------------------------------------------------------------ stages
+    def write_sink(self, layer: int, k, v) -> None:
+        self.kv.write_sink(layer, k, v, stream=self.stream)
+
+    def forward(self, layer: int, q, k, v):
+        """Append this chunk's K/V to the layer's cache and run the layer's attention for the stage."""
+        torch = self.torch
+        if self.stage == WARMUP and self.chunks[layer] >= self.warmup_chunks:
+            raise RuntimeError(f"layer {layer}: warmup chunks done; call transition() first")
+        self.kv.append_chunk(layer, k, v, stream=self.stream)
+        self.chunks[layer] += 1
+        shape, kc, vc = self._shape(layer, q.shape[0])
+        out = torch.empty((shape.n_q, self.d), dtype=self.dtype, device="cuda")
+        if self.stage == WARMUP:
+            if shape.n_q > self.chunk_rows:
+                raise ValueError("a warmup chunk has at most chunk_rows queries")
+            dual_attn(shape, q, kc, vc, a_full=out, a_loc_t=self.a_t, delta_a_t=self.da_t, ld_stat=self.ld,
+                      workspace=self._ws(CALL_DUAL_ATTN, shape), stream=self.stream)
+            first = self.stats[layer] is None
+            if first:
+                self.stats[layer] = tuple(torch.empty((self.d, self.d), device="cuda") for _ in range(3))
+            G, C, D = self.stats[layer]
+            gram_accum(self.a_t, self.da_t, shape.n_q, G, C, D, accumulate=not first, stream=self.stream)
+            return out, False
+        if self.roles[layer] == 1:
+            local_attn_fused_proj(shape, q, kc, vc, self.w_new[layer], out,
+                                  self._ws(CALL_LOCAL_ATTN_PROJ, shape), stream=self.stream)
+            return out, True
+        dual_attn(shape, q, kc, vc, a_full=out, workspace=self._ws(CALL_DUAL_ATTN, shape), stream=self.stream)
+        return out, False
+
+    def transition(self, weights: Sequence) -> List[int]:
+        """Absorb every layer (dW, epsilon, W_new), convert the k_local lowest-epsilon layers and release
+        their history.  weights[l] is layer l's output projection W [d, d] (y = A W), in the io dtype.
+        Returns the role map: 1 = converted (local attention with W_new), 0 = full attention."""
+        torch = self.torch
+        if self.stage != WARMUP:
+            raise RuntimeError("transition() runs once, after the warmup")
+        if any(s is None for s in self.stats):
+            raise RuntimeError("every layer needs at least one warmup chunk before the transition")
+        if len(weights) != self.n_layers:
+            raise ValueError("one weight matrix per layer")
+        d = self.d
+        ws = self._ws(CALL_ABSORB_SOLVE, None, d)
+        dw = torch.empty((d, d), device="cuda")
+        for layer in range(self.n_layers):
+            G, C, D = self.stats[layer]
+            w_new = torch.empty((d, d), dtype=weights[layer].dtype, device="cuda")
+            if self.keep_delta_w:
+                dw = torch.empty((d, d), device="cuda")
+            absorb_solve(G, C, weights[layer], self.lam, self.lam_relative, dw, self.info[layer:layer + 1], ws,
+                         D=D, w_new=w_new, eps=self.eps[layer:layer + 1],
+                         lambda_out=self.lambdas[layer:layer + 1], refine=self.refine, stream=self.stream)
+            self.w_new[layer] = w_new
+            if self.keep_delta_w:
+                self.delta_w[layer] = dw
+        # a layer whose factorisation failed (info != 0) has no valid epsilon and ranks last
+        select_layers(self.eps, self.k_local, self.role, self.order, info=self.info, stream=self.stream)
+        self.roles = [int(r) for r in self.role.cpu().tolist()]      # the one read-back (synchronises)
+        for layer, r in enumerate(self.roles):
+            if r == 1:
+                self.kv.release_history(layer, stream=self.stream)
+            else:
+                self.w_new[layer] = None
+        self.stats = [None] * self.n_layers
+        self.stage = STEADY
+        return list(self.roles)
+
+    def close(self) -> None:
+        self.kv.close()
+
+    def converted(self) -> List[int]:
+        if self.roles is None:
+            raise IspaError(1, "converted(): no transition yet")
+        return [i for i, r in enumerate(self.roles) if r == 1]

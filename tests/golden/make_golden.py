@@ -8,8 +8,9 @@ file per workload in this directory.
   epsilon, and a Gaussian sketch S^T dW X (S, X seeded [d, 16]) from which the
   tests estimate ||dW_gpu - dW||_F / ||dW||_F without storing dW.
 * warmup_1p3b_30x4: for each of the 30 layers (4 warmup chunks of 3 frames,
-  per-layer temporal correlation), lambda, epsilon and ||dW||_F, and the 15
-  layers selected for conversion (lowest epsilon).
+  per-layer temporal correlation), lambda, epsilon, ||dW||_F, the sketch of
+  dW, and G, C, D (accumulated over the 4 x 4680 warmup tokens) at seeded
+  sampled entries; the 15 layers selected for conversion (lowest epsilon).
 
 Usage: OMP_NUM_THREADS=1 python tests/golden/make_golden.py [layer_1p3b_bf16 layer_14b_bf16 warmup_1p3b_30x4]
 """
@@ -36,6 +37,14 @@ THREADS = int(os.environ.get("GOLDEN_THREADS", "8"))
 
 def sketch_mats(d: int):
     return wl.normal((d, SKETCH_K), SKETCH_CFG, 0, 0, 0), wl.normal((d, SKETCH_K), SKETCH_CFG, 0, 1, 0)
+
+
+def sample_entries(d: int, n: int = 64, n_diag: int = 16):
+    """Seeded (row, column) pairs of a d x d statistic: n random pairs, then n_diag diagonal entries."""
+    rng = np.random.default_rng(np.random.SeedSequence([wl.ROOT_SEED, SKETCH_CFG, d, 2]))
+    ii, jj = rng.integers(0, d, n), rng.integers(0, d, n)
+    dg = rng.integers(0, d, n_diag)
+    return np.concatenate([ii, dg]), np.concatenate([jj, dg])
 
 
 def layer_golden(w: wl.Workload) -> dict:
@@ -79,11 +88,17 @@ def warmup_golden(w: wl.Workload, n_chunks: int = 4, k_local: int = 15) -> dict:
         lam = oracle.ridge_lambda(G, w.lam, w.lam_relative)
         dW = oracle.solve_delta_w(G, C, W, lam)
         eps = oracle.recon_error_direct(np.concatenate(loc), np.concatenate(full), W, dW)
+        S, X = sketch_mats(G.shape[0])
+        ii, jj = sample_entries(G.shape[0])
         layers.append({"layer": layer, "rho": wl.layer_rho(layer, w.n_layers, w.cfg), "lambda": lam,
-                       "eps": eps, "dw_fro": float(np.linalg.norm(dW)), "seconds": round(time.time() - t0, 1)})
+                       "eps": eps, "dw_fro": float(np.linalg.norm(dW)), "dw_sketch": (S.T @ dW @ X).tolist(),
+                       "g_samples": G[ii, jj].tolist(), "c_samples": C[ii, jj].tolist(),
+                       "d_samples": D[ii, jj].tolist(), "seconds": round(time.time() - t0, 1)})
         print(f"layer {layer}: eps {eps:.6f} ({layers[-1]['seconds']} s)", flush=True)
     eps = [l["eps"] for l in layers]
+    ii, jj = sample_entries(w.shape.d)
     return {"workload": w.name, "n_chunks": n_chunks, "k_local": k_local, "layers": layers,
+            "sample_rows": ii.tolist(), "sample_cols": jj.tolist(),
             "selected": [int(i) for i in oracle.select_local_layers(eps, k_local)]}
 
 

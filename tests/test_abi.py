@@ -175,3 +175,17 @@ def test_w8a8_calls_reject_bad_arguments(L):
     assert f(wq=0) == EINVAL
     assert f(ws=0) == EWORKSPACE
     assert f(wsb=need - 1) == EWORKSPACE
+
+
+def test_select_layers_validation(L):
+    f = lambda n=30, eps=FAKE, k=15, role=FAKE, order=None, info=None: L.ispa_select_layers(n, eps, info, k, role,
+                                                                                          order, None)
+    assert f(n=0) == EINVAL
+    assert f(n=4097) == EINVAL
+    assert f(k=-1) == EINVAL
+    assert f(k=31) == EINVAL
+    assert f(eps=None) == EINVAL
+    assert f(role=None) == EINVAL
+    assert f(eps=FAKE + 2) == EINVAL
+    assert f(order=FAKE + 1) == EINVAL
+    assert f(info=FAKE + 2) == EINVAL

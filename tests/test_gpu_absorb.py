@@ -16,16 +16,16 @@ from gpu_util import dev, host, maxrel, relfro, run_dual, torch, tdtype
 pytestmark = pytest.mark.gpu
 
 
-def _stat_dev(x_tokens_major: np.ndarray, dtype: str, ld: int):
-    """Feature-major [d, ld] device buffer whose first n columns hold x^T (extra columns are garbage)."""
+def _stat_dev(x_tokens_major: np.ndarray, dtype: str, ld: int, pad=1234.0):
+    """Feature-major [d, ld] device buffer whose first n columns hold x^T (extra columns hold `pad`)."""
     t = torch()
     n, d = x_tokens_major.shape
-    buf = t.full((d, ld), 1234.0, dtype=tdtype(dtype), device="cuda")
+    buf = t.full((d, ld), pad, dtype=tdtype(dtype), device="cuda")
     buf[:, :n] = dev(x_tokens_major.T.copy(), dtype)
     return buf
 
 
-def _gram_gpu(chunks, dtype, d, with_d=True):
+def _gram_gpu(chunks, dtype, d, with_d=True, pad=1234.0):
     import kv_cache_attention_ispa_amd as ispa
     t = torch()
     G = t.full((d, d), float("nan"), device="cuda")
@@ -34,7 +34,7 @@ def _gram_gpu(chunks, dtype, d, with_d=True):
     for i, (a, da) in enumerate(chunks):
         n = a.shape[0]
         ld = ((n + 7) // 8) * 8 + 8
-        ispa.gram_accum(_stat_dev(a, dtype, ld), _stat_dev(da, dtype, ld), n, G, C, D, accumulate=i > 0)
+        ispa.gram_accum(_stat_dev(a, dtype, ld, pad), _stat_dev(da, dtype, ld, pad), n, G, C, D, accumulate=i > 0)
     t.cuda.synchronize()
     return host(G), host(C), (host(D) if with_d else None)
 
@@ -59,6 +59,19 @@ def test_gram_without_d(dtype, d, n):
     G, C, _ = _gram_gpu(chunks, dtype, d, with_d=False)
     Gr, Cr, _ = oracle.gram_stats(chunks)
     assert maxrel(G, Gr) <= 1e-4 and maxrel(C, Cr) <= 1e-4
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d,n", [(384, 33), (640, 77), (256, 517), (160, 1)])
+def test_gram_nan_padding(dtype, d, n):
+    """Token columns past n hold NaN (e.g. an uninitialised buffer): they are never read as data, even
+    in the chunk of 8 tokens that straddles n, for every row of X and of Y."""
+    rng = np.random.default_rng(7 * d + n)
+    chunks = [(wl.round_to(rng.standard_normal((n, d)) * 0.05, dtype), wl.round_to(rng.standard_normal((n, d)) * 0.03, dtype))]
+    G, C, D = _gram_gpu(chunks, dtype, d, pad=float("nan"))
+    Gr, Cr, Dr = oracle.gram_stats(chunks)
+    assert np.isfinite(G).all() and np.isfinite(C).all() and np.isfinite(D).all()
+    assert maxrel(G, Gr) <= 1e-4 and maxrel(C, Cr) <= 1e-4 and maxrel(D, Dr) <= 1e-4
 
 
 def _spd_problem(d, n, seed, w_dtype="f32"):

@@ -48,7 +48,7 @@ def test_row_codes_and_scales_bit_exact(x_dtype, cols):
     t = torch()
     rows, ld = 70, cols + 16
     rng = np.random.default_rng(12)
-    X = wl.round_to(rng.standard_normal((rows, cols)) * rng.uniform(1e-3 if x_dtype == "f16" else 1e-4, 50, (rows, 1)),
+    X = wl.round_to(rng.standard_normal((rows, cols)) * rng.uniform(1e-4, 50, (rows, 1)),
                     x_dtype)
     X[3] = 0.0
     Xp = np.zeros((rows, ld))

@@ -6,9 +6,11 @@ is one of:
   * properties that hold at any size (the normal equations of the solve, sketched
     with a seeded Gaussian block so the host work stays small);
   * values stored by tests/golden/make_golden.py, which calls only the oracle
-    (lambda, epsilon, ||dW|| and a Gaussian sketch S^T dW X of dW).
+    (lambda, epsilon, ||dW|| and a Gaussian sketch S^T dW X of dW);
+  * at the 1.3B layer, the whole dW from the oracle run in the test.
 Tolerances follow the bf16 workloads: attention max-rel 2e-2, dW rel-Frobenius 1e-2
-(estimated from the 16 x 16 sketch), epsilon relative 1e-2.
+(the whole matrix at the 1.3B layer, the 16 x 16 sketch at the 14B layer), epsilon relative 1e-2.
+The 30-layer warmup workload runs through the driver in test_gpu_runtime.py.
 """
 import json
 import math
@@ -117,13 +119,25 @@ def _check_layer(w, refine):
 
 
 def test_layer_1p3b_full_size():
+    """The whole dW at the 1.3B layer, element by element: the oracle's own dual-stream passes, Gram
+    and float64 solve run here on the host (about half a minute), rel-Frobenius 1e-2."""
     w = wl.LAYER_1P3B
+    s = w.shape
     L, dW, S, X = _check_layer(w, refine=False)
     g = _golden(w.name)
     ref = np.array(g["dw_sketch"])
     assert np.linalg.norm(S.T @ dW @ X - ref) <= 1e-2 * np.linalg.norm(ref)
     assert abs(float(L.eps.item()) - g["eps"]) <= 1e-2 * g["eps"]
     assert abs(float(L.lam.item()) - g["lambda"]) <= 1e-2 * g["lambda"]
+    x = wl.layer_inputs(w)
+    r = oracle.dual_stream(x["q"], x["k"], x["v"], s.n_sink, s.n_hist, s.n_cur, s.n_heads,
+                           threads=min(16, len(os.sched_getaffinity(0))))
+    G, C, _ = oracle.gram_stats([(r["a_loc"], r["delta_a"])])
+    lam = oracle.ridge_lambda(G, w.lam, w.lam_relative)
+    dW_ref = oracle.solve_delta_w(G, C, x["w"], lam)
+    err = relfro(dW, dW_ref)
+    print(f"1.3B layer: dW rel-Frobenius {err:.3e} (full matrix)")
+    assert err <= 1e-2
 
 
 def test_layer_14b_full_size():
@@ -137,49 +151,6 @@ def test_layer_14b_full_size():
     print(f"14B layer: dW sketch rel-Frobenius {err:.3e}, eps {float(L.eps.item()):.6f} vs {g['eps']:.6f}")
     assert err <= 1e-2
     assert abs(float(L.eps.item()) - g["eps"]) <= 1e-2 * g["eps"]
-
-
-def test_warmup_30_layers_selection():
-    """30 layers x 4 warmup chunks (3 frames each, growing history), per-layer epsilon and the
-    15 layers converted; compared with the oracle's values."""
-    import kv_cache_attention_ispa_amd as ispa
-    t = torch()
-    g = _golden(wl.WARMUP_1P3B.name)
-    w = wl.WARMUP_1P3B
-    d = w.shape.d
-    eps_gpu = []
-    ld = ((w.chunk_frames * w.frame + 7) // 8) * 8
-    a_t = t.empty((d, ld), dtype=t.float16, device="cuda")
-    da_t = t.empty((d, ld), dtype=t.float16, device="cuda")
-    G, C, D, dW = (t.empty((d, d), device="cuda") for _ in range(4))
-    info = t.empty((1,), dtype=t.int32, device="cuda")
-    eps = t.empty((1,), device="cuda")
-    wss = t.empty(ispa.workspace_bytes(ispa.CALL_ABSORB_SOLVE, None, d), dtype=t.uint8, device="cuda")
-    for layer in range(w.n_layers):
-        fr = wl.rollout_frames(w, layer, 13)
-        qd, kd, vd = dev(fr["q"], "bf16"), dev(fr["k"], "bf16"), dev(fr["v"], "bf16")
-        for c in range(4):
-            sh = ispa.AttnShape.of(wl.chunk_shape(w, c))
-            qs, n_rows = wl.chunk_rows(w, c)
-            ws = t.empty(ispa.workspace_bytes(ispa.CALL_DUAL_ATTN, sh), dtype=t.uint8, device="cuda")
-            ispa.dual_attn(sh, qd[qs], kd[:n_rows], vd[:n_rows], a_loc_t=a_t, delta_a_t=da_t, ld_stat=ld,
-                           workspace=ws)
-            ispa.gram_accum(a_t, da_t, sh.n_q, G, C, D, accumulate=c > 0)
-        ispa.absorb_solve(G, C, dev(wl.rollout_weight(w, layer), "bf16"), w.lam, w.lam_relative, dW, info, wss, D=D,
-                          eps=eps)
-        t.cuda.synchronize()
-        assert int(info.item()) == 0
-        eps_gpu.append(float(eps.item()))
-    eps_ref = np.array([l["eps"] for l in g["layers"]])
-    eps_gpu = np.array(eps_gpu)
-    assert np.max(np.abs(eps_gpu - eps_ref) / eps_ref) <= 1e-2
-    sel = set(int(i) for i in oracle.select_local_layers(eps_gpu, g["k_local"]))
-    ref = set(g["selected"])
-    if sel != ref:
-        # several selections are correct only when the K-th and (K+1)-th errors are within 1e-3
-        srt = np.sort(eps_ref)
-        k = g["k_local"]
-        assert abs(srt[k] - srt[k - 1]) <= 1e-3 * srt[k - 1], (sorted(sel), sorted(ref))
 
 
 @pytest.mark.parametrize("chunk", [0, 4, 20, 39])
