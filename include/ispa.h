@@ -175,6 +175,24 @@ int ispa_absorb_solve(int d, const float* G, const float* C, const float* D,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ispa_absorb_solve_batched -- ispa_absorb_solve for n_layers independent
+ * layers in one call (the transition absorbs every layer at once; each layer's
+ * solve alone leaves most of the GPU idle, since its Cholesky panels are a
+ * sequential chain).  Same arguments, results and errors as ispa_absorb_solve,
+ * per layer l:
+ *   G, C, D, W, delta_w, w_new  [n_layers, d, d] contiguous (layer l at l*d*d),
+ *   eps, lambda_out, info       [n_layers] (nullable as in ispa_absorb_solve),
+ *   workspace: n_layers * ispa_workspace_bytes(ISPA_CALL_ABSORB_SOLVE, NULL, d)
+ *   bytes, layer l's part at l times that size.  1 <= n_layers <= 65535.
+ * Layer l's results equal those of ispa_absorb_solve on layer l's arrays, bit for
+ * bit (the same kernels with the layer as a grid dimension).
+ */
+int ispa_absorb_solve_batched(int n_layers, int d, const float* G, const float* C, const float* D,
+                              int w_dtype, const void* W, float lambda, int lambda_relative, int refine,
+                              float* delta_w, void* w_new, float* eps, float* lambda_out, int* info,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * ispa_select_layers -- which layers become local-attention layers.
  * Technical summary section 2, "Dynamic layer selection": after the warmup the
  * layers are ranked by their reconstruction error epsilon (ispa_absorb_solve's

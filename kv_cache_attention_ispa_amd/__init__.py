@@ -14,7 +14,8 @@ from typing import Optional
 __all__ = ["IspaError", "AttnShape", "lib", "dual_attn", "gram_accum", "absorb_solve",
            "local_attn_fused_proj", "workspace_bytes", "CALL_DUAL_ATTN", "CALL_ABSORB_SOLVE",
            "CALL_LOCAL_ATTN_PROJ", "CALL_LOCAL_ATTN_PROJ_W8A8", "library_path", "KVCache",
-           "quantize_weight_fp8", "quantize_rows_fp8", "local_attn_fused_proj_w8a8", "select_layers"]
+           "quantize_weight_fp8", "quantize_rows_fp8", "local_attn_fused_proj_w8a8", "select_layers",
+           "absorb_solve_batched"]
 
 F32, BF16, F16 = 0, 1, 2
 CALL_DUAL_ATTN, CALL_ABSORB_SOLVE, CALL_LOCAL_ATTN_PROJ, CALL_LOCAL_ATTN_PROJ_W8A8 = 0, 1, 2, 3
@@ -79,10 +80,13 @@ def lib() -> ctypes.CDLL:
         L.ispa_kv_layer.argtypes = [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_i32)]
         L.ispa_kv_bytes.argtypes = [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
         L.ispa_select_layers.argtypes = [_i32, _vp, _vp, _i32, _vp, _vp, _vp]
+        L.ispa_absorb_solve_batched.argtypes = [_i32, _i32, _vp, _vp, _vp, _i32, _vp, _f32, _i32, _i32, _vp, _vp, _vp,
+                                                _vp, _vp, _vp, _sz, _vp]
         for f in ("ispa_dual_attn", "ispa_gram_accum", "ispa_absorb_solve", "ispa_local_attn_fused_proj",
                   "ispa_quantize_weight_fp8", "ispa_quantize_rows_fp8", "ispa_local_attn_fused_proj_w8a8",
                   "ispa_kv_create", "ispa_kv_destroy", "ispa_kv_write_sink", "ispa_kv_append_chunk",
-                  "ispa_kv_release_history", "ispa_kv_layer", "ispa_kv_bytes", "ispa_select_layers"):
+                  "ispa_kv_release_history", "ispa_kv_layer", "ispa_kv_bytes", "ispa_select_layers",
+                  "ispa_absorb_solve_batched"):
             getattr(L, f).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -249,6 +253,28 @@ def absorb_solve(G, C, W, lam: float, relative: bool, delta_w, info, workspace, 
                                    int(refine), _ptr(delta_w), _ptr(w_new), _ptr(eps), _ptr(lambda_out), _ptr(info),
                                    _ptr(workspace), _ws_bytes(workspace), _stream(stream)),
            "ispa_absorb_solve")
+
+
+def absorb_solve_batched(G, C, W, lam: float, relative: bool, delta_w, info, workspace, D=None, w_new=None,
+                         eps=None, lambda_out=None, refine: int = 0, stream=None) -> None:
+    """ispa_absorb_solve_batched: one absorption per layer for [n_layers, d, d] statistics and weights;
+    eps, lambda_out, info are [n_layers]."""
+    import torch
+    if G.dim() != 3 or G.shape[1] != G.shape[2]:
+        raise ValueError("G must be [n_layers, d, d]")
+    n, d = G.shape[0], G.shape[1]
+    for n_, t in (("G", G), ("C", C), ("D", D), ("delta_w", delta_w)):
+        _want(t, n_, torch.float32, (n, d, d))
+    _want(W, "W", _io_dtypes(), (n, d, d))
+    _want(w_new, "w_new", W.dtype, (n, d, d))
+    _want(info, "info", torch.int32, (n,))
+    _want(eps, "eps", torch.float32, (n,))
+    _want(lambda_out, "lambda_out", torch.float32, (n,))
+    _same_device(G, C, D, W, delta_w, w_new, info, eps, lambda_out, workspace)
+    _check(lib().ispa_absorb_solve_batched(n, d, _ptr(G), _ptr(C), _ptr(D), _dtype_code(W), _ptr(W), float(lam),
+                                           int(relative), int(refine), _ptr(delta_w), _ptr(w_new), _ptr(eps),
+                                           _ptr(lambda_out), _ptr(info), _ptr(workspace), _ws_bytes(workspace),
+                                           _stream(stream)), "ispa_absorb_solve_batched")
 
 
 def _l_layer_args(shape, q, k, v, out):

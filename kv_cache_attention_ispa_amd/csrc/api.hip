@@ -173,9 +173,11 @@ int ispa_gram_accum(int d, int n, int stat_dtype, const void* a_loc_t, const voi
   return hip_status(launch_gram(L, (hipStream_t)stream));
 }
 
-int ispa_absorb_solve(int d, const float* G, const float* C, const float* D, int w_dtype, const void* W,
-                      float lambda, int lambda_relative, int refine, float* delta_w, void* w_new, float* eps,
-                      float* lambda_out, int* info, void* workspace, size_t workspace_bytes, void* stream) {
+int ispa_absorb_solve_batched(int n_layers, int d, const float* G, const float* C, const float* D, int w_dtype,
+                              const void* W, float lambda, int lambda_relative, int refine, float* delta_w,
+                              void* w_new, float* eps, float* lambda_out, int* info, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (n_layers < 1 || n_layers > 65535) return ISPA_EINVAL;
   if (d < 32 || d > 16384 || d % 32 != 0) return ISPA_EINVAL;
   if (!valid_dtype(w_dtype)) return ISPA_EUNSUPPORTED;
   if (!G || !C || !W || !delta_w || !info) return ISPA_EINVAL;
@@ -185,8 +187,11 @@ int ispa_absorb_solve(int d, const float* G, const float* C, const float* D, int
   if (!aligned16(G) || !aligned16(C) || !aligned16(D) || !aligned16(W) || !aligned16(delta_w) || !aligned16(w_new) ||
       !aligned4(eps) || !aligned4(lambda_out) || !aligned4(info))
     return ISPA_EINVAL;
-  if (!workspace || workspace_bytes < solve_workspace_bytes(d) || !aligned16(workspace)) return ISPA_EWORKSPACE;
+  if (!workspace || workspace_bytes / (size_t)n_layers < solve_workspace_bytes(d) ||
+      workspace_bytes < (size_t)n_layers * solve_workspace_bytes(d) || !aligned16(workspace))
+    return ISPA_EWORKSPACE;
   SolveLaunch L;
+  L.batch = n_layers;
   L.d = d;
   L.G = G;
   L.C = C;
@@ -203,6 +208,13 @@ int ispa_absorb_solve(int d, const float* G, const float* C, const float* D, int
   L.info = info;
   L.ws = workspace;
   return hip_status(launch_solve(L, (hipStream_t)stream));
+}
+
+int ispa_absorb_solve(int d, const float* G, const float* C, const float* D, int w_dtype, const void* W,
+                      float lambda, int lambda_relative, int refine, float* delta_w, void* w_new, float* eps,
+                      float* lambda_out, int* info, void* workspace, size_t workspace_bytes, void* stream) {
+  return ispa_absorb_solve_batched(1, d, G, C, D, w_dtype, W, lambda, lambda_relative, refine, delta_w, w_new, eps,
+                                   lambda_out, info, workspace, workspace_bytes, stream);
 }
 
 int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k,

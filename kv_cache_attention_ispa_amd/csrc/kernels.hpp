@@ -80,7 +80,11 @@ hipError_t launch_quant_weight(int dtype, const void* w, int d_in, int d_out, ui
 hipError_t launch_proj8(int out_dtype, const uint8_t* aq, const float* sa, const uint8_t* wq_t, const float* sw,
                         void* out, int m, int n, int k, hipStream_t s);
 
+// One solve per layer for `batch` layers side by side: the caller's d x d arrays (G, C, D, W, delta_w,
+// w_new) are [batch, d, d] and eps, lambda_out, info [batch]; layer l's workspace starts at
+// ws + l * solve_workspace_bytes(d).
 struct SolveLaunch {
+  int batch;
   int d;
   const float* G;
   const float* C;

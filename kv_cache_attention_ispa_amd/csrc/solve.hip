@@ -28,6 +28,13 @@ namespace {
 constexpr int NB = 64;          // Cholesky panel width
 constexpr int NT = 256;
 
+// Layers are solved side by side: blockIdx.y is the layer, and every array of the call is reached
+// through a per-layer step in bytes (0 for arrays shared by all layers).
+template <typename P>
+__device__ __forceinline__ P* at_layer(P* p, int64_t step_bytes) {
+  return p ? (P*)((char*)p + (int64_t)blockIdx.y * step_bytes) : p;
+}
+
 // ------------------------------------------------------------------------------------------
 // Triangular fp32 GEMM on MFMA (32x32x2): C = alpha * op(A) B + beta * C for d x d row-major
 // matrices, op(A) = A lower triangular (TA = false: only k < m0 + 64 contributes to a row block at
@@ -54,6 +61,7 @@ struct TrGemm {
   const void* W;  // optional fold: Wn = W + C (final value), in dtype wdt
   void* Wn;
   int wdt;
+  int64_t sa, sb, sc, sw;   // per-layer steps (bytes) of A, B, C and of W / Wn
 };
 
 // Wn[e] = W[e] + v, rounded to nearest in W's dtype
@@ -76,6 +84,11 @@ __device__ __forceinline__ int tg_rank(int b, int n) {
 
 template <bool TA>
 __global__ __launch_bounds__(NT, 2) void trgemm_kernel(TrGemm g) {
+  g.A = at_layer(g.A, g.sa);
+  g.B = at_layer(g.B, g.sb);
+  g.C = at_layer(g.C, g.sc);
+  g.W = at_layer(g.W, g.sw);
+  g.Wn = at_layer(g.Wn, g.sw);
   __shared__ __attribute__((aligned(16))) char a0[TG_STAGE], a1[TG_STAGE], a2[TG_STAGE], a3[TG_STAGE];
   __shared__ __attribute__((aligned(16))) char b0[TG_STAGE], b1[TG_STAGE], b2[TG_STAGE], b3[TG_STAGE];
   const int T = g.tiles, d = g.d;
@@ -191,16 +204,25 @@ __global__ __launch_bounds__(NT, 2) void trgemm_kernel(TrGemm g) {
   }
 }
 
-// C = alpha op(L) B + beta C with L = A lower triangular (op = identity or transpose)
-hipError_t run_trgemm(bool transA, const float* A, const float* B, float* C, int d, float alpha, float beta,
-                      hipStream_t s, const void* W = nullptr, void* Wn = nullptr, int wdt = 0) {
+// Per-layer byte steps of the arrays a solve touches: the workspace and the caller's d x d matrices
+// (fp32, and W / W_new in W's dtype).
+struct Steps {
+  int64_t ws, mat, wmat;
+  int batch;
+};
+
+// C = alpha op(L) B + beta C with L = A lower triangular (op = identity or transpose), per layer
+hipError_t run_trgemm(bool transA, const float* A, int64_t sa, const float* B, int64_t sb, float* C, int64_t sc,
+                      int d, float alpha, float beta, int batch, hipStream_t s, const void* W = nullptr,
+                      void* Wn = nullptr, int wdt = 0, int64_t sw = 0) {
   TrGemm g;
   g.W = W; g.Wn = Wn; g.wdt = wdt;
   g.A = A; g.B = B; g.C = C;
+  g.sa = sa; g.sb = sb; g.sc = sc; g.sw = sw;
   g.d = d;
   g.tiles = (d + TG_TILE - 1) / TG_TILE;
   g.alpha = alpha; g.beta = beta;
-  const dim3 grid(g.tiles * g.tiles);
+  const dim3 grid(g.tiles * g.tiles, batch);
   if (transA) hipLaunchKernelGGL(trgemm_kernel<true>, grid, dim3(NT), 0, s, g);
   else hipLaunchKernelGGL(trgemm_kernel<false>, grid, dim3(NT), 0, s, g);
   return hipGetLastError();
@@ -219,7 +241,12 @@ struct Scalars {
 // Wf = W as fp32.
 template <typename WT>
 __global__ __launch_bounds__(NT) void setup_kernel(const float* G, const typename WT::storage* W, int d, float* Mx,
-                                                   float* Bx, float* Wf) {
+                                                   float* Bx, float* Wf, Steps st) {
+  G = at_layer(G, st.mat);
+  W = at_layer(W, st.wmat);
+  Mx = at_layer(Mx, st.ws);
+  Bx = at_layer(Bx, st.ws);
+  Wf = at_layer(Wf, st.ws);
   const int64_t n = (int64_t)d * d;
   for (int64_t e = blockIdx.x * (int64_t)NT + threadIdx.x; e < n; e += (int64_t)gridDim.x * NT) {
     const int i = (int)(e / d), j = (int)(e % d);
@@ -270,6 +297,7 @@ struct SweepArgs {
   float lam;
   int relative;
   float* lambda_out;
+  Steps st;
 };
 
 // 64 x 64 block (row block rb, column block cb) of a d x d row-major matrix into LDS, zeros outside.
@@ -451,6 +479,17 @@ __device__ __forceinline__ void sw_factor(const float (*D)[BP], float (*curb)[2]
 }
 
 __global__ __launch_bounds__(SW_THREADS) void sweep_kernel(SweepArgs a) {
+  a.Mx = at_layer(a.Mx, a.st.ws);
+  a.Bx = at_layer(a.Bx, a.st.ws);
+  a.Tb = at_layer(a.Tb, a.st.ws);
+  a.sc = at_layer(a.sc, a.st.ws);
+  a.Wf = at_layer(a.Wf, a.st.ws);
+  a.R = at_layer(a.R, a.st.ws);
+  a.P = at_layer(a.P, a.st.ws);
+  a.C = at_layer(a.C, a.st.mat);
+  a.G = at_layer(a.G, a.st.mat);
+  a.info = at_layer(a.info, (int64_t)sizeof(int));
+  a.lambda_out = at_layer(a.lambda_out, (int64_t)sizeof(float));
   // four blocks (plus the factorization's few hundred bytes) keep two work-groups on a CU
   __shared__ __attribute__((aligned(16))) float L0[NB][BP], L1[NB][BP], L2[NB][BP], L3[NB][BP];
   __shared__ __attribute__((aligned(16))) float curb[2][2][2][NB];
@@ -621,8 +660,13 @@ typedef double f64x2 __attribute__((ext_vector_type(2)));
 constexpr int G64_AP = 17, G64_BP = 130;   // LDS pitches in doubles
 
 template <int MODE>
-__global__ __launch_bounds__(NT, 2) void gemm64_kernel(const float* A, const float* B, int d, const Scalars* sc,
-                                                       double* R64, float* r) {
+__global__ __launch_bounds__(NT, 2) void gemm64_kernel(const float* A, int64_t sa, const float* B, int64_t sb, int d,
+                                                       const Scalars* sc, double* R64, float* r, int64_t sws) {
+  A = at_layer(A, sa);
+  B = at_layer(B, sb);
+  sc = at_layer(sc, sws);
+  R64 = at_layer(R64, sws);
+  r = at_layer(r, sws);
   __shared__ double as[2][128 * G64_AP];
   __shared__ __attribute__((aligned(16))) double bs[2][16 * G64_BP];
   const int tpd = (d + 127) / 128;
@@ -703,7 +747,14 @@ __global__ __launch_bounds__(NT, 2) void gemm64_kernel(const float* A, const flo
 // Only the lower 64-block triangle of P is formed; D and G are symmetric, so blocks below the
 // diagonal count twice and the upper ones are skipped.
 __global__ __launch_bounds__(NT) void dots_kernel(const float* D, const float* G, const float* P, const float* Wf,
-                                                  const float* R, const float* dW, int d, double* part) {
+                                                  const float* R, const float* dW, int d, double* part, Steps st) {
+  D = at_layer(D, st.mat);
+  G = at_layer(G, st.mat);
+  dW = at_layer(dW, st.mat);
+  P = at_layer(P, st.ws);
+  Wf = at_layer(Wf, st.ws);
+  R = at_layer(R, st.ws);
+  part = at_layer(part, st.ws);
   double s[5] = {0, 0, 0, 0, 0};
   for (int r = blockIdx.x; r < d; r += gridDim.x)
     for (int c = 4 * (int)threadIdx.x; c < d; c += 4 * NT) {
@@ -737,7 +788,11 @@ __global__ __launch_bounds__(NT) void dots_kernel(const float* D, const float* G
   if (threadIdx.x < 5) part[blockIdx.x * 5 + threadIdx.x] = red[threadIdx.x][0];
 }
 
-__global__ __launch_bounds__(NT) void eps_kernel(const double* part, int nblk, const Scalars* sc, float* eps) {
+__global__ __launch_bounds__(NT) void eps_kernel(const double* part, int nblk, const Scalars* sc, float* eps,
+                                                 Steps st) {
+  part = at_layer(part, st.ws);
+  sc = at_layer(sc, st.ws);
+  eps = at_layer(eps, (int64_t)sizeof(float));
   __shared__ double red[5][NT];
   double t[5] = {0, 0, 0, 0, 0};
   for (int b = threadIdx.x; b < nblk; b += NT)
@@ -798,22 +853,29 @@ WsLayout carve(void* ws, int d) {
 }  // namespace
 
 size_t solve_workspace_bytes(int d) {
-  return (size_t)d * d * sizeof(float) * 6 + 3 * NB * NB * sizeof(float) + 256 + DOT_BLOCKS * 5 * sizeof(double) +
-         (size_t)d * d * sizeof(double) + 256;
+  const size_t b = (size_t)d * d * sizeof(float) * 6 + 3 * NB * NB * sizeof(float) + 256 +
+                   DOT_BLOCKS * 5 * sizeof(double) + (size_t)d * d * sizeof(double) + 256;
+  return (b + 255) / 256 * 256;
 }
 
 hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
-  const int d = L.d;
+  const int d = L.d, nb_l = L.batch;
   WsLayout w = carve(L.ws, d);
   const int64_t dd = (int64_t)d * d;
+  Steps st;
+  st.ws = (int64_t)solve_workspace_bytes(d);
+  st.mat = dd * (int64_t)sizeof(float);
+  st.wmat = dd * (L.w_dtype == DT_F32 ? 4 : 2);
+  st.batch = nb_l;
   const int eb = (int)((dd + NT - 1) / NT > 2048 ? 2048 : (dd + NT - 1) / NT);
+  const dim3 eg(eb, nb_l);
 
   if (L.w_dtype == DT_BF16)
-    hipLaunchKernelGGL(setup_kernel<BF16>, dim3(eb), dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, w.Mx, w.Bx, w.Wf);
+    hipLaunchKernelGGL(setup_kernel<BF16>, eg, dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, w.Mx, w.Bx, w.Wf, st);
   else if (L.w_dtype == DT_F16)
-    hipLaunchKernelGGL(setup_kernel<F16>, dim3(eb), dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, w.Mx, w.Bx, w.Wf);
+    hipLaunchKernelGGL(setup_kernel<F16>, eg, dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, w.Mx, w.Bx, w.Wf, st);
   else
-    hipLaunchKernelGGL(setup_kernel<F32>, dim3(eb), dim3(NT), 0, s, L.G, (const float*)L.W, d, w.Mx, w.Bx, w.Wf);
+    hipLaunchKernelGGL(setup_kernel<F32>, eg, dim3(NT), 0, s, L.G, (const float*)L.W, d, w.Mx, w.Bx, w.Wf, st);
   ISPA_TRY(hipGetLastError());
 
   // Cholesky sweep (one launch per panel, plus one that finishes the last two block rows of L^-1)
@@ -864,35 +926,41 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
       a.kb1 = (range + 1) * nP / n_range;
       a.fill0 = (int)((int64_t)n_out * slot / n_slots);
       a.n_fill = a.kb0 < a.kb1 ? (int)((int64_t)n_out * (slot + 1) / n_slots) - a.fill0 : 0;
+      a.st = st;
       const int grid = (k < nP ? 1 : 0) + a.n_fill + a.n_a + a.n_i + n_f;
-      hipLaunchKernelGGL(sweep_kernel, dim3(grid), dim3(SW_THREADS), 0, s, a);
+      hipLaunchKernelGGL(sweep_kernel, dim3(grid, nb_l), dim3(SW_THREADS), 0, s, a);
       ISPA_TRY(hipGetLastError());
     }
   }
   // Z = L^-1 R (L^-1 lower triangular: only k < m0 + 64 contributes), into Mx (no longer needed)
-  ISPA_TRY(run_trgemm(false, w.Bx, w.Rc, w.Mx, d, 1.f, 0.f, s));
+  ISPA_TRY(run_trgemm(false, w.Bx, st.ws, w.Rc, st.ws, w.Mx, st.ws, d, 1.f, 0.f, nb_l, s));
   // dW = (L^-1)^T Z   (op(A) upper triangular: only k >= m0 contributes)
   // (W_new = W + dW is written by the last product that updates dW)
-  ISPA_TRY(run_trgemm(true, w.Bx, w.Mx, L.delta_w, d, 1.f, 0.f, s, L.W, L.refine > 0 ? nullptr : L.w_new, L.w_dtype));
+  ISPA_TRY(run_trgemm(true, w.Bx, st.ws, w.Mx, st.ws, L.delta_w, st.mat, d, 1.f, 0.f, nb_l, s, L.W,
+                      L.refine > 0 ? nullptr : L.w_new, L.w_dtype, st.wmat));
   if (L.refine > 0) {
     // iterative refinement: r = C W - (G + lambda I) dW with fp64 accumulation (C W formed once in
     // fp64), then dW += (L^-1)^T (L^-1 r) with the fp32 factor
     const int tpd = (d + 127) / 128;
-    hipLaunchKernelGGL(gemm64_kernel<0>, dim3(tpd * tpd), dim3(NT), 0, s, L.C, w.Wf, d, w.sc, w.R64, nullptr);
+    const dim3 g64(tpd * tpd, nb_l);
+    hipLaunchKernelGGL(gemm64_kernel<0>, g64, dim3(NT), 0, s, L.C, st.mat, w.Wf, st.ws, d, w.sc, w.R64,
+                       (float*)nullptr, st.ws);
     ISPA_TRY(hipGetLastError());
     for (int it = 0; it < L.refine; ++it) {
-      hipLaunchKernelGGL(gemm64_kernel<1>, dim3(tpd * tpd), dim3(NT), 0, s, L.G, L.delta_w, d, w.sc, w.R64, w.Rs);
+      hipLaunchKernelGGL(gemm64_kernel<1>, g64, dim3(NT), 0, s, L.G, st.mat, L.delta_w, st.mat, d, w.sc, w.R64,
+                         w.Rs, st.ws);
       ISPA_TRY(hipGetLastError());
       // t = L^-1 r (into Mx, no longer needed), dW += (L^-1)^T t
-      ISPA_TRY(run_trgemm(false, w.Bx, w.Rs, w.Mx, d, 1.f, 0.f, s));
-      ISPA_TRY(run_trgemm(true, w.Bx, w.Mx, L.delta_w, d, 1.f, 1.f, s, L.W, it + 1 == L.refine ? L.w_new : nullptr,
-                          L.w_dtype));
+      ISPA_TRY(run_trgemm(false, w.Bx, st.ws, w.Rs, st.ws, w.Mx, st.ws, d, 1.f, 0.f, nb_l, s));
+      ISPA_TRY(run_trgemm(true, w.Bx, st.ws, w.Mx, st.ws, L.delta_w, st.mat, d, 1.f, 1.f, nb_l, s, L.W,
+                          it + 1 == L.refine ? L.w_new : nullptr, L.w_dtype, st.wmat));
     }
   }
   if (L.eps) {
-    hipLaunchKernelGGL(dots_kernel, dim3(DOT_BLOCKS), dim3(NT), 0, s, L.D, L.G, w.P, w.Wf, w.Rc, L.delta_w, d, w.part);
+    hipLaunchKernelGGL(dots_kernel, dim3(DOT_BLOCKS, nb_l), dim3(NT), 0, s, L.D, L.G, w.P, w.Wf, w.Rc, L.delta_w,
+                       d, w.part, st);
     ISPA_TRY(hipGetLastError());
-    hipLaunchKernelGGL(eps_kernel, dim3(1), dim3(NT), 0, s, w.part, DOT_BLOCKS, w.sc, L.eps);
+    hipLaunchKernelGGL(eps_kernel, dim3(1, nb_l), dim3(NT), 0, s, w.part, DOT_BLOCKS, w.sc, L.eps, st);
     ISPA_TRY(hipGetLastError());
   }
   return hipSuccess;

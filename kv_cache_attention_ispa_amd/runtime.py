@@ -20,7 +20,7 @@ from __future__ import annotations
 from typing import List, Optional, Sequence, Tuple
 
 from . import (AttnShape, CALL_ABSORB_SOLVE, CALL_DUAL_ATTN, CALL_LOCAL_ATTN_PROJ, IspaError, KVCache,
-               absorb_solve, dual_attn, gram_accum, local_attn_fused_proj, select_layers, workspace_bytes)
+               absorb_solve_batched, dual_attn, gram_accum, local_attn_fused_proj, select_layers, workspace_bytes)
 
 WARMUP, STEADY = "warmup", "steady"
 
@@ -56,7 +56,9 @@ class IspaRuntime:
         self.stat_dtype = stat_dtype or torch.float16
         self.lam, self.lam_relative, self.refine = lam, lam_relative, refine
         self.keep_delta_w = keep_delta_w
-        self.stream = stream
+        # every call goes to one torch stream; buffers made per call are recorded on it so the caching
+        # allocator never hands them out while that stream may still use them
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
         dev = "cuda"
         self.kv = KVCache(n_layers, self.d, self.dtype, sink_rows, chunk_rows, max_chunks)
         self.chunks = [0] * n_layers
@@ -65,7 +67,9 @@ class IspaRuntime:
         self.ld = (chunk_rows + 7) // 8 * 8
         self.a_t = torch.empty((d, self.ld), dtype=self.stat_dtype, device=dev)
         self.da_t = torch.empty((d, self.ld), dtype=self.stat_dtype, device=dev)
-        self.stats: List[Optional[Tuple]] = [None] * n_layers       # (G, C, D) per layer, fp32 [d, d]
+        # G, C, D of every layer, fp32 [n_layers, d, d]; started[l] once layer l's first chunk is in
+        self.G, self.C, self.D = (torch.empty((n_layers, d, d), device=dev) for _ in range(3))
+        self.started = [False] * n_layers
         self.eps = torch.full((n_layers,), float("nan"), device=dev)
         self.lambdas = torch.zeros((n_layers,), device=dev)
         self.info = torch.zeros((n_layers,), dtype=torch.int32, device=dev)
@@ -73,15 +77,21 @@ class IspaRuntime:
         self.order = torch.zeros((n_layers,), dtype=torch.int32, device=dev)
         self.roles: Optional[List[int]] = None
         self.w_new = [None] * n_layers
-        self.delta_w = [None] * n_layers
+        self.delta_w = None
 
     # ------------------------------------------------------------------ helpers
     def _shape(self, layer: int, n_q: int) -> Tuple[AttnShape, object, object]:
         k, v, (n_s, n_h, n_c) = self.kv.layer(layer)
         return AttnShape(n_q, n_s, n_h, n_c, self.n_heads, self.head_dim, 0.0), k, v
 
-    def _ws(self, call: int, shape: Optional[AttnShape], d: int = 0):
-        return self.torch.empty(workspace_bytes(call, shape, d), dtype=self.torch.uint8, device="cuda")
+    def _buf(self, *shape, dtype=None):
+        t = self.torch.empty(shape, dtype=dtype or self.torch.float32, device="cuda")
+        if self.stream != self.torch.cuda.current_stream():
+            t.record_stream(self.stream)
+        return t
+
+    def _ws(self, call: int, shape: Optional[AttnShape], d: int = 0, count: int = 1):
+        return self._buf(count * workspace_bytes(call, shape, d), dtype=self.torch.uint8)
 
     # ------------------------------------------------------------------ stages
     def write_sink(self, layer: int, k, v) -> None:
@@ -95,17 +105,15 @@ class IspaRuntime:
         self.kv.append_chunk(layer, k, v, stream=self.stream)
         self.chunks[layer] += 1
         shape, kc, vc = self._shape(layer, q.shape[0])
-        out = torch.empty((shape.n_q, self.d), dtype=self.dtype, device="cuda")
+        out = self._buf(shape.n_q, self.d, dtype=self.dtype)
         if self.stage == WARMUP:
             if shape.n_q > self.chunk_rows:
                 raise ValueError("a warmup chunk has at most chunk_rows queries")
             dual_attn(shape, q, kc, vc, a_full=out, a_loc_t=self.a_t, delta_a_t=self.da_t, ld_stat=self.ld,
                       workspace=self._ws(CALL_DUAL_ATTN, shape), stream=self.stream)
-            first = self.stats[layer] is None
-            if first:
-                self.stats[layer] = tuple(torch.empty((self.d, self.d), device="cuda") for _ in range(3))
-            G, C, D = self.stats[layer]
-            gram_accum(self.a_t, self.da_t, shape.n_q, G, C, D, accumulate=not first, stream=self.stream)
+            gram_accum(self.a_t, self.da_t, shape.n_q, self.G[layer], self.C[layer], self.D[layer],
+                       accumulate=self.started[layer], stream=self.stream)
+            self.started[layer] = True
             return out, False
         if self.roles[layer] == 1:
             local_attn_fused_proj(shape, q, kc, vc, self.w_new[layer], out,
@@ -121,33 +129,34 @@ class IspaRuntime:
         torch = self.torch
         if self.stage != WARMUP:
             raise RuntimeError("transition() runs once, after the warmup")
-        if any(s is None for s in self.stats):
+        if not all(self.started):
             raise RuntimeError("every layer needs at least one warmup chunk before the transition")
         if len(weights) != self.n_layers:
             raise ValueError("one weight matrix per layer")
-        d = self.d
-        ws = self._ws(CALL_ABSORB_SOLVE, None, d)
-        dw = torch.empty((d, d), device="cuda")
-        for layer in range(self.n_layers):
-            G, C, D = self.stats[layer]
-            w_new = torch.empty((d, d), dtype=weights[layer].dtype, device="cuda")
-            if self.keep_delta_w:
-                dw = torch.empty((d, d), device="cuda")
-            absorb_solve(G, C, weights[layer], self.lam, self.lam_relative, dw, self.info[layer:layer + 1], ws,
-                         D=D, w_new=w_new, eps=self.eps[layer:layer + 1],
-                         lambda_out=self.lambdas[layer:layer + 1], refine=self.refine, stream=self.stream)
-            self.w_new[layer] = w_new
-            if self.keep_delta_w:
-                self.delta_w[layer] = dw
+        d, n = self.d, self.n_layers
+        with torch.cuda.stream(self.stream):
+            W = torch.stack(list(weights))
+        w_new = self._buf(n, d, d, dtype=W.dtype)
+        self.delta_w = self._buf(n, d, d)
+        ws = self._ws(CALL_ABSORB_SOLVE, None, d, count=n)
+        # all layers' absorptions in one batched solve: each layer's Cholesky chain is sequential, side
+        # by side they fill the GPU
+        absorb_solve_batched(self.G, self.C, W, self.lam, self.lam_relative, self.delta_w, self.info, ws, D=self.D,
+                             w_new=w_new, eps=self.eps, lambda_out=self.lambdas, refine=self.refine,
+                             stream=self.stream)
+        self.w_new = [w_new[l] for l in range(n)]
         # a layer whose factorisation failed (info != 0) has no valid epsilon and ranks last
         select_layers(self.eps, self.k_local, self.role, self.order, info=self.info, stream=self.stream)
-        self.roles = [int(r) for r in self.role.cpu().tolist()]      # the one read-back (synchronises)
+        self.stream.synchronize()                                     # the one wait: read the role map back
+        self.roles = [int(r) for r in self.role.cpu().tolist()]
         for layer, r in enumerate(self.roles):
             if r == 1:
                 self.kv.release_history(layer, stream=self.stream)
             else:
                 self.w_new[layer] = None
-        self.stats = [None] * self.n_layers
+        self.G = self.C = self.D = None
+        if not self.keep_delta_w:
+            self.delta_w = None
         self.stage = STEADY
         return list(self.roles)
 

@@ -189,3 +189,17 @@ def test_select_layers_validation(L):
     assert f(eps=FAKE + 2) == EINVAL
     assert f(order=FAKE + 1) == EINVAL
     assert f(info=FAKE + 2) == EINVAL
+
+
+def test_batched_solve_validation(L):
+    need = ispa.workspace_bytes(ispa.CALL_ABSORB_SOLVE, None, 256)
+
+    def f(n=3, d=256, ws=FAKE, wsb=None, eps=FAKE, D=FAKE, refine=0):
+        return L.ispa_absorb_solve_batched(n, d, FAKE, FAKE, D, 1, FAKE, 1e-3, 1, refine, FAKE, None, eps, None,
+                                           FAKE, ws, 3 * need if wsb is None else wsb, None)
+    assert f(n=0) == EINVAL
+    assert f(d=100) == EINVAL
+    assert f(eps=FAKE, D=None) == EINVAL
+    assert f(refine=9) == EINVAL
+    assert f(wsb=3 * need - 1) == EWORKSPACE
+    assert f(ws=None) == EWORKSPACE

@@ -199,3 +199,48 @@ def test_bf16_small_end_to_end():
     assert got["info"] == 0
     assert relfro(got["dW"], dW) <= 1e-2
     assert abs(got["eps"] - eps) <= 1e-2 * eps
+
+
+@pytest.mark.parametrize("d,layers,refine", [(256, 3, 0), (1536, 4, 0), (320, 2, 1)])
+def test_batched_solve_equals_per_layer_calls(d, layers, refine):
+    """ispa_absorb_solve_batched: every layer's dW, W_new, eps, lambda and info equal those of a
+    separate ispa_absorb_solve call, bit for bit; one layer is indefinite (info set, others intact);
+    the per-layer results also match the oracle."""
+    import kv_cache_attention_ispa_amd as ispa
+    t = torch()
+    probs = [_spd_problem(d, 2 * d + 7 * l, 100 + l, "bf16") for l in range(layers)]
+    G = t.stack([dev(p[0], "f32") for p in probs])
+    C = t.stack([dev(p[1], "f32") for p in probs])
+    D = t.stack([dev(p[2], "f32") for p in probs])
+    W = t.stack([dev(p[3], "bf16") for p in probs])
+    bad = layers - 1 if layers > 2 else None
+    if bad is not None:
+        G[bad, 5, 5] = -1e3                       # not positive definite: info = 6
+    dW = t.full((layers, d, d), float("nan"), device="cuda")
+    w_new = t.empty((layers, d, d), dtype=t.bfloat16, device="cuda")
+    eps = t.full((layers,), float("nan"), device="cuda")
+    lam = t.full((layers,), float("nan"), device="cuda")
+    info = t.full((layers,), -7, dtype=t.int32, device="cuda")
+    ws_one = ispa.workspace_bytes(ispa.CALL_ABSORB_SOLVE, None, d)
+    ws = t.empty(layers * ws_one, dtype=t.uint8, device="cuda")
+    ispa.absorb_solve_batched(G, C, W, 1e-3, True, dW, info, ws, D=D, w_new=w_new, eps=eps, lambda_out=lam,
+                              refine=refine)
+    t.cuda.synchronize()
+    for l in range(layers):
+        dW1 = t.empty((d, d), device="cuda")
+        wn1 = t.empty((d, d), dtype=t.bfloat16, device="cuda")
+        e1, l1 = t.empty((1,), device="cuda"), t.empty((1,), device="cuda")
+        i1 = t.empty((1,), dtype=t.int32, device="cuda")
+        ispa.absorb_solve(G[l].contiguous(), C[l].contiguous(), W[l].contiguous(), 1e-3, True, dW1, i1,
+                          ws[:ws_one], D=D[l].contiguous(), w_new=wn1, eps=e1, lambda_out=l1, refine=refine)
+        t.cuda.synchronize()
+        assert int(info[l].item()) == int(i1.item())
+        if l == bad:
+            assert int(i1.item()) == 6
+            continue
+        assert int(i1.item()) == 0
+        assert t.equal(dW[l], dW1) and t.equal(w_new[l], wn1)
+        assert t.equal(eps[l:l + 1], e1) and t.equal(lam[l:l + 1], l1)
+        Gp, Cp, Dp, Wp = probs[l]
+        lam_ref = oracle.ridge_lambda(Gp, 1e-3, True)
+        assert relfro(host(dW1), oracle.solve_delta_w(Gp, Cp, Wp, lam_ref)) <= 1e-3
