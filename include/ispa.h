@@ -231,6 +231,27 @@ int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype,
                                void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ispa_local_attn_fused_proj_noalloc -- ispa_local_attn_fused_proj without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and checks as ispa_local_attn_fused_proj
+ * (bit for bit: the same kernels run), but the scratch is a fixed array of
+ * ispa_noalloc_scratch_bytes() = 64 MiB that the library holds on each GPU it
+ * runs on until the process ends; the call allocates nothing.  A shape whose
+ * scratch (ispa_workspace_bytes(ISPA_CALL_LOCAL_ATTN_PROJ, shape, 0)) exceeds
+ * it returns ISPA_EWORKSPACE (e.g. n_q 4680, sink 1560, current 4680, d 1536
+ * needs 38 MiB and fits; d 5120 does not).  Every call on one GPU uses that
+ * GPU's array: calls that overlap in time on one GPU (other streams or host
+ * threads) race and must be ordered by the caller.  The first call on a device
+ * looks the array's address up (hipGetSymbolAddress) and keeps it; ISPA_EHIP if
+ * that fails.
+ */
+int ispa_local_attn_fused_proj_noalloc(const ispa_attn_shape* shape, int io_dtype,
+                                       const void* q, const void* k, const void* v, const void* w_new,
+                                       void* out, void* stream);
+size_t ispa_noalloc_scratch_bytes(void);
+
+/*
  * W8A8 variant of the L-layer step (FP8 weights and activations).
  * Technical summary section 4 "Results": the method combined with W8A8
  * post-training quantisation gives the largest overall speed-up; the pages

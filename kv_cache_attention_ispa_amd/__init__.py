@@ -15,7 +15,7 @@ __all__ = ["IspaError", "AttnShape", "lib", "dual_attn", "gram_accum", "absorb_s
            "local_attn_fused_proj", "workspace_bytes", "CALL_DUAL_ATTN", "CALL_ABSORB_SOLVE",
            "CALL_LOCAL_ATTN_PROJ", "CALL_LOCAL_ATTN_PROJ_W8A8", "library_path", "KVCache",
            "quantize_weight_fp8", "quantize_rows_fp8", "local_attn_fused_proj_w8a8", "select_layers",
-           "absorb_solve_batched"]
+           "local_attn_fused_proj_noalloc", "absorb_solve_batched"]
 
 F32, BF16, F16 = 0, 1, 2
 CALL_DUAL_ATTN, CALL_ABSORB_SOLVE, CALL_LOCAL_ATTN_PROJ, CALL_LOCAL_ATTN_PROJ_W8A8 = 0, 1, 2, 3
@@ -82,11 +82,14 @@ def lib() -> ctypes.CDLL:
         L.ispa_select_layers.argtypes = [_i32, _vp, _vp, _i32, _vp, _vp, _vp]
         L.ispa_absorb_solve_batched.argtypes = [_i32, _i32, _vp, _vp, _vp, _i32, _vp, _f32, _i32, _i32, _vp, _vp, _vp,
                                                 _vp, _vp, _vp, _sz, _vp]
+        L.ispa_local_attn_fused_proj_noalloc.argtypes = [ctypes.POINTER(AttnShape), _i32, _vp, _vp, _vp, _vp, _vp,
+                                                         _vp]
+        L.ispa_noalloc_scratch_bytes.restype = ctypes.c_size_t
         for f in ("ispa_dual_attn", "ispa_gram_accum", "ispa_absorb_solve", "ispa_local_attn_fused_proj",
                   "ispa_quantize_weight_fp8", "ispa_quantize_rows_fp8", "ispa_local_attn_fused_proj_w8a8",
                   "ispa_kv_create", "ispa_kv_destroy", "ispa_kv_write_sink", "ispa_kv_append_chunk",
                   "ispa_kv_release_history", "ispa_kv_layer", "ispa_kv_bytes", "ispa_select_layers",
-                  "ispa_absorb_solve_batched"):
+                  "ispa_local_attn_fused_proj_noalloc", "ispa_absorb_solve_batched"):
             getattr(L, f).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -297,6 +300,17 @@ def local_attn_fused_proj(shape: AttnShape, q, k, v, w_new, out, workspace, stre
                                             _ptr(w_new), _ptr(out), _ptr(workspace), _ws_bytes(workspace),
                                             _stream(stream)),
            "ispa_local_attn_fused_proj")
+
+
+def local_attn_fused_proj_noalloc(shape: AttnShape, q, k, v, w_new, out, stream=None) -> None:
+    """ispa_local_attn_fused_proj_noalloc: the L-layer step with the library's fixed per-GPU scratch
+    instead of a workspace (allocates nothing; calls overlapping on one GPU race)."""
+    d = _l_layer_args(shape, q, k, v, out)
+    _want(w_new, "w_new", q.dtype, (d, d))
+    _same_device(q, k, v, w_new, out)
+    _check(lib().ispa_local_attn_fused_proj_noalloc(ctypes.byref(shape), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
+                                                    _ptr(w_new), _ptr(out), _stream(stream)),
+           "ispa_local_attn_fused_proj_noalloc")
 
 
 def quantize_weight_fp8(w, wq_t, w_scales, stream=None) -> None:

@@ -5,6 +5,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 using namespace ispa;
 
 namespace {
@@ -59,6 +61,29 @@ bool fits_buffer(const ispa_attn_shape* s) {
   const int64_t n_k = (int64_t)s->n_sink + s->n_hist + s->n_cur;
   const int64_t d = (int64_t)s->n_heads * s->head_dim;
   return n_k * d * 2 < INT32_MAX && (int64_t)attn_vt_bytes(n_k, d) < INT32_MAX;
+}
+
+// Scratch of ispa_local_attn_fused_proj_noalloc: one array per GPU, part of the code object (so it
+// exists once the library is loaded on a device and is never allocated by a call).  Its host-side
+// name is only a stand-in; the device address comes from hipGetSymbolAddress, looked up once per
+// device on that device's first call and kept.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, or nullptr when the lookup failed.
+void* noalloc_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -267,6 +292,24 @@ int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype, const
   P.b = w_new;
   P.out = out;
   return hip_status(launch_proj(P, s));
+}
+
+size_t ispa_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+int ispa_local_attn_fused_proj_noalloc(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k,
+                                       const void* v, const void* w_new, void* out, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  const size_t need = ispa_workspace_bytes(ISPA_CALL_LOCAL_ATTN_PROJ, shape, 0);
+  if (need > kNoAllocScratchBytes) return ISPA_EWORKSPACE;
+  // the remaining checks are those of the workspace variant; argument errors come before the lookup
+  if (io_dtype != ISPA_BF16 && io_dtype != ISPA_F16) return ISPA_EUNSUPPORTED;
+  if (shape->head_dim != 128 || !fits_buffer(shape)) return ISPA_EUNSUPPORTED;
+  if (!q || !k || !v || !w_new || !out) return ISPA_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(w_new) || !aligned16(out)) return ISPA_EINVAL;
+  void* ws = noalloc_scratch();
+  if (!ws) return ISPA_EHIP;
+  return ispa_local_attn_fused_proj(shape, io_dtype, q, k, v, w_new, out, ws, kNoAllocScratchBytes, stream);
 }
 
 int ispa_quantize_weight_fp8(int d_in, int d_out, int w_dtype, const void* w, void* wq_t, float* w_scales,

@@ -191,6 +191,21 @@ def test_select_layers_validation(L):
     assert f(info=FAKE + 2) == EINVAL
 
 
+def test_noalloc_validation(L):
+    """The no-allocation L-layer step rejects what does not fit its fixed scratch, and bad arguments,
+    before any device work."""
+    assert L.ispa_noalloc_scratch_bytes() == 64 << 20
+    big = ispa.AttnShape(4680, 1560, 0, 4680, 40, 128, 0.0)
+    ok = ispa.AttnShape(4680, 1560, 0, 4680, 12, 128, 0.0)
+    assert ispa.workspace_bytes(ispa.CALL_LOCAL_ATTN_PROJ, ok) <= L.ispa_noalloc_scratch_bytes()
+    f = lambda s, io=1, q=FAKE, w=FAKE: L.ispa_local_attn_fused_proj_noalloc(ctypes.byref(s), io, q, FAKE, FAKE, w,
+                                                                              FAKE, None)
+    assert f(big) == EWORKSPACE
+    assert f(ok, io=0) == EUNSUPPORTED
+    assert f(ok, q=None) == EINVAL
+    assert f(ok, w=FAKE + 8) == EINVAL
+
+
 def test_batched_solve_validation(L):
     need = ispa.workspace_bytes(ispa.CALL_ABSORB_SOLVE, None, 256)
 
