@@ -100,6 +100,72 @@ def w8a8_matmul(A, W) -> np.ndarray:
     return prod * sa.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :]
 
 
+def local_attention_fp8(q, k, v, n_sink: int, n_cur: int, n_heads: int, scale: Optional[float] = None,
+                        quantize: bool = True) -> np.ndarray:
+    """Attention of a converted layer with its operands in FP8 E4M3 (the W8A8 reading of the attention).
+
+    The layer's key rows are its whole (local) cache: sink rows + current chunk.  Per head h:
+      * Q per query token: s_q[i] = max_c |Q[i, c]| / 448, codes E4M3(Q / s_q);
+      * K and V with one scale each over all key rows: s_k = max |K| / 448, s_v = max |V| / 448;
+      * scores S = s_q s_k (dec(Qq) dec(Kq)^T), in log2 units x = S * scale * log2(e);
+      * row reference M = ceil(max_j x) (an integer, so the largest probability is in (1/2, 1]);
+        P = 2^(x - M) and its codes E4M3(256 P) (a fixed power-of-two scale: 256 P <= 256 < 448);
+      * l = sum_j dec(Pq) / 256, O = s_v (dec(Pq) / 256) dec(Vq) / l.
+    Scales and quotients are float32 operations, so every code is a float32 decision (as for the
+    projection); S and the sums are exact (float64).  quantize=False skips every rounding (the codes
+    become the values themselves), which is plain softmax attention over the same rows.
+    """
+    from .attention import branch_rows, default_scale
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n_q, d = q.shape
+    dh = d // n_heads
+    scale = default_scale(dh) if scale is None else scale
+    rows = branch_rows(n_sink, 0, n_cur)["local"]
+    out = np.zeros((n_q, d))
+    log2e = 1.0 / np.log(2.0)
+
+    def codes(x, s):
+        y = np.clip((np.asarray(x, dtype=np.float32) / np.float32(s)).astype(np.float32), -E4M3_MAX, E4M3_MAX)
+        return e4m3_decode(e4m3_encode(y))
+
+    def tensor_scale(x):
+        a = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
+        return np.float32(a / np.float32(E4M3_MAX)) if a > 0 else np.float32(1.0)
+
+    for h in range(n_heads):
+        c = slice(h * dh, (h + 1) * dh)
+        qh, kh, vh = q[:, c], k[rows, c], v[rows, c]
+        if quantize:
+            amax = np.max(np.abs(qh.astype(np.float32)), axis=1)
+            sq = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+            sk, sv = tensor_scale(kh.astype(np.float32)), tensor_scale(vh.astype(np.float32))
+            qd = np.stack([codes(qh[i], sq[i]) for i in range(n_q)]) if n_q else qh
+            kd, vd = codes(kh, sk), codes(vh, sv)
+            S = (qd @ kd.T) * sq.astype(np.float64)[:, None] * float(sk)
+        else:
+            S, vd, sv = qh @ kh.T, vh, 1.0
+        x = S * scale * log2e
+        M = np.ceil(np.max(x, axis=1, keepdims=True))
+        P = np.exp2(x - M)
+        if quantize:
+            Pq = e4m3_decode(e4m3_encode((256.0 * P).astype(np.float32))) / 256.0
+        else:
+            Pq = P
+        l = Pq.sum(axis=1, keepdims=True)
+        out[:, c] = float(sv) * (Pq @ vd) / l
+    return out
+
+
+def local_layer_output_w8a8_fp8attn(q, k, v, n_sink: int, n_cur: int, n_heads: int, W,
+                                    scale: Optional[float] = None) -> np.ndarray:
+    """The converted layer in W8A8 end to end: FP8 attention (local_attention_fp8), its output stored in
+    bfloat16, then the W8A8 projection by W."""
+    a = local_attention_fp8(q, k, v, n_sink, n_cur, n_heads, scale)
+    return w8a8_matmul(round_bf16(a.astype(np.float32)), W)
+
+
 def local_layer_output_w8a8(q, k, v, n_sink: int, n_cur: int, n_heads: int, W,
                             scale: Optional[float] = None, threads: int = 1) -> np.ndarray:
     """An L-layer step with the W8A8 projection: local attention (float64), its output stored in

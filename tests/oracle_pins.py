@@ -387,6 +387,39 @@ def check_golden_w8a8_l_layer(impl):
     assert np.array_equal(out, np.array(g["expect"]["out"]))
 
 
+def check_golden_fp8_attention(impl):
+    """Hand-worked FP8 attention of a converted layer: dominant key, rounding against the integer
+    reference, Q = 0."""
+    g = _golden("fp8_attention_hand.json")
+    q, k, v = (np.array(g[x], dtype=np.float64) for x in ("q", "k", "v"))
+    out = impl.local_attention_fp8(q, k, v, g["n_sink"], g["n_cur"], g["n_heads"], scale=g["scale"])
+    assert np.allclose(out, np.array(g["expect"]["out"]), rtol=1e-13, atol=1e-12)
+    c = g["case2"]
+    q, k, v = (np.array(c[x], dtype=np.float64) for x in ("q", "k", "v"))
+    out = impl.local_attention_fp8(q, k, v, c["n_sink"], c["n_cur"], c["n_heads"], scale=c["scale"])
+    assert np.allclose(out, np.array(c["expect"]["out"]), rtol=1e-13, atol=1e-12)
+
+
+def check_fp8_attention_structure(impl, seed=11):
+    """Without rounding the FP8 attention is plain softmax attention over the layer's rows; with it the
+    error is quantisation-sized; V scaled by a power of two scales the output exactly (codes and
+    probabilities unchanged); the order of the key rows within each segment does not matter."""
+    rng = _rng(seed)
+    n_sink, n_cur, H, dh = 7, 25, 2, 16
+    q = rng.standard_normal((9, H * dh))
+    k = rng.standard_normal((n_sink + n_cur, H * dh))
+    v = rng.standard_normal((n_sink + n_cur, H * dh))
+    exact, _ = impl.softmax_attention(q, k, v, np.arange(n_sink + n_cur), H)
+    plain = impl.local_attention_fp8(q, k, v, n_sink, n_cur, H, quantize=False)
+    assert np.allclose(plain, exact, atol=1e-13)
+    got = impl.local_attention_fp8(q, k, v, n_sink, n_cur, H)
+    err = np.max(np.abs(got - exact)) / np.max(np.abs(exact))
+    assert 1e-3 < err < 0.25, err
+    assert np.array_equal(impl.local_attention_fp8(q, k, 4.0 * v, n_sink, n_cur, H), 4.0 * got)
+    perm = np.concatenate([rng.permutation(n_sink), n_sink + rng.permutation(n_cur)])
+    assert np.allclose(impl.local_attention_fp8(q, k[perm], v[perm], n_sink, n_cur, H), got, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------
 # accounting
 # ----------------------------------------------------------------------------
@@ -423,6 +456,7 @@ ATTENTION_PINS = [check_brute_force, check_golden_attention, check_q_zero, check
 ABSORB_PINS = [check_golden_ridge, check_residual, check_augmented_lstsq, check_lambda_limits,
                check_relative_lambda, check_linearity_in_w, check_optimality, check_rowspace,
                check_eps_two_ways, check_zero_absorb, check_gram_associativity, check_selection,
-               check_golden_l_layer, check_golden_residual_and_fold, check_golden_w8a8_l_layer]
+               check_golden_l_layer, check_golden_residual_and_fold, check_golden_w8a8_l_layer,
+               check_golden_fp8_attention, check_fp8_attention_structure]
 ACCOUNTING_PINS = [check_kv_bytes, check_flops]
 ALL_PINS = ATTENTION_PINS + ABSORB_PINS + ACCOUNTING_PINS

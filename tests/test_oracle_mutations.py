@@ -17,7 +17,7 @@ from oracle_pins import ALL_PINS
 NAMES = ["branch_rows", "softmax_attention", "dual_stream", "lse_merge", "gram_stats", "ridge_lambda",
          "solve_delta_w", "normal_equation_residual", "recon_error_direct", "recon_error_traces",
          "select_local_layers", "fold_weights", "local_layer_output", "attn_flops", "kv_cache_bytes",
-         "kv_removed_fraction", "default_scale", "local_layer_output_w8a8"]
+         "kv_removed_fraction", "default_scale", "local_layer_output_w8a8", "local_attention_fp8"]
 
 
 def _ns(**over):
@@ -164,6 +164,48 @@ def _w8a8_no_bf16_rounding(q, k, v, n_sink, n_cur, n_heads, W, scale=None, threa
     return fp8.w8a8_matmul(a.astype(np.float32), W)
 
 
+def _fp8_attention_variant(reference="ceil", p_scale=256.0, l_from="codes", k_scale="head"):
+    def attn(q, k, v, n_sink, n_cur, n_heads, scale=None, quantize=True):
+        if not quantize:   # the planted mistakes are in the rounding only
+            return oracle.local_attention_fp8(q, k, v, n_sink, n_cur, n_heads, scale, quantize=False)
+        q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+        n_q, d = q.shape
+        dh = d // n_heads
+        scale = 1.0 / math.sqrt(dh) if scale is None else scale
+        rows = oracle.branch_rows(n_sink, 0, n_cur)["local"]
+        out = np.zeros((n_q, d))
+
+        def codes(x, s):
+            y = np.clip((np.asarray(x, dtype=np.float32) / np.float32(s)).astype(np.float32), -448.0, 448.0)
+            return fp8.e4m3_decode(fp8.e4m3_encode(y))
+
+        def sc(a):
+            m = np.float32(np.max(np.abs(a)))
+            return np.float32(m / np.float32(448.0)) if m > 0 else np.float32(1.0)
+        for h in range(n_heads):
+            c = slice(h * dh, (h + 1) * dh)
+            qh, kh, vh = q[:, c], k[rows, c], v[rows, c]
+            sq = [sc(qh[i]) for i in range(n_q)]
+            qd = np.stack([codes(qh[i], sq[i]) for i in range(n_q)])
+            if k_scale == "head":
+                sk = [sc(kh)] * len(rows)
+            else:
+                sk = [sc(kh[j]) for j in range(len(rows))]
+            kd = np.stack([codes(kh[j], sk[j]) for j in range(len(rows))])
+            sv = sc(vh)
+            vd = codes(vh, sv)
+            S = (qd @ kd.T) * np.array(sq, dtype=np.float64)[:, None] * np.array(sk, dtype=np.float64)[None, :]
+            x = S * scale / math.log(2.0)
+            m = np.max(x, axis=1, keepdims=True)
+            M = np.ceil(m) if reference == "ceil" else m
+            P = np.exp2(x - M)
+            Pq = fp8.e4m3_decode(fp8.e4m3_encode(np.minimum(p_scale * P, 448.0).astype(np.float32))) / p_scale
+            l = (Pq if l_from == "codes" else P).sum(axis=1, keepdims=True)
+            out[:, c] = float(sv) * (Pq @ vd) / l
+        return out
+    return attn
+
+
 MUTANTS = {
     "scale_1_over_d": dict(softmax_attention=_softmax_variant(scale_fn=lambda dh: 1.0 / dh),
                            dual_stream=_dual_with(_softmax_variant(scale_fn=lambda dh: 1.0 / dh))),
@@ -189,6 +231,10 @@ MUTANTS = {
     "residual_returns_zero": dict(normal_equation_residual=_residual_zero),
     "residual_drops_lambda": dict(normal_equation_residual=_residual_no_lambda),
     "w8a8_skips_bf16_storage": dict(local_layer_output_w8a8=_w8a8_no_bf16_rounding),
+    "fp8_reference_not_integer": dict(local_attention_fp8=_fp8_attention_variant(reference="max")),
+    "fp8_probabilities_scaled_448": dict(local_attention_fp8=_fp8_attention_variant(p_scale=448.0)),
+    "fp8_row_sum_unquantised": dict(local_attention_fp8=_fp8_attention_variant(l_from="exact")),
+    "fp8_key_scales_per_token": dict(local_attention_fp8=_fp8_attention_variant(k_scale="token")),
 }
 
 
