@@ -158,6 +158,38 @@ def secondary(torch, ispa, wl, stream, run_attn_1p3b) -> dict:
     flops = sum(4.0 * s2.n_q * (sh_.n_sink + sh_.n_hist + sh_.n_cur) * d for sh_ in shapes)
     out["warmup_1p3b_per_layer"] = {"chunks": 4, "tokens": 4 * s2.n_q, "ms": t_warm,
                                     "attn_gflop": round(flops / 1e9, 2)}
+
+    # the transition of the 30-layer 1.3B model: every layer's absorption in one batched solve (with
+    # epsilon and W_new), statistics of the 18720-token warmup of one layer replicated per layer (the
+    # solve's time does not depend on the values)
+    n_l = 30
+    ld4 = ((4 * s2.n_q + 7) // 8) * 8
+    a_t = torch.empty((d, ld4), dtype=torch.float16, device="cuda")
+    da_t = torch.empty((d, ld4), dtype=torch.float16, device="cuda")
+    for c, shc in enumerate(shapes):
+        n_k = shc.n_sink + shc.n_hist + shc.n_cur
+        ispa.dual_attn(shc, q, k[:n_k], v[:n_k], a_loc_t=a_t[:, c * s2.n_q:], delta_a_t=da_t[:, c * s2.n_q:],
+                       ld_stat=ld4, workspace=b["ws"], stream=stream)
+    ispa.gram_accum(a_t, da_t, 4 * s2.n_q, b["G"], b["C"], b["D"], stream=stream)
+    G30, C30, D30 = (x.unsqueeze(0).repeat(n_l, 1, 1).contiguous() for x in (b["G"], b["C"], b["D"]))
+    W30 = W.unsqueeze(0).repeat(n_l, 1, 1).contiguous()
+    dW30 = torch.empty_like(G30)
+    Wn30 = torch.empty_like(W30)
+    e30 = torch.empty((n_l,), device="cuda")
+    i30 = torch.zeros((n_l,), dtype=torch.int32, device="cuda")
+    ws30 = torch.empty(n_l * ispa.workspace_bytes(ispa.CALL_ABSORB_SOLVE, None, d), dtype=torch.uint8, device="cuda")
+    t_b = timed(torch, lambda: ispa.absorb_solve_batched(G30, C30, W30, 1e-3, True, dW30, i30, ws30, D=D30,
+                                                         w_new=Wn30, eps=e30, stream=stream), 3, 1, stream)
+    if int(i30.max().item()) != 0:
+        raise RuntimeError("batched solve reported a non-positive pivot")
+    t_g = timed(torch, lambda: ispa.gram_accum(a_t, da_t, 4 * s2.n_q, b["G"], b["C"], b["D"], stream=stream), 5, 1,
+                stream)
+    out["transition_1p3b_30_layers"] = {
+        "batched_solve_ms": t_b, "solve_ms_per_layer": round(t_b["median"] / n_l, 4),
+        "gram_18720_tokens_ms": t_g,
+        "absorb_ms_per_layer": round(t_b["median"] / n_l + t_g["median"], 4),
+        "note": "Gram over one layer's 4 warmup chunks (18720 tokens) + 1/30 of the solve of all 30 layers at once"}
+    del G30, C30, D30, W30, dW30, Wn30, ws30, a_t, da_t
     del q, k, v, W, b
 
     # rollout of the 1.3B model: F-layer (full attention over 1560 (3c + 4) rows) at chunks 4, 20, 39

@@ -121,14 +121,21 @@ struct AttnParams {
 // lane l on slot 64 inst + l of the tile: row (64 inst + l) / SLOTS, 16-byte chunk (64 inst + l) % SLOTS;
 // a lane on a padding slot loads its row's last chunk again (padding is never read).  A lane's byte
 // offset within the tile is fixed; the tile's first key is the scalar offset.
+// Buffer offsets are 32-bit, the caches are not: the V^T descriptor covers this work-group's head only
+// (128 rows of the copy), and every K tile gets a descriptor based at its own first row, so no offset
+// grows with the cache length (a 14B-shaped layer's K passes 2^31 bytes at 209,716 rows).
 struct Loader {
-  __amdgpu_buffer_rsrc_t rk, rv;
+  __amdgpu_buffer_rsrc_t rv;
+  const char* kb;    // K [n_k, d] as bytes
+  int64_t kbytes;    // n_k * d * 2
   uint32_t off[LOADS_PER_WAVE];
-  __device__ __forceinline__ void init(const AttnParams& p, int n_k, int wave, int lane) {
-    // raw buffers over K [n_k, d] and V^T [d, ldv]; reads past the end return zeros.  Word 3
-    // (0x00020000) is the untyped-access descriptor of gfx9.
-    rk = __builtin_amdgcn_make_buffer_rsrc((void*)p.k, (short)0, (int)((int64_t)n_k * p.d * 2), 0x00020000);
-    rv = __builtin_amdgcn_make_buffer_rsrc((void*)p.vt, (short)0, (int)((int64_t)p.d * p.ldv * 2), 0x00020000);
+  __device__ __forceinline__ void init(const AttnParams& p, int n_k, int wave, int lane, int head) {
+    // raw buffers: reads past the end return zeros.  Word 3 (0x00020000) is the untyped-access
+    // descriptor of gfx9.
+    kb = (const char*)p.k;
+    kbytes = (int64_t)n_k * p.d * 2;
+    rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.vt + (int64_t)head * HD * p.ldv), (short)0,
+                                           (int)((int64_t)HD * p.ldv * 2), 0x00020000);
 #pragma unroll
     for (int j = 0; j < LOADS_PER_WAVE; ++j) {
       const int idx = wave + WAVES * j;
@@ -145,7 +152,8 @@ struct Loader {
   // sequence (then a valid tile is loaded again into a ring slot nobody reads), so the number of
   // loads in flight is the same on every path and one wait count fits all iterations.
   struct Group {
-    uint32_t sk, sv;   // byte offsets of the K tile and the V^T tile
+    __amdgpu_buffer_rsrc_t rk;   // K from the tile's first row to the end of the cache
+    uint32_t sk, sv;             // byte offsets of the head's columns in K and of the V^T tile
     char* kt;
     char* vt;
   };
@@ -153,13 +161,16 @@ struct Loader {
                                          char* vt) const {
     const int tk = min(k, sc.n - 1);
     const int tv = min(max(k - 1, 0), sc.n - 1);
-    return Group{(uint32_t)(sc.row(tk) * p.d + head * HD) * 2u, (uint32_t)(head * HD * p.ldv + sc.row(tv)) * 2u,
-                 kt, vt};
+    const int64_t k0 = (int64_t)sc.row(tk) * p.d * 2;
+    const int64_t rest = kbytes - k0;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kb + k0), (short)0, (int)(rest < INT32_MAX ? rest : INT32_MAX), 0x00020000);
+    return Group{rk, (uint32_t)(head * HD * 2), (uint32_t)sc.row(tv) * 2u, kt, vt};
   }
   __device__ __forceinline__ void issue_one(const Group& g, int j, int wave) const {
     const int idx = wave + WAVES * j;
     if (idx < K_INST) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(g.kt + 1024 * idx), 16, off[j], g.sk, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(g.rk, (lds_void*)(g.kt + 1024 * idx), 16, off[j], g.sk, 0, 0);
     } else {
       const int vi = min(idx - K_INST, V_INST - 1);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(g.vt + 1024 * vi), 16, off[j], g.sv, 0, 0);
@@ -454,7 +465,7 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void attn_mfma_kernel(AttnParams p
   }
 
   Loader ld;
-  ld.init(p, n_k, wave, lane);
+  ld.init(p, n_k, wave, lane, head);
   // Ring slots are chosen at compile time (the iteration loop below is unrolled by the ring depth),
   // so the compiler's memory-dependency analysis sees which slot each in-flight load writes.
   auto kslot = [&](auto J) -> char* {

@@ -197,3 +197,45 @@ def test_layer_1p3b_sampled_rows():
     assert maxrel(got["delta_a"][rows], r["a_full"] - r["a_loc"]) <= 2e-2
     assert maxrel(got["lse_loc"][:, rows], r["lse_loc"]) <= 2e-2
     assert maxrel(got["lse_hist"][:, rows], r["lse_hist"]) <= 2e-2
+
+
+def test_long_cache_14b_past_2gib():
+    """A 14B-shaped layer (40 heads x 128) over 216,840 cached rows (1560-row sink, 139 frames in
+    all): K and V are 2.2 GB each, past 2^31 bytes.  Dual stream (bf16, fp16 statistics) for 256
+    queries; A_full, A_loc and both LSEs of sampled rows in heads 0, 17 and 39 against the oracle
+    (max-rel 2e-2).  Inputs are seeded N(0, 1) drawn on the device."""
+    import kv_cache_attention_ispa_amd as ispa
+    t = torch()
+    H, dh, n_q, n_sink, n_cur = 40, 128, 256, 1560, 4680
+    n_k = 1560 * 139
+    n_hist = n_k - n_sink - n_cur
+    d = H * dh
+    assert n_k * d * 2 > 2 ** 31
+    g = t.Generator(device="cuda").manual_seed(20260701)
+    q = t.randn((n_q, d), generator=g, device="cuda").to(t.bfloat16)
+    k = t.randn((n_k, d), generator=g, device="cuda").to(t.bfloat16)
+    v = t.randn((n_k, d), generator=g, device="cuda").to(t.bfloat16)
+    shape = ispa.AttnShape(n_q, n_sink, n_hist, n_cur, H, dh, 0.0)
+    ws = t.empty(ispa.workspace_bytes(ispa.CALL_DUAL_ATTN, shape), dtype=t.uint8, device="cuda")
+    a_full = t.empty((n_q, d), dtype=t.bfloat16, device="cuda")
+    a_loc_t = t.empty((d, n_q), dtype=t.float16, device="cuda")
+    lse_l = t.empty((H, n_q), device="cuda")
+    lse_h = t.empty((H, n_q), device="cuda")
+    ispa.dual_attn(shape, q, k, v, a_full=a_full, a_loc_t=a_loc_t, ld_stat=n_q, lse_loc=lse_l, lse_hist=lse_h,
+                   workspace=ws)
+    t.cuda.synchronize()
+    del ws
+    rows = np.array([0, 97, 255])
+    br = oracle.branch_rows(n_sink, n_hist, n_cur)
+    for h in (0, 17, 39):
+        c = slice(h * dh, (h + 1) * dh)
+        qh = q[rows, c].float().cpu().numpy().astype(np.float64)
+        kh = k[:, c].float().cpu().numpy()
+        vh = v[:, c].float().cpu().numpy()
+        full, _ = oracle.softmax_attention(qh, kh, vh, br["full"], 1)
+        loc, l_loc = oracle.softmax_attention(qh, kh, vh, br["local"], 1)
+        _, l_hist = oracle.softmax_attention(qh, kh, vh, br["hist"], 1)
+        assert maxrel(host(a_full)[rows, c], full) <= 2e-2, h
+        assert maxrel(host(a_loc_t)[c, :][:, rows].T, loc) <= 2e-2, h
+        assert maxrel(host(lse_l)[h, rows], l_loc[0]) <= 2e-2, h
+        assert maxrel(host(lse_h)[h, rows], l_hist[0]) <= 2e-2, h

@@ -91,7 +91,7 @@ def test_runtime_warmup_absorb_select_steady():
                                         dev(fr["v"][qs], "bf16"))
             assert not projected and out.shape == (qs.stop - qs.start, d)
         del fr
-        G, C, D = (host(x) for x in rt.stats[layer])
+        G, C, D = host(rt.G[layer]), host(rt.C[layer]), host(rt.D[layer])
         ref = g["layers"][layer]
         for M, key in ((G, "g_samples"), (C, "c_samples"), (D, "d_samples")):
             stat_err.append(maxrel(M[ii, jj], np.array(ref[key])))
