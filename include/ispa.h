@@ -56,7 +56,7 @@ enum {
 
 /* call ids for ispa_workspace_bytes */
 enum { ISPA_CALL_DUAL_ATTN = 0, ISPA_CALL_ABSORB_SOLVE = 1, ISPA_CALL_LOCAL_ATTN_PROJ = 2,
-       ISPA_CALL_LOCAL_ATTN_PROJ_W8A8 = 3 };
+       ISPA_CALL_LOCAL_ATTN_PROJ_W8A8 = 3, ISPA_CALL_LOCAL_ATTN_FP8 = 4, ISPA_CALL_LOCAL_ATTN_FP8_PROJ_W8A8 = 5 };
 
 /*
  * One layer's KV cache, rows in this order:
@@ -106,8 +106,9 @@ typedef struct ispa_attn_shape {
  * a transposed copy of V there, which the attention kernel streams, and the dual
  * stream parks the local-branch outputs there while the history branch runs.
  * Calls that share a workspace must not overlap in time.  F32 inputs
- * need none (workspace may be NULL).  The 16-bit path addresses K and the copy
- * with 32-bit byte offsets: n_k * d * 2 must stay below 2^31 (EUNSUPPORTED).
+ * need none (workspace may be NULL).  The 16-bit path addresses one head's
+ * rows of the copy with 32-bit byte offsets: n_k must stay below 8,388,544
+ * (EUNSUPPORTED); K and V themselves may exceed 2^31 bytes.
  * Precision: QK^T and PV run on MFMA with fp32 accumulation.  With BF16 inputs
  * and F16 or F32 statistics (dual mode) the PV product uses fp16 probabilities
  * and the V copy is converted to fp16, for all outputs, A_full included.  That
@@ -223,8 +224,8 @@ int ispa_select_layers(int n_layers, const float* eps, const int32_t* info, int 
  *   if any, are skipped), w_new [d, d], out [n_q, d]; all io_dtype BF16 or F16.
  *   workspace: at least ispa_workspace_bytes(ISPA_CALL_LOCAL_ATTN_PROJ, shape, d)
  *   bytes, 16-byte aligned (the local attention output between the two kernels,
- *   the transposed copy of V and a transposed copy of w_new); n_k * d * 2 and
- *   n_q * d * 2 below 2^31 (ISPA_EUNSUPPORTED otherwise).
+ *   the transposed copy of V and a transposed copy of w_new); n_k below
+ *   8,388,544 and n_q * d * 2 below 2^31 (ISPA_EUNSUPPORTED otherwise).
  */
 int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype,
                                const void* q, const void* k, const void* v, const void* w_new,
@@ -292,6 +293,40 @@ int ispa_local_attn_fused_proj_w8a8(const ispa_attn_shape* shape, int io_dtype,
                                     void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * FP8 attention of a converted layer (the W8A8 variant extended to the attention).
+ * Technical summary section 4 "Results" pairs the method with W8A8 quantisation
+ * without naming a scheme; read here for the attention of an L-layer as FP8 E4M3
+ * operands of both products:
+ *   Q: one scale per query token and head, s_q = absmax / 448, codes E4M3(q / s_q);
+ *   K, V: one scale per head over the call's key rows (sink + current chunk);
+ *   scores in log2 units x = s_q s_k (Qq . Kq) * scale * log2(e);
+ *   P = 2^(x - M), M the integer ceiling of the row maximum, coded as E4M3(256 P);
+ *   l = sum of the decoded P codes, out = s_v sum_j dec(Pq_j) dec(Vq_j) / l.
+ * Scales and quotients are float32 operations (absmax / 448, 1 for an all-zero
+ * head or token).  The kernel moves its reference M by whole powers of two only,
+ * so its codes equal those taken against the row's final M (up to probabilities
+ * below 2^-14 of the row's largest, which E4M3 holds as subnormals).
+ *
+ *   ispa_local_attn_fp8: out [n_q, d] (io dtype BF16 or F16) = that attention over
+ *     the local rows of `shape` (history rows, if any, are not read); q, k, v as in
+ *     ispa_local_attn_fused_proj.  workspace: ispa_workspace_bytes(
+ *     ISPA_CALL_LOCAL_ATTN_FP8, shape, 0) bytes (K codes, transposed V codes,
+ *     scales of the local rows), 16-byte aligned.  head_dim 128; n_sink + n_cur
+ *     below 8,388,544 and
+ *     n_q * d * 2 below 2^31 (EUNSUPPORTED).
+ *   ispa_local_attn_fp8_proj_w8a8: the converted layer in W8A8 end to end: the FP8
+ *     attention, its output rounded to the io dtype, then the W8A8 projection of
+ *     ispa_local_attn_fused_proj_w8a8 (wq_t, w_scales from
+ *     ispa_quantize_weight_fp8).  workspace: ispa_workspace_bytes(
+ *     ISPA_CALL_LOCAL_ATTN_FP8_PROJ_W8A8, shape, 0) bytes.
+ */
+int ispa_local_attn_fp8(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k, const void* v,
+                        void* out, void* workspace, size_t workspace_bytes, void* stream);
+int ispa_local_attn_fp8_proj_w8a8(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k,
+                                  const void* v, const void* wq_t, const float* w_scales, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * KV-cache manager -- the K/V storage on either side of the hot path.
  * Technical summary section 2, stage 3 "Memory-Efficient Inference": after the
  * warmup the F-layers keep attending to the whole growing cache while the
@@ -300,38 +335,46 @@ int ispa_local_attn_fused_proj_w8a8(const ispa_attn_shape* shape, int io_dtype,
  * K and V rows in the order of ispa_attn_shape (sink | history | current),
  * ready to pass to ispa_dual_attn / ispa_local_attn_fused_proj.
  *
- * Unlike the calls above, a cache OWNS device memory: ispa_kv_create
- * allocates it (hipMalloc), ispa_kv_release_history reallocates one layer and
- * ispa_kv_destroy frees everything (hipMalloc/hipFree, so these three may
- * synchronise the device).  A handle is not thread-safe: calls on one handle
- * must come from one host thread at a time.  Row data is copied with
- * hipMemcpyAsync on `stream`; the caller's source rows must stay valid until
- * the stream reaches the copy.  HIP allocation or copy failures return
- * ISPA_EHIP.
+ * Unlike the calls above, a cache OWNS device memory.  Each layer's K rows and
+ * V rows live in virtual address ranges reserved by ispa_kv_create for
+ * sink_rows + max_chunks * chunk_rows rows (address space only); physical
+ * memory is mapped behind them as rows arrive (HIP virtual memory management,
+ * in whole allocation granules; the sink rows of every layer are mapped by
+ * ispa_kv_create) and the pieces past the sink and current chunk are released
+ * when a layer is converted.  So the device memory a cache uses follows the
+ * rows it holds: nothing beyond the sink rows is committed up front, and the
+ * peak over a rollout is the peak of the rows held.  Rows keep their addresses: a
+ * layer's K and V pointers stay valid until ispa_kv_destroy.  The calls that
+ * map or release memory (write_sink, append_chunk and release_history when they
+ * grow or shrink a layer, destroy) may synchronise the device.  A handle is not
+ * thread-safe: calls on one handle must come from one host thread at a time.
+ * Row data is copied with hipMemcpyAsync on `stream`; the caller's source rows
+ * must stay valid until the stream reaches the copy.  HIP failures (mapping,
+ * copies) return ISPA_EHIP.
  *
  *   ispa_kv_create: n_layers >= 1 layers of rows of width d (d % 8 == 0) in
- *     dtype (F32, BF16 or F16); sink_rows >= 0 sink rows, chunks of
- *     chunk_rows >= 1 rows; every layer reserves sink_rows +
- *     max_chunks * chunk_rows rows of K and of V (max_chunks >= 1, total
- *     below 2^31 rows).  *out receives the handle (NULL on error).
- *   ispa_kv_destroy: frees the handle and its memory (NULL is a no-op).
+ *     dtype (F32, BF16 or F16) on the current device; sink_rows >= 0 sink
+ *     rows, chunks of chunk_rows >= 1 rows, at most max_chunks >= 1 chunks per
+ *     full layer (total below 2^31 rows).  *out receives the handle (NULL on
+ *     error).
+ *   ispa_kv_destroy: waits for the device, then frees the handle and its
+ *     memory (NULL is a no-op).
  *   ispa_kv_write_sink: copies sink_rows rows of k and v ([sink_rows, d]
  *     each) into the sink rows of `layer`.
  *   ispa_kv_append_chunk: copies one chunk (chunk_rows rows of k and v).  A
  *     full layer appends it after its rows (the previous current chunk becomes
  *     history; EINVAL once max_chunks chunks are held); a converted layer
  *     overwrites its current chunk.
- *   ispa_kv_release_history: converts a full layer: a new allocation of
- *     sink_rows + chunk_rows rows receives the sink and the current chunk, the
- *     stream is synchronised and the old allocation freed.  EINVAL if the layer
- *     is already converted.
- *   ispa_kv_layer: the layer's K and V base pointers (valid until the next
- *     ispa_kv_release_history of that layer or ispa_kv_destroy) and
- *     rows[0..2] = n_sink, n_hist, n_cur for ispa_attn_shape.
+ *   ispa_kv_release_history: converts a full layer: its current chunk is
+ *     copied next to the sink rows, the stream is synchronised (earlier work may
+ *     still read the history) and the memory past sink + current chunk is
+ *     released.  EINVAL if the layer is already converted.
+ *   ispa_kv_layer: the layer's K and V base pointers and rows[0..2] = n_sink,
+ *     n_hist, n_cur for ispa_attn_shape.
  *   ispa_kv_bytes: *held_bytes = bytes of K and V rows the layers hold
  *     (sink + history + current of full layers, sink + current of converted
  *     ones: the quantity the method reduces); *reserved_bytes = bytes of device
- *     memory the cache has allocated.
+ *     memory mapped behind them (held bytes rounded up to allocation granules).
  */
 typedef struct ispa_kv_cache ispa_kv_cache;
 

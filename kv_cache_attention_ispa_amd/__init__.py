@@ -15,10 +15,12 @@ __all__ = ["IspaError", "AttnShape", "lib", "dual_attn", "gram_accum", "absorb_s
            "local_attn_fused_proj", "workspace_bytes", "CALL_DUAL_ATTN", "CALL_ABSORB_SOLVE",
            "CALL_LOCAL_ATTN_PROJ", "CALL_LOCAL_ATTN_PROJ_W8A8", "library_path", "KVCache",
            "quantize_weight_fp8", "quantize_rows_fp8", "local_attn_fused_proj_w8a8", "select_layers",
-           "local_attn_fused_proj_noalloc", "absorb_solve_batched"]
+           "local_attn_fused_proj_noalloc", "absorb_solve_batched", "local_attn_fp8", "local_attn_fp8_proj_w8a8",
+           "CALL_LOCAL_ATTN_FP8", "CALL_LOCAL_ATTN_FP8_PROJ_W8A8"]
 
 F32, BF16, F16 = 0, 1, 2
 CALL_DUAL_ATTN, CALL_ABSORB_SOLVE, CALL_LOCAL_ATTN_PROJ, CALL_LOCAL_ATTN_PROJ_W8A8 = 0, 1, 2, 3
+CALL_LOCAL_ATTN_FP8, CALL_LOCAL_ATTN_FP8_PROJ_W8A8 = 4, 5
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -80,6 +82,9 @@ def lib() -> ctypes.CDLL:
         L.ispa_kv_layer.argtypes = [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_i32)]
         L.ispa_kv_bytes.argtypes = [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
         L.ispa_select_layers.argtypes = [_i32, _vp, _vp, _i32, _vp, _vp, _vp]
+        L.ispa_local_attn_fp8.argtypes = [ctypes.POINTER(AttnShape), _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.ispa_local_attn_fp8_proj_w8a8.argtypes = [ctypes.POINTER(AttnShape), _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                    _vp, _sz, _vp]
         L.ispa_absorb_solve_batched.argtypes = [_i32, _i32, _vp, _vp, _vp, _i32, _vp, _f32, _i32, _i32, _vp, _vp, _vp,
                                                 _vp, _vp, _vp, _sz, _vp]
         L.ispa_local_attn_fused_proj_noalloc.argtypes = [ctypes.POINTER(AttnShape), _i32, _vp, _vp, _vp, _vp, _vp,
@@ -89,7 +94,8 @@ def lib() -> ctypes.CDLL:
                   "ispa_quantize_weight_fp8", "ispa_quantize_rows_fp8", "ispa_local_attn_fused_proj_w8a8",
                   "ispa_kv_create", "ispa_kv_destroy", "ispa_kv_write_sink", "ispa_kv_append_chunk",
                   "ispa_kv_release_history", "ispa_kv_layer", "ispa_kv_bytes", "ispa_select_layers",
-                  "ispa_local_attn_fused_proj_noalloc", "ispa_absorb_solve_batched"):
+                  "ispa_local_attn_fused_proj_noalloc", "ispa_absorb_solve_batched", "ispa_local_attn_fp8",
+                  "ispa_local_attn_fp8_proj_w8a8"):
             getattr(L, f).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -313,6 +319,28 @@ def local_attn_fused_proj_noalloc(shape: AttnShape, q, k, v, w_new, out, stream=
            "ispa_local_attn_fused_proj_noalloc")
 
 
+def local_attn_fp8(shape: AttnShape, q, k, v, out, workspace, stream=None) -> None:
+    """ispa_local_attn_fp8: out = FP8 attention over the local rows (sink + current chunk)."""
+    _l_layer_args(shape, q, k, v, out)
+    _same_device(q, k, v, out, workspace)
+    _check(lib().ispa_local_attn_fp8(ctypes.byref(shape), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                     _ptr(workspace), _ws_bytes(workspace), _stream(stream)), "ispa_local_attn_fp8")
+
+
+def local_attn_fp8_proj_w8a8(shape: AttnShape, q, k, v, wq_t, w_scales, out, workspace, stream=None) -> None:
+    """ispa_local_attn_fp8_proj_w8a8: the converted layer in W8A8 end to end (FP8 attention, then the W8A8
+    projection by the codes and scales of quantize_weight_fp8)."""
+    import torch
+    d = _l_layer_args(shape, q, k, v, out)
+    _want(wq_t, "wq_t", torch.uint8, (d, d))
+    _want(w_scales, "w_scales", torch.float32, (d,))
+    _same_device(q, k, v, wq_t, w_scales, out, workspace)
+    _check(lib().ispa_local_attn_fp8_proj_w8a8(ctypes.byref(shape), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
+                                               _ptr(wq_t), _ptr(w_scales), _ptr(out), _ptr(workspace),
+                                               _ws_bytes(workspace), _stream(stream)),
+           "ispa_local_attn_fp8_proj_w8a8")
+
+
 def quantize_weight_fp8(w, wq_t, w_scales, stream=None) -> None:
     """ispa_quantize_weight_fp8: w [d_in, d_out] -> wq_t [d_out, d_in] E4M3 codes (uint8), w_scales [d_out]."""
     import torch
@@ -431,6 +459,9 @@ class KVCache:
         kp, vp, rows = _vp(), _vp(), (_i32 * 3)()
         _check(lib().ispa_kv_layer(self._h, layer, ctypes.byref(kp), ctypes.byref(vp), rows), "ispa_kv_layer")
         n = rows[0] + rows[1] + rows[2]
+        if n == 0:
+            e = torch.empty((0, self.d), dtype=self.dtype, device="cuda")
+            return e, e, (0, 0, 0)
         views = []
         for p in (kp.value, vp.value):
             t = torch.as_tensor(_DeviceRows(p, n, self.d, self._code), device="cuda")

@@ -50,17 +50,22 @@ size_t w8a8_act_bytes(const ispa_attn_shape* s) {
   return w8a8_codes_bytes(s) + ((size_t)s->n_q * 4 + 255) / 256 * 256;
 }
 
+// The FP8 attention's codes of K and V and their scales.
+size_t fp8_attn_ws(const ispa_attn_shape* s) {
+  return attn_fp8_workspace_bytes((int64_t)s->n_sink + s->n_cur, (int64_t)s->n_heads * s->head_dim);
+}
+
 // ispa_dual_attn's workspace (16-bit inputs): the V^T copy, then the parked local outputs.
 size_t dual_ws_bytes(const ispa_attn_shape* s) {
   return attn_vt_bytes_aligned((int64_t)s->n_sink + s->n_hist + s->n_cur, (int64_t)s->n_heads * s->head_dim) +
          attn_stash_bytes(s->n_q, s->n_heads);
 }
 
-// Buffer addressing of the 16-bit path uses 32-bit byte offsets into K and V^T.
+// The 16-bit path addresses one head's 128 rows of the V^T copy with 32-bit byte offsets (K tiles get
+// descriptors of their own, so K has no such limit).
 bool fits_buffer(const ispa_attn_shape* s) {
   const int64_t n_k = (int64_t)s->n_sink + s->n_hist + s->n_cur;
-  const int64_t d = (int64_t)s->n_heads * s->head_dim;
-  return n_k * d * 2 < INT32_MAX && (int64_t)attn_vt_bytes(n_k, d) < INT32_MAX;
+  return 128 * attn_vt_ld(n_k) * 2 < INT32_MAX;
 }
 
 // Scratch of ispa_local_attn_fused_proj_noalloc: one array per GPU, part of the code object (so it
@@ -119,6 +124,12 @@ size_t ispa_workspace_bytes(int call_id, const ispa_attn_shape* shape, int d) {
       return local_a_bytes(shape) + attn_vt_bytes_aligned((int64_t)shape->n_sink + shape->n_hist + shape->n_cur,
                                                           (int64_t)shape->n_heads * shape->head_dim) +
              w8a8_act_bytes(shape);
+    case ISPA_CALL_LOCAL_ATTN_FP8:
+      if (!shape || shape->n_q < 1 || shape->n_heads < 1) return 0;
+      return fp8_attn_ws(shape);
+    case ISPA_CALL_LOCAL_ATTN_FP8_PROJ_W8A8:
+      if (!shape || shape->n_q < 1 || shape->n_heads < 1) return 0;
+      return local_a_bytes(shape) + fp8_attn_ws(shape) + w8a8_act_bytes(shape);
     default: return (size_t)-1;
   }
 }
@@ -310,6 +321,76 @@ int ispa_local_attn_fused_proj_noalloc(const ispa_attn_shape* shape, int io_dtyp
   void* ws = noalloc_scratch();
   if (!ws) return ISPA_EHIP;
   return ispa_local_attn_fused_proj(shape, io_dtype, q, k, v, w_new, out, ws, kNoAllocScratchBytes, stream);
+}
+
+// shared by the two FP8-attention calls: argument checks and the attention launch into `a` (io dtype)
+static int fp8_attention(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k, const void* v,
+                         void* a, void* ws, hipStream_t s) {
+  AttnLaunch L;
+  L.mode = 2;
+  L.io = io_dtype;
+  L.stat = ISPA_F16;
+  L.q = q;
+  L.k = k;
+  L.v = v;
+  L.a_full = a;
+  L.a_loc_t = nullptr;
+  L.delta_a_t = nullptr;
+  L.ld_stat = 0;
+  L.lse_loc = nullptr;
+  L.lse_hist = nullptr;
+  L.n_q = shape->n_q;
+  L.n_sink = shape->n_sink;
+  L.n_hist = shape->n_hist;
+  L.n_cur = shape->n_cur;
+  L.n_heads = shape->n_heads;
+  L.head_dim = shape->head_dim;
+  L.scale = eff_scale(shape);
+  L.ws = ws;
+  L.ws_bytes = fp8_attn_ws(shape);
+  return hip_status(launch_attention_fp8(L, s));
+}
+
+static int fp8_attn_checks(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k, const void* v,
+                           const void* out) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if (io_dtype != ISPA_BF16 && io_dtype != ISPA_F16) return ISPA_EUNSUPPORTED;
+  if (shape->head_dim != 128) return ISPA_EUNSUPPORTED;
+  const int64_t n_loc = (int64_t)shape->n_sink + shape->n_cur;
+  const int64_t d = (int64_t)shape->n_heads * shape->head_dim;
+  if (128 * attn_vt_ld(n_loc) >= INT32_MAX || (int64_t)shape->n_q * d * 2 >= INT32_MAX) return ISPA_EUNSUPPORTED;
+  if (!q || !k || !v || !out) return ISPA_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ISPA_EINVAL;
+  return ISPA_OK;
+}
+
+int ispa_local_attn_fp8(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k, const void* v,
+                        void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = fp8_attn_checks(shape, io_dtype, q, k, v, out);
+  if (st) return st;
+  if (!workspace || workspace_bytes < fp8_attn_ws(shape) || !aligned16(workspace)) return ISPA_EWORKSPACE;
+  return fp8_attention(shape, io_dtype, q, k, v, out, workspace, (hipStream_t)stream);
+}
+
+int ispa_local_attn_fp8_proj_w8a8(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k,
+                                  const void* v, const void* wq_t, const float* w_scales, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  int st = fp8_attn_checks(shape, io_dtype, q, k, v, out);
+  if (st) return st;
+  if (!wq_t || !w_scales || !aligned16(wq_t) || !aligned4(w_scales)) return ISPA_EINVAL;
+  const size_t need = ispa_workspace_bytes(ISPA_CALL_LOCAL_ATTN_FP8_PROJ_W8A8, shape, 0);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return ISPA_EWORKSPACE;
+  const hipStream_t s = (hipStream_t)stream;
+  const int d = shape->n_heads * shape->head_dim;
+  char* a = (char*)workspace;
+  char* fws = a + local_a_bytes(shape);
+  uint8_t* aq = (uint8_t*)(fws + fp8_attn_ws(shape));
+  float* sa = (float*)(aq + w8a8_codes_bytes(shape));
+  st = fp8_attention(shape, io_dtype, q, k, v, a, fws, s);
+  if (st) return st;
+  if (launch_quant_rows(io_dtype, a, d, shape->n_q, d, aq, d, sa, s) != hipSuccess) return ISPA_EHIP;
+  return hip_status(launch_proj8(io_dtype, aq, sa, (const uint8_t*)wq_t, w_scales, out, shape->n_q, d, d, s));
 }
 
 int ispa_quantize_weight_fp8(int d_in, int d_out, int w_dtype, const void* w, void* wq_t, float* w_scales,

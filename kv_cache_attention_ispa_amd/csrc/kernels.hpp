@@ -45,6 +45,11 @@ inline bool attn_needs_f16_values(const AttnLaunch& L) {
   return L.mode == 0 && L.io == DT_BF16 && (L.stat == DT_F16 || L.stat == DT_F32) && (L.a_loc_t || L.delta_a_t);
 }
 hipError_t launch_attention(const AttnLaunch& L, hipStream_t s);
+// FP8 attention over the local rows (sink + current chunk; history rows are not read) into L.a_full
+// (io dtype), with the codes and scales of those rows of K and V written into L.ws first
+// (attn_fp8_workspace_bytes of n_sink + n_cur rows).
+size_t attn_fp8_workspace_bytes(int64_t n_loc, int64_t d);
+hipError_t launch_attention_fp8(const AttnLaunch& L, hipStream_t s);
 
 // Gram statistics: out_z (+)= X_z Y_z^T for z in {G: (A, A), C: (A, dA), D: (dA, dA)}.
 struct GramLaunch {

@@ -87,6 +87,14 @@ def test_dual_attn_rejects_bad_arguments(L):
     assert _dual(L, s, io=0, stat=2) == EUNSUPPORTED        # fp32 inputs need fp32 statistics
     s64 = ispa.AttnShape(64, 8, 16, 64, 2, 64, 0.0)
     assert _dual(L, s64, io=1) == EUNSUPPORTED              # 16-bit path is head_dim 128
+    # one head's rows of the V^T copy are addressed with 32-bit offsets: n_k < 8,388,544; K and V
+    # themselves may pass 2^31 bytes (d = 5120 with 216,840 cached rows)
+    big = ispa.AttnShape(64, 8, 8388544 - 8 - 64, 64, 2, 128, 0.0)
+    assert _dual(L, big, io=1) == EWORKSPACE               # size accepted (workspace missing)
+    big.n_hist += 1
+    assert _dual(L, big, io=1) == EUNSUPPORTED
+    long14b = ispa.AttnShape(64, 1560, 216840 - 1560 - 4680, 4680, 40, 128, 0.0)
+    assert _dual(L, long14b, io=1) == EWORKSPACE
     # full-only mode needs a_full
     assert L.ispa_dual_attn(ctypes.byref(s), 1, FAKE, FAKE, FAKE, None, 2, None, None, 0, None, None, None, 0,
                             None) == EINVAL
@@ -218,3 +226,23 @@ def test_batched_solve_validation(L):
     assert f(refine=9) == EINVAL
     assert f(wsb=3 * need - 1) == EWORKSPACE
     assert f(ws=None) == EWORKSPACE
+
+
+def test_fp8_attention_validation(L):
+    s = ispa.AttnShape(300, 100, 0, 333, 2, 128, 0.0)
+    need = ispa.workspace_bytes(ispa.CALL_LOCAL_ATTN_FP8, s)
+    need2 = ispa.workspace_bytes(ispa.CALL_LOCAL_ATTN_FP8_PROJ_W8A8, s)
+    assert 433 * 256 <= need < need2      # K codes, transposed V codes and scales; then the projection's
+    f = lambda io=1, q=FAKE, ws=FAKE, wsb=need: L.ispa_local_attn_fp8(ctypes.byref(s), io, q, FAKE, FAKE, FAKE,
+                                                                       ws, wsb, None)
+    assert f(io=0) == EUNSUPPORTED
+    assert f(q=None) == EINVAL
+    assert f(q=FAKE + 8) == EINVAL
+    assert f(ws=None) == EWORKSPACE
+    assert f(wsb=need - 1) == EWORKSPACE
+    g = lambda wq=FAKE, wsb=need2: L.ispa_local_attn_fp8_proj_w8a8(ctypes.byref(s), 1, FAKE, FAKE, FAKE, wq, FAKE,
+                                                                   FAKE, FAKE, wsb, None)
+    assert g(wq=None) == EINVAL
+    assert g(wsb=need2 - 1) == EWORKSPACE
+    s64 = ispa.AttnShape(300, 100, 0, 333, 2, 64, 0.0)
+    assert L.ispa_local_attn_fp8(ctypes.byref(s64), 1, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == EUNSUPPORTED

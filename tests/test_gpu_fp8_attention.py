@@ -1,0 +1,203 @@
+"""GPU: FP8 attention of a converted layer (ispa_local_attn_fp8) and the W8A8 converted layer with it
+(ispa_local_attn_fp8_proj_w8a8), against the oracle's reading (oracle.fp8.local_attention_fp8): per-token
+Q scales, per-head K/V scales over the layer's rows, integer log2 reference, E4M3(256 P).
+
+The kernel takes the same codes as the oracle up to probabilities below 2^-14 of a row's largest and
+float32 rounding of the scores, so the attention output is compared element by element with max-rel
+2e-2 (the bf16 bar), and on the hand-worked inputs (every operand an exact E4M3 value) to float32
+rounding.  The end-to-end layer adds the W8A8 projection, compared like the existing W8A8 tests.
+"""
+import json
+import math
+import os
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from oracle import fp8
+from gpu_util import dev, host, maxrel, relfro, torch, tdtype
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _attn_fp8_gpu(shape, q, k, v, io, scale=0.0):
+    import kv_cache_attention_ispa_amd as ispa
+    t = torch()
+    s = ispa.AttnShape(shape.n_q, shape.n_sink, shape.n_hist, shape.n_cur, shape.n_heads, shape.head_dim, scale)
+    ws = t.empty(ispa.workspace_bytes(ispa.CALL_LOCAL_ATTN_FP8, s), dtype=t.uint8, device="cuda")
+    out = t.full((shape.n_q, shape.d), float("nan"), dtype=tdtype(io), device="cuda")
+    ispa.local_attn_fp8(s, dev(q, io), dev(k, io), dev(v, io), out, ws)
+    t.cuda.synchronize()
+    return host(out)
+
+
+def _local(shape, k, v):
+    loc = oracle.branch_rows(shape.n_sink, shape.n_hist, shape.n_cur)["local"]
+    return k[loc], v[loc]
+
+
+@pytest.mark.parametrize("io,shape", [
+    ("bf16", wl.AttnShape(300, 100, 0, 333, 2, 128)),
+    ("bf16", wl.AttnShape(64, 0, 0, 64, 1, 128)),
+    ("f16", wl.AttnShape(257, 1, 70, 190, 3, 128)),     # history rows present: skipped
+    ("bf16", wl.AttnShape(513, 64, 129, 64, 2, 128)),
+])
+def test_fp8_attention_matches_oracle(io, shape):
+    rng = np.random.default_rng(shape.n_q + shape.n_k)
+    q = wl.round_to(rng.standard_normal((shape.n_q, shape.d)) * rng.uniform(0.2, 3, (shape.n_q, 1)), io)
+    k = wl.round_to(rng.standard_normal((shape.n_k, shape.d)), io)
+    v = wl.round_to(rng.standard_normal((shape.n_k, shape.d)), io)
+    got = _attn_fp8_gpu(shape, q, k, v, io)
+    kl, vl = _local(shape, k, v)
+    ref = fp8.local_attention_fp8(q, kl, vl, shape.n_sink, shape.n_cur, shape.n_heads)
+    err = maxrel(got, ref)
+    exact = oracle.local_layer_output(q, kl, vl, shape.n_sink, shape.n_cur, shape.n_heads, np.eye(shape.d))
+    print(f"fp8 attention {shape}: max-rel {err:.2e} vs the oracle's FP8 reading, "
+          f"{maxrel(got, exact):.2e} vs unquantised attention")
+    assert err <= 2e-2
+
+
+def test_fp8_attention_hand_worked_values():
+    """The hand-worked fixture (tests/golden/fp8_attention_hand.json) embedded in head_dim 128: its two
+    dims first, zeros elsewhere, so every scale and code is the fixture's own."""
+    with open(os.path.join(GOLDEN, "fp8_attention_hand.json")) as f:
+        g = json.load(f)
+    for case in (g, g["case2"]):
+        q, k, v = (np.array(case[x], dtype=np.float64) for x in ("q", "k", "v"))
+        pad = lambda a: np.concatenate([a, np.zeros((a.shape[0], 126))], axis=1)
+        shape = wl.AttnShape(q.shape[0], case["n_sink"], 0, case["n_cur"], 1, 128)
+        got = _attn_fp8_gpu(shape, pad(q), pad(k), pad(v), "bf16", scale=case["scale"])
+        want = np.array(case["expect"]["out"])
+        # bf16 storage of the output: relative rounding 2^-9
+        assert np.allclose(got[:, :2], want, rtol=2.0 ** -8, atol=0), (got[:, :2], want)
+        assert np.all(got[:, 2:] == 0.0)
+
+
+def test_fp8_attention_1p3b_sampled_rows():
+    """The 1.3B-shaped converted layer: 4680 queries over sink 1560 + current chunk 4680, 12 heads."""
+    w = wl.LAYER_1P3B
+    s = w.shape
+    x = wl.layer_inputs(w, with_w=False)
+    kl, vl = _local(s, x["k"], x["v"])
+    shape = wl.AttnShape(s.n_q, s.n_sink, 0, s.n_cur, s.n_heads, s.head_dim)
+    got = _attn_fp8_gpu(shape, x["q"], kl, vl, "bf16")
+    rows = np.unique(np.concatenate([np.linspace(0, s.n_q - 1, 10).astype(int), [255, 256, s.n_q - 1]]))
+    ref = fp8.local_attention_fp8(x["q"][rows], kl, vl, s.n_sink, s.n_cur, s.n_heads)
+    err = maxrel(got[rows], ref)
+    print(f"fp8 attention, 1.3B layer: max-rel {err:.2e} on {len(rows)} rows")
+    assert err <= 2e-2
+
+
+def _w8a8_fp8_layer_gpu(shape, q, k, v, W):
+    import kv_cache_attention_ispa_amd as ispa
+    t = torch()
+    s = ispa.AttnShape.of(shape)
+    wq = t.empty((shape.d, shape.d), dtype=t.uint8, device="cuda")
+    sw = t.empty((shape.d,), device="cuda")
+    ispa.quantize_weight_fp8(dev(W, "bf16"), wq, sw)
+    ws = t.empty(ispa.workspace_bytes(ispa.CALL_LOCAL_ATTN_FP8_PROJ_W8A8, s), dtype=t.uint8, device="cuda")
+    out = t.empty((shape.n_q, shape.d), dtype=t.bfloat16, device="cuda")
+    ispa.local_attn_fp8_proj_w8a8(s, dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), wq, sw, out, ws)
+    t.cuda.synchronize()
+    return host(out)
+
+
+@pytest.mark.parametrize("shape", [
+    wl.AttnShape(530, 64, 0, 192, 5, 128),      # d = 640, 256 local rows
+    wl.AttnShape(300, 100, 37, 156, 12, 128),   # d = 1536, history rows present (not read)
+])
+def test_w8a8_fp8_attention_layer_exact(shape):
+    """The whole converted layer on inputs whose FP8 attention output is exact on both sides: Q = 0
+    gives every score 0, so M = 0 and every probability code is E4M3(256) = 256; every local V row is
+    the same bf16 vector c, so out = s_v dec(E4M3(c / s_v)), rounded once in float32 whatever the order
+    of the final multiply and divide (the local row count is a power of two, so l = 256 n_loc scales
+    by a power of two).  The activation codes then agree, and each output may differ from the oracle's
+    only by its own bf16 rounding (half a unit; one unit where the float32 sums sit at a tie)."""
+    assert (shape.n_sink + shape.n_cur) & (shape.n_sink + shape.n_cur - 1) == 0
+    rng = np.random.default_rng(shape.d + 1)
+    q = np.zeros((shape.n_q, shape.d))
+    k = wl.round_to(rng.standard_normal((shape.n_k, shape.d)), "bf16")
+    v = np.repeat(wl.round_to(rng.standard_normal((1, shape.d)), "bf16"), shape.n_k, axis=0)
+    v[shape.n_sink:shape.n_sink + shape.n_hist] *= 4.0   # history rows: not part of the V scale
+    W = wl.round_to(rng.standard_normal((shape.d, shape.d)) / math.sqrt(shape.d), "bf16")
+    got = _w8a8_fp8_layer_gpu(shape, q, k, v, W)
+    kl, vl = _local(shape, k, v)
+    ref = fp8.local_layer_output_w8a8_fp8attn(q, kl, vl, shape.n_sink, shape.n_cur, shape.n_heads, W)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("shape", [wl.AttnShape(200, 64, 0, 130, 2, 128), wl.AttnShape(97, 33, 40, 64, 4, 128)])
+def test_w8a8_layer_with_fp8_attention(shape):
+    """Random inputs.  The FP8 attention output agrees with the oracle's to about 5e-3 of its scale,
+    so after bf16 rounding some elements differ by one unit, and a few of those move an activation code
+    by one E4M3 step (1/8 of the value).  One such flip moves an output by about 1/(8 sqrt(d)) of its
+    row's scale, 1/128 at d = 256: the element-wise bar allows a few flips in a row (5e-2 of the
+    output's largest), and the Frobenius bar (1e-2), which flips barely move, keeps the rest tight."""
+    rng = np.random.default_rng(7 + shape.n_q)
+    q = wl.round_to(rng.standard_normal((shape.n_q, shape.d)), "bf16")
+    k = wl.round_to(rng.standard_normal((shape.n_k, shape.d)), "bf16")
+    v = wl.round_to(rng.standard_normal((shape.n_k, shape.d)), "bf16")
+    W = wl.round_to(rng.standard_normal((shape.d, shape.d)) / math.sqrt(shape.d), "bf16")
+    got = _w8a8_fp8_layer_gpu(shape, q, k, v, W)
+    kl, vl = _local(shape, k, v)
+    ref = fp8.local_layer_output_w8a8_fp8attn(q, kl, vl, shape.n_sink, shape.n_cur, shape.n_heads, W)
+    err, fro = maxrel(got, ref), relfro(got, ref)
+    print(f"W8A8 layer with FP8 attention {shape}: max-rel {err:.2e}, rel-Frobenius {fro:.2e}")
+    assert err <= 5e-2
+    assert fro <= 1e-2
+
+
+def test_fp8_layer_step_faster_than_16bit():
+    """At the 1.3B converted layer the W8A8 step with FP8 attention (pre-pass, attention, activation
+    codes, FP8 product) is faster than the 16-bit step.  Times are the best of three rounds of
+    20-call medians, the variants alternating, so a clock change hits them alike.  The W8A8 step with
+    16-bit attention is printed beside them: its attention kernel costs about what the FP8 one does
+    (both are bound by the same softmax and pipeline work, not by the matrix cores), so the two W8A8
+    variants are close."""
+    import kv_cache_attention_ispa_amd as ispa
+    t = torch()
+    s = wl.LAYER_1P3B.shape
+    d = s.d
+    g = t.Generator(device="cuda").manual_seed(3)
+    q = t.randn((s.n_q, d), generator=g, device="cuda").to(t.bfloat16)
+    k = t.randn((s.n_sink + s.n_cur, d), generator=g, device="cuda").to(t.bfloat16)
+    v = t.randn((s.n_sink + s.n_cur, d), generator=g, device="cuda").to(t.bfloat16)
+    W = (t.randn((d, d), generator=g, device="cuda") / math.sqrt(d)).to(t.bfloat16)
+    sh = ispa.AttnShape(s.n_q, s.n_sink, 0, s.n_cur, s.n_heads, s.head_dim, 0.0)
+    wq = t.empty((d, d), dtype=t.uint8, device="cuda")
+    sw = t.empty((d,), device="cuda")
+    ispa.quantize_weight_fp8(W, wq, sw)
+    out = t.empty((s.n_q, d), dtype=t.bfloat16, device="cuda")
+    ws = {c: t.empty(ispa.workspace_bytes(c, sh), dtype=t.uint8, device="cuda")
+          for c in (ispa.CALL_LOCAL_ATTN_PROJ, ispa.CALL_LOCAL_ATTN_PROJ_W8A8, ispa.CALL_LOCAL_ATTN_FP8_PROJ_W8A8,
+                    ispa.CALL_LOCAL_ATTN_FP8)}
+    calls = {
+        "bf16": lambda: ispa.local_attn_fused_proj(sh, q, k, v, W, out, ws[ispa.CALL_LOCAL_ATTN_PROJ]),
+        "w8a8_16bit_attention": lambda: ispa.local_attn_fused_proj_w8a8(sh, q, k, v, wq, sw, out,
+                                                                        ws[ispa.CALL_LOCAL_ATTN_PROJ_W8A8]),
+        "w8a8_fp8_attention": lambda: ispa.local_attn_fp8_proj_w8a8(sh, q, k, v, wq, sw, out,
+                                                                    ws[ispa.CALL_LOCAL_ATTN_FP8_PROJ_W8A8]),
+        "fp8_attention_only": lambda: ispa.local_attn_fp8(sh, q, k, v, out, ws[ispa.CALL_LOCAL_ATTN_FP8]),
+    }
+    ms = {}
+    for _ in range(3):
+        for name, fn in calls.items():
+            for _ in range(3):
+                fn()
+            t.cuda.synchronize()
+            spans = []
+            for _ in range(20):
+                e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                spans.append((e0, e1))
+            t.cuda.synchronize()
+            med = sorted(a.elapsed_time(b) for a, b in spans)[10]
+            ms[name] = min(ms.get(name, med), med)
+    print("1.3B converted layer step (ms): " + ", ".join(f"{n} {v:.4f}" for n, v in ms.items()))
+    assert ms["w8a8_fp8_attention"] < ms["bf16"]
