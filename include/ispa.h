@@ -149,7 +149,9 @@ int ispa_gram_accum(int d, int n, int stat_dtype, const void* a_loc_t, const voi
  * ||A_loc (W + dW) - A_full W||_F^2 + lambda ||dW||_F^2 is
  * dW = (G + lambda I)^-1 C W, obtained without iteration.  Computed as
  * R = C W, a blocked Cholesky factorisation G + lambda I = L L^T, and the two
- * triangular solves, all in fp32; refine = n (0..8) adds n steps of iterative
+ * triangular solves, all to fp32 accuracy (R, and W W^T for eps, on the bf16
+ * matrix cores from three-part bf16 splits of C and W that carry all 24 bits
+ * of their fp32 values); refine = n (0..8) adds n steps of iterative
  * refinement whose residual C W - (G + lambda I) dW is accumulated in fp64 (C W
  * formed once in fp64).  Ill-conditioned systems (features > warmup tokens)
  * need refinement to reach fp64-solve accuracy.

@@ -271,7 +271,6 @@ __global__ __launch_bounds__(NT) void setup_kernel(const float* G, const typenam
 // MFMA 16x16x4 (fp32), one 16 x 16 quadrant per wave.
 // ------------------------------------------------------------------------------------------
 constexpr int SW_THREADS = 1024;
-constexpr int SW_FILL_RANGES = 6;   // K ranges of the R / P products (4 blocks each at d = 1536)
 static_assert(SW_THREADS >= 512, "the diagonal factorization uses 512 threads");
 constexpr int BP = NB + 4;   // LDS pitch of a 64 x 64 block: 16 rows of a wave hit 16 distinct 4-bank groups
 
@@ -282,14 +281,6 @@ struct SweepArgs {
   int* info;
   int d, nP, k;
   int n_a, n_i, f_row0, f_rows;   // work items: A blocks, identity blocks, final rows [f_row0, +f_rows)
-  // products that do not depend on the sweep ride along in its launches, one K range at a time:
-  // R = C W (always) and the lower block triangle of P = W W^T (for epsilon); this launch computes output blocks
-  // [fill0, fill0 + n_fill) of K range [kb0, kb1) (in 64-blocks), added to earlier ranges when kb0 > 0
-  const float* C;
-  const float* Wf;
-  float* R;
-  float* P;
-  int n_fill, fill0, kb0, kb1;
   // lambda (absolute, or lam * tr(G) / d): set by the first launch's diagonal work-group (which
   // also clears *info) in sc, and added to each diagonal block as it is factored
   Scalars* sc;
@@ -309,18 +300,6 @@ __device__ __forceinline__ void sw_load(float (*dst)[BP], const float* src, int 
   if (gr < d && gc < d) v = *(const f32x4*)(src + (int64_t)gr * d + gc);
   *(f32x4*)&dst[r][c] = v;
 }
-// The same block in two halves: this thread's 16 bytes from global memory, then into LDS.
-__device__ __forceinline__ f32x4 sw_gload(const float* src, int d, int rb, int cb) {
-  const int t = threadIdx.x;
-  const int gr = rb * NB + (t >> 4), gc = cb * NB + (t & 15) * 4;
-  f32x4 v = {0.f, 0.f, 0.f, 0.f};
-  if (gr < d && gc < d) v = *(const f32x4*)(src + (int64_t)gr * d + gc);
-  return v;
-}
-__device__ __forceinline__ void sw_lput(float (*dst)[BP], f32x4 v) {
-  const int t = threadIdx.x;
-  *(f32x4*)&dst[t >> 4][(t & 15) * 4] = v;
-}
 __device__ __forceinline__ void sw_load_t(float (*dst)[BP], const float* Tk) {
   const int t = threadIdx.x;
   const int r = t >> 4, c = (t & 15) * 4;
@@ -334,6 +313,166 @@ __device__ __forceinline__ void tri_decode(int p, int& ii, int& jj) {
   while (r * (r + 1) / 2 > p) --r;
   ii = r;
   jj = p - r * (r + 1) / 2;
+}
+
+// ------------------------------------------------------------------------------------------
+// R = C W and (for epsilon) the lower block triangle of P = W W^T on bf16 MFMA (32x32x16), before
+// the sweep.  An fp32 operand x is split into three bf16 parts x = x1 + x2 + x3 + r with x1 =
+// bf16(x), x2 = bf16(x - x1), x3 = bf16(x - x1 - x2) (each difference is exact in fp32; the three
+// parts carry 24 significant bits, so |r| is at most about 2^-24 |x|, the fp32 rounding).  A product
+// term takes the parts x_i y_j with i + j <= 4, accumulated in fp32 (the dropped ones are below
+// 2^-24 of the term): the result is an fp32 product up to the order of the sums.  A bf16 W (WPARTS
+// 1) is its own single part: R takes three MFMAs per 16-deep step, and P one, whose bf16 x bf16
+// products are exact in fp32.
+// split_kernel writes the parts once per call into the workspace (bf16, [part][row][col]): C in
+// three parts, W and W^T in WPARTS; both products are then NT products (k-contiguous rows on both
+// sides): R[i][j] = sum_k C[i][k] W^T[j][k], P[i][j] = sum_k W[i][k] W[j][k].
+// ------------------------------------------------------------------------------------------
+constexpr int RP_K = 32;
+constexpr int RP_PITCH = RP_K + 8;   // bf16 per LDS row (80 bytes: 16-byte aligned rows)
+
+__device__ __forceinline__ void bf16_split3(float x, uint16_t (&part)[3]) {
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    part[i] = Cvt<BF16>::from_f(x);
+    x -= Cvt<BF16>::to_f(part[i]);
+  }
+}
+
+// Work-group (bi, bj): the 64 x 64 block (bi, bj) of C and of W (from Wf), split; W's parts also go
+// to the transposed block through LDS.  Thread t covers row t / 4, 16 columns from 16 (t % 4).
+template <int WPARTS>
+__global__ __launch_bounds__(256) void split_kernel(const float* __restrict__ C, const float* __restrict__ Wf,
+                                                    uint16_t* __restrict__ sp, int d, Steps st) {
+  C = at_layer(C, st.mat);
+  Wf = at_layer(Wf, st.ws);
+  sp = at_layer(sp, st.ws);
+  const int64_t dd = (int64_t)d * d;
+  __shared__ uint16_t tile[WPARTS][64][66];   // W parts of the block, [row][col]
+  const int nT = (d + 63) / 64, bi = blockIdx.x / nT, bj = blockIdx.x % nT;
+  const int t = threadIdx.x, r = t >> 2, c = 16 * (t & 3);
+  auto put = [](uint16_t* dst, const uint16_t (&v)[16][3], int i) {
+    u32x4 w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[h][e] = v[8 * h + 2 * e][i] | (uint32_t)v[8 * h + 2 * e + 1][i] << 16;
+    *(u32x4*)dst = w[0];
+    *(u32x4*)(dst + 8) = w[1];
+  };
+  // d is a multiple of 32, so a row's 16 columns are all in range or all out
+  const int gr = 64 * bi + r, gc = 64 * bj + c;
+  if (gr < d && gc < d) {
+    uint16_t v[16][3];
+    const int64_t o = (int64_t)gr * d + gc;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const f32x4 x = *(const f32x4*)(C + o + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bf16_split3(x[e], v[4 * h + e]);
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) put(sp + i * dd + o, v, i);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const f32x4 x = *(const f32x4*)(Wf + o + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bf16_split3(x[e], v[4 * h + e]);
+    }
+#pragma unroll
+    for (int i = 0; i < WPARTS; ++i) {
+      put(sp + (3 + i) * dd + o, v, i);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) tile[i][r][c + e] = v[e][i];
+    }
+  }
+  __syncthreads();
+  // W^T block (bj, bi): row 64 bj + r holds column r of the W block, columns 64 bi + c .. + 15
+  const int tr = 64 * bj + r, tc = 64 * bi + c;
+  if (tr < d && tc < d) {
+    uint16_t v[16][3];
+#pragma unroll
+    for (int i = 0; i < WPARTS; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e][i] = tile[i][c + e][r];
+#pragma unroll
+    for (int i = 0; i < WPARTS; ++i) put(sp + (6 + i) * dd + (int64_t)tr * d + tc, v, i);
+  }
+}
+
+// Work-group: one 64 x 64 output block (R blocks first, then P's lower blocks), 4 waves of 32 x 32;
+// K steps of 32 pass through registers, one step ahead, into LDS (every part of both operands).
+template <int WPARTS>
+__global__ __launch_bounds__(256) void rp_kernel(const uint16_t* __restrict__ sp, float* __restrict__ R,
+                                                 float* __restrict__ P, int d, int n_r, Steps st) {
+  sp = at_layer(sp, st.ws);
+  R = at_layer(R, st.ws);
+  P = at_layer(P, st.ws);
+  const int64_t dd = (int64_t)d * d;
+  __shared__ __attribute__((aligned(16))) uint16_t As[3][64][RP_PITCH], Bs[WPARTS][64][RP_PITCH];
+  const int nT = (d + 63) / 64, t = threadIdx.x;
+  const bool is_p = (int)blockIdx.x >= n_r;
+  int bi, bj;
+  if (is_p) {
+    tri_decode(blockIdx.x - n_r, bi, bj);
+  } else {
+    bi = blockIdx.x / nT;
+    bj = blockIdx.x % nT;
+  }
+  const int a_parts = is_p ? WPARTS : 3;
+  const uint16_t* A = sp + (is_p ? 3 * dd : 0) + (int64_t)64 * bi * d;        // W or C rows of block bi
+  const uint16_t* B = sp + (is_p ? 3 * dd : 6 * dd) + (int64_t)64 * bj * d;   // W or W^T rows of block bj
+  const int lr = t >> 2, lk = 8 * (t & 3);
+  const bool a_in = 64 * bi + lr < d, b_in = 64 * bj + lr < d;
+  u32x4 ra[3], rb[WPARTS];
+  auto load = [&](int k0) {
+    const int64_t o = (int64_t)lr * d + k0 + lk;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      if (i < a_parts) ra[i] = a_in ? *(const u32x4*)(A + i * dd + o) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < WPARTS; ++j) rb[j] = b_in ? *(const u32x4*)(B + j * dd + o) : u32x4{0u, 0u, 0u, 0u};
+  };
+  const int lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
+  const int mrow = 32 * wm + (lane & 31), nrow = 32 * wn + (lane & 31), kk = 8 * (lane >> 5);
+  f32x16 acc = {};
+  load(0);
+  for (int k0 = 0; k0 < d; k0 += RP_K) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      if (i < a_parts) *(u32x4*)&As[i][lr][lk] = ra[i];
+#pragma unroll
+    for (int j = 0; j < WPARTS; ++j) *(u32x4*)&Bs[j][lr][lk] = rb[j];
+    __syncthreads();
+    if (k0 + RP_K < d) load(k0 + RP_K);
+#pragma unroll
+    for (int s = 0; s < RP_K; s += 16) {
+      u32x4 ap[3], bp[WPARTS];
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        if (i < a_parts) ap[i] = *(const u32x4*)&As[i][mrow][s + kk];
+#pragma unroll
+      for (int j = 0; j < WPARTS; ++j) bp[j] = *(const u32x4*)&Bs[j][nrow][s + kk];
+      // smallest terms first
+#pragma unroll
+      for (int sum = 2; sum >= 0; --sum)
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          const int j = sum - i;
+          if (j >= 0 && j < WPARTS && i < a_parts) acc = mfma32x32x16<BF16>(ap[i], bp[j], acc);
+        }
+    }
+  }
+  float* out = is_p ? P : R;
+  const int col = 64 * bj + 32 * wn + (lane & 31);
+  if (col < d) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 64 * bi + 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (row < d) out[(int64_t)row * d + col] = acc[r];
+    }
+  }
 }
 
 // Quadrant (wave / 4, wave % 4) of X op(Y) over k < 64 (op(Y) = Y^T when ty): 16x16x4 MFMA,
@@ -483,15 +622,11 @@ __global__ __launch_bounds__(SW_THREADS) void sweep_kernel(SweepArgs a) {
   a.Bx = at_layer(a.Bx, a.st.ws);
   a.Tb = at_layer(a.Tb, a.st.ws);
   a.sc = at_layer(a.sc, a.st.ws);
-  a.Wf = at_layer(a.Wf, a.st.ws);
-  a.R = at_layer(a.R, a.st.ws);
-  a.P = at_layer(a.P, a.st.ws);
-  a.C = at_layer(a.C, a.st.mat);
   a.G = at_layer(a.G, a.st.mat);
   a.info = at_layer(a.info, (int64_t)sizeof(int));
   a.lambda_out = at_layer(a.lambda_out, (int64_t)sizeof(float));
-  // four blocks (plus the factorization's few hundred bytes) keep two work-groups on a CU
-  __shared__ __attribute__((aligned(16))) float L0[NB][BP], L1[NB][BP], L2[NB][BP], L3[NB][BP];
+  // three blocks (plus the factorization's few hundred bytes) keep two work-groups on a CU
+  __shared__ __attribute__((aligned(16))) float L0[NB][BP], L1[NB][BP], L2[NB][BP];
   __shared__ __attribute__((aligned(16))) float curb[2][2][2][NB];
   __shared__ float pivs[NB];
   const int k = a.k, d = a.d;
@@ -546,54 +681,6 @@ __global__ __launch_bounds__(SW_THREADS) void sweep_kernel(SweepArgs a) {
     }
     --q;
   }
-  if (q < a.n_fill) {
-    // block (i, j) of R = C W (all blocks) or P = W W^T (j <= i: P is symmetric) over K blocks
-    // [kb0, kb1)
-    const int nT = a.nP;
-    const int g = a.fill0 + q;
-    const bool is_p = g >= nT * nT;
-    int i = g / nT, j = g % nT;
-    if (is_p) tri_decode(g - nT * nT, i, j);
-    const float* X = is_p ? a.Wf : a.C;
-    // K block kb0 + t passes through registers (loaded two steps ahead) into LDS slot t % 2
-    const int n = a.kb1 - a.kb0;
-    auto gx = [&](int t) { return sw_gload(X, d, i, a.kb0 + t); };
-    auto gy = [&](int t) { return is_p ? sw_gload(a.Wf, d, j, a.kb0 + t) : sw_gload(a.Wf, d, a.kb0 + t, j); };
-    f32x4 rx[2], ry[2];
-    sw_lput(L0, gx(0));
-    sw_lput(L1, gy(0));
-    if (n > 1) {
-      rx[1] = gx(1);
-      ry[1] = gy(1);
-    }
-    if (n > 2) {
-      rx[0] = gx(2);
-      ry[0] = gy(2);
-    }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    auto step = [&](auto bc, int t) {
-      constexpr int b = decltype(bc)::value;
-      __syncthreads();
-      const f32x4 v = b ? sw_mm(L2, L3, is_p) : sw_mm(L0, L1, is_p);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] += v[r];
-      if (t + 1 < n) {
-        sw_lput(b ? L0 : L2, rx[b ^ 1]);
-        sw_lput(b ? L1 : L3, ry[b ^ 1]);
-      }
-      if (t + 3 < n) {
-        rx[b ^ 1] = gx(t + 3);
-        ry[b ^ 1] = gy(t + 3);
-      }
-    };
-    for (int t = 0; t < n; t += 2) {
-      step(std::integral_constant<int, 0>{}, t);
-      if (t + 1 < n) step(std::integral_constant<int, 1>{}, t + 1);
-    }
-    sw_store(is_p ? a.P : a.R, d, i, j, acc, a.kb0 > 0);
-    return;
-  }
-  q -= a.n_fill;
   if (q < a.n_a) {
     // trailing block (i, j) of A, k <= j <= i < nP, other than (k, k): A_ij -= X_i X_j^T
     int ii, jj;
@@ -825,6 +912,7 @@ struct WsLayout {
   Scalars* sc;
   double* part;
   double* R64; // d x d, C W accumulated in fp64 (refinement only)
+  uint16_t* sp; // 9 d x d bf16: three parts of C, of W and of W^T (split_kernel)
 };
 
 WsLayout carve(void* ws, int d) {
@@ -840,7 +928,8 @@ WsLayout carve(void* ws, int d) {
   w.T = (float*)p; p += 3 * NB * NB * sizeof(float);
   w.sc = (Scalars*)p; p += 256;
   w.part = (double*)p; p += DOT_BLOCKS * 5 * sizeof(double);
-  w.R64 = (double*)p;
+  w.R64 = (double*)p; p += (size_t)d * d * sizeof(double);
+  w.sp = (uint16_t*)p;
   return w;
 }
 
@@ -854,7 +943,7 @@ WsLayout carve(void* ws, int d) {
 
 size_t solve_workspace_bytes(int d) {
   const size_t b = (size_t)d * d * sizeof(float) * 6 + 3 * NB * NB * sizeof(float) + 256 +
-                   DOT_BLOCKS * 5 * sizeof(double) + (size_t)d * d * sizeof(double) + 256;
+                   DOT_BLOCKS * 5 * sizeof(double) + (size_t)d * d * sizeof(double) + (size_t)d * d * 18 + 256;
   return (b + 255) / 256 * 256;
 }
 
@@ -878,15 +967,23 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
     hipLaunchKernelGGL(setup_kernel<F32>, eg, dim3(NT), 0, s, L.G, (const float*)L.W, d, w.Mx, w.Bx, w.Wf, st);
   ISPA_TRY(hipGetLastError());
 
+  // R = C W and, for epsilon, the lower block triangle of P = W W^T, from bf16 parts of C and W
+  {
+    const int nT = (d + 63) / 64, n_r = nT * nT, n_p = L.eps ? nT * (nT + 1) / 2 : 0;
+    const dim3 sg(n_r, nb_l), rg(n_r + n_p, nb_l);
+    if (L.w_dtype == DT_BF16) {
+      hipLaunchKernelGGL(split_kernel<1>, sg, dim3(256), 0, s, L.C, w.Wf, w.sp, d, st);
+      hipLaunchKernelGGL(rp_kernel<1>, rg, dim3(256), 0, s, w.sp, w.Rc, w.P, d, n_r, st);
+    } else {
+      hipLaunchKernelGGL(split_kernel<3>, sg, dim3(256), 0, s, L.C, w.Wf, w.sp, d, st);
+      hipLaunchKernelGGL(rp_kernel<3>, rg, dim3(256), 0, s, w.sp, w.Rc, w.P, d, n_r, st);
+    }
+    ISPA_TRY(hipGetLastError());
+  }
+
   // Cholesky sweep (one launch per panel, plus one that finishes the last two block rows of L^-1)
   {
     const int nP = (d + NB - 1) / NB;
-    // R = C W and (for epsilon) the lower block triangle of P = W W^T ride along, split into
-    // SW_FILL_RANGES K ranges spread over the launches in order, so a range is added only after the
-    // one before it is complete
-    const int n_launch = nP + 1;
-    const int n_out = nP * nP + (L.eps ? nP * (nP + 1) / 2 : 0);
-    const int n_range = n_launch < SW_FILL_RANGES ? n_launch : SW_FILL_RANGES;   // launch k works on range k * n_range / n_launch
     for (int k = 0; k <= nP; ++k) {
       SweepArgs a;
       a.Mx = w.Mx;
@@ -909,25 +1006,13 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
         a.f_rows = k >= 2 ? 1 : 0;
         n_f = k >= 2 ? k - 1 : 0;
       }
-      const int range = k * n_range / n_launch;
-      const int first = (range * n_launch + n_range - 1) / n_range;   // first launch of this range
-      const int next = ((range + 1) * n_launch + n_range - 1) / n_range;
-      const int slot = k - first, n_slots = next - first;
       a.sc = w.sc;
       a.G = L.G;
       a.lam = L.lambda;
       a.relative = L.lambda_relative;
       a.lambda_out = L.lambda_out;
-      a.C = L.C;
-      a.Wf = w.Wf;
-      a.R = w.Rc;
-      a.P = w.P;
-      a.kb0 = range * nP / n_range;
-      a.kb1 = (range + 1) * nP / n_range;
-      a.fill0 = (int)((int64_t)n_out * slot / n_slots);
-      a.n_fill = a.kb0 < a.kb1 ? (int)((int64_t)n_out * (slot + 1) / n_slots) - a.fill0 : 0;
       a.st = st;
-      const int grid = (k < nP ? 1 : 0) + a.n_fill + a.n_a + a.n_i + n_f;
+      const int grid = (k < nP ? 1 : 0) + a.n_a + a.n_i + n_f;
       hipLaunchKernelGGL(sweep_kernel, dim3(grid, nb_l), dim3(SW_THREADS), 0, s, a);
       ISPA_TRY(hipGetLastError());
     }
