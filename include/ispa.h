@@ -19,7 +19,11 @@
  *    never frees them and never keeps them after the call returns.
  *  * Every call only enqueues work on `stream` (a hipStream_t, 0 = the null
  *    stream) and returns without synchronising.  Outputs are ready when the
- *    stream reaches that point.
+ *    stream reaches that point.  The solves (ispa_absorb_solve, _batched) fork
+ *    the part that the factorisation does not read to an auxiliary stream of
+ *    the current device (owned by the library, created on first use, default
+ *    priority) and join it back onto `stream` by events before they return,
+ *    so under graph capture it joins the capture.
  *  * Dense row-major layouts.  Token tensors are [tokens, d] with heads as
  *    contiguous column blocks: head h owns columns [h*head_dim, (h+1)*head_dim).
  *    The projection convention is y = A W with W [d_in, d_out] (a PyTorch
@@ -29,8 +33,10 @@
  *    check (arguments, sizes, workspace, launch errors).  When a call returns
  *    an error nothing has been enqueued, except ISPA_EHIP, which reports a
  *    failed launch.  NaN/Inf inputs are propagated, not detected.
- *  * Calls are reentrant: no global mutable state; calls on different streams
- *    may run concurrently if their outputs do not overlap.
+ *  * Calls are reentrant; calls on different streams may run concurrently if
+ *    their outputs do not overlap.  The only global state is per device: the
+ *    solves' auxiliary stream (its fork-join sequence runs under a mutex) and
+ *    the scratch array of ispa_local_attn_fused_proj_noalloc.
  */
 #ifndef ISPA_H
 #define ISPA_H

@@ -18,6 +18,8 @@
 //
 // Every step is a HIP kernel enqueued on the caller's stream; the host never
 // waits.  A non-positive pivot sets *info to its 1-based index.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -933,6 +935,35 @@ WsLayout carve(void* ws, int d) {
   return w;
 }
 
+// One auxiliary stream per device (default priority) and a fork and a join event: work that the
+// sweep does not read runs beside it.  The mutex is held from the fork to the join so that calls
+// from several host threads do not interleave their records and waits.
+struct AuxStream {
+  std::mutex mu;
+  bool tried = false;
+  hipStream_t st = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+AuxStream g_aux[kMaxDevices];
+
+// the device's auxiliary stream, created on first use; nullptr if it cannot be (the work then stays
+// on the caller's stream)
+AuxStream* aux_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  AuxStream& a = g_aux[dev];
+  std::lock_guard<std::mutex> lock(a.mu);
+  if (!a.tried) {
+    a.tried = true;
+    if (hipStreamCreateWithFlags(&a.st, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&a.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&a.join, hipEventDisableTiming) != hipSuccess)
+      a.st = nullptr;
+  }
+  return a.st ? &a : nullptr;
+}
+
 #define ISPA_TRY(x)                      \
   do {                                   \
     hipError_t e_ = (x);                 \
@@ -967,18 +998,30 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
     hipLaunchKernelGGL(setup_kernel<F32>, eg, dim3(NT), 0, s, L.G, (const float*)L.W, d, w.Mx, w.Bx, w.Wf, st);
   ISPA_TRY(hipGetLastError());
 
-  // R = C W and, for epsilon, the lower block triangle of P = W W^T, from bf16 parts of C and W
+  // R = C W and, for epsilon, the lower block triangle of P = W W^T, from bf16 parts of C and W.
+  // Nothing reads them before the triangular products, so they run on the auxiliary stream beside
+  // the sweep (whose launches are latency-bound and leave most of the device idle).
+  AuxStream* ax = aux_stream();
+  std::unique_lock<std::mutex> aux_lock;
+  hipStream_t sr = s;
+  if (ax) {
+    aux_lock = std::unique_lock<std::mutex>(ax->mu);
+    ISPA_TRY(hipEventRecord(ax->fork, s));
+    ISPA_TRY(hipStreamWaitEvent(ax->st, ax->fork, 0));
+    sr = ax->st;
+  }
   {
     const int nT = (d + 63) / 64, n_r = nT * nT, n_p = L.eps ? nT * (nT + 1) / 2 : 0;
     const dim3 sg(n_r, nb_l), rg(n_r + n_p, nb_l);
     if (L.w_dtype == DT_BF16) {
-      hipLaunchKernelGGL(split_kernel<1>, sg, dim3(256), 0, s, L.C, w.Wf, w.sp, d, st);
-      hipLaunchKernelGGL(rp_kernel<1>, rg, dim3(256), 0, s, w.sp, w.Rc, w.P, d, n_r, st);
+      hipLaunchKernelGGL(split_kernel<1>, sg, dim3(256), 0, sr, L.C, w.Wf, w.sp, d, st);
+      hipLaunchKernelGGL(rp_kernel<1>, rg, dim3(256), 0, sr, w.sp, w.Rc, w.P, d, n_r, st);
     } else {
-      hipLaunchKernelGGL(split_kernel<3>, sg, dim3(256), 0, s, L.C, w.Wf, w.sp, d, st);
-      hipLaunchKernelGGL(rp_kernel<3>, rg, dim3(256), 0, s, w.sp, w.Rc, w.P, d, n_r, st);
+      hipLaunchKernelGGL(split_kernel<3>, sg, dim3(256), 0, sr, L.C, w.Wf, w.sp, d, st);
+      hipLaunchKernelGGL(rp_kernel<3>, rg, dim3(256), 0, sr, w.sp, w.Rc, w.P, d, n_r, st);
     }
     ISPA_TRY(hipGetLastError());
+    if (ax) ISPA_TRY(hipEventRecord(ax->join, sr));
   }
 
   // Cholesky sweep (one launch per panel, plus one that finishes the last two block rows of L^-1)
@@ -1016,6 +1059,10 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
       hipLaunchKernelGGL(sweep_kernel, dim3(grid, nb_l), dim3(SW_THREADS), 0, s, a);
       ISPA_TRY(hipGetLastError());
     }
+  }
+  if (ax) {
+    ISPA_TRY(hipStreamWaitEvent(s, ax->join, 0));
+    aux_lock.unlock();
   }
   // Z = L^-1 R (L^-1 lower triangular: only k < m0 + 64 contributes), into Mx (no longer needed)
   ISPA_TRY(run_trgemm(false, w.Bx, st.ws, w.Rc, st.ws, w.Mx, st.ws, d, 1.f, 0.f, nb_l, s));

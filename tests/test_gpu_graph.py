@@ -1,5 +1,7 @@
-"""The hot path under HIP graph capture: every call only enqueues kernels on the caller's stream (no
-allocation, copy, memset or host synchronisation), so the whole step -- dual attention, Gram
+"""The hot path under HIP graph capture: every call only enqueues kernels on the caller's stream (the
+solve forks part of its work to the library's auxiliary stream and joins it back by events, which
+brings that stream into the capture; no allocation, copy, memset or host synchronisation), so the
+whole step -- dual attention, Gram
 statistics, solve with epsilon and W_new, and both L-layer variants -- can be captured once and
 replayed.  Each replay, with eager work and synchronisation between replays, must reproduce the eager
 results bit for bit (the kernels are deterministic)."""
