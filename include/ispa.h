@@ -115,13 +115,13 @@ typedef struct ispa_attn_shape {
  * need none (workspace may be NULL).  The 16-bit path addresses one head's
  * rows of the copy with 32-bit byte offsets: n_k must stay below 8,388,544
  * (EUNSUPPORTED); K and V themselves may exceed 2^31 bytes.
- * Precision: QK^T and PV run on MFMA with fp32 accumulation.  With BF16 inputs
- * and F16 or F32 statistics (dual mode) the PV product uses fp16 probabilities
- * and the V copy is converted to fp16, for all outputs, A_full included.  That
- * conversion is exact for bf16 values with 2^-17 <= |v| <= 65504 and for 0;
- * smaller magnitudes become fp16 subnormals and lose low bits (below 2^-25 they
- * become 0) and larger ones become inf.  BF16 statistics, the single-stream
- * modes and F16 inputs use the input type for P and V.
+ * Precision: QK^T and PV run on MFMA with fp32 accumulation.  In dual mode
+ * (any statistics dtype, or none) the PV product uses fp16 probabilities; with
+ * BF16 inputs the V copy is converted to fp16, for all outputs, A_full
+ * included.  That conversion is exact for bf16 values with
+ * 2^-17 <= |v| <= 65504 and for 0; smaller magnitudes become fp16 subnormals and
+ * lose low bits (below 2^-25 they become 0) and larger ones become inf.  The
+ * single-stream mode and F16 inputs use the input type for P and V.
  */
 int ispa_dual_attn(const ispa_attn_shape* shape, int io_dtype,
                    const void* q, const void* k, const void* v,

@@ -344,51 +344,37 @@ template <typename ST>
 struct OlStash {
   static constexpr int NREG = 32;
   uint32_t* slot;
-  uint32_t h[4][8];
-  __device__ __forceinline__ void keep(const f32x16 (&o)[4]) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) h[t][j] = pack2<F16>(o[t][2 * j], o[t][2 * j + 1]);
-  }
   __device__ __forceinline__ void save(const f32x16 (&o)[4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) slot[(8 * t + j) * 64] = pack2<F16>(o[t][2 * j], o[t][2 * j + 1]);
+      for (int q = 0; q < 2; ++q)
+        *(u32x4*)(slot + 8 * t + 4 * q) =
+            u32x4{pack2<F16>(o[t][8 * q + 0], o[t][8 * q + 1]), pack2<F16>(o[t][8 * q + 2], o[t][8 * q + 3]),
+                  pack2<F16>(o[t][8 * q + 4], o[t][8 * q + 5]), pack2<F16>(o[t][8 * q + 6], o[t][8 * q + 7])};
   }
-  __device__ __forceinline__ void fetch() {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) h[t][j] = slot[(8 * t + j) * 64];
-  }
-  __device__ __forceinline__ float get(int t, int r) const {
-    return f16_bits_to_float((uint16_t)(h[t][r >> 1] >> (16 * (r & 1))));
+  // the two values (t, 2j) and (t, 2j + 1), read back
+  __device__ __forceinline__ void load2(int t, int j, float& a, float& b) const {
+    const uint32_t w = slot[8 * t + j];
+    a = f16_bits_to_float((uint16_t)(w & 0xFFFFu));
+    b = f16_bits_to_float((uint16_t)(w >> 16));
   }
 };
 template <>
 struct OlStash<F32> {
   static constexpr int NREG = 64;
   uint32_t* slot;
-  f32x16 o[4];
-  __device__ __forceinline__ void keep(const f32x16 (&x)[4]) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) o[t] = x[t];
-  }
   __device__ __forceinline__ void save(const f32x16 (&x)[4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) slot[(16 * t + r) * 64] = __float_as_uint(x[t][r]);
+      for (int q = 0; q < 4; ++q)
+        *(f32x4*)(slot + 16 * t + 4 * q) = f32x4{x[t][4 * q], x[t][4 * q + 1], x[t][4 * q + 2], x[t][4 * q + 3]};
   }
-  __device__ __forceinline__ void fetch() {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[t][r] = __uint_as_float(slot[(16 * t + r) * 64]);
+  __device__ __forceinline__ void load2(int t, int j, float& a, float& b) const {
+    a = __uint_as_float(slot[16 * t + 2 * j]);
+    b = __uint_as_float(slot[16 * t + 2 * j + 1]);
   }
-  __device__ __forceinline__ float get(int t, int r) const { return o[t][r]; }
 };
 static_assert(OlStash<F32>::NREG * 64 * 4 * WAVES == kAttnStashBytesPerBlock && BM == kAttnQueriesPerBlock,
               "stash slot size");
@@ -492,7 +478,7 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void attn_mfma_kernel(AttnParams p
   f32x16 s[2];
   u32x4 pf[2][2];
   OlStash<ST> ol;
-  ol.slot = (uint32_t*)p.stash + (size_t)(blockIdx.x * WAVES + wave) * OlStash<ST>::NREG * 64 + lane;
+  ol.slot = (uint32_t*)p.stash + ((size_t)(blockIdx.x * WAVES + wave) * 64 + lane) * OlStash<ST>::NREG;
   float m_loc = -INFINITY, l_loc = 0.f;
 
   // Matrix phase M(t) = QK(t+1) + PV(t) reads K slot (t+1) % 3 and V slot t % 3.  M(-1) only needs
@@ -573,55 +559,55 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void attn_mfma_kernel(AttnParams p
   }
 
   // ---- dual stream: merge the local and history states through their log-sum-exp
-  float m_h = -INFINITY, l_h = 0.f;
-  if (sc.n > sc.t_hist) {
-    m_h = st.m;
-    l_h = close_branch(st);
-  } else {
+  if (!(sc.n > sc.t_hist)) {
+    // no history rows: the live state is the local branch; dA = 0 and A_full = A_loc
     m_loc = st.m;
     l_loc = close_branch(st);
-    ol.keep(st.o);
+    if (p.lse_loc && qok && hi == 0) p.lse_loc[(int64_t)head * p.n_q + qrow] = (m_loc + __log2f(l_loc)) * kLn2;
+    if (p.lse_hist && qok && hi == 0) p.lse_hist[(int64_t)head * p.n_q + qrow] = -INFINITY;
+    if (qok) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t c = col0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (p.a_loc_t) store_stat<ST>(p.a_loc_t, c * p.ld_stat + qrow, st.o[t][r]);
+          if (p.delta_a_t) store_stat<ST>(p.delta_a_t, c * p.ld_stat + qrow, 0.f);
+        }
+    }
+    if (p.a_full) store_token_major<T>(p.a_full, p.d, col0, qrow, qok, st.o);
+    return;
   }
-  if (sc.n > sc.t_hist) {
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));   // this wave's stash stores have completed
-    ol.fetch();
-  }
+  // the live state is the history branch; the local one is parked in the stash
+  const float m_h = st.m;
+  const float l_h = close_branch(st);
   if (p.lse_loc && qok && hi == 0) p.lse_loc[(int64_t)head * p.n_q + qrow] = (m_loc + __log2f(l_loc)) * kLn2;
   if (p.lse_hist && qok && hi == 0)
     p.lse_hist[(int64_t)head * p.n_q + qrow] = l_h > 0.f ? (m_h + __log2f(l_h)) * kLn2 : -INFINITY;
-  if (p.a_loc_t && qok) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = col0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
-        store_stat<ST>(p.a_loc_t, (int64_t)c * p.ld_stat + qrow, ol.get(t, r));
-      }
-  }
   const float mm = fmaxf(m_loc, m_h);
   const float a = l_loc * __builtin_amdgcn_exp2f(m_loc - mm);
   const float b = l_h > 0.f ? l_h * __builtin_amdgcn_exp2f(m_h - mm) : 0.f;
   const float w = b / (a + b);
+  __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));   // this wave's stash stores have completed
+  // per pair of values: A_loc read back from the stash, dA = w (O_H - A_loc), A_full = A_loc + dA
+  // (st.o becomes A_full)
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st.o[t][r] = l_h > 0.f ? w * (st.o[t][r] - ol.get(t, r)) : 0.f;  // dA
-  if (p.delta_a_t && qok) {
+    for (int j = 0; j < 8; ++j) {
+      float lo[2];
+      ol.load2(t, j, lo[0], lo[1]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = col0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
-        store_stat<ST>(p.delta_a_t, (int64_t)c * p.ld_stat + qrow, st.o[t][r]);
+      for (int e = 0; e < 2; ++e) {
+        const int r = 2 * j + e;
+        const int64_t c = col0 + 32 * t + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const float da = l_h > 0.f ? w * (st.o[t][r] - lo[e]) : 0.f;
+        if (qok && p.a_loc_t) store_stat<ST>(p.a_loc_t, c * p.ld_stat + qrow, lo[e]);
+        if (qok && p.delta_a_t) store_stat<ST>(p.delta_a_t, c * p.ld_stat + qrow, da);
+        st.o[t][r] = lo[e] + da;
       }
-  }
-  if (p.a_full) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.o[t][r] += ol.get(t, r);
-    store_token_major<T>(p.a_full, p.d, col0, qrow, qok, st.o);
-  }
+    }
+  if (p.a_full) store_token_major<T>(p.a_full, p.d, col0, qrow, qok, st.o);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -846,7 +832,12 @@ hipError_t launch_mfma_mode(AttnParams p, const AttnLaunch& L, hipStream_t s) {
                        p.ldv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return f16_values ? launch_mfma_stat<T, F16, MODE>(p, L.stat, s) : launch_mfma_stat<T, T, MODE>(p, L.stat, s);
+  // the dual stream's PV product always runs on fp16 probabilities (with an fp16 V^T copy from bf16
+  // inputs); the single streams keep the input type
+  if constexpr (MODE == 0)
+    return launch_mfma_stat<T, F16, MODE>(p, L.stat, s);
+  else
+    return launch_mfma_stat<T, T, MODE>(p, L.stat, s);
 }
 
 template <int HDF, int MODE>

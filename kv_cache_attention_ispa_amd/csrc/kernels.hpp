@@ -38,12 +38,10 @@ inline size_t attn_vt_bytes_aligned(int64_t n_k, int64_t d) { return (attn_vt_by
 inline size_t attn_stash_bytes(int64_t n_q, int64_t n_heads) {
   return (size_t)((n_q + kAttnQueriesPerBlock - 1) / kAttnQueriesPerBlock * n_heads) * kAttnStashBytesPerBlock;
 }
-// Dual stream from bf16 inputs with fp16 or fp32 statistics: the PV product runs on fp16
-// probabilities and the V^T copy is converted to fp16 (bf16 probabilities cost the absorption about
-// three times the error of fp16 ones; bf16 statistics keep bf16 throughout).
-inline bool attn_needs_f16_values(const AttnLaunch& L) {
-  return L.mode == 0 && L.io == DT_BF16 && (L.stat == DT_F16 || L.stat == DT_F32) && (L.a_loc_t || L.delta_a_t);
-}
+// Dual stream from bf16 inputs: the PV product runs on fp16 probabilities and the V^T copy is
+// converted to fp16 (bf16 probabilities cost the absorption about three times the error of fp16
+// ones), whatever the statistics' dtype.
+inline bool attn_needs_f16_values(const AttnLaunch& L) { return L.mode == 0 && L.io == DT_BF16; }
 hipError_t launch_attention(const AttnLaunch& L, hipStream_t s);
 // FP8 attention over the local rows (sink + current chunk; history rows are not read) into L.a_full
 // (io dtype), with the codes and scales of those rows of K and V written into L.ws first
