@@ -59,6 +59,12 @@ __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
   w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
   return (uint32_t)w;
 }
+// the same for values known to lie in [0, 448] (no clamp)
+__device__ __forceinline__ uint32_t pack4_in_range(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
 
 // ------------------------------------------------------------------------------------------------
 // Pre-pass over the layer's own rows, numbered r = 0 .. n_loc - 1: the sink rows, then the current
@@ -334,7 +340,8 @@ __device__ __forceinline__ void softmax8(f32x16 (&s)[2], int valid, float c, int
       float e[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) e[j] = __builtin_amdgcn_exp2f(fmaf(s[kt][4 * q + j], c, off));
-      w[4 * kt + q] = pack4(e[0], e[1], e[2], e[3]);
+      // M is the ceiling of every score of the tile, so 256 P <= 256: in range without a clamp
+      w[4 * kt + q] = pack4_in_range(e[0], e[1], e[2], e[3]);
     }
   pf = i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3], (int)w[4], (int)w[5], (int)w[6], (int)w[7]};
 }
