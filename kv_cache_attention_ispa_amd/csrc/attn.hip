@@ -338,31 +338,34 @@ __device__ __forceinline__ void softmax_phase(f32x16 (&s)[2], int valid, float s
 
 // The local-branch output O_L of a wave, parked in the workspace while the history branch runs
 // (registers are the scarce resource there): fp16 pairs, or fp32 when the statistics are fp32.  A
-// wave's slot holds NREG dwords per lane, register-major, so every store and load moves 256
-// contiguous bytes per wave.  After fetch() the values are in registers again.
+// wave's slot holds NREG dwords per lane; the merge reads them back two values at a time.
 template <typename ST>
 struct OlStash {
   static constexpr int NREG = 32;
+  static constexpr bool kInterleaved = true;   // word k of lane l at slot[64 k + l]: 256 contiguous bytes per store
   uint32_t* slot;
   __device__ __forceinline__ void save(const f32x16 (&o)[4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
-        *(u32x4*)(slot + 8 * t + 4 * q) =
-            u32x4{pack2<F16>(o[t][8 * q + 0], o[t][8 * q + 1]), pack2<F16>(o[t][8 * q + 2], o[t][8 * q + 3]),
-                  pack2<F16>(o[t][8 * q + 4], o[t][8 * q + 5]), pack2<F16>(o[t][8 * q + 6], o[t][8 * q + 7])};
+      for (int j = 0; j < 8; ++j) slot[(8 * t + j) * 64] = pack2<F16>(o[t][2 * j], o[t][2 * j + 1]);
   }
-  // the two values (t, 2j) and (t, 2j + 1), read back
-  __device__ __forceinline__ void load2(int t, int j, float& a, float& b) const {
-    const uint32_t w = slot[8 * t + j];
-    a = f16_bits_to_float((uint16_t)(w & 0xFFFFu));
-    b = f16_bits_to_float((uint16_t)(w >> 16));
+  // the words of output tile t (NREG / 4), read back; then the values (t, 2j) and (t, 2j + 1)
+  __device__ __forceinline__ void load_words(int t, uint32_t (&w)[NREG / 4]) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = slot[(8 * t + j) * 64];
+  }
+  __device__ __forceinline__ void decode(const uint32_t (&w)[NREG / 4], int j, float& a, float& b) const {
+    a = f16_bits_to_float((uint16_t)(w[j] & 0xFFFFu));
+    b = f16_bits_to_float((uint16_t)(w[j] >> 16));
   }
 };
 template <>
 struct OlStash<F32> {
   static constexpr int NREG = 64;
+  // each lane's 64 words contiguous (one base address, 16-byte stores): the word-major layout of the
+  // fp16 stash needs more address registers here than the kernel has to spare
+  static constexpr bool kInterleaved = false;
   uint32_t* slot;
   __device__ __forceinline__ void save(const f32x16 (&x)[4]) {
 #pragma unroll
@@ -371,9 +374,17 @@ struct OlStash<F32> {
       for (int q = 0; q < 4; ++q)
         *(f32x4*)(slot + 16 * t + 4 * q) = f32x4{x[t][4 * q], x[t][4 * q + 1], x[t][4 * q + 2], x[t][4 * q + 3]};
   }
-  __device__ __forceinline__ void load2(int t, int j, float& a, float& b) const {
-    a = __uint_as_float(slot[16 * t + 2 * j]);
-    b = __uint_as_float(slot[16 * t + 2 * j + 1]);
+  __device__ __forceinline__ void load_words(int t, uint32_t (&w)[NREG / 4]) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 v = *(const u32x4*)(slot + 16 * t + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[4 * q + e] = v[e];
+    }
+  }
+  __device__ __forceinline__ void decode(const uint32_t (&w)[NREG / 4], int j, float& a, float& b) const {
+    a = __uint_as_float(w[2 * j]);
+    b = __uint_as_float(w[2 * j + 1]);
   }
 };
 static_assert(OlStash<F32>::NREG * 64 * 4 * WAVES == kAttnStashBytesPerBlock && BM == kAttnQueriesPerBlock,
@@ -478,7 +489,8 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void attn_mfma_kernel(AttnParams p
   f32x16 s[2];
   u32x4 pf[2][2];
   OlStash<ST> ol;
-  ol.slot = (uint32_t*)p.stash + ((size_t)(blockIdx.x * WAVES + wave) * 64 + lane) * OlStash<ST>::NREG;
+  ol.slot = (uint32_t*)p.stash + (size_t)(blockIdx.x * WAVES + wave) * OlStash<ST>::NREG * 64 +
+            (OlStash<ST>::kInterleaved ? lane : lane * OlStash<ST>::NREG);
   float m_loc = -INFINITY, l_loc = 0.f;
 
   // Matrix phase M(t) = QK(t+1) + PV(t) reads K slot (t+1) % 3 and V slot t % 3.  M(-1) only needs
@@ -589,14 +601,22 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void attn_mfma_kernel(AttnParams p
   const float b = l_h > 0.f ? l_h * __builtin_amdgcn_exp2f(m_h - mm) : 0.f;
   const float w = b / (a + b);
   __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));   // this wave's stash stores have completed
-  // per pair of values: A_loc read back from the stash, dA = w (O_H - A_loc), A_full = A_loc + dA
-  // (st.o becomes A_full)
+  // A_loc read back from the stash (the loads of a tile, or of all four for the fp16 stash, issued
+  // together, ahead of the stores), then per pair of values dA = w (O_H - A_loc) and
+  // A_full = A_loc + dA (st.o becomes A_full)
+  constexpr int WPT = OlStash<ST>::NREG / 4;
+  constexpr bool all_first = OlStash<ST>::NREG == 32;
+  uint32_t words[4][WPT];
+  if constexpr (all_first)
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t) ol.load_words(t, words[t]);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if constexpr (!all_first) ol.load_words(t, words[t]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float lo[2];
-      ol.load2(t, j, lo[0], lo[1]);
+      ol.decode(words[t], j, lo[0], lo[1]);
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int r = 2 * j + e;
@@ -607,6 +627,7 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void attn_mfma_kernel(AttnParams p
         st.o[t][r] = lo[e] + da;
       }
     }
+  }
   if (p.a_full) store_token_major<T>(p.a_full, p.d, col0, qrow, qok, st.o);
 }
 
