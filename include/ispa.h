@@ -212,8 +212,10 @@ int ispa_absorb_solve_batched(int n_layers, int d, const float* G, const float* 
  *         with info != 0 (its factorisation failed, its eps is undefined) ranks
  *         as if its eps were NaN.
  *   k     how many layers to convert, 0 <= k <= n_layers.
- *   role  [n_layers] int32, device, out: 1 for the k converted layers, 0 for the
- *         layers that keep full attention.
+ *   role  [n_layers] int32, device, out: 1 for the converted layers -- the first
+ *         k in rank order whose eps is a number (a layer with NaN eps or info != 0
+ *         is never converted, so fewer than k are when fewer than k errors are
+ *         numbers) -- and 0 for the layers that keep full attention.
  *   order [n_layers] int32, device, out (nullable): the layer indices in rank order.
  * Ranking: ascending eps; equal values rank the lower layer index first (a
  * stable sort); NaN ranks after every number.  1 <= n_layers <= 4096.

@@ -7,7 +7,9 @@
 //
 // Order: ascending epsilon; equal values keep the lower layer index first (a stable sort); NaN ranks
 // after every number, and a layer whose factorisation failed (info != 0: its epsilon is undefined)
-// ranks as NaN.  Layer i's rank is the number of
+// ranks as NaN.  The first k in that order are converted, except those whose epsilon is NaN (their
+// absorbed weights are undefined), so fewer than k are converted when fewer than k errors are
+// numbers.  Layer i's rank is the number of
 // layers that come before it in that order, so ranks are a permutation of 0 .. n - 1 and each thread
 // finds its layer's rank by one pass over the errors held in LDS.
 #include "../../include/ispa.h"
@@ -35,7 +37,7 @@ __global__ __launch_bounds__(1024) void select_kernel(const float* __restrict__ 
     const float x = e[i];
     int rank = 0;
     for (int j = 0; j < n; ++j) rank += ranks_before(e[j], j, x, i) ? 1 : 0;
-    role[i] = rank < k ? 1 : 0;
+    role[i] = rank < k && x == x ? 1 : 0;
     if (order) order[rank] = i;
   }
 }

@@ -95,9 +95,14 @@ def recon_error_traces(G, C, D, W, dW, lam: Optional[float] = None) -> float:
 
 
 def select_local_layers(eps, k: int) -> np.ndarray:
-    """Indices of the k layers with the lowest epsilon (stable: ties keep the lower index)."""
-    order = np.argsort(np.asarray(eps, dtype=np.float64), kind="stable")
-    return np.sort(order[:k])
+    """Indices of the k layers with the lowest epsilon (stable: ties keep the lower index).
+
+    Technical summary section 2, "Dynamic layer selection": the layers are ranked by epsilon and the
+    lowest-error ones converted.  A NaN epsilon (an undefined error: the layer's absorption failed)
+    ranks last and is never converted, so fewer than k come back when fewer than k are numbers."""
+    e = np.asarray(eps, dtype=np.float64)
+    order = np.argsort(e, kind="stable")[:k]
+    return np.sort(order[~np.isnan(e[order])])
 
 
 def fold_weights(W, dW) -> np.ndarray:

@@ -357,6 +357,8 @@ def check_selection(impl):
     assert list(impl.select_local_layers(eps, 2)) == [1, 3]
     assert list(impl.select_local_layers(eps, 4)) == [1, 2, 3, 5]
     assert list(impl.select_local_layers(eps, 0)) == []
+    # a NaN error (a failed absorption) ranks last and is never converted: two numbers for k = 3
+    assert list(impl.select_local_layers([0.5, float("nan"), 0.3, float("nan")], 3)) == [0, 2]
 
 
 def check_golden_l_layer(impl):

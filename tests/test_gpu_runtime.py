@@ -25,7 +25,7 @@ pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
-SELECT_CASES = ["random", "ties", "nan", "info", "all", "none"]
+SELECT_CASES = ["random", "ties", "nan", "info", "all", "none", "fewer_numbers_than_k"]
 
 
 @pytest.mark.parametrize("case", SELECT_CASES)
@@ -49,6 +49,10 @@ def test_select_layers_matches_stable_sort(case):
         k = n
     elif case == "none":
         k = 0
+    elif case == "fewer_numbers_than_k":
+        eps[::2] = np.nan          # 15 NaN errors, one more failed solve: 14 numbers for k = 20
+        info[5] = 2
+        k = 20
     role = t.full((n,), 7, dtype=t.int32, device="cuda")
     order = t.full((n,), -1, dtype=t.int32, device="cuda")
     ispa.select_layers(t.from_numpy(eps).cuda(), k, role, order, info=t.from_numpy(info).cuda())
@@ -57,6 +61,7 @@ def test_select_layers_matches_stable_sort(case):
     ref_sel = set(int(i) for i in oracle.select_local_layers(ref_eps, k))
     got = role.cpu().numpy()
     assert set(np.nonzero(got == 1)[0].tolist()) == ref_sel and set(got.tolist()) <= {0, 1}
+    assert not np.any((got == 1) & np.isnan(ref_eps))
     assert order.cpu().numpy().tolist() == np.argsort(ref_eps, kind="stable").tolist()
 
 

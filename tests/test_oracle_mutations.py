@@ -127,6 +127,10 @@ def _traces_sign(G, C, D, W, dW, lam=None):
     return float(np.sqrt(max(num2, 0.0) / den2))
 
 
+def _select_converts_nan(eps, k):
+    return np.sort(np.argsort(np.asarray(eps, dtype=np.float64), kind="stable")[:k])
+
+
 def _select_highest(eps, k):
     order = np.argsort(-np.asarray(eps, dtype=np.float64), kind="stable")
     return np.sort(order[:k])
@@ -224,6 +228,7 @@ MUTANTS = {
     "relative_lambda_not_over_d": dict(ridge_lambda=_lambda_no_d),
     "eps_cross_sign": dict(recon_error_traces=_traces_sign),
     "select_highest": dict(select_local_layers=_select_highest),
+    "select_converts_nan_layers": dict(select_local_layers=_select_converts_nan),
     "kv_rows_drop_sink": dict(kv_cache_bytes=_kv_off_by_one),
     "flops_half": dict(attn_flops=_flops_half),
     "l_layer_projects_by_w_transposed": dict(local_layer_output=_l_layer_w_transposed),
