@@ -242,6 +242,25 @@ int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype,
                                void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ispa_local_attn_fused_proj_wt -- the same L-layer step with the projection
+ * given transposed: w_new_t [d_out, d_in] = W_new^T (io_dtype), as
+ * ispa_transpose16 writes it once per converted layer at the fold (W_new does
+ * not change after the transition, so the per-call transpose of
+ * ispa_local_attn_fused_proj is skipped).  Arguments, limits and workspace as
+ * ispa_local_attn_fused_proj; the output is bit-identical to it.
+ */
+int ispa_local_attn_fused_proj_wt(const ispa_attn_shape* shape, int io_dtype,
+                                  const void* q, const void* k, const void* v, const void* w_new_t,
+                                  void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ispa_transpose16 -- dst [cols, rows] = src [rows, cols]^T for BF16 or F16
+ * (dtype), both row-major device arrays, 16-byte aligned, not overlapping;
+ * rows and cols multiples of 16, at most 65536 (ISPA_EINVAL otherwise).
+ */
+int ispa_transpose16(int rows, int cols, int dtype, const void* src, void* dst, void* stream);
+
+/*
  * ispa_local_attn_fused_proj_noalloc -- ispa_local_attn_fused_proj without a
  * workspace argument, for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid

@@ -65,6 +65,9 @@ def lib() -> ctypes.CDLL:
                                         _sz, _vp]
         L.ispa_local_attn_fused_proj.argtypes = [ctypes.POINTER(AttnShape), _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                                  _vp]
+        L.ispa_local_attn_fused_proj_wt.argtypes = [ctypes.POINTER(AttnShape), _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                    _sz, _vp]
+        L.ispa_transpose16.argtypes = [_i32, _i32, _i32, _vp, _vp, _vp]
         L.ispa_workspace_bytes.argtypes = [_i32, ctypes.POINTER(AttnShape), _i32]
         L.ispa_workspace_bytes.restype = ctypes.c_size_t
         L.ispa_status_string.argtypes = [_i32]
@@ -306,6 +309,31 @@ def local_attn_fused_proj(shape: AttnShape, q, k, v, w_new, out, workspace, stre
                                             _ptr(w_new), _ptr(out), _ptr(workspace), _ws_bytes(workspace),
                                             _stream(stream)),
            "ispa_local_attn_fused_proj")
+
+
+def local_attn_fused_proj_wt(shape: AttnShape, q, k, v, w_new_t, out, workspace, stream=None) -> None:
+    """ispa_local_attn_fused_proj_wt: the L-layer step with W_new given transposed (w_new_t = W_new^T,
+    e.g. from transpose16 once at the fold)."""
+    d = _l_layer_args(shape, q, k, v, out)
+    _want(w_new_t, "w_new_t", q.dtype, (d, d))
+    _same_device(q, k, v, w_new_t, out, workspace)
+    _check(lib().ispa_local_attn_fused_proj_wt(ctypes.byref(shape), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
+                                               _ptr(w_new_t), _ptr(out), _ptr(workspace), _ws_bytes(workspace),
+                                               _stream(stream)),
+           "ispa_local_attn_fused_proj_wt")
+
+
+def transpose16(src, dst, stream=None) -> None:
+    """ispa_transpose16: dst = src^T for 2-D bf16/fp16 device tensors (dims multiples of 16)."""
+    import torch
+    if src.dim() != 2:
+        raise ValueError("src must be 2-D")
+    rows, cols = src.shape
+    _want(src, "src", (torch.bfloat16, torch.float16))
+    _want(dst, "dst", src.dtype, (cols, rows))
+    _same_device(src, dst)
+    _check(lib().ispa_transpose16(rows, cols, _dtype_code(src), _ptr(src), _ptr(dst), _stream(stream)),
+           "ispa_transpose16")
 
 
 def local_attn_fused_proj_noalloc(shape: AttnShape, q, k, v, w_new, out, stream=None) -> None:

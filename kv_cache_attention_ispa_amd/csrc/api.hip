@@ -253,16 +253,19 @@ int ispa_absorb_solve(int d, const float* G, const float* C, const float* D, int
                                    lambda_out, info, workspace, workspace_bytes, stream);
 }
 
-int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k,
-                               const void* v, const void* w_new, void* out, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+// The 16-bit L-layer step: local attention into the workspace, then the projection by W_new (w_new
+// transposed into the workspace first) or by a W_new^T the caller already holds (w_new_t).
+static int local_attn_proj16(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k, const void* v,
+                             const void* w_new, const void* w_new_t, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   int st = check_shape(shape);
   if (st) return st;
   if (io_dtype != ISPA_BF16 && io_dtype != ISPA_F16) return ISPA_EUNSUPPORTED;
   if (shape->head_dim != 128 || !fits_buffer(shape)) return ISPA_EUNSUPPORTED;
   if ((int64_t)shape->n_q * shape->n_heads * shape->head_dim * 2 >= INT32_MAX) return ISPA_EUNSUPPORTED;
-  if (!q || !k || !v || !w_new || !out) return ISPA_EINVAL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(w_new) || !aligned16(out)) return ISPA_EINVAL;
+  const void* w = w_new ? w_new : w_new_t;
+  if (!q || !k || !v || !w || !out) return ISPA_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(w) || !aligned16(out)) return ISPA_EINVAL;
   const size_t need = ispa_workspace_bytes(ISPA_CALL_LOCAL_ATTN_PROJ, shape, 0);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return ISPA_EWORKSPACE;
   const hipStream_t s = (hipStream_t)stream;
@@ -293,6 +296,7 @@ int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype, const
   hipError_t e = launch_attention(L, s);
   if (e != hipSuccess) return ISPA_EHIP;
   const int d = shape->n_heads * shape->head_dim;
+  if (w_new_t) return hip_status(launch_proj_nt(io_dtype, shape->n_q, d, d, workspace, w_new_t, out, s));
   ProjLaunch P;
   P.bt = (char*)workspace + local_a_bytes(shape) + vt_bytes;
   P.io = io_dtype;
@@ -303,6 +307,28 @@ int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype, const
   P.b = w_new;
   P.out = out;
   return hip_status(launch_proj(P, s));
+}
+
+int ispa_local_attn_fused_proj(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k,
+                               const void* v, const void* w_new, void* out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (!w_new) return ISPA_EINVAL;
+  return local_attn_proj16(shape, io_dtype, q, k, v, w_new, nullptr, out, workspace, workspace_bytes, stream);
+}
+
+int ispa_local_attn_fused_proj_wt(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k,
+                                  const void* v, const void* w_new_t, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!w_new_t) return ISPA_EINVAL;
+  return local_attn_proj16(shape, io_dtype, q, k, v, nullptr, w_new_t, out, workspace, workspace_bytes, stream);
+}
+
+int ispa_transpose16(int rows, int cols, int dtype, const void* src, void* dst, void* stream) {
+  if (dtype != ISPA_BF16 && dtype != ISPA_F16) return ISPA_EUNSUPPORTED;
+  if (rows < 16 || cols < 16 || rows % 16 != 0 || cols % 16 != 0 || rows > 65536 || cols > 65536)
+    return ISPA_EINVAL;
+  if (!src || !dst || src == dst || !aligned16(src) || !aligned16(dst)) return ISPA_EINVAL;
+  return hip_status(launch_transpose16(src, rows, cols, dst, (hipStream_t)stream));
 }
 
 size_t ispa_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }

@@ -73,6 +73,9 @@ struct ProjLaunch {
   void* out;       // [m, n]
 };
 hipError_t launch_proj(const ProjLaunch& L, hipStream_t s);
+// W [k, n] 16-bit -> W^T [n, k] (k, n multiples of 16), and out [m, n] = A [m, k] (B^T [n, k])^T.
+hipError_t launch_transpose16(const void* w, int k, int n, void* wt, hipStream_t s);
+hipError_t launch_proj_nt(int io, int m, int n, int k, const void* a, const void* bt, void* out, hipStream_t s);
 
 // W8A8 projection (fp8.hip): per-row E4M3 codes + scales of a [rows, cols] matrix; the weights per
 // output channel, written transposed; out[m, n] = (Aq Wq) s_a s_w^T (k % 64 == 0).

@@ -270,13 +270,21 @@ hipError_t launch_nt(const void* a, const void* b, const float* sa, const float*
 
 }  // namespace
 
+hipError_t launch_transpose16(const void* w, int k, int n, void* wt, hipStream_t s) {
+  const dim3 gt((n + 127) / 128, (k + 63) / 64);
+  hipLaunchKernelGGL(transpose16_kernel, gt, dim3(256), 0, s, (const uint16_t*)w, k, n, (uint16_t*)wt);
+  return hipGetLastError();
+}
+
+hipError_t launch_proj_nt(int io, int m, int n, int k, const void* a, const void* bt, void* out, hipStream_t s) {
+  if (io == DT_BF16) return launch_nt<1, BF16, BF16>(a, bt, nullptr, nullptr, out, m, n, k * 2, s);
+  return launch_nt<2, F16, F16>(a, bt, nullptr, nullptr, out, m, n, k * 2, s);
+}
+
 hipError_t launch_proj(const ProjLaunch& L, hipStream_t s) {
-  const dim3 gt((L.n + 127) / 128, (L.k + 63) / 64);
-  hipLaunchKernelGGL(transpose16_kernel, gt, dim3(256), 0, s, (const uint16_t*)L.b, L.k, L.n, (uint16_t*)L.bt);
-  const hipError_t e = hipGetLastError();
+  const hipError_t e = launch_transpose16(L.b, L.k, L.n, L.bt, s);
   if (e != hipSuccess) return e;
-  if (L.io == DT_BF16) return launch_nt<1, BF16, BF16>(L.a, L.bt, nullptr, nullptr, L.out, L.m, L.n, L.k * 2, s);
-  return launch_nt<2, F16, F16>(L.a, L.bt, nullptr, nullptr, L.out, L.m, L.n, L.k * 2, s);
+  return launch_proj_nt(L.io, L.m, L.n, L.k, L.a, L.bt, L.out, s);
 }
 
 hipError_t launch_proj8(int out_dtype, const uint8_t* aq, const float* sa, const uint8_t* wq_t, const float* sw,

@@ -20,7 +20,8 @@ from __future__ import annotations
 from typing import List, Optional, Sequence, Tuple
 
 from . import (AttnShape, CALL_ABSORB_SOLVE, CALL_DUAL_ATTN, CALL_LOCAL_ATTN_PROJ, IspaError, KVCache,
-               absorb_solve_batched, dual_attn, gram_accum, local_attn_fused_proj, select_layers, workspace_bytes)
+               absorb_solve_batched, dual_attn, gram_accum, local_attn_fused_proj_wt, select_layers, transpose16,
+               workspace_bytes)
 
 WARMUP, STEADY = "warmup", "steady"
 
@@ -77,6 +78,7 @@ class IspaRuntime:
         self.order = torch.zeros((n_layers,), dtype=torch.int32, device=dev)
         self.roles: Optional[List[int]] = None
         self.w_new = [None] * n_layers
+        self.w_new_t = [None] * n_layers   # W_new^T of the converted layers, transposed once at the fold
         self.delta_w = None
 
     # ------------------------------------------------------------------ helpers
@@ -116,8 +118,8 @@ class IspaRuntime:
             self.started[layer] = True
             return out, False
         if self.roles[layer] == 1:
-            local_attn_fused_proj(shape, q, kc, vc, self.w_new[layer], out,
-                                  self._ws(CALL_LOCAL_ATTN_PROJ, shape), stream=self.stream)
+            local_attn_fused_proj_wt(shape, q, kc, vc, self.w_new_t[layer], out,
+                                     self._ws(CALL_LOCAL_ATTN_PROJ, shape), stream=self.stream)
             return out, True
         dual_attn(shape, q, kc, vc, a_full=out, workspace=self._ws(CALL_DUAL_ATTN, shape), stream=self.stream)
         return out, False
@@ -152,6 +154,9 @@ class IspaRuntime:
         for layer, r in enumerate(self.roles):
             if r == 1:
                 self.kv.release_history(layer, stream=self.stream)
+                # W_new is fixed from here on: the steady-state step takes it transposed
+                self.w_new_t[layer] = self._buf(d, d, dtype=W.dtype)
+                transpose16(self.w_new[layer], self.w_new_t[layer], stream=self.stream)
             else:
                 self.w_new[layer] = None
         self.G = self.C = self.D = None

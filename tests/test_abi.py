@@ -137,6 +137,26 @@ def test_local_proj_rejects_bad_arguments(L):
     assert f(w=0) == EINVAL
     assert f(ws=0) == EWORKSPACE
     assert f(wsb=need - 1) == EWORKSPACE
+    # the same checks with W_new given transposed
+    g = lambda io=1, ws=FAKE, wsb=need, w=FAKE: L.ispa_local_attn_fused_proj_wt(ctypes.byref(sh), io, FAKE, FAKE,
+                                                                                FAKE, w, FAKE, ws, wsb, None)
+    assert g(io=0) == EUNSUPPORTED
+    assert g(w=0) == EINVAL
+    assert g(w=FAKE + 8) == EINVAL            # 16-byte alignment
+    assert g(ws=0) == EWORKSPACE
+    assert g(wsb=need - 1) == EWORKSPACE
+
+
+def test_transpose16_validation(L):
+    t = lambda r=64, c=128, dt=1, src=FAKE, dst=FAKE + 4096: L.ispa_transpose16(r, c, dt, src, dst, None)
+    assert t(dt=0) == EUNSUPPORTED                 # fp32 is not a 16-bit type
+    assert t(dt=7) == EUNSUPPORTED
+    for r, c in ((8, 128), (64, 120), (0, 64), (65552, 16), (64, -16)):
+        assert t(r=r, c=c) == EINVAL, (r, c)
+    assert t(src=0) == EINVAL
+    assert t(dst=0) == EINVAL
+    assert t(dst=FAKE) == EINVAL                   # in place
+    assert t(src=FAKE + 2) == EINVAL               # alignment
 
 
 def test_kv_cache_rejects_bad_arguments_without_allocating(L):

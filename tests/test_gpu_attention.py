@@ -157,6 +157,29 @@ def test_local_attn_fused_proj(io, n_hist):
                                     np.concatenate([v[:shape.n_sink], v[shape.n_sink + n_hist:]]),
                                     shape.n_sink, shape.n_cur, shape.n_heads, w_new)
     assert maxrel(host(out), ref) <= TOL[io]
+    # W_new given transposed (ispa_transpose16 once, then the step without its own transpose): the
+    # transpose is exact and the step runs the same kernels, so the output is bit-identical
+    wd = dev(w_new, io)
+    wt = t.empty_like(wd)
+    ispa.transpose16(wd, wt)
+    out_t = t.full_like(out, float("nan"))
+    ispa.local_attn_fused_proj_wt(s, dev(q, io), dev(k, io), dev(v, io), wt, out_t, ws)
+    t.cuda.synchronize()
+    assert t.equal(wt, wd.t().contiguous())
+    assert t.equal(out_t, out)
+
+
+@pytest.mark.parametrize("rows,cols", [(1536, 1536), (640, 5120), (48, 16), (80, 208)])
+def test_transpose16_exact(rows, cols):
+    """Rows and columns that are and are not multiples of the 64 x 128 blocks."""
+    import kv_cache_attention_ispa_amd as ispa
+    t = torch()
+    g = t.Generator(device="cuda").manual_seed(rows + cols)
+    src = t.randn((rows, cols), generator=g, device="cuda").to(t.bfloat16)
+    dst = t.full((cols, rows), float("nan"), dtype=t.bfloat16, device="cuda")
+    ispa.transpose16(src, dst)
+    t.cuda.synchronize()
+    assert t.equal(dst, src.t().contiguous())
 
 
 @pytest.mark.parametrize("io", ["bf16", "f16"])
