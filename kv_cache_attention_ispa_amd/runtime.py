@@ -19,11 +19,12 @@ from __future__ import annotations
 
 from typing import List, Optional, Sequence, Tuple
 
-from . import (AttnShape, CALL_ABSORB_SOLVE, CALL_DUAL_ATTN, CALL_LOCAL_ATTN_PROJ, IspaError, KVCache,
-               absorb_solve_batched, dual_attn, gram_accum, local_attn_fused_proj_wt, select_layers, transpose16,
-               workspace_bytes)
+from . import (AttnShape, CALL_ABSORB_SOLVE, CALL_DUAL_ATTN, CALL_LOCAL_ATTN_FP8_PROJ_W8A8, CALL_LOCAL_ATTN_PROJ,
+               IspaError, KVCache, absorb_solve_batched, dual_attn, gram_accum, local_attn_fp8_proj_w8a8,
+               local_attn_fused_proj_wt, quantize_weight_fp8, select_layers, transpose16, workspace_bytes)
 
 WARMUP, STEADY = "warmup", "steady"
+L_LAYER_KINDS = ("bf16", "w8a8_fp8")
 
 
 class IspaRuntime:
@@ -37,15 +38,22 @@ class IspaRuntime:
         projected = True.
     transition(weights) runs the absorption for every layer, ranks the layers by epsilon, converts
     the k_local lowest and releases their history rows.
+    l_layer selects the converted layers' step: "bf16" (16-bit attention, projection by W_new^T
+    transposed once at the fold) or "w8a8_fp8" (the method combined with W8A8: W_new coded once to
+    FP8 E4M3 per output channel at the fold; FP8 attention, per-token activation codes and the FP8
+    product per step).
     """
 
     def __init__(self, n_layers: int, n_heads: int, head_dim: int, sink_rows: int, chunk_rows: int,
                  warmup_chunks: int, max_chunks: int, k_local: int, dtype=None, stat_dtype=None,
                  lam: float = 1e-3, lam_relative: bool = True, refine: int = 0, keep_delta_w: bool = False,
-                 stream=None):
+                 l_layer: str = "bf16", stream=None):
         import torch
         if not 0 <= k_local <= n_layers:
             raise ValueError("k_local must be in [0, n_layers]")
+        if l_layer not in L_LAYER_KINDS:
+            raise ValueError(f"l_layer must be one of {L_LAYER_KINDS}")
+        self.l_layer = l_layer
         if warmup_chunks < 1 or warmup_chunks > max_chunks:
             raise ValueError("need 1 <= warmup_chunks <= max_chunks")
         self.torch = torch
@@ -79,6 +87,7 @@ class IspaRuntime:
         self.roles: Optional[List[int]] = None
         self.w_new = [None] * n_layers
         self.w_new_t = [None] * n_layers   # W_new^T of the converted layers, transposed once at the fold
+        self.w_codes = [None] * n_layers   # ("w8a8_fp8") their FP8 codes W_new^T and per-channel scales
         self.delta_w = None
 
     # ------------------------------------------------------------------ helpers
@@ -118,8 +127,13 @@ class IspaRuntime:
             self.started[layer] = True
             return out, False
         if self.roles[layer] == 1:
-            local_attn_fused_proj_wt(shape, q, kc, vc, self.w_new_t[layer], out,
-                                     self._ws(CALL_LOCAL_ATTN_PROJ, shape), stream=self.stream)
+            if self.l_layer == "w8a8_fp8":
+                wq, sw = self.w_codes[layer]
+                local_attn_fp8_proj_w8a8(shape, q, kc, vc, wq, sw, out, self._ws(CALL_LOCAL_ATTN_FP8_PROJ_W8A8, shape),
+                                         stream=self.stream)
+            else:
+                local_attn_fused_proj_wt(shape, q, kc, vc, self.w_new_t[layer], out,
+                                         self._ws(CALL_LOCAL_ATTN_PROJ, shape), stream=self.stream)
             return out, True
         dual_attn(shape, q, kc, vc, a_full=out, workspace=self._ws(CALL_DUAL_ATTN, shape), stream=self.stream)
         return out, False
@@ -154,9 +168,15 @@ class IspaRuntime:
         for layer, r in enumerate(self.roles):
             if r == 1:
                 self.kv.release_history(layer, stream=self.stream)
-                # W_new is fixed from here on: the steady-state step takes it transposed
-                self.w_new_t[layer] = self._buf(d, d, dtype=W.dtype)
-                transpose16(self.w_new[layer], self.w_new_t[layer], stream=self.stream)
+                # W_new is fixed from here on: the steady-state step takes it transposed (or coded)
+                if self.l_layer == "w8a8_fp8":
+                    wq = self._buf(d, d, dtype=torch.uint8)
+                    sw = self._buf(d)
+                    quantize_weight_fp8(self.w_new[layer], wq, sw, stream=self.stream)
+                    self.w_codes[layer] = (wq, sw)
+                else:
+                    self.w_new_t[layer] = self._buf(d, d, dtype=W.dtype)
+                    transpose16(self.w_new[layer], self.w_new_t[layer], stream=self.stream)
             else:
                 self.w_new[layer] = None
         self.G = self.C = self.D = None
