@@ -62,7 +62,8 @@ enum {
 
 /* call ids for ispa_workspace_bytes */
 enum { ISPA_CALL_DUAL_ATTN = 0, ISPA_CALL_ABSORB_SOLVE = 1, ISPA_CALL_LOCAL_ATTN_PROJ = 2,
-       ISPA_CALL_LOCAL_ATTN_PROJ_W8A8 = 3, ISPA_CALL_LOCAL_ATTN_FP8 = 4, ISPA_CALL_LOCAL_ATTN_FP8_PROJ_W8A8 = 5 };
+       ISPA_CALL_LOCAL_ATTN_PROJ_W8A8 = 3, ISPA_CALL_LOCAL_ATTN_FP8 = 4, ISPA_CALL_LOCAL_ATTN_FP8_PROJ_W8A8 = 5,
+       ISPA_CALL_DUAL_ATTN_VT = 6 };
 
 /*
  * One layer's KV cache, rows in this order:
@@ -129,6 +130,46 @@ int ispa_dual_attn(const ispa_attn_shape* shape, int io_dtype,
                    int stat_dtype, void* a_loc_t, void* delta_a_t, int64_t ld_stat,
                    float* lse_loc, float* lse_hist,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ispa_dual_attn_vt -- ispa_dual_attn with V supplied transposed by the caller.
+ * The same operation (technical summary section 2, stage 1 "Dual-Stream
+ * Warmup"), for callers that keep V^T next to their cache: the cached rows of
+ * V are then transposed once, when they are appended (ispa_transpose_rows),
+ * instead of on every call.  Outputs are bit-identical to ispa_dual_attn's on
+ * the same values.
+ *
+ *   vt      [d, ldv] in vt_dtype: vt[c*ldv + r] = V[r, c] for the n_k cache rows
+ *           r (same row order as ispa_dual_attn's v).  vt_dtype is the type the
+ *           PV product runs on: F16 in dual mode (BF16 or F16 inputs; bf16 values
+ *           converted as ispa_dual_attn does), io_dtype in single-stream mode;
+ *           EINVAL otherwise.  ldv >= n_k, ldv % 8 == 0, 128 * ldv * 2 < 2^31
+ *           (EUNSUPPORTED).  The kernel streams up to 63 columns past a
+ *           segment's last row as masked keys, whose probabilities are zero:
+ *           columns [n_k, min(ldv, n_k + 64)) must hold finite values (the zeros
+ *           ispa_transpose_rows leaves after the rows it writes qualify).
+ *   Other arguments as ispa_dual_attn; io_dtype BF16 or F16 only (F32:
+ *   EUNSUPPORTED).  Workspace: ispa_workspace_bytes(ISPA_CALL_DUAL_ATTN_VT,
+ *   shape, 0) bytes in dual mode (the parked local outputs); none (NULL) in
+ *   single-stream mode.  vt is only read.
+ */
+int ispa_dual_attn_vt(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k, int vt_dtype,
+                      const void* vt, int64_t ldv, void* a_full, int stat_dtype, void* a_loc_t, void* delta_a_t,
+                      int64_t ld_stat, float* lse_loc, float* lse_hist, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * ispa_transpose_rows -- appends cache rows to a caller-owned V^T.
+ * Writes vt[c*ldv + col0 + r] = V[r, c] for r < rows, c < d, from v [rows, d]
+ * (row-major, v_dtype BF16 or F16), converted to vt_dtype (F16, or v_dtype;
+ * bf16 -> fp16 as ispa_dual_attn converts), then sets the next 64 to 127
+ * columns (those below ldv) to zero, so the columns past the last rows a call
+ * wrote are finite for ispa_dual_attn_vt.  Requires d % 64 == 0, d <= 65536,
+ * rows >= 0, col0 and ldv multiples of 8, col0 + rows <= ldv, v and vt 16-byte
+ * aligned.  Stream-ordered, no workspace.
+ */
+int ispa_transpose_rows(int rows, int d, int v_dtype, const void* v, int vt_dtype, void* vt, int64_t ldv,
+                        int64_t col0, void* stream);
 
 /*
  * ispa_gram_accum -- the absorption statistics over warmup tokens.

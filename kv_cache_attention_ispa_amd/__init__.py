@@ -16,11 +16,12 @@ __all__ = ["IspaError", "AttnShape", "lib", "dual_attn", "gram_accum", "absorb_s
            "CALL_LOCAL_ATTN_PROJ", "CALL_LOCAL_ATTN_PROJ_W8A8", "library_path", "KVCache",
            "quantize_weight_fp8", "quantize_rows_fp8", "local_attn_fused_proj_w8a8", "select_layers",
            "local_attn_fused_proj_noalloc", "absorb_solve_batched", "local_attn_fp8", "local_attn_fp8_proj_w8a8",
-           "CALL_LOCAL_ATTN_FP8", "CALL_LOCAL_ATTN_FP8_PROJ_W8A8"]
+           "CALL_LOCAL_ATTN_FP8", "CALL_LOCAL_ATTN_FP8_PROJ_W8A8", "dual_attn_vt", "transpose_rows",
+           "CALL_DUAL_ATTN_VT", "local_attn_fused_proj_wt", "transpose16"]
 
 F32, BF16, F16 = 0, 1, 2
 CALL_DUAL_ATTN, CALL_ABSORB_SOLVE, CALL_LOCAL_ATTN_PROJ, CALL_LOCAL_ATTN_PROJ_W8A8 = 0, 1, 2, 3
-CALL_LOCAL_ATTN_FP8, CALL_LOCAL_ATTN_FP8_PROJ_W8A8 = 4, 5
+CALL_LOCAL_ATTN_FP8, CALL_LOCAL_ATTN_FP8_PROJ_W8A8, CALL_DUAL_ATTN_VT = 4, 5, 6
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -60,6 +61,9 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(path)
         L.ispa_dual_attn.argtypes = [ctypes.POINTER(AttnShape), _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _vp,
                                      _vp, _vp, _sz, _vp]
+        L.ispa_dual_attn_vt.argtypes = [ctypes.POINTER(AttnShape), _i32, _vp, _vp, _i32, _vp, _i64, _vp, _i32, _vp,
+                                        _vp, _i64, _vp, _vp, _vp, _sz, _vp]
+        L.ispa_transpose_rows.argtypes = [_i32, _i32, _i32, _vp, _i32, _vp, _i64, _i64, _vp]
         L.ispa_gram_accum.argtypes = [_i32, _i32, _i32, _vp, _vp, _i64, _i32, _vp, _vp, _vp, _vp]
         L.ispa_absorb_solve.argtypes = [_i32, _vp, _vp, _vp, _i32, _vp, _f32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _sz, _vp]
@@ -93,7 +97,7 @@ def lib() -> ctypes.CDLL:
         L.ispa_local_attn_fused_proj_noalloc.argtypes = [ctypes.POINTER(AttnShape), _i32, _vp, _vp, _vp, _vp, _vp,
                                                          _vp]
         L.ispa_noalloc_scratch_bytes.restype = ctypes.c_size_t
-        for f in ("ispa_dual_attn", "ispa_gram_accum", "ispa_absorb_solve", "ispa_local_attn_fused_proj",
+        for f in ("ispa_dual_attn", "ispa_dual_attn_vt", "ispa_transpose_rows", "ispa_gram_accum", "ispa_absorb_solve", "ispa_local_attn_fused_proj",
                   "ispa_quantize_weight_fp8", "ispa_quantize_rows_fp8", "ispa_local_attn_fused_proj_w8a8",
                   "ispa_kv_create", "ispa_kv_destroy", "ispa_kv_write_sink", "ispa_kv_append_chunk",
                   "ispa_kv_release_history", "ispa_kv_layer", "ispa_kv_bytes", "ispa_select_layers",
@@ -195,16 +199,10 @@ def workspace_bytes(call_id: int, shape: Optional[AttnShape] = None, d: int = 0)
     return int(lib().ispa_workspace_bytes(call_id, ctypes.byref(shape) if shape is not None else None, d))
 
 
-def dual_attn(shape: AttnShape, q, k, v, a_full=None, a_loc_t=None, delta_a_t=None, ld_stat: Optional[int] = None,
-              lse_loc=None, lse_hist=None, workspace=None, stream=None) -> None:
-    """ispa_dual_attn: see include/ispa.h.  Stat outputs are feature-major [d, ld_stat] views;
-    workspace (bytes from workspace_bytes(CALL_DUAL_ATTN, shape)) is needed for bf16/fp16 inputs."""
+def _dual_outputs(shape, q, a_full, a_loc_t, delta_a_t, ld_stat, lse_loc, lse_hist):
+    """Checks the outputs of ispa_dual_attn(_vt); returns (stat dtype code, ld_stat)."""
     import torch
     d = shape.n_heads * shape.head_dim
-    n_k = shape.n_sink + shape.n_hist + shape.n_cur
-    _want(q, "q", _io_dtypes(), (shape.n_q, d))
-    _want(k, "k", q.dtype, (n_k, d))
-    _want(v, "v", q.dtype, (n_k, d))
     _want(a_full, "a_full", q.dtype, (shape.n_q, d))
     for n_, t in (("lse_loc", lse_loc), ("lse_hist", lse_hist)):
         _want(t, n_, torch.float32, (shape.n_heads, shape.n_q))
@@ -221,11 +219,60 @@ def dual_attn(shape: AttnShape, q, k, v, a_full=None, a_loc_t=None, delta_a_t=No
             ld_stat = lds[0]
         elif ld_stat != lds[0]:
             raise ValueError(f"ld_stat {ld_stat} differs from the statistics' row stride {lds[0]}")
-    st = _dtype_code(stat) if stat is not None else F16
+    return (_dtype_code(stat) if stat is not None else F16), int(ld_stat or 0)
+
+
+def dual_attn(shape: AttnShape, q, k, v, a_full=None, a_loc_t=None, delta_a_t=None, ld_stat: Optional[int] = None,
+              lse_loc=None, lse_hist=None, workspace=None, stream=None) -> None:
+    """ispa_dual_attn: see include/ispa.h.  Stat outputs are feature-major [d, ld_stat] views;
+    workspace (bytes from workspace_bytes(CALL_DUAL_ATTN, shape)) is needed for bf16/fp16 inputs."""
+    d = shape.n_heads * shape.head_dim
+    n_k = shape.n_sink + shape.n_hist + shape.n_cur
+    _want(q, "q", _io_dtypes(), (shape.n_q, d))
+    _want(k, "k", q.dtype, (n_k, d))
+    _want(v, "v", q.dtype, (n_k, d))
+    st, ld = _dual_outputs(shape, q, a_full, a_loc_t, delta_a_t, ld_stat, lse_loc, lse_hist)
     _same_device(q, k, v, a_full, a_loc_t, delta_a_t, lse_loc, lse_hist, workspace)
     _check(lib().ispa_dual_attn(ctypes.byref(shape), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(a_full), st,
-                                _ptr(a_loc_t), _ptr(delta_a_t), int(ld_stat or 0), _ptr(lse_loc), _ptr(lse_hist),
+                                _ptr(a_loc_t), _ptr(delta_a_t), ld, _ptr(lse_loc), _ptr(lse_hist),
                                 _ptr(workspace), _ws_bytes(workspace), _stream(stream)), "ispa_dual_attn")
+
+
+def dual_attn_vt(shape: AttnShape, q, k, vt, a_full=None, a_loc_t=None, delta_a_t=None,
+                 ld_stat: Optional[int] = None, lse_loc=None, lse_hist=None, workspace=None, stream=None) -> None:
+    """ispa_dual_attn_vt: V given as the caller's V^T, a [d, ldv] tensor (unit stride along rows of
+    the cache, ldv = its row stride) in fp16 for the dual stream or the input dtype for the single
+    stream.  Workspace (workspace_bytes(CALL_DUAL_ATTN_VT, shape)) only in dual mode."""
+    import torch
+    d = shape.n_heads * shape.head_dim
+    n_k = shape.n_sink + shape.n_hist + shape.n_cur
+    _want(q, "q", (torch.bfloat16, torch.float16), (shape.n_q, d))
+    _want(k, "k", q.dtype, (n_k, d))
+    _want(vt, "vt", (torch.bfloat16, torch.float16), contiguous=False)
+    ldv = _stat_view(vt, "vt", d, n_k)
+    st, ld = _dual_outputs(shape, q, a_full, a_loc_t, delta_a_t, ld_stat, lse_loc, lse_hist)
+    _same_device(q, k, vt, a_full, a_loc_t, delta_a_t, lse_loc, lse_hist, workspace)
+    _check(lib().ispa_dual_attn_vt(ctypes.byref(shape), _dtype_code(q), _ptr(q), _ptr(k), _dtype_code(vt), _ptr(vt),
+                                   int(ldv), _ptr(a_full), st, _ptr(a_loc_t), _ptr(delta_a_t), ld, _ptr(lse_loc),
+                                   _ptr(lse_hist), _ptr(workspace), _ws_bytes(workspace), _stream(stream)),
+           "ispa_dual_attn_vt")
+
+
+def transpose_rows(v, vt, col0: int, stream=None) -> None:
+    """ispa_transpose_rows: the rows of v [rows, d] (bf16/fp16) into columns [col0, col0 + rows) of
+    the V^T view vt [d, ldv] (fp16 or v's dtype, unit stride along columns), zeros after them."""
+    import torch
+    _want(v, "v", (torch.bfloat16, torch.float16))
+    if v.dim() != 2:
+        raise ValueError("v must be 2-D")
+    rows, d = v.shape
+    _want(vt, "vt", (torch.float16, v.dtype), contiguous=False)
+    ldv = _stat_view(vt, "vt", d, 0)
+    if col0 < 0 or col0 + rows > vt.shape[1]:
+        raise ValueError(f"columns [{col0}, {col0 + rows}) do not fit in vt of {vt.shape[1]} columns")
+    _same_device(v, vt)
+    _check(lib().ispa_transpose_rows(rows, d, _dtype_code(v), _ptr(v), _dtype_code(vt), _ptr(vt), int(ldv),
+                                     int(col0), _stream(stream)), "ispa_transpose_rows")
 
 
 def gram_accum(a_loc_t, delta_a_t, n: int, G, C, D=None, accumulate: bool = False, stream=None) -> None:

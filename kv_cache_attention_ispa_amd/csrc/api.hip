@@ -61,6 +61,9 @@ size_t dual_ws_bytes(const ispa_attn_shape* s) {
          attn_stash_bytes(s->n_q, s->n_heads);
 }
 
+// ispa_dual_attn_vt's workspace: only the dual stream's parked local outputs.
+size_t dual_vt_ws_bytes(const ispa_attn_shape* s, bool dual) { return dual ? attn_stash_bytes(s->n_q, s->n_heads) : 0; }
+
 // The 16-bit path addresses one head's 128 rows of the V^T copy with 32-bit byte offsets (K tiles get
 // descriptors of their own, so K has no such limit).
 bool fits_buffer(const ispa_attn_shape* s) {
@@ -91,6 +94,69 @@ void* noalloc_scratch() {
   return g_scratch_ptr[dev];
 }
 
+// ispa_dual_attn and ispa_dual_attn_vt: V row-major (v, copied to V^T in the workspace by the call)
+// or the caller's V^T (vt, ldv, in vt_dtype).
+int dual_attn_call(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k, const void* v,
+                   const void* vt, int64_t ldv, int vt_dtype, void* a_full, int stat_dtype, void* a_loc_t,
+                   void* delta_a_t, int64_t ld_stat, float* lse_loc, float* lse_hist, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if (!valid_dtype(io_dtype)) return ISPA_EUNSUPPORTED;
+  if (!q || !k || (!v && !vt)) return ISPA_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(vt) || !aligned16(a_full)) return ISPA_EINVAL;
+  const bool dual = a_loc_t || delta_a_t || lse_loc || lse_hist;
+  if (!dual && !a_full) return ISPA_EINVAL;
+  if (a_loc_t || delta_a_t) {
+    if (!valid_dtype(stat_dtype)) return ISPA_EUNSUPPORTED;
+    if (ld_stat < shape->n_q || ld_stat % 8 != 0) return ISPA_EINVAL;
+    if (!aligned16(a_loc_t) || !aligned16(delta_a_t)) return ISPA_EINVAL;
+  }
+  if (!aligned4(lse_loc) || !aligned4(lse_hist)) return ISPA_EINVAL;
+  if (io_dtype == ISPA_F32) {
+    if (vt) return ISPA_EUNSUPPORTED;
+    if ((a_loc_t || delta_a_t) && stat_dtype != ISPA_F32) return ISPA_EUNSUPPORTED;
+  } else {
+    if (shape->head_dim != 128 || !fits_buffer(shape)) return ISPA_EUNSUPPORTED;
+  }
+  const int64_t n_k = (int64_t)shape->n_sink + shape->n_hist + shape->n_cur;
+  if (vt) {
+    // the PV product's type: fp16 for the dual stream, the input type for the single stream
+    if (vt_dtype != (dual ? ISPA_F16 : io_dtype)) return ISPA_EINVAL;
+    if (ldv < n_k || ldv % 8 != 0) return ISPA_EINVAL;
+    if (128 * ldv * 2 >= INT32_MAX) return ISPA_EUNSUPPORTED;
+  }
+  AttnLaunch L;
+  L.mode = dual ? 0 : 1;
+  L.io = io_dtype;
+  L.stat = stat_dtype;
+  L.q = q;
+  L.k = k;
+  L.v = v;
+  L.vt = vt;
+  L.ldv = ldv;
+  L.a_full = a_full;
+  L.a_loc_t = a_loc_t;
+  L.delta_a_t = delta_a_t;
+  L.ld_stat = ld_stat;
+  L.lse_loc = lse_loc;
+  L.lse_hist = lse_hist;
+  L.n_q = shape->n_q;
+  L.n_sink = shape->n_sink;
+  L.n_hist = shape->n_hist;
+  L.n_cur = shape->n_cur;
+  L.n_heads = shape->n_heads;
+  L.head_dim = shape->head_dim;
+  L.scale = eff_scale(shape);
+  L.ws = workspace;
+  L.ws_bytes = workspace_bytes;
+  if (io_dtype != ISPA_F32) {
+    const size_t need = vt ? dual_vt_ws_bytes(shape, dual) : dual_ws_bytes(shape);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return ISPA_EWORKSPACE;
+  }
+  return hip_status(launch_attention(L, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -113,6 +179,9 @@ size_t ispa_workspace_bytes(int call_id, const ispa_attn_shape* shape, int d) {
     case ISPA_CALL_DUAL_ATTN:
       if (!shape || shape->n_heads < 1) return 0;
       return dual_ws_bytes(shape);
+    case ISPA_CALL_DUAL_ATTN_VT:
+      if (!shape || shape->n_heads < 1) return 0;
+      return dual_vt_ws_bytes(shape, true);
     case ISPA_CALL_ABSORB_SOLVE: return d > 0 ? solve_workspace_bytes(d) : 0;
     case ISPA_CALL_LOCAL_ATTN_PROJ:
       if (!shape || shape->n_q < 1 || shape->n_heads < 1) return 0;
@@ -137,50 +206,29 @@ size_t ispa_workspace_bytes(int call_id, const ispa_attn_shape* shape, int d) {
 int ispa_dual_attn(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k, const void* v,
                    void* a_full, int stat_dtype, void* a_loc_t, void* delta_a_t, int64_t ld_stat, float* lse_loc,
                    float* lse_hist, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_shape(shape);
-  if (st) return st;
-  if (!valid_dtype(io_dtype)) return ISPA_EUNSUPPORTED;
-  if (!q || !k || !v) return ISPA_EINVAL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(a_full)) return ISPA_EINVAL;
-  const bool dual = a_loc_t || delta_a_t || lse_loc || lse_hist;
-  if (!dual && !a_full) return ISPA_EINVAL;
-  if (a_loc_t || delta_a_t) {
-    if (!valid_dtype(stat_dtype)) return ISPA_EUNSUPPORTED;
-    if (ld_stat < shape->n_q || ld_stat % 8 != 0) return ISPA_EINVAL;
-    if (!aligned16(a_loc_t) || !aligned16(delta_a_t)) return ISPA_EINVAL;
-  }
-  if (!aligned4(lse_loc) || !aligned4(lse_hist)) return ISPA_EINVAL;
-  if (io_dtype == ISPA_F32) {
-    if ((a_loc_t || delta_a_t) && stat_dtype != ISPA_F32) return ISPA_EUNSUPPORTED;
-  } else {
-    if (shape->head_dim != 128 || !fits_buffer(shape)) return ISPA_EUNSUPPORTED;
-  }
-  AttnLaunch L;
-  L.mode = dual ? 0 : 1;
-  L.io = io_dtype;
-  L.stat = stat_dtype;
-  L.q = q;
-  L.k = k;
-  L.v = v;
-  L.a_full = a_full;
-  L.a_loc_t = a_loc_t;
-  L.delta_a_t = delta_a_t;
-  L.ld_stat = ld_stat;
-  L.lse_loc = lse_loc;
-  L.lse_hist = lse_hist;
-  L.n_q = shape->n_q;
-  L.n_sink = shape->n_sink;
-  L.n_hist = shape->n_hist;
-  L.n_cur = shape->n_cur;
-  L.n_heads = shape->n_heads;
-  L.head_dim = shape->head_dim;
-  L.scale = eff_scale(shape);
-  L.ws = workspace;
-  L.ws_bytes = workspace_bytes;
-  if (io_dtype != ISPA_F32) {
-    if (!workspace || workspace_bytes < dual_ws_bytes(shape) || !aligned16(workspace)) return ISPA_EWORKSPACE;
-  }
-  return hip_status(launch_attention(L, (hipStream_t)stream));
+  return dual_attn_call(shape, io_dtype, q, k, v, nullptr, 0, 0, a_full, stat_dtype, a_loc_t, delta_a_t, ld_stat,
+                        lse_loc, lse_hist, workspace, workspace_bytes, stream);
+}
+
+int ispa_dual_attn_vt(const ispa_attn_shape* shape, int io_dtype, const void* q, const void* k, int vt_dtype,
+                      const void* vt, int64_t ldv, void* a_full, int stat_dtype, void* a_loc_t, void* delta_a_t,
+                      int64_t ld_stat, float* lse_loc, float* lse_hist, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!vt) return ISPA_EINVAL;
+  return dual_attn_call(shape, io_dtype, q, k, nullptr, vt, ldv, vt_dtype, a_full, stat_dtype, a_loc_t, delta_a_t,
+                        ld_stat, lse_loc, lse_hist, workspace, workspace_bytes, stream);
+}
+
+int ispa_transpose_rows(int rows, int d, int v_dtype, const void* v, int vt_dtype, void* vt, int64_t ldv,
+                        int64_t col0, void* stream) {
+  if (rows < 0 || d < 64 || d % 64 != 0 || d > 65536) return ISPA_EINVAL;
+  if (v_dtype != ISPA_BF16 && v_dtype != ISPA_F16) return ISPA_EUNSUPPORTED;
+  if (vt_dtype != ISPA_F16 && vt_dtype != v_dtype) return ISPA_EUNSUPPORTED;
+  if ((rows > 0 && !v) || !vt || !aligned16(v) || !aligned16(vt)) return ISPA_EINVAL;
+  if (col0 < 0 || col0 % 8 != 0 || ldv % 8 != 0 || col0 + rows > ldv) return ISPA_EINVAL;
+  if (ldv - col0 > (int64_t)64 * 65536 * 64) return ISPA_EUNSUPPORTED;
+  return hip_status(launch_transpose_rows(v, rows, d, v_dtype == ISPA_BF16 && vt_dtype == ISPA_F16, vt, ldv, col0,
+                                          (hipStream_t)stream));
 }
 
 int ispa_gram_accum(int d, int n, int stat_dtype, const void* a_loc_t, const void* delta_a_t, int64_t ld,

@@ -789,14 +789,15 @@ AttnParams make_params(const AttnLaunch& L) {
   return p;
 }
 
-// V^T copy for the 16-bit path: vt[c, key] = v[key, c] for c < d, key < n_k; keys [n_k, ldv) are
-// zero, so every V^T tile the attention kernel streams is finite.  With CONVERT the values go from
-// bf16 to fp16 (exact for |v| < 65504), for the fp16 PV product of the statistics path.  One
-// work-group transposes a 64-key x 64-column block through LDS; global reads and writes are
-// 16 bytes per lane along rows.
+// V^T copy for the 16-bit path: vt[c, key] = v[key, c] for c < d, key < n_k, and zero for the keys
+// [n_k, 64 * gridDim.x) below n_cols (the attention kernel streams up to 63 keys past a segment's
+// last row, masked, so they must be finite).  vt points at the first column written, ldv is its row
+// pitch.  With CONVERT the values go from bf16 to fp16 (exact for 2^-17 <= |v| <= 65504), for the
+// fp16 PV product of the dual stream.  One work-group transposes a 64-key x 64-column block through
+// LDS; global reads and writes are 16 bytes per lane along rows.
 template <bool CONVERT>
 __global__ __launch_bounds__(256) void vt_kernel(const uint16_t* __restrict__ v, uint16_t* __restrict__ vt, int n_k,
-                                                 int d, int ldv) {
+                                                 int d, int64_t ldv, int64_t n_cols) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];   // [key][column]
   const int key0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const int r = threadIdx.x >> 3, ch = threadIdx.x & 7;
@@ -813,6 +814,7 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint16_t* __restrict__ v,
     *(u32x4*)&tile[r + 32 * pass][8 * ch] = x;
   }
   __syncthreads();
+  if (key0 + 8 * ch >= n_cols) return;   // n_cols is a multiple of 8: whole 16-byte chunks
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int c = r + 32 * pass;
@@ -840,19 +842,26 @@ template <typename T, int MODE>
 hipError_t launch_mfma_mode(AttnParams p, const AttnLaunch& L, hipStream_t s) {
   p.n_qblk = (p.n_q + BM - 1) / BM;
   const int n_k = L.n_sink + L.n_hist + L.n_cur;
-  p.ldv = (int)attn_vt_ld(n_k);
-  p.vt = (const uint16_t*)L.ws;
-  p.stash = (char*)L.ws + attn_vt_bytes_aligned(n_k, p.d);
-  const dim3 tgrid(p.ldv / 64, p.d / 64);
-  // statistics requested in fp16 from bf16 inputs: P and V in fp16 for the PV product
-  const bool f16_values = attn_needs_f16_values(L);
-  if (f16_values)
-    hipLaunchKernelGGL(vt_kernel<true>, tgrid, dim3(256), 0, s, (const uint16_t*)L.v, (uint16_t*)L.ws, n_k, p.d, p.ldv);
-  else
-    hipLaunchKernelGGL(vt_kernel<false>, tgrid, dim3(256), 0, s, (const uint16_t*)L.v, (uint16_t*)L.ws, n_k, p.d,
-                       p.ldv);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (L.vt) {
+    // the caller's V^T, already in the PV product's type
+    p.ldv = (int)L.ldv;
+    p.vt = (const uint16_t*)L.vt;
+    p.stash = L.ws;
+  } else {
+    p.ldv = (int)attn_vt_ld(n_k);
+    p.vt = (const uint16_t*)L.ws;
+    p.stash = (char*)L.ws + attn_vt_bytes_aligned(n_k, p.d);
+    const dim3 tgrid(p.ldv / 64, p.d / 64);
+    // bf16 inputs of the dual stream: P and V in fp16 for the PV product
+    if (attn_needs_f16_values(L))
+      hipLaunchKernelGGL(vt_kernel<true>, tgrid, dim3(256), 0, s, (const uint16_t*)L.v, (uint16_t*)L.ws, n_k, p.d,
+                         (int64_t)p.ldv, (int64_t)p.ldv);
+    else
+      hipLaunchKernelGGL(vt_kernel<false>, tgrid, dim3(256), 0, s, (const uint16_t*)L.v, (uint16_t*)L.ws, n_k, p.d,
+                         (int64_t)p.ldv, (int64_t)p.ldv);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   // the dual stream's PV product always runs on fp16 probabilities (with an fp16 V^T copy from bf16
   // inputs); the single streams keep the input type
   if constexpr (MODE == 0)
@@ -870,6 +879,21 @@ hipError_t launch_f32_mode(AttnParams p, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_transpose_rows(const void* v, int rows, int d, bool convert, void* vt, int64_t ldv, int64_t col0,
+                                 hipStream_t s) {
+  const int64_t n_cols = ldv - col0;
+  const int64_t span = ((int64_t)rows + 63) / 64 * 64 + 64;   // the rows, then at least 64 zero columns
+  const int64_t cover = span < n_cols ? span : (n_cols + 63) / 64 * 64;
+  if (cover == 0) return hipSuccess;   // col0 == ldv: no column to write
+  const dim3 grid((unsigned)(cover / 64), (unsigned)(d / 64));
+  uint16_t* dst = (uint16_t*)vt + col0;
+  if (convert)
+    hipLaunchKernelGGL(vt_kernel<true>, grid, dim3(256), 0, s, (const uint16_t*)v, dst, rows, d, ldv, n_cols);
+  else
+    hipLaunchKernelGGL(vt_kernel<false>, grid, dim3(256), 0, s, (const uint16_t*)v, dst, rows, d, ldv, n_cols);
+  return hipGetLastError();
+}
 
 hipError_t launch_attention(const AttnLaunch& L, hipStream_t s) {
   AttnParams p = make_params(L);

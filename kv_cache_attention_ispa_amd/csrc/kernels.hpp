@@ -25,6 +25,10 @@ struct AttnLaunch {
   float scale;
   void* ws;          // device workspace (16-bit inputs: the transposed copy of V, see attn_vt_bytes)
   size_t ws_bytes;
+  // 16-bit path: a V^T [d, ldv] the caller keeps (in the PV product's type; columns [n_k, n_k + 64)
+  // finite).  When set, no copy is made and the workspace holds only the parked local outputs.
+  const void* vt = nullptr;
+  int64_t ldv = 0;
 };
 // The 16-bit (MFMA) path streams V from a transposed copy V^T [d, ldv] (ldv = n_k rounded up to
 // 64 keys, pad keys zero) that the call writes into the workspace first.
@@ -43,6 +47,11 @@ inline size_t attn_stash_bytes(int64_t n_q, int64_t n_heads) {
 // ones), whatever the statistics' dtype.
 inline bool attn_needs_f16_values(const AttnLaunch& L) { return L.mode == 0 && L.io == DT_BF16; }
 hipError_t launch_attention(const AttnLaunch& L, hipStream_t s);
+// V rows [rows, d] (16-bit) into columns [col0, col0 + rows) of V^T [d, ldv] (dst[c * ldv + col0 + r]),
+// converted from bf16 to fp16 when `convert`; the following 64..127 columns (up to ldv) are set to
+// zero.  d % 64 == 0; col0 and ldv multiples of 8.
+hipError_t launch_transpose_rows(const void* v, int rows, int d, bool convert, void* vt, int64_t ldv, int64_t col0,
+                                 hipStream_t s);
 // FP8 attention over the local rows (sink + current chunk; history rows are not read) into L.a_full
 // (io dtype), with the codes and scales of those rows of K and V written into L.ws first
 // (attn_fp8_workspace_bytes of n_sink + n_cur rows).

@@ -19,9 +19,10 @@ from __future__ import annotations
 
 from typing import List, Optional, Sequence, Tuple
 
-from . import (AttnShape, CALL_ABSORB_SOLVE, CALL_DUAL_ATTN, CALL_LOCAL_ATTN_FP8_PROJ_W8A8, CALL_LOCAL_ATTN_PROJ,
-               IspaError, KVCache, absorb_solve_batched, dual_attn, gram_accum, local_attn_fp8_proj_w8a8,
-               local_attn_fused_proj_wt, quantize_weight_fp8, select_layers, transpose16, workspace_bytes)
+from . import (AttnShape, CALL_ABSORB_SOLVE, CALL_DUAL_ATTN, CALL_DUAL_ATTN_VT, CALL_LOCAL_ATTN_FP8_PROJ_W8A8,
+               CALL_LOCAL_ATTN_PROJ, IspaError, KVCache, absorb_solve_batched, dual_attn, dual_attn_vt, gram_accum,
+               local_attn_fp8_proj_w8a8, local_attn_fused_proj_wt, quantize_weight_fp8, select_layers, transpose16,
+               transpose_rows, workspace_bytes)
 
 WARMUP, STEADY = "warmup", "steady"
 L_LAYER_KINDS = ("bf16", "w8a8_fp8")
@@ -42,6 +43,13 @@ class IspaRuntime:
     transposed once at the fold) or "w8a8_fp8" (the method combined with W8A8: W_new coded once to
     FP8 E4M3 per output channel at the fold; FP8 attention, per-token activation codes and the FP8
     product per step).
+    During the warmup each layer also keeps V^T in fp16 (the dual stream's PV type) for the rows the
+    warmup can hold, so a chunk's V rows are transposed once, when appended, instead of the whole
+    cache on every call (when sink_rows and chunk_rows are multiples of 8, which the V^T columns'
+    16-byte alignment needs; otherwise each call copies).  These buffers are freed at the
+    transition; the layers that keep full attention then grow their cache for the rest of the
+    rollout, and each of their calls transposes it (a V^T of the whole rollout would be committed
+    up front, while the cache's memory follows the rows it holds).
     """
 
     def __init__(self, n_layers: int, n_heads: int, head_dim: int, sink_rows: int, chunk_rows: int,
@@ -89,8 +97,20 @@ class IspaRuntime:
         self.w_new_t = [None] * n_layers   # W_new^T of the converted layers, transposed once at the fold
         self.w_codes = [None] * n_layers   # ("w8a8_fp8") their FP8 codes W_new^T and per-channel scales
         self.delta_w = None
+        self.vt_resident = (sink_rows % 8 == 0 and chunk_rows % 8 == 0
+                            and self.dtype in (torch.bfloat16, torch.float16))
+        self.ldv_warm = (sink_rows + warmup_chunks * chunk_rows + 7) // 8 * 8 + 64
+        self.vt: List[Optional[object]] = [None] * n_layers
 
     # ------------------------------------------------------------------ helpers
+    def _vt(self, layer: int):
+        """The layer's warmup V^T [d, ldv_warm] (fp16), made on first use."""
+        if self.vt[layer] is None:
+            self.vt[layer] = self._buf(self.d, self.ldv_warm, dtype=self.torch.float16)
+            with self.torch.cuda.stream(self.stream):
+                self.vt[layer].zero_()
+        return self.vt[layer]
+
     def _shape(self, layer: int, n_q: int) -> Tuple[AttnShape, object, object]:
         k, v, (n_s, n_h, n_c) = self.kv.layer(layer)
         return AttnShape(n_q, n_s, n_h, n_c, self.n_heads, self.head_dim, 0.0), k, v
@@ -107,6 +127,8 @@ class IspaRuntime:
     # ------------------------------------------------------------------ stages
     def write_sink(self, layer: int, k, v) -> None:
         self.kv.write_sink(layer, k, v, stream=self.stream)
+        if self.vt_resident and self.stage == WARMUP:
+            transpose_rows(v, self._vt(layer), 0, stream=self.stream)
 
     def forward(self, layer: int, q, k, v):
         """Append this chunk's K/V to the layer's cache and run the layer's attention for the stage."""
@@ -114,14 +136,21 @@ class IspaRuntime:
         if self.stage == WARMUP and self.chunks[layer] >= self.warmup_chunks:
             raise RuntimeError(f"layer {layer}: warmup chunks done; call transition() first")
         self.kv.append_chunk(layer, k, v, stream=self.stream)
+        if self.stage == WARMUP and self.vt_resident:
+            transpose_rows(v, self._vt(layer), self.sink_rows + self.chunks[layer] * self.chunk_rows,
+                           stream=self.stream)
         self.chunks[layer] += 1
         shape, kc, vc = self._shape(layer, q.shape[0])
         out = self._buf(shape.n_q, self.d, dtype=self.dtype)
         if self.stage == WARMUP:
             if shape.n_q > self.chunk_rows:
                 raise ValueError("a warmup chunk has at most chunk_rows queries")
-            dual_attn(shape, q, kc, vc, a_full=out, a_loc_t=self.a_t, delta_a_t=self.da_t, ld_stat=self.ld,
-                      workspace=self._ws(CALL_DUAL_ATTN, shape), stream=self.stream)
+            if self.vt_resident:
+                dual_attn_vt(shape, q, kc, self._vt(layer), a_full=out, a_loc_t=self.a_t, delta_a_t=self.da_t,
+                             ld_stat=self.ld, workspace=self._ws(CALL_DUAL_ATTN_VT, shape), stream=self.stream)
+            else:
+                dual_attn(shape, q, kc, vc, a_full=out, a_loc_t=self.a_t, delta_a_t=self.da_t, ld_stat=self.ld,
+                          workspace=self._ws(CALL_DUAL_ATTN, shape), stream=self.stream)
             gram_accum(self.a_t, self.da_t, shape.n_q, self.G[layer], self.C[layer], self.D[layer],
                        accumulate=self.started[layer], stream=self.stream)
             self.started[layer] = True
@@ -180,6 +209,7 @@ class IspaRuntime:
             else:
                 self.w_new[layer] = None
         self.G = self.C = self.D = None
+        self.vt = [None] * n
         if not self.keep_delta_w:
             self.delta_w = None
         self.stage = STEADY

@@ -159,6 +159,45 @@ def test_transpose16_validation(L):
     assert t(src=FAKE + 2) == EINVAL               # alignment
 
 
+def _dual_vt(L, shape, io=1, vt_dtype=2, vt=FAKE, ldv=None, a_loc=FAKE, ws=None, wsb=0):
+    ldv = shape.n_sink + shape.n_hist + shape.n_cur if ldv is None else ldv
+    return L.ispa_dual_attn_vt(ctypes.byref(shape), io, FAKE, FAKE, vt_dtype, vt, ldv, FAKE, 2, a_loc, a_loc,
+                               shape.n_q, FAKE if a_loc else None, FAKE if a_loc else None, ws, wsb, None)
+
+
+def test_dual_attn_vt_validation(L):
+    s = ispa.AttnShape(64, 8, 16, 64, 2, 128, 0.0)
+    need = ispa.workspace_bytes(ispa.CALL_DUAL_ATTN_VT, s)
+    # only the parked local outputs: no room for a V^T copy
+    assert 0 < need < ispa.workspace_bytes(ispa.CALL_DUAL_ATTN, s)
+    assert need == 256 * 128 * 4 * 2                 # one 256-query block per head
+    assert _dual_vt(L, s) == EWORKSPACE              # every other argument accepted
+    assert _dual_vt(L, s, ws=FAKE, wsb=need - 16) == EWORKSPACE
+    assert _dual_vt(L, s, vt=0) == EINVAL            # NULL V^T
+    assert _dual_vt(L, s, vt=FAKE + 8) == EINVAL     # misaligned V^T
+    assert _dual_vt(L, s, vt_dtype=1) == EINVAL      # the dual stream's PV product is fp16
+    assert _dual_vt(L, s, ldv=87) == EINVAL          # ldv < n_k
+    assert _dual_vt(L, s, ldv=92) == EINVAL          # ldv not a multiple of 8
+    assert _dual_vt(L, s, ldv=96) == EWORKSPACE      # ldv > n_k is fine
+    assert _dual_vt(L, s, ldv=8388600) == EWORKSPACE
+    assert _dual_vt(L, s, ldv=8388608) == EUNSUPPORTED   # 128 rows of V^T reach 2^31 bytes
+    assert _dual_vt(L, s, io=0, vt_dtype=0) == EUNSUPPORTED   # no fp32 variant
+    # single stream: V^T in the input type (bf16 here); fp16 is rejected before any launch
+    assert _dual_vt(L, s, vt_dtype=2, a_loc=0) == EINVAL
+    s64 = ispa.AttnShape(64, 8, 16, 64, 2, 64, 0.0)
+    assert _dual_vt(L, s64) == EUNSUPPORTED
+
+
+def test_transpose_rows_validation(L):
+    t = lambda rows=100, d=128, vd=1, v=FAKE, td=2, vt=FAKE + 65536, ldv=256, col0=8: L.ispa_transpose_rows(
+        rows, d, vd, v, td, vt, ldv, col0, None)
+    assert t(vd=0) == EUNSUPPORTED                  # fp32 rows
+    assert t(vd=2, td=1) == EUNSUPPORTED            # fp16 -> bf16 is not offered
+    for kw in (dict(d=96), dict(d=0), dict(rows=-1), dict(col0=4), dict(ldv=252), dict(col0=160),
+               dict(v=0), dict(vt=0), dict(v=FAKE + 2), dict(col0=-8)):
+        assert t(**kw) == EINVAL, kw
+
+
 def test_kv_cache_rejects_bad_arguments_without_allocating(L):
     """ispa_kv_*: invalid sizes, dtypes and NULL handles fail on the host before any HIP call."""
     h = ctypes.c_void_p(FAKE)
