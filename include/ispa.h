@@ -19,9 +19,10 @@
  *    never frees them and never keeps them after the call returns.
  *  * Every call only enqueues work on `stream` (a hipStream_t, 0 = the null
  *    stream) and returns without synchronising.  Outputs are ready when the
- *    stream reaches that point.  The solves (ispa_absorb_solve, _batched) fork
- *    the part that the factorisation does not read to an auxiliary stream of
- *    the current device (owned by the library, created on first use, default
+ *    stream reaches that point.  The solves that factorise panel by panel
+ *    (ispa_absorb_solve_batched, and ispa_absorb_solve for d > 2048) fork the
+ *    part that the factorisation does not read to an auxiliary stream of the
+ *    current device (owned by the library, created on first use, default
  *    priority) and join it back onto `stream` by events before they return,
  *    so under graph capture it joins the capture.
  *  * Dense row-major layouts.  Token tensors are [tokens, d] with heads as
@@ -215,6 +216,14 @@ int ispa_gram_accum(int d, int n, int stat_dtype, const void* a_loc_t, const voi
  *   info   device int out (required): 0 on success; k > 0 when the leading
  *          minor of order k of G + lambda I is not positive definite (LAPACK
  *          potrf convention); then delta_w, w_new and eps are undefined.
+ *          -2: a wait inside the one-launch factorisation (one layer,
+ *          d <= 2048) timed out, which needs the device to be held by other
+ *          work for about a second; the outputs are then undefined.
+ *   Execution: for one layer with d <= 2048 the factorisation runs as one
+ *   launch whose work-groups exchange blocks through device memory and
+ *   version flags (each work-group takes a CU; work-group 0 carries the
+ *   chain of diagonal blocks); otherwise, and for every batched call, as one
+ *   launch per 64-wide panel.  Both give the same results bit for bit.
  *   workspace: at least ispa_workspace_bytes(ISPA_CALL_ABSORB_SOLVE, NULL, d) bytes.
  *   d % 32 == 0, 32 <= d <= 16384.
  */

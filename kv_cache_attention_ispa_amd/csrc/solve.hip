@@ -18,6 +18,7 @@
 //
 // Every step is a HIP kernel enqueued on the caller's stream; the host never
 // waits.  A non-positive pivot sets *info to its 1-based index.
+#include <algorithm>
 #include <mutex>
 
 #include "common.hpp"
@@ -239,18 +240,28 @@ struct Scalars {
   double dots[8];
 };
 
-// Mx = G (lambda joins the diagonal blocks as the sweep factors them); Bx = I (becomes L^-1);
-// Wf = W as fp32.
+// Wf = W as fp32.  Per-panel launches (state == nullptr): Mx = G (lambda joins the diagonal blocks as
+// the sweep factors them) and Bx = I (becomes L^-1).  One-launch sweep: the sweep reads G itself and
+// starts the identity part implicitly; its state and block versions (n_state ints) and *info are
+// cleared instead.
 template <typename WT>
 __global__ __launch_bounds__(NT) void setup_kernel(const float* G, const typename WT::storage* W, int d, float* Mx,
-                                                   float* Bx, float* Wf, Steps st) {
+                                                   float* Bx, float* Wf, Steps st, int* state, int n_state,
+                                                   int* info) {
   G = at_layer(G, st.mat);
   W = at_layer(W, st.wmat);
   Mx = at_layer(Mx, st.ws);
   Bx = at_layer(Bx, st.ws);
   Wf = at_layer(Wf, st.ws);
   const int64_t n = (int64_t)d * d;
-  for (int64_t e = blockIdx.x * (int64_t)NT + threadIdx.x; e < n; e += (int64_t)gridDim.x * NT) {
+  const int64_t g0 = blockIdx.x * (int64_t)NT + threadIdx.x, gs = (int64_t)gridDim.x * NT;
+  if (state) {
+    for (int64_t e = g0; e < n_state; e += gs) state[e] = 0;
+    if (g0 == 0) *info = 0;
+    for (int64_t e = g0; e < n; e += gs) Wf[e] = Cvt<WT>::to_f(W[e]);
+    return;
+  }
+  for (int64_t e = g0; e < n; e += gs) {
     const int i = (int)(e / d), j = (int)(e % d);
     Mx[e] = G[e];
     Bx[e] = (i == j) ? 1.f : 0.f;
@@ -402,29 +413,28 @@ __global__ __launch_bounds__(256) void split_kernel(const float* __restrict__ C,
   }
 }
 
-// Work-group: one 64 x 64 output block (R blocks first, then P's lower blocks), 4 waves of 32 x 32;
-// K steps of 32 pass through registers, one step ahead, into LDS (every part of both operands).
+// One 64 x 64 output block q (R blocks first, then P's lower blocks), computed by the first 256
+// threads as 4 waves of 32 x 32 (every thread of the work-group takes part in the barriers); K steps
+// of 32 pass through registers, one step ahead, into LDS (every part of both operands).
 template <int WPARTS>
-__global__ __launch_bounds__(256) void rp_kernel(const uint16_t* __restrict__ sp, float* __restrict__ R,
-                                                 float* __restrict__ P, int d, int n_r, Steps st) {
-  sp = at_layer(sp, st.ws);
-  R = at_layer(R, st.ws);
-  P = at_layer(P, st.ws);
+__device__ __forceinline__ void rp_tile(const uint16_t* __restrict__ sp, float* __restrict__ R, float* __restrict__ P,
+                                        int d, int n_r, int q, uint16_t (*As)[64][RP_PITCH],
+                                        uint16_t (*Bs)[64][RP_PITCH]) {
   const int64_t dd = (int64_t)d * d;
-  __shared__ __attribute__((aligned(16))) uint16_t As[3][64][RP_PITCH], Bs[WPARTS][64][RP_PITCH];
   const int nT = (d + 63) / 64, t = threadIdx.x;
-  const bool is_p = (int)blockIdx.x >= n_r;
+  const bool on = t < 256;
+  const bool is_p = q >= n_r;
   int bi, bj;
   if (is_p) {
-    tri_decode(blockIdx.x - n_r, bi, bj);
+    tri_decode(q - n_r, bi, bj);
   } else {
-    bi = blockIdx.x / nT;
-    bj = blockIdx.x % nT;
+    bi = q / nT;
+    bj = q % nT;
   }
   const int a_parts = is_p ? WPARTS : 3;
   const uint16_t* A = sp + (is_p ? 3 * dd : 0) + (int64_t)64 * bi * d;        // W or C rows of block bi
   const uint16_t* B = sp + (is_p ? 3 * dd : 6 * dd) + (int64_t)64 * bj * d;   // W or W^T rows of block bj
-  const int lr = t >> 2, lk = 8 * (t & 3);
+  const int lr = (t & 255) >> 2, lk = 8 * (t & 3);
   const bool a_in = 64 * bi + lr < d, b_in = 64 * bj + lr < d;
   u32x4 ra[3], rb[WPARTS];
   auto load = [&](int k0) {
@@ -435,18 +445,21 @@ __global__ __launch_bounds__(256) void rp_kernel(const uint16_t* __restrict__ sp
 #pragma unroll
     for (int j = 0; j < WPARTS; ++j) rb[j] = b_in ? *(const u32x4*)(B + j * dd + o) : u32x4{0u, 0u, 0u, 0u};
   };
-  const int lane = t & 63, wave = t >> 6, wm = wave >> 1, wn = wave & 1;
+  const int lane = t & 63, wave = (t & 255) >> 6, wm = wave >> 1, wn = wave & 1;
   const int mrow = 32 * wm + (lane & 31), nrow = 32 * wn + (lane & 31), kk = 8 * (lane >> 5);
   f32x16 acc = {};
-  load(0);
+  if (on) load(0);
   for (int k0 = 0; k0 < d; k0 += RP_K) {
     __syncthreads();
+    if (on) {
 #pragma unroll
-    for (int i = 0; i < 3; ++i)
-      if (i < a_parts) *(u32x4*)&As[i][lr][lk] = ra[i];
+      for (int i = 0; i < 3; ++i)
+        if (i < a_parts) *(u32x4*)&As[i][lr][lk] = ra[i];
 #pragma unroll
-    for (int j = 0; j < WPARTS; ++j) *(u32x4*)&Bs[j][lr][lk] = rb[j];
+      for (int j = 0; j < WPARTS; ++j) *(u32x4*)&Bs[j][lr][lk] = rb[j];
+    }
     __syncthreads();
+    if (!on) continue;
     if (k0 + RP_K < d) load(k0 + RP_K);
 #pragma unroll
     for (int s = 0; s < RP_K; s += 16) {
@@ -468,7 +481,7 @@ __global__ __launch_bounds__(256) void rp_kernel(const uint16_t* __restrict__ sp
   }
   float* out = is_p ? P : R;
   const int col = 64 * bj + 32 * wn + (lane & 31);
-  if (col < d) {
+  if (on && col < d) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 64 * bi + 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -477,27 +490,74 @@ __global__ __launch_bounds__(256) void rp_kernel(const uint16_t* __restrict__ sp
   }
 }
 
-// Quadrant (wave / 4, wave % 4) of X op(Y) over k < 64 (op(Y) = Y^T when ty): 16x16x4 MFMA,
-// register r of lane l holds row 4 (l / 16) + r, column l % 16 of the quadrant.
-__device__ __forceinline__ f32x4 sw_mm(const float (*X)[BP], const float (*Y)[BP], bool ty) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m0 = (wave >> 2) * 16, n0 = (wave & 3) * 16;
-  const int a = lane & 15, kk = lane >> 4;
+template <int WPARTS>
+__global__ __launch_bounds__(256) void rp_kernel(const uint16_t* __restrict__ sp, float* __restrict__ R,
+                                                 float* __restrict__ P, int d, int n_r, Steps st) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[3][64][RP_PITCH], Bs[WPARTS][64][RP_PITCH];
+  rp_tile<WPARTS>(at_layer(sp, st.ws), at_layer(R, st.ws), at_layer(P, st.ws), d, n_r, blockIdx.x, As, Bs);
+}
+
+// Quadrant qd (rows 16 (qd / 4) .., columns 16 (qd % 4) ..) of X op(Y) over k < 64 (op(Y) = Y^T when
+// ty): 16x16x4 MFMA, register r of lane l holds row 4 (l / 16) + r, column l % 16 of the quadrant.
+// MFMA step s sums k = s, 16 + s, 32 + s, 48 + s (lane group g = l / 16 supplies k = 16 g + s), so a
+// lane's sixteen X values (and Y values when ty) are one contiguous row piece: four 16-byte reads.
+// sw_mm / sw_put take the quadrant of the calling wave (16 waves cover the block).
+__device__ __forceinline__ f32x4 sw_mm_q(const float (*X)[BP], const float (*Y)[BP], bool ty, int qd) {
+  const int lane = threadIdx.x & 63;
+  const int m0 = (qd >> 2) * 16, n0 = (qd & 3) * 16;
+  const int a = lane & 15, k0 = 16 * (lane >> 4);
+  f32x4 xv[4], yv[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    xv[u] = *(const f32x4*)&X[m0 + a][k0 + 4 * u];
+    if (ty) {
+      yv[u] = *(const f32x4*)&Y[n0 + a][k0 + 4 * u];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) yv[u][e] = Y[k0 + 4 * u + e][n0 + a];
+    }
+  }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s4 = 0; s4 < NB; s4 += 4) {
-    const float x = X[m0 + a][s4 + kk];
-    const float y = ty ? Y[n0 + a][s4 + kk] : Y[s4 + kk][n0 + a];
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, acc, 0, 0, 0);
-  }
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[u][e], yv[u][e], acc, 0, 0, 0);
   return acc;
 }
-__device__ __forceinline__ void sw_put(float (*dst)[BP], f32x4 v) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m0 = (wave >> 2) * 16 + 4 * (lane >> 4), n = (wave & 3) * 16 + (lane & 15);
+// Half h of sw_mm_q's MFMA steps (s = 8 h .. 8 h + 7) added to acc: the two halves in order give
+// sw_mm_q's result bit for bit.
+__device__ __forceinline__ f32x4 sw_mm_q_half(const float (*X)[BP], const float (*Y)[BP], bool ty, int qd, int h,
+                                              f32x4 acc) {
+  const int lane = threadIdx.x & 63;
+  const int m0 = (qd >> 2) * 16, n0 = (qd & 3) * 16;
+  const int a = lane & 15, k0 = 16 * (lane >> 4) + 8 * h;
+  f32x4 xv[2], yv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    xv[u] = *(const f32x4*)&X[m0 + a][k0 + 4 * u];
+    if (ty) {
+      yv[u] = *(const f32x4*)&Y[n0 + a][k0 + 4 * u];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) yv[u][e] = Y[k0 + 4 * u + e][n0 + a];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[u][e], yv[u][e], acc, 0, 0, 0);
+  return acc;
+}
+__device__ __forceinline__ f32x4 sw_mm(const float (*X)[BP], const float (*Y)[BP], bool ty) {
+  return sw_mm_q(X, Y, ty, threadIdx.x >> 6);
+}
+__device__ __forceinline__ void sw_put_q(float (*dst)[BP], f32x4 v, int qd) {
+  const int lane = threadIdx.x & 63;
+  const int m0 = (qd >> 2) * 16 + 4 * (lane >> 4), n = (qd & 3) * 16 + (lane & 15);
 #pragma unroll
   for (int r = 0; r < 4; ++r) dst[m0 + r][n] = v[r];
 }
+__device__ __forceinline__ void sw_put(float (*dst)[BP], f32x4 v) { sw_put_q(dst, v, threadIdx.x >> 6); }
 // global block (rb, cb) of a d x d matrix: C = beta C + v (beta 0 or 1)
 __device__ __forceinline__ void sw_store(float* C, int d, int rb, int cb, f32x4 v, bool accumulate) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -524,9 +584,15 @@ __device__ __forceinline__ void sw_store(float* C, int d, int rb, int cb, f32x4 
 // row 2p+1 is (u_2p+1 - g u_2p) / sqrt(p1) with p0 = d00, g = d01 / p0, p1 = d11 - g d01.  The
 // pivots p0, p1 are the scalar Cholesky pivots; a non-positive one sets *info to its 1-based index
 // (k0 + j + 1) and the block is then replaced by I (the results are undefined).  Rows past nb (last
-// panel) hold the identity.
+// panel) hold the identity.  T goes to Tk (global) and/or Tl (LDS), whichever is set.
+// Threads 512 .. 1023 take no part in the factorization: before each step's barrier they call
+// side(step) (step = 0 .. 31), so work of their own runs between the factorization's barriers.
+struct NoSide {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+template <typename Side>
 __device__ __forceinline__ void sw_factor(const float (*D)[BP], float (*curb)[2][2][NB], float* pivs, int nb, int k0,
-                                          float* Tk, int* info) {
+                                          float* Tk, int* info, float (*Tl)[BP], Side side) {
   __shared__ __attribute__((aligned(16))) float binv[2][4];
   const int t = threadIdx.x;
   const bool act = t < 512;
@@ -557,6 +623,7 @@ __device__ __forceinline__ void sw_factor(const float (*D)[BP], float (*curb)[2]
       *(f32x4*)&cur[1][c0] = f32x4{w[1][0], w[1][1], w[1][2], w[1][3]};
       if (cg == 0) *(f32x4*)&binv[par][0] = f32x4{b00, b01, b11, 0.f};
     }
+    if (!act) side(s);
     __syncthreads();
     if (act && p > s) {
       const f32x4 bv = *(const f32x4*)&binv[par][0];
@@ -584,6 +651,7 @@ __device__ __forceinline__ void sw_factor(const float (*D)[BP], float (*curb)[2]
       if (p == s + 1) invert();
     }
   };
+#pragma unroll
   for (int s = 0; s < NB / 2; s += 2) {
     step(std::integral_constant<int, 0>{}, s);
     step(std::integral_constant<int, 1>{}, s + 1);
@@ -614,8 +682,14 @@ __device__ __forceinline__ void sw_factor(const float (*D)[BP], float (*curb)[2]
       o0[e] = u0 * s0;
       o1[e] = fmaf(-g, u0, u1) * s1;
     }
-    *(f32x4*)(Tk + j * NB + c0) = f32x4{o0[0], o0[1], o0[2], o0[3]};
-    *(f32x4*)(Tk + (j + 1) * NB + c0) = f32x4{o1[0], o1[1], o1[2], o1[3]};
+    if (Tk) {
+      *(f32x4*)(Tk + j * NB + c0) = f32x4{o0[0], o0[1], o0[2], o0[3]};
+      *(f32x4*)(Tk + (j + 1) * NB + c0) = f32x4{o1[0], o1[1], o1[2], o1[3]};
+    }
+    if (Tl) {
+      *(f32x4*)&Tl[j][c0] = f32x4{o0[0], o0[1], o0[2], o0[3]};
+      *(f32x4*)&Tl[j + 1][c0] = f32x4{o1[0], o1[1], o1[2], o1[3]};
+    }
   }
 }
 
@@ -678,7 +752,7 @@ __global__ __launch_bounds__(SW_THREADS) void sweep_kernel(SweepArgs a) {
         if ((int)threadIdx.x < nb) L1[threadIdx.x][threadIdx.x] += a.sc->lambda;  // G + lambda I
       }
       __syncthreads();
-      sw_factor(L1, curb, pivs, nb, k * NB, a.Tb + (k % 3) * NB * NB, a.info);
+      sw_factor(L1, curb, pivs, nb, k * NB, a.Tb + (k % 3) * NB * NB, a.info, (float(*)[BP]) nullptr, NoSide{});
       return;
     }
     --q;
@@ -732,6 +806,516 @@ __global__ __launch_bounds__(SW_THREADS) void sweep_kernel(SweepArgs a) {
   __syncthreads();
   const f32x4 v = sw_mm(L2, L1, false);
   sw_store(a.Bx, d, r, q, v, false);
+}
+
+// ------------------------------------------------------------------------------------------
+// One-launch sweep (one layer, nP <= PS_MAX_PANELS).  The same factorization and identity part as
+// the per-panel launches above, bit for bit, with the launch boundaries replaced by version flags:
+//   * work-group 0 carries the diagonal chain.  At step k it factors D_k (ready in LDS), publishes
+//     T_k and X_{k+1} = (k+1, k) T_k^T, and applies panel k to (k+1, k+1), which gives D_{k+1}.
+//     So the chain never waits for a launch.
+//   * work-groups 1 and 2 bring row k+1 up to the chain: work-group 2 applies panel k-2 to its
+//     blocks (k+1, k-1 .. k+1) from the workers' versions, work-group 1 then applies panel k-1 to
+//     (k+1, k) and (k+1, k+1).  At each panel p the blocks of rows p+1 .. p+3 right of the panel are
+//     these three work-groups', never the workers'.
+//   * the other work-groups take tasks from a queue ordered by panel: the trailing update of a block
+//     by a panel (A task), the identity-part update (B task) and the final T_r B_rc (F task, into
+//     L^-1).  A task waits for the versions it reads; tasks are handed out in an order in which
+//     every wait is for a task handed out earlier, so the queue always makes progress.
+// A version is the number of panels applied to a block (identity part: updates applied).  Version 0
+// of an A block is G itself; later versions live in Mx.
+// Coherence across the XCDs: every block that one work-group writes and another reads (Mx, Bx, the
+// T slots) and every flag goes through device-scope (sc1) loads and stores, which bypass the
+// XCD-local caches, so no cache write-back or invalidation is needed.  A writer's stores complete
+// (s_waitcnt) before its flag is set; a reader loads the data only after it has seen the flag.
+// Every wait is bounded: a wait that times out sets *info = -2 (results undefined) and makes every
+// later wait return at once.
+// ------------------------------------------------------------------------------------------
+constexpr int PS_MAX_PANELS = 32;
+// Every work-group of the sweep takes a whole CU (one fits by LDS); nothing else runs beside it, so
+// the chain's CU is never shared.
+constexpr int PS_WORKERS = 253;
+constexpr int PS_WAIT_SPINS = 1 << 21;
+constexpr int PS_STATE_INTS = 64;   // [0] T blocks published, [1] next task, [2] a wait timed out
+constexpr int kSc1 = 16;            // cache policy of a buffer access: device scope (sc1)
+
+struct PsArgs {
+  const float* G;
+  float* Mx;     // A blocks at versions >= 1
+  float* Bx;     // identity part as it is updated
+  float* Linv;   // L^-1, lower blocks
+  float* Tb;     // T_k in slot k
+  float* Xs;     // X_{k+1} = (k+1, k) T_k^T (panels < k applied) in slot k
+  int* st;       // state, then the A versions [nP][nP], then the identity-part versions [nP][nP]
+  const uint16_t* sp;   // bf16 parts of C, W and W^T (split_kernel)
+  float* Rc;            // R = C W
+  float* P;             // lower block triangle of W W^T (with eps)
+  int wparts, n_r, n_rp, rp_share;   // R blocks, R and P blocks, R/P blocks per panel
+  int* info;
+  Scalars* sc;
+  float lam;
+  int relative;
+  float* lambda_out;
+  int d, nP, n_tasks;
+};
+
+__device__ __forceinline__ int ps_load(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ps_store(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// one thread: wait until *f >= v; false after a time-out (of this wait or of an earlier one)
+__device__ bool ps_wait(const PsArgs& a, const int* f, int v) {
+  if (ps_load(f) >= v) return true;
+  for (int n = 0; n < PS_WAIT_SPINS; ++n) {
+    __builtin_amdgcn_s_sleep(2);
+    if (ps_load(f) >= v) return true;
+    if ((n & 63) == 63 && ps_load(a.st + 2)) return false;
+  }
+  ps_store(a.st + 2, 1);
+  ps_store(a.info, -2);
+  return false;
+}
+// one thread: wait until f[i] >= v[i] for i < n; the flags are read together, so the satisfied ones
+// cost one round trip in all
+template <int N>
+__device__ __forceinline__ void ps_wait_all(const PsArgs& a, const int* const (&f)[N], const int (&v)[N], int n) {
+  int got[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) got[i] = i < n ? ps_load(f[i]) : 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (i < n && got[i] < v[i]) ps_wait(a, f[i], v[i]);
+}
+// all threads: this work-group's stores have completed; then thread 0 sets flag = v
+__device__ __forceinline__ void ps_publish(int* flag, int v) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) ps_store(flag, v);
+}
+
+// device-scope block access through a buffer over a d x d fp32 matrix (offsets past the end read 0)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ps_rsrc(const float* p, int64_t elems) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)(elems * 4), 0x00020000);
+}
+__device__ __forceinline__ f32x4 ps_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
+}
+__device__ __forceinline__ void ps_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kSc1);
+}
+__device__ __forceinline__ float ps_ld1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSc1));
+}
+__device__ __forceinline__ void ps_st1(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, kSc1);
+}
+constexpr uint32_t kOut = 0x80000000u;   // an offset past every buffer: loads return 0
+// offset = in ? off : kOut, kept a value (v_cndmask): left visible, the compiler turns the selected
+// load into two loads in branches with a wait for the first between them
+__device__ __forceinline__ uint32_t ps_off(bool in, uint32_t off) {
+  uint32_t o = in ? off : kOut;
+  asm volatile("" : "+v"(o));
+  return o;
+}
+// block (rb, cb) into LDS (1024 threads), zeros outside the matrix
+__device__ __forceinline__ void ps_load_blk(float (*dst)[BP], __amdgpu_buffer_rsrc_t r, int d, int rb, int cb) {
+  const int t = threadIdx.x;
+  const int rr = t >> 4, c = (t & 15) * 4;
+  const int gr = rb * NB + rr, gc = cb * NB + c;
+  *(f32x4*)&dst[rr][c] = ps_ld4(r, ps_off(gr < d && gc < d, (uint32_t)((gr * d + gc) * 4)));
+}
+// global block (rb, cb) = src + v (src and dst buffers may differ; accumulate = false: dst = v)
+__device__ __forceinline__ void ps_store_blk(__amdgpu_buffer_rsrc_t dst, __amdgpu_buffer_rsrc_t src, int d, int rb,
+                                             int cb, f32x4 v, bool accumulate) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m0 = rb * NB + (wave >> 2) * 16 + 4 * (lane >> 4), n = cb * NB + (wave & 3) * 16 + (lane & 15);
+  if (n >= d) return;
+  float o[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) o[r] = accumulate ? ps_ld1(src, ps_off(m0 + r < d, (uint32_t)(((m0 + r) * d + n) * 4))) : 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (m0 + r < d) ps_st1(dst, (uint32_t)(((m0 + r) * d + n) * 4), accumulate ? o[r] + v[r] : v[r]);
+}
+
+// Tasks of panel p (m = nP - 1 - p block rows below it): A tasks over blocks (i, j), p < j <= i,
+// in row order without the first six (rows p+1 .. p+3: the chain's); B tasks (i, c), i > p >= c;
+// F tasks (p, c), c < p; then a share of the R = C W and W W^T blocks, which wait for nothing.
+constexpr int PS_CHAIN_ENTRIES = 6;
+__host__ __device__ __forceinline__ int ps_n_a(int m) {
+  return m * (m + 1) / 2 > PS_CHAIN_ENTRIES ? m * (m + 1) / 2 - PS_CHAIN_ENTRIES : 0;
+}
+__host__ __device__ __forceinline__ int ps_count(int nP, int p) {
+  const int m = nP - 1 - p;
+  return ps_n_a(m) + m * (p + 1) + p;
+}
+__host__ __device__ __forceinline__ int ps_rp_count(int n_rp, int share, int p) {
+  const int left = n_rp - p * share;
+  return left <= 0 ? 0 : (left < share ? left : share);
+}
+
+__global__ __launch_bounds__(SW_THREADS) void psweep_kernel(PsArgs a) {
+  __shared__ __attribute__((aligned(16))) float B0[NB][BP], B1[NB][BP], B2[NB][BP], B3[NB][BP], B4[NB][BP],
+      B5[NB][BP], B6[NB][BP];
+  __shared__ __attribute__((aligned(16))) float curb[2][2][2][NB];
+  __shared__ float pivs[NB];
+  __shared__ int sq;
+  const int d = a.d, nP = a.nP, t = threadIdx.x;
+  const int64_t dd = (int64_t)d * d;
+  int* verA = a.st + PS_STATE_INTS;
+  int* verB = verA + nP * nP;
+  const int* tflag = a.st;
+  const __amdgpu_buffer_rsrc_t rG = ps_rsrc(a.G, dd), rM = ps_rsrc(a.Mx, dd), rB = ps_rsrc(a.Bx, dd),
+                               rT = ps_rsrc(a.Tb, (int64_t)nP * NB * NB), rX = ps_rsrc(a.Xs, (int64_t)nP * NB * NB);
+
+  // a 64 x 64 slot (T or X) into LDS / an LDS block into a slot (1024 threads)
+  auto slot_load = [&](float(*dst)[BP], __amdgpu_buffer_rsrc_t r, int k) {
+    const int rr = t >> 4, c = (t & 15) * 4;
+    *(f32x4*)&dst[rr][c] = ps_ld4(r, (uint32_t)(((k * NB + rr) * NB + c) * 4));
+  };
+  auto slot_store = [&](__amdgpu_buffer_rsrc_t r, int k, const float(*src)[BP]) {
+    const int rr = t >> 4, c = (t & 15) * 4;
+    ps_st4(r, (uint32_t)(((k * NB + rr) * NB + c) * 4), *(const f32x4*)&src[rr][c]);
+  };
+  // block (rb, cb) of Mx from LDS (1024 threads), inside the matrix only
+  auto blk_store = [&](int rb, int cb, const float(*src)[BP]) {
+    const int rr = t >> 4, c = (t & 15) * 4;
+    const int gr = rb * NB + rr, gc = cb * NB + c;
+    if (gr < d && gc < d) ps_st4(rM, (uint32_t)((gr * d + gc) * 4), *(const f32x4*)&src[rr][c]);
+  };
+  const int lane = t & 63, wave = t >> 6;
+  const int qm = (wave >> 2) * 16 + 4 * (lane >> 4), qn = (wave & 3) * 16 + (lane & 15);   // quadrant element
+
+  if (blockIdx.x == 0) {
+    // ---------------- the diagonal chain ----------------
+    float(*D)[BP] = B0;    // the block being factored
+    float(*Tc)[BP] = B1;   // T_k
+    float(*S1)[BP] = B2;   // (k+1, k), panels < k applied
+    float(*S2)[BP] = B3;   // (k+1, k+1), panels < k applied
+    float(*Xk)[BP] = B4;   // X_{k+1} = S1 T_k^T
+    sw_load(D, a.G, d, 0, 0);
+    float lam;
+    {
+      // tr(G) in fp64 over the 16 waves, then lambda (S1 is free until step 0's side work)
+      double tr = 0.0;
+      for (int i = t; i < d; i += SW_THREADS) tr += (double)a.G[(int64_t)i * d + i];
+      for (int o = 32; o > 0; o >>= 1) tr += __shfl_xor(tr, o);
+      double* red = (double*)&S1[0][0];
+      if ((t & 63) == 0) red[t >> 6] = tr;
+      __syncthreads();
+      if (t == 0) {
+        double sum = 0.0;
+        for (int w2 = 0; w2 < SW_THREADS / 64; ++w2) sum += red[w2];
+        const float l = a.relative ? (float)((double)a.lam * sum / (double)d) : a.lam;
+        a.sc->lambda = l;
+        if (a.lambda_out) *a.lambda_out = l;
+        red[0] = l;
+      }
+      __syncthreads();
+      lam = (float)red[0];
+      if (t < min(NB, d)) D[t][t] += lam;   // G + lambda I
+      __syncthreads();
+    }
+    const int tt = t - 512;                     // side threads
+    const int lr = tt >> 3, lc = 8 * (tt & 7);  // side loads: row lr, columns lc .. lc + 7
+    for (int k = 0; k < nP; ++k) {
+      const int nb = min(NB, d - k * NB);
+      const bool next = k + 1 < nP;
+      // side work: S1, S2 as work-group 1 leaves them (G itself for k = 0).  The flag is read at
+      // step 20 and checked at step 22 (waiting only if work-group 1 is late); the blocks are
+      // loaded at step 23 and put into LDS after the factorization.
+      f32x4 tmp[2][2];
+      int fl = 0;
+      auto side = [&](int s) {
+        if (!next) return;
+        if (s == 20) {
+          if (tt == 0 && k >= 1) fl = ps_load(verA + (k + 1) * nP + k + 1);
+        } else if (s == 22) {
+          if (tt == 0 && k >= 1 && fl < k) ps_wait(a, verA + (k + 1) * nP + k + 1, k);
+        } else if (s == 23) {
+          const __amdgpu_buffer_rsrc_t src = k == 0 ? rG : rM;   // version k
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            const int gr = (k + 1) * NB + lr, gc = (k + b) * NB + lc;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              tmp[b][h] = ps_ld4(src, ps_off(gr < d && gc + 4 * h < d, (uint32_t)((gr * d + gc + 4 * h) * 4)));
+          }
+        }
+      };
+      sw_factor(D, curb, pivs, nb, k * NB, (float*)nullptr, a.info, Tc, side);
+      __syncthreads();
+      if (t >= 512 && next) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          *(f32x4*)&S1[lr][lc + 4 * h] = tmp[0][h];
+          *(f32x4*)&S2[lr][lc + 4 * h] = tmp[1][h];
+        }
+      }
+      // T_k into its slot (read by the workers and work-groups 1 and 2) and into L^-1 block (k, k)
+      slot_store(rT, k, Tc);
+      {
+        const int rr = t >> 4, c = (t & 15) * 4;
+        const int gr = k * NB + rr, gc = k * NB + c;
+        if (gr < d && gc < d) *(f32x4*)(a.Linv + (int64_t)gr * d + gc) = *(const f32x4*)&Tc[rr][c];
+      }
+      __syncthreads();
+      // panel k on (k+1, k+1): X_{k+1} = S1 T_k^T (published with T_k) and
+      // D_{k+1} = S2 - X_{k+1} X_{k+1}^T + lambda I, while the stores complete; then the flag
+      if (next) {
+        const f32x4 x = sw_mm(S1, Tc, true);
+        sw_put(Xk, x);
+        __syncthreads();
+        slot_store(rX, k, Xk);
+        const f32x4 xx = sw_mm(Xk, Xk, true);
+        const int nb1 = min(NB, d - (k + 1) * NB);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = S2[qm + r][qn] - xx[r];
+          if (qm + r == qn && qn < nb1) v += lam;
+          D[qm + r][qn] = v;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (t == 0) ps_store(a.st, k + 1);
+    }
+    return;
+  }
+
+  if (blockIdx.x == 1) {
+    // ---------------- panel k-1 on row k+1 ----------------
+    // Round k (1 <= k <= nP-2), r = k+1: from (r, k-1), (r, k), (r, r) with panels < k-1 applied
+    // (work-group 2's, G for k = 1) and, once T_{k-1} is out, X_k = X slot k-1:
+    //   X_r = (r, k-1) T_{k-1}^T,  (r, k) -= X_r X_k^T,  (r, r) -= X_r X_r^T,
+    // published as version k ((r, k) is also the workers' panel-k block; (r, r)'s version is work-group
+    // 0's flag).
+    float(*T)[BP] = B0;
+    float(*Xp)[BP] = B1;
+    float(*R1)[BP] = B2;
+    float(*R2)[BP] = B3;
+    float(*R3)[BP] = B4;
+    for (int k = 1; k + 1 < nP; ++k) {
+      const int r = k + 1;
+      if (t == 0 && k >= 2) ps_wait(a, verA + r * nP + r, k - 1);
+      __syncthreads();
+      const __amdgpu_buffer_rsrc_t src = k == 1 ? rG : rM;   // version k - 1
+      ps_load_blk(R1, src, d, r, k - 1);
+      ps_load_blk(R2, src, d, r, k);
+      ps_load_blk(R3, src, d, r, r);
+      if (t == 0) {
+        for (int n = 0; n < 4096 && ps_load(tflag) < k; ++n) {
+        }
+        ps_wait(a, tflag, k);
+      }
+      __syncthreads();
+      slot_load(T, rT, k - 1);
+      slot_load(Xp, rX, k - 1);
+      __syncthreads();
+      const f32x4 xr = sw_mm(R1, T, true);
+      __syncthreads();
+      sw_put(R1, xr);
+      __syncthreads();
+      const f32x4 u2 = sw_mm(R1, Xp, true);
+      const f32x4 u3 = sw_mm(R1, R1, true);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        R2[qm + q][qn] -= u2[q];
+        R3[qm + q][qn] -= u3[q];
+      }
+      __syncthreads();
+      blk_store(r, k, R2);
+      blk_store(r, r, R3);
+      ps_publish(verA + r * nP + k, k);
+      if (t == 0) ps_store(verA + r * nP + r, k);
+    }
+    return;
+  }
+
+  if (blockIdx.x == 2) {
+    // ---------------- panel k-2 on row k+1 ----------------
+    // Round k (2 <= k <= nP-2), r = k+1: from the workers' versions k-2 of (r, k-2 .. k) and (r, r)
+    // (G for k = 2) and, once T_{k-2} is out, X_{k-1} = X slot k-2 and (k, k-2) (kept from the
+    // previous round):
+    //   X_r = (r, k-2) T_{k-2}^T,  X_k = (k, k-2) T_{k-2}^T,
+    //   (r, k-1) -= X_r X_{k-1}^T,  (r, k) -= X_r X_k^T,  (r, r) -= X_r X_r^T,
+    // published as version k-1 ((r, k-1) is also the workers' panel-(k-1) block).
+    float(*T)[BP] = B0;
+    float(*Xp)[BP] = B1;   // X_{k-1}
+    float(*Kp)[BP] = B2;   // (k, k-2)
+    float(*R0)[BP] = B3;
+    float(*R1)[BP] = B4;
+    float(*R2)[BP] = B5;
+    float(*R3)[BP] = B6;
+    for (int k = 2; k + 1 < nP; ++k) {
+      const int r = k + 1;
+      if (t == 0 && k >= 3) {
+        const int* const f[4] = {verA + r * nP + (k - 2), verA + r * nP + (k - 1), verA + r * nP + k, verA + r * nP + r};
+        const int v[4] = {k - 2, k - 2, k - 2, k - 2};
+        ps_wait_all(a, f, v, 4);
+      }
+      __syncthreads();
+      const __amdgpu_buffer_rsrc_t src = k == 2 ? rG : rM;   // version k - 2
+      ps_load_blk(R0, src, d, r, k - 2);
+      ps_load_blk(R1, src, d, r, k - 1);
+      ps_load_blk(R2, src, d, r, k);
+      ps_load_blk(R3, src, d, r, r);
+      if (k == 2) ps_load_blk(Kp, rG, d, 2, 0);
+      if (t == 0) ps_wait(a, tflag, k - 1);
+      __syncthreads();
+      slot_load(T, rT, k - 2);
+      slot_load(Xp, rX, k - 2);
+      __syncthreads();
+      const f32x4 xk = sw_mm(Kp, T, true);
+      const f32x4 xr = sw_mm(R0, T, true);
+      __syncthreads();
+      sw_put(Kp, xk);
+      sw_put(R0, xr);
+      __syncthreads();
+      const f32x4 u1 = sw_mm(R0, Xp, true);
+      const f32x4 u2 = sw_mm(R0, Kp, true);
+      const f32x4 u3 = sw_mm(R0, R0, true);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        R1[qm + q][qn] -= u1[q];
+        R2[qm + q][qn] -= u2[q];
+        R3[qm + q][qn] -= u3[q];
+      }
+      __syncthreads();
+      blk_store(r, k - 1, R1);
+      blk_store(r, k, R2);
+      blk_store(r, r, R3);
+      ps_publish(verA + r * nP + (k - 1), k - 1);
+      if (t == 0) {
+        ps_store(verA + r * nP + k, k - 1);
+        ps_store(verA + r * nP + r, k - 1);
+      }
+      // (r, k-1) is the next round's (k, k-2)
+      float(*f0)[BP] = Kp;
+      Kp = R1;
+      R1 = f0;
+    }
+    return;
+  }
+
+  // ---------------- workers ----------------
+  float(*L0)[BP] = B0;
+  float(*L1)[BP] = B1;
+  float(*L2)[BP] = B2;
+  for (;;) {
+    if (t == 0) sq = __hip_atomic_fetch_add(a.st + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    int q = sq;
+    if (q >= a.n_tasks) return;
+    int p = 0;
+    bool rp = false;
+    for (; p < nP; ++p) {
+      const int c = ps_count(nP, p);
+      if (q < c) break;
+      q -= c;
+      const int c2 = ps_rp_count(a.n_rp, a.rp_share, p);
+      if (q < c2) {
+        rp = true;
+        break;
+      }
+      q -= c2;
+    }
+    if (p >= nP) return;   // (n_tasks is the sum of ps_count and ps_rp_count over the panels)
+    if (rp) {
+      // R / P block p * share + q
+      uint16_t(*As)[64][RP_PITCH] = (uint16_t(*)[64][RP_PITCH]) & B0[0][0];
+      uint16_t(*Bs)[64][RP_PITCH] = (uint16_t(*)[64][RP_PITCH]) & B1[0][0];
+      if (a.wparts == 1) rp_tile<1>(a.sp, a.Rc, a.P, d, a.n_r, p * a.rp_share + q, As, Bs);
+      else rp_tile<3>(a.sp, a.Rc, a.P, d, a.n_r, p * a.rp_share + q, As, Bs);
+      __syncthreads();
+      continue;
+    }
+    const int m = nP - 1 - p, nA = ps_n_a(m), nBt = m * (p + 1);
+    const __amdgpu_buffer_rsrc_t srcP = p == 0 ? rG : rM;   // A blocks at version p
+    const uint32_t toff = (uint32_t)(p * NB * NB * 4);
+    auto load_t = [&]() {   // T_p into L2
+      const int rr = t >> 4, c = (t & 15) * 4;
+      *(f32x4*)&L2[rr][c] = ps_ld4(rT, toff + (uint32_t)((rr * NB + c) * 4));
+    };
+    if (q < nA) {
+      // A task: (i, j) -= X_i X_j^T, X = (., p) T_p^T
+      int ii, jj;
+      tri_decode(q + PS_CHAIN_ENTRIES, ii, jj);
+      const int i = p + 1 + ii, j = p + 1 + jj;
+      if (t == 0) {
+        const int* const f[4] = {tflag, verA + i * nP + p, verA + j * nP + p, verA + i * nP + j};
+        const int v[4] = {p + 1, p, p, p};
+        ps_wait_all(a, f, v, 4);
+      }
+      __syncthreads();
+      ps_load_blk(L0, srcP, d, i, p);
+      load_t();
+      if (i != j) ps_load_blk(L1, srcP, d, j, p);
+      __syncthreads();
+      const f32x4 xi = sw_mm(L0, L2, true);
+      const f32x4 xj = i != j ? sw_mm(L1, L2, true) : xi;
+      __syncthreads();
+      sw_put(L0, xi);
+      sw_put(L1, xj);
+      __syncthreads();
+      const f32x4 v = sw_mm(L0, L1, true);
+      ps_store_blk(rM, srcP, d, i, j, -v, true);
+      ps_publish(verA + i * nP + j, p + 1);
+      continue;
+    }
+    q -= nA;
+    if (q < nBt) {
+      // B task: B_ic -= X_i (T_p B_pc), with B_pp = I and B_ic = 0 before its first update
+      const int i = p + 1 + q / (p + 1), c = q % (p + 1);
+      if (t == 0) {
+        const int* const f[4] = {tflag, verA + i * nP + p, verB + p * nP + c, verB + i * nP + c};
+        const int v[4] = {p + 1, p, p - c, p - c};
+        ps_wait_all(a, f, v, c < p ? 4 : 2);
+      }
+      __syncthreads();
+      ps_load_blk(L0, srcP, d, i, p);
+      load_t();
+      if (c < p) ps_load_blk(L1, rB, d, p, c);
+      __syncthreads();
+      const f32x4 xi = sw_mm(L0, L2, true);
+      f32x4 tb;
+      if (c < p) {
+        tb = sw_mm(L2, L1, false);
+      } else {
+        const int lane = t & 63, wave = t >> 6;
+        const int m0 = (wave >> 2) * 16 + 4 * (lane >> 4), n = (wave & 3) * 16 + (lane & 15);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tb[r] = L2[m0 + r][n];
+      }
+      __syncthreads();
+      sw_put(L0, xi);
+      sw_put(L1, tb);
+      __syncthreads();
+      const f32x4 v = sw_mm(L0, L1, false);
+      ps_store_blk(rB, rB, d, i, c, -v, c < p);
+      ps_publish(verB + i * nP + c, p - c + 1);
+      continue;
+    }
+    q -= nBt;
+    {
+      // F task: L^-1 block (p, c) = T_p B_pc
+      const int c = q;
+      if (t == 0) {
+        const int* const f[2] = {tflag, verB + p * nP + c};
+        const int v[2] = {p + 1, p - c};
+        ps_wait_all(a, f, v, 2);
+      }
+      __syncthreads();
+      ps_load_blk(L1, rB, d, p, c);
+      load_t();
+      __syncthreads();
+      const f32x4 v = sw_mm(L2, L1, false);
+      sw_store(a.Linv, d, p, c, v, false);
+      __syncthreads();
+    }
+  }
 }
 
 // out = A B accumulated in fp64 (A, B fp32 [d, d] row-major; products of fp32 values are exact in
@@ -905,17 +1489,24 @@ constexpr int DOT_BLOCKS = 512;
 
 struct WsLayout {
   float* Mx;   // d x d
-  float* Bx;   // d x d: I, then L^-1
+  float* Bx;   // d x d: I, then L^-1 (per-panel launches); the identity part as updated (one launch)
   float* Rs;   // d x d: refinement residual
   float* Rc;   // d x d
   float* Wf;   // d x d
   float* P;    // d x d (W W^T)
-  float* T;    // three NB x NB slots
+  float* T;    // NB x NB slots, one per panel (at least three)
   Scalars* sc;
   double* part;
   double* R64; // d x d, C W accumulated in fp64 (refinement only)
   uint16_t* sp; // 9 d x d bf16: three parts of C, of W and of W^T (split_kernel)
+  float* Linv; // d x d: L^-1 (one-launch sweep)
+  float* Xs;   // NB x NB slots, one per panel (one-launch sweep)
+  int* st;     // one-launch sweep: state and block versions
 };
+
+int n_panels(int d) { return (d + NB - 1) / NB; }
+size_t t_slots_bytes(int d) { return (size_t)std::max(3, n_panels(d)) * NB * NB * sizeof(float); }
+size_t state_bytes(int d) { return (size_t)(PS_STATE_INTS + 2 * n_panels(d) * n_panels(d)) * sizeof(int); }
 
 WsLayout carve(void* ws, int d) {
   char* p = (char*)ws;
@@ -927,10 +1518,13 @@ WsLayout carve(void* ws, int d) {
   w.Rc = (float*)p; p += dd;
   w.Wf = (float*)p; p += dd;
   w.P = (float*)p; p += dd;
-  w.T = (float*)p; p += 3 * NB * NB * sizeof(float);
+  w.Linv = (float*)p; p += dd;
+  w.T = (float*)p; p += t_slots_bytes(d);
+  w.Xs = (float*)p; p += t_slots_bytes(d);
   w.sc = (Scalars*)p; p += 256;
   w.part = (double*)p; p += DOT_BLOCKS * 5 * sizeof(double);
   w.R64 = (double*)p; p += (size_t)d * d * sizeof(double);
+  w.st = (int*)p; p += (state_bytes(d) + 255) / 256 * 256;
   w.sp = (uint16_t*)p;
   return w;
 }
@@ -973,8 +1567,8 @@ AuxStream* aux_stream() {
 }  // namespace
 
 size_t solve_workspace_bytes(int d) {
-  const size_t b = (size_t)d * d * sizeof(float) * 6 + 3 * NB * NB * sizeof(float) + 256 +
-                   DOT_BLOCKS * 5 * sizeof(double) + (size_t)d * d * sizeof(double) + (size_t)d * d * 18 + 256;
+  const size_t b = (size_t)d * d * sizeof(float) * 7 + 2 * t_slots_bytes(d) + 256 + DOT_BLOCKS * 5 * sizeof(double) +
+                   (size_t)d * d * sizeof(double) + (state_bytes(d) + 255) / 256 * 256 + (size_t)d * d * 18 + 256;
   return (b + 255) / 256 * 256;
 }
 
@@ -989,19 +1583,31 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
   st.batch = nb_l;
   const int eb = (int)((dd + NT - 1) / NT > 2048 ? 2048 : (dd + NT - 1) / NT);
   const dim3 eg(eb, nb_l);
+  const int nP = n_panels(d);
+  // One layer with few panels: the whole sweep in one launch (the trailing updates then fit beside
+  // the diagonal chain); otherwise one launch per panel, with the layers side by side.
+  const bool one_launch = nb_l == 1 && nP <= PS_MAX_PANELS;
+  int* state = one_launch ? w.st : nullptr;
+  const int n_state = PS_STATE_INTS + 2 * nP * nP;
 
   if (L.w_dtype == DT_BF16)
-    hipLaunchKernelGGL(setup_kernel<BF16>, eg, dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, w.Mx, w.Bx, w.Wf, st);
+    hipLaunchKernelGGL(setup_kernel<BF16>, eg, dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, w.Mx, w.Bx, w.Wf, st,
+                       state, n_state, L.info);
   else if (L.w_dtype == DT_F16)
-    hipLaunchKernelGGL(setup_kernel<F16>, eg, dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, w.Mx, w.Bx, w.Wf, st);
+    hipLaunchKernelGGL(setup_kernel<F16>, eg, dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, w.Mx, w.Bx, w.Wf, st,
+                       state, n_state, L.info);
   else
-    hipLaunchKernelGGL(setup_kernel<F32>, eg, dim3(NT), 0, s, L.G, (const float*)L.W, d, w.Mx, w.Bx, w.Wf, st);
+    hipLaunchKernelGGL(setup_kernel<F32>, eg, dim3(NT), 0, s, L.G, (const float*)L.W, d, w.Mx, w.Bx, w.Wf, st,
+                       state, n_state, L.info);
   ISPA_TRY(hipGetLastError());
 
   // R = C W and, for epsilon, the lower block triangle of P = W W^T, from bf16 parts of C and W.
-  // Nothing reads them before the triangular products, so they run on the auxiliary stream beside
-  // the sweep (whose launches are latency-bound and leave most of the device idle).
-  AuxStream* ax = aux_stream();
+  // Nothing reads them before the triangular products.  Per-panel launches: they run on the
+  // auxiliary stream beside the sweep, whose launches are latency-bound and leave most of the device
+  // idle.  One launch: the parts are made first on the caller's stream and the blocks of R and P
+  // are tasks of the sweep's queue, run by the workers while they would otherwise wait (beside the
+  // sweep, kernels would share its CUs, the diagonal chain's included).
+  AuxStream* ax = one_launch ? nullptr : aux_stream();
   std::unique_lock<std::mutex> aux_lock;
   hipStream_t sr = s;
   if (ax) {
@@ -1015,18 +1621,47 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
     const dim3 sg(n_r, nb_l), rg(n_r + n_p, nb_l);
     if (L.w_dtype == DT_BF16) {
       hipLaunchKernelGGL(split_kernel<1>, sg, dim3(256), 0, sr, L.C, w.Wf, w.sp, d, st);
-      hipLaunchKernelGGL(rp_kernel<1>, rg, dim3(256), 0, sr, w.sp, w.Rc, w.P, d, n_r, st);
+      if (!one_launch) hipLaunchKernelGGL(rp_kernel<1>, rg, dim3(256), 0, sr, w.sp, w.Rc, w.P, d, n_r, st);
     } else {
       hipLaunchKernelGGL(split_kernel<3>, sg, dim3(256), 0, sr, L.C, w.Wf, w.sp, d, st);
-      hipLaunchKernelGGL(rp_kernel<3>, rg, dim3(256), 0, sr, w.sp, w.Rc, w.P, d, n_r, st);
+      if (!one_launch) hipLaunchKernelGGL(rp_kernel<3>, rg, dim3(256), 0, sr, w.sp, w.Rc, w.P, d, n_r, st);
     }
     ISPA_TRY(hipGetLastError());
     if (ax) ISPA_TRY(hipEventRecord(ax->join, sr));
   }
 
-  // Cholesky sweep (one launch per panel, plus one that finishes the last two block rows of L^-1)
-  {
-    const int nP = (d + NB - 1) / NB;
+  if (one_launch) {
+    PsArgs a;
+    a.G = L.G;
+    a.Mx = w.Mx;
+    a.Bx = w.Bx;
+    a.Linv = w.Linv;
+    a.Tb = w.T;
+    a.Xs = w.Xs;
+    a.st = w.st;
+    a.info = L.info;
+    a.sc = w.sc;
+    a.lam = L.lambda;
+    a.relative = L.lambda_relative;
+    a.lambda_out = L.lambda_out;
+    a.d = d;
+    a.nP = nP;
+    const int nT = (d + 63) / 64;
+    a.sp = w.sp;
+    a.Rc = w.Rc;
+    a.P = w.P;
+    a.wparts = L.w_dtype == DT_BF16 ? 1 : 3;
+    a.n_r = nT * nT;
+    a.n_rp = a.n_r + (L.eps ? nT * (nT + 1) / 2 : 0);
+    a.rp_share = (a.n_rp + nP - 1) / nP;
+    int n_tasks = 0;
+    for (int p = 0; p < nP; ++p) n_tasks += ps_count(nP, p) + ps_rp_count(a.n_rp, a.rp_share, p);
+    a.n_tasks = n_tasks;
+    const int grid = 3 + std::min(PS_WORKERS, n_tasks);
+    hipLaunchKernelGGL(psweep_kernel, dim3(grid), dim3(SW_THREADS), 0, s, a);
+    ISPA_TRY(hipGetLastError());
+  } else {
+    // Cholesky sweep (one launch per panel, plus one that finishes the last two block rows of L^-1)
     for (int k = 0; k <= nP; ++k) {
       SweepArgs a;
       a.Mx = w.Mx;
@@ -1064,11 +1699,12 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
     ISPA_TRY(hipStreamWaitEvent(s, ax->join, 0));
     aux_lock.unlock();
   }
+  const float* Li = one_launch ? w.Linv : w.Bx;   // L^-1
   // Z = L^-1 R (L^-1 lower triangular: only k < m0 + 64 contributes), into Mx (no longer needed)
-  ISPA_TRY(run_trgemm(false, w.Bx, st.ws, w.Rc, st.ws, w.Mx, st.ws, d, 1.f, 0.f, nb_l, s));
+  ISPA_TRY(run_trgemm(false, Li, st.ws, w.Rc, st.ws, w.Mx, st.ws, d, 1.f, 0.f, nb_l, s));
   // dW = (L^-1)^T Z   (op(A) upper triangular: only k >= m0 contributes)
   // (W_new = W + dW is written by the last product that updates dW)
-  ISPA_TRY(run_trgemm(true, w.Bx, st.ws, w.Mx, st.ws, L.delta_w, st.mat, d, 1.f, 0.f, nb_l, s, L.W,
+  ISPA_TRY(run_trgemm(true, Li, st.ws, w.Mx, st.ws, L.delta_w, st.mat, d, 1.f, 0.f, nb_l, s, L.W,
                       L.refine > 0 ? nullptr : L.w_new, L.w_dtype, st.wmat));
   if (L.refine > 0) {
     // iterative refinement: r = C W - (G + lambda I) dW with fp64 accumulation (C W formed once in
@@ -1083,8 +1719,8 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
                          w.Rs, st.ws);
       ISPA_TRY(hipGetLastError());
       // t = L^-1 r (into Mx, no longer needed), dW += (L^-1)^T t
-      ISPA_TRY(run_trgemm(false, w.Bx, st.ws, w.Rs, st.ws, w.Mx, st.ws, d, 1.f, 0.f, nb_l, s));
-      ISPA_TRY(run_trgemm(true, w.Bx, st.ws, w.Mx, st.ws, L.delta_w, st.mat, d, 1.f, 1.f, nb_l, s, L.W,
+      ISPA_TRY(run_trgemm(false, Li, st.ws, w.Rs, st.ws, w.Mx, st.ws, d, 1.f, 0.f, nb_l, s));
+      ISPA_TRY(run_trgemm(true, Li, st.ws, w.Mx, st.ws, L.delta_w, st.mat, d, 1.f, 1.f, nb_l, s, L.W,
                           it + 1 == L.refine ? L.w_new : nullptr, L.w_dtype, st.wmat));
     }
   }
