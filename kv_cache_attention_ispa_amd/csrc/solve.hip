@@ -240,32 +240,25 @@ struct Scalars {
   double dots[8];
 };
 
-// Wf = W as fp32.  Per-panel launches (state == nullptr): Mx = G (lambda joins the diagonal blocks as
-// the sweep factors them) and Bx = I (becomes L^-1).  One-launch sweep: the sweep reads G itself and
-// starts the identity part implicitly; its state and block versions (n_state ints) and *info are
-// cleared instead.
+// Per-panel launches: Mx = G (lambda joins the diagonal blocks as the sweep factors them) and Bx = I
+// (becomes L^-1).  With refinement: Wf = W as fp32 (the fp64 product C W reads it).  Either part may
+// be off (null pointers).
 template <typename WT>
 __global__ __launch_bounds__(NT) void setup_kernel(const float* G, const typename WT::storage* W, int d, float* Mx,
-                                                   float* Bx, float* Wf, Steps st, int* state, int n_state,
-                                                   int* info) {
+                                                   float* Bx, float* Wf, Steps st) {
   G = at_layer(G, st.mat);
   W = at_layer(W, st.wmat);
   Mx = at_layer(Mx, st.ws);
   Bx = at_layer(Bx, st.ws);
   Wf = at_layer(Wf, st.ws);
   const int64_t n = (int64_t)d * d;
-  const int64_t g0 = blockIdx.x * (int64_t)NT + threadIdx.x, gs = (int64_t)gridDim.x * NT;
-  if (state) {
-    for (int64_t e = g0; e < n_state; e += gs) state[e] = 0;
-    if (g0 == 0) *info = 0;
-    for (int64_t e = g0; e < n; e += gs) Wf[e] = Cvt<WT>::to_f(W[e]);
-    return;
-  }
-  for (int64_t e = g0; e < n; e += gs) {
-    const int i = (int)(e / d), j = (int)(e % d);
-    Mx[e] = G[e];
-    Bx[e] = (i == j) ? 1.f : 0.f;
-    Wf[e] = Cvt<WT>::to_f(W[e]);
+  for (int64_t e = blockIdx.x * (int64_t)NT + threadIdx.x; e < n; e += (int64_t)gridDim.x * NT) {
+    if (Mx) {
+      const int i = (int)(e / d), j = (int)(e % d);
+      Mx[e] = G[e];
+      Bx[e] = (i == j) ? 1.f : 0.f;
+    }
+    if (Wf) Wf[e] = Cvt<WT>::to_f(W[e]);
   }
 }
 
@@ -352,14 +345,21 @@ __device__ __forceinline__ void bf16_split3(float x, uint16_t (&part)[3]) {
   }
 }
 
-// Work-group (bi, bj): the 64 x 64 block (bi, bj) of C and of W (from Wf), split; W's parts also go
-// to the transposed block through LDS.  Thread t covers row t / 4, 16 columns from 16 (t % 4).
-template <int WPARTS>
-__global__ __launch_bounds__(256) void split_kernel(const float* __restrict__ C, const float* __restrict__ Wf,
-                                                    uint16_t* __restrict__ sp, int d, Steps st) {
+// Work-group (bi, bj): the 64 x 64 block (bi, bj) of C and of W (read in its own type), split; W's
+// parts also go to the transposed block through LDS.  Thread t covers row t / 4, 16 columns from
+// 16 (t % 4).  When state is set, the work-groups also clear the one-launch sweep's n_state state
+// ints and *info.
+template <int WPARTS, typename WT>
+__global__ __launch_bounds__(256) void split_kernel(const float* __restrict__ C, const typename WT::storage* __restrict__ W,
+                                                    uint16_t* __restrict__ sp, int d, Steps st, int* state,
+                                                    int n_state, int* info) {
   C = at_layer(C, st.mat);
-  Wf = at_layer(Wf, st.ws);
+  W = at_layer(W, st.wmat);
   sp = at_layer(sp, st.ws);
+  if (state) {
+    for (int e = blockIdx.x * 256 + (int)threadIdx.x; e < n_state; e += gridDim.x * 256) state[e] = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *info = 0;
+  }
   const int64_t dd = (int64_t)d * d;
   __shared__ uint16_t tile[WPARTS][64][66];   // W parts of the block, [row][col]
   const int nT = (d + 63) / 64, bi = blockIdx.x / nT, bj = blockIdx.x % nT;
@@ -387,11 +387,7 @@ __global__ __launch_bounds__(256) void split_kernel(const float* __restrict__ C,
 #pragma unroll
     for (int i = 0; i < 3; ++i) put(sp + i * dd + o, v, i);
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const f32x4 x = *(const f32x4*)(Wf + o + 4 * h);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) bf16_split3(x[e], v[4 * h + e]);
-    }
+    for (int e = 0; e < 16; ++e) bf16_split3(Cvt<WT>::to_f(W[o + e]), v[e]);
 #pragma unroll
     for (int i = 0; i < WPARTS; ++i) {
       put(sp + (3 + i) * dd + o, v, i);
@@ -1419,20 +1415,25 @@ __global__ __launch_bounds__(NT, 2) void gemm64_kernel(const float* A, int64_t s
 // Partial dot products for epsilon: <D,P>, <G,P>, <W,R>, <dW,R>, <dW,dW> (fp64 per block), row by row.
 // Only the lower 64-block triangle of P is formed; D and G are symmetric, so blocks below the
 // diagonal count twice and the upper ones are skipped.
-__global__ __launch_bounds__(NT) void dots_kernel(const float* D, const float* G, const float* P, const float* Wf,
-                                                  const float* R, const float* dW, int d, double* part, Steps st) {
+template <typename WT>
+__global__ __launch_bounds__(NT) void dots_kernel(const float* D, const float* G, const float* P,
+                                                  const typename WT::storage* W, const float* R, const float* dW,
+                                                  int d, double* part, Steps st) {
   D = at_layer(D, st.mat);
   G = at_layer(G, st.mat);
   dW = at_layer(dW, st.mat);
   P = at_layer(P, st.ws);
-  Wf = at_layer(Wf, st.ws);
+  W = at_layer(W, st.wmat);
   R = at_layer(R, st.ws);
   part = at_layer(part, st.ws);
   double s[5] = {0, 0, 0, 0, 0};
   for (int r = blockIdx.x; r < d; r += gridDim.x)
     for (int c = 4 * (int)threadIdx.x; c < d; c += 4 * NT) {
       const int64_t e = (int64_t)r * d + c;
-      const f32x4 rv = *(const f32x4*)(R + e), dv = *(const f32x4*)(dW + e), wv = *(const f32x4*)(Wf + e);
+      const f32x4 rv = *(const f32x4*)(R + e), dv = *(const f32x4*)(dW + e);
+      f32x4 wv;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) wv[u] = Cvt<WT>::to_f(W[e + u]);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         s[2] += (double)wv[u] * rv[u];
@@ -1590,16 +1591,20 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
   int* state = one_launch ? w.st : nullptr;
   const int n_state = PS_STATE_INTS + 2 * nP * nP;
 
-  if (L.w_dtype == DT_BF16)
-    hipLaunchKernelGGL(setup_kernel<BF16>, eg, dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, w.Mx, w.Bx, w.Wf, st,
-                       state, n_state, L.info);
-  else if (L.w_dtype == DT_F16)
-    hipLaunchKernelGGL(setup_kernel<F16>, eg, dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, w.Mx, w.Bx, w.Wf, st,
-                       state, n_state, L.info);
-  else
-    hipLaunchKernelGGL(setup_kernel<F32>, eg, dim3(NT), 0, s, L.G, (const float*)L.W, d, w.Mx, w.Bx, w.Wf, st,
-                       state, n_state, L.info);
-  ISPA_TRY(hipGetLastError());
+  // Mx and Bx for the per-panel launches, W as fp32 for the refinement (the one-launch sweep reads G
+  // itself and starts the identity part implicitly)
+  if (!one_launch || L.refine > 0) {
+    float* Mx = one_launch ? nullptr : w.Mx;
+    float* Bx = one_launch ? nullptr : w.Bx;
+    float* Wf = L.refine > 0 ? w.Wf : nullptr;
+    if (L.w_dtype == DT_BF16)
+      hipLaunchKernelGGL(setup_kernel<BF16>, eg, dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, Mx, Bx, Wf, st);
+    else if (L.w_dtype == DT_F16)
+      hipLaunchKernelGGL(setup_kernel<F16>, eg, dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, Mx, Bx, Wf, st);
+    else
+      hipLaunchKernelGGL(setup_kernel<F32>, eg, dim3(NT), 0, s, L.G, (const float*)L.W, d, Mx, Bx, Wf, st);
+    ISPA_TRY(hipGetLastError());
+  }
 
   // R = C W and, for epsilon, the lower block triangle of P = W W^T, from bf16 parts of C and W.
   // Nothing reads them before the triangular products.  Per-panel launches: they run on the
@@ -1620,10 +1625,16 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
     const int nT = (d + 63) / 64, n_r = nT * nT, n_p = L.eps ? nT * (nT + 1) / 2 : 0;
     const dim3 sg(n_r, nb_l), rg(n_r + n_p, nb_l);
     if (L.w_dtype == DT_BF16) {
-      hipLaunchKernelGGL(split_kernel<1>, sg, dim3(256), 0, sr, L.C, w.Wf, w.sp, d, st);
+      hipLaunchKernelGGL((split_kernel<1, BF16>), sg, dim3(256), 0, sr, L.C, (const uint16_t*)L.W, w.sp, d, st, state,
+                         n_state, L.info);
       if (!one_launch) hipLaunchKernelGGL(rp_kernel<1>, rg, dim3(256), 0, sr, w.sp, w.Rc, w.P, d, n_r, st);
     } else {
-      hipLaunchKernelGGL(split_kernel<3>, sg, dim3(256), 0, sr, L.C, w.Wf, w.sp, d, st);
+      if (L.w_dtype == DT_F16)
+        hipLaunchKernelGGL((split_kernel<3, F16>), sg, dim3(256), 0, sr, L.C, (const uint16_t*)L.W, w.sp, d, st,
+                           state, n_state, L.info);
+      else
+        hipLaunchKernelGGL((split_kernel<3, F32>), sg, dim3(256), 0, sr, L.C, (const float*)L.W, w.sp, d, st, state,
+                           n_state, L.info);
       if (!one_launch) hipLaunchKernelGGL(rp_kernel<3>, rg, dim3(256), 0, sr, w.sp, w.Rc, w.P, d, n_r, st);
     }
     ISPA_TRY(hipGetLastError());
@@ -1725,8 +1736,15 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
     }
   }
   if (L.eps) {
-    hipLaunchKernelGGL(dots_kernel, dim3(DOT_BLOCKS, nb_l), dim3(NT), 0, s, L.D, L.G, w.P, w.Wf, w.Rc, L.delta_w,
-                       d, w.part, st);
+    if (L.w_dtype == DT_BF16)
+      hipLaunchKernelGGL(dots_kernel<BF16>, dim3(DOT_BLOCKS, nb_l), dim3(NT), 0, s, L.D, L.G, w.P,
+                         (const uint16_t*)L.W, w.Rc, L.delta_w, d, w.part, st);
+    else if (L.w_dtype == DT_F16)
+      hipLaunchKernelGGL(dots_kernel<F16>, dim3(DOT_BLOCKS, nb_l), dim3(NT), 0, s, L.D, L.G, w.P,
+                         (const uint16_t*)L.W, w.Rc, L.delta_w, d, w.part, st);
+    else
+      hipLaunchKernelGGL(dots_kernel<F32>, dim3(DOT_BLOCKS, nb_l), dim3(NT), 0, s, L.D, L.G, w.P, (const float*)L.W,
+                         w.Rc, L.delta_w, d, w.part, st);
     ISPA_TRY(hipGetLastError());
     hipLaunchKernelGGL(eps_kernel, dim3(1, nb_l), dim3(NT), 0, s, w.part, DOT_BLOCKS, w.sc, L.eps, st);
     ISPA_TRY(hipGetLastError());

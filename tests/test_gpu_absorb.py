@@ -104,7 +104,7 @@ def _solve_gpu(G, C, D, W, lam, relative, w_dtype="f32", refine=False):
             "info": int(info.item())}
 
 
-@pytest.mark.parametrize("d,n", [(128, 400), (160, 500), (256, 200), (320, 2000)])
+@pytest.mark.parametrize("d,n", [(32, 50), (96, 70), (128, 400), (160, 500), (256, 200), (320, 2000)])
 @pytest.mark.parametrize("refine", [False, True])
 def test_solve_matches_oracle(d, n, refine):
     G, C, D, W = _spd_problem(d, n, d + n)
@@ -201,11 +201,13 @@ def test_bf16_small_end_to_end():
     assert abs(got["eps"] - eps) <= 1e-2 * eps
 
 
-@pytest.mark.parametrize("d,layers,refine", [(256, 3, 0), (1536, 4, 0), (320, 2, 1)])
+@pytest.mark.parametrize("d,layers,refine", [(96, 2, 0), (256, 3, 0), (1536, 4, 0), (320, 2, 1), (2048, 2, 0)])
 def test_batched_solve_equals_per_layer_calls(d, layers, refine):
     """ispa_absorb_solve_batched: every layer's dW, W_new, eps, lambda and info equal those of a
     separate ispa_absorb_solve call, bit for bit; one layer is indefinite (info set, others intact);
-    the per-layer results also match the oracle."""
+    the per-layer results also match the oracle.  A batched call factorises panel by panel, a single
+    call with d <= 2048 in one launch, so this also checks the two factorisations against each other
+    (d = 96: two panels, the second partial; d = 2048: the largest one-launch size)."""
     import kv_cache_attention_ispa_amd as ispa
     t = torch()
     probs = [_spd_problem(d, 2 * d + 7 * l, 100 + l, "bf16") for l in range(layers)]
