@@ -142,6 +142,24 @@ __device__ __forceinline__ void store_wave_tile_64(const f32x16 (&acc)[2][2], ch
   }
 }
 
+// Hand-overs between work-groups on different XCDs.  Device-scope (sc1) buffer accesses bypass the
+// XCD-local L2s, so data that one work-group stores this way and another loads this way needs no cache
+// write-back or invalidation; flags are relaxed device-wide atomics.  A writer's stores complete
+// (s_waitcnt) before it sets the flag, and a reader loads the data only after it has seen the flag.
+constexpr int kSc1 = 16;   // cache policy bits of a buffer access: device scope
+__device__ __forceinline__ f32x4 sc1_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
+}
+__device__ __forceinline__ void sc1_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kSc1);
+}
+__device__ __forceinline__ int flag_load(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void flag_store(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ float wave_max_xor32(float x) {
   return fmaxf(x, __shfl_xor(x, 32));
 }

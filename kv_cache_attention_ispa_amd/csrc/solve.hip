@@ -833,7 +833,6 @@ constexpr int PS_MAX_PANELS = 32;
 constexpr int PS_WORKERS = 253;
 constexpr int PS_WAIT_SPINS = 1 << 21;
 constexpr int PS_STATE_INTS = 64;   // [0] T blocks published, [1] next task, [2] a wait timed out
-constexpr int kSc1 = 16;            // cache policy of a buffer access: device scope (sc1)
 
 struct PsArgs {
   const float* G;
@@ -855,22 +854,16 @@ struct PsArgs {
   int d, nP, n_tasks;
 };
 
-__device__ __forceinline__ int ps_load(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void ps_store(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // one thread: wait until *f >= v; false after a time-out (of this wait or of an earlier one)
 __device__ bool ps_wait(const PsArgs& a, const int* f, int v) {
-  if (ps_load(f) >= v) return true;
+  if (flag_load(f) >= v) return true;
   for (int n = 0; n < PS_WAIT_SPINS; ++n) {
     __builtin_amdgcn_s_sleep(2);
-    if (ps_load(f) >= v) return true;
-    if ((n & 63) == 63 && ps_load(a.st + 2)) return false;
+    if (flag_load(f) >= v) return true;
+    if ((n & 63) == 63 && flag_load(a.st + 2)) return false;
   }
-  ps_store(a.st + 2, 1);
-  ps_store(a.info, -2);
+  flag_store(a.st + 2, 1);
+  flag_store(a.info, -2);
   return false;
 }
 // one thread: wait until f[i] >= v[i] for i < n; the flags are read together, so the satisfied ones
@@ -879,7 +872,7 @@ template <int N>
 __device__ __forceinline__ void ps_wait_all(const PsArgs& a, const int* const (&f)[N], const int (&v)[N], int n) {
   int got[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) got[i] = i < n ? ps_load(f[i]) : 0;
+  for (int i = 0; i < N; ++i) got[i] = i < n ? flag_load(f[i]) : 0;
 #pragma unroll
   for (int i = 0; i < N; ++i)
     if (i < n && got[i] < v[i]) ps_wait(a, f[i], v[i]);
@@ -888,18 +881,12 @@ __device__ __forceinline__ void ps_wait_all(const PsArgs& a, const int* const (&
 __device__ __forceinline__ void ps_publish(int* flag, int v) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) ps_store(flag, v);
+  if (threadIdx.x == 0) flag_store(flag, v);
 }
 
 // device-scope block access through a buffer over a d x d fp32 matrix (offsets past the end read 0)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ps_rsrc(const float* p, int64_t elems) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)(elems * 4), 0x00020000);
-}
-__device__ __forceinline__ f32x4 ps_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
-}
-__device__ __forceinline__ void ps_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kSc1);
 }
 __device__ __forceinline__ float ps_ld1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSc1));
@@ -920,7 +907,7 @@ __device__ __forceinline__ void ps_load_blk(float (*dst)[BP], __amdgpu_buffer_rs
   const int t = threadIdx.x;
   const int rr = t >> 4, c = (t & 15) * 4;
   const int gr = rb * NB + rr, gc = cb * NB + c;
-  *(f32x4*)&dst[rr][c] = ps_ld4(r, ps_off(gr < d && gc < d, (uint32_t)((gr * d + gc) * 4)));
+  *(f32x4*)&dst[rr][c] = sc1_ld4(r, ps_off(gr < d && gc < d, (uint32_t)((gr * d + gc) * 4)));
 }
 // global block (rb, cb) = src + v (src and dst buffers may differ; accumulate = false: dst = v)
 __device__ __forceinline__ void ps_store_blk(__amdgpu_buffer_rsrc_t dst, __amdgpu_buffer_rsrc_t src, int d, int rb,
@@ -969,17 +956,17 @@ __global__ __launch_bounds__(SW_THREADS) void psweep_kernel(PsArgs a) {
   // a 64 x 64 slot (T or X) into LDS / an LDS block into a slot (1024 threads)
   auto slot_load = [&](float(*dst)[BP], __amdgpu_buffer_rsrc_t r, int k) {
     const int rr = t >> 4, c = (t & 15) * 4;
-    *(f32x4*)&dst[rr][c] = ps_ld4(r, (uint32_t)(((k * NB + rr) * NB + c) * 4));
+    *(f32x4*)&dst[rr][c] = sc1_ld4(r, (uint32_t)(((k * NB + rr) * NB + c) * 4));
   };
   auto slot_store = [&](__amdgpu_buffer_rsrc_t r, int k, const float(*src)[BP]) {
     const int rr = t >> 4, c = (t & 15) * 4;
-    ps_st4(r, (uint32_t)(((k * NB + rr) * NB + c) * 4), *(const f32x4*)&src[rr][c]);
+    sc1_st4(r, (uint32_t)(((k * NB + rr) * NB + c) * 4), *(const f32x4*)&src[rr][c]);
   };
   // block (rb, cb) of Mx from LDS (1024 threads), inside the matrix only
   auto blk_store = [&](int rb, int cb, const float(*src)[BP]) {
     const int rr = t >> 4, c = (t & 15) * 4;
     const int gr = rb * NB + rr, gc = cb * NB + c;
-    if (gr < d && gc < d) ps_st4(rM, (uint32_t)((gr * d + gc) * 4), *(const f32x4*)&src[rr][c]);
+    if (gr < d && gc < d) sc1_st4(rM, (uint32_t)((gr * d + gc) * 4), *(const f32x4*)&src[rr][c]);
   };
   const int lane = t & 63, wave = t >> 6;
   const int qm = (wave >> 2) * 16 + 4 * (lane >> 4), qn = (wave & 3) * 16 + (lane & 15);   // quadrant element
@@ -1027,7 +1014,7 @@ __global__ __launch_bounds__(SW_THREADS) void psweep_kernel(PsArgs a) {
       auto side = [&](int s) {
         if (!next) return;
         if (s == 20) {
-          if (tt == 0 && k >= 1) fl = ps_load(verA + (k + 1) * nP + k + 1);
+          if (tt == 0 && k >= 1) fl = flag_load(verA + (k + 1) * nP + k + 1);
         } else if (s == 22) {
           if (tt == 0 && k >= 1 && fl < k) ps_wait(a, verA + (k + 1) * nP + k + 1, k);
         } else if (s == 23) {
@@ -1037,7 +1024,7 @@ __global__ __launch_bounds__(SW_THREADS) void psweep_kernel(PsArgs a) {
             const int gr = (k + 1) * NB + lr, gc = (k + b) * NB + lc;
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-              tmp[b][h] = ps_ld4(src, ps_off(gr < d && gc + 4 * h < d, (uint32_t)((gr * d + gc + 4 * h) * 4)));
+              tmp[b][h] = sc1_ld4(src, ps_off(gr < d && gc + 4 * h < d, (uint32_t)((gr * d + gc + 4 * h) * 4)));
           }
         }
       };
@@ -1076,7 +1063,7 @@ __global__ __launch_bounds__(SW_THREADS) void psweep_kernel(PsArgs a) {
       }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (t == 0) ps_store(a.st, k + 1);
+      if (t == 0) flag_store(a.st, k + 1);
     }
     return;
   }
@@ -1102,7 +1089,7 @@ __global__ __launch_bounds__(SW_THREADS) void psweep_kernel(PsArgs a) {
       ps_load_blk(R2, src, d, r, k);
       ps_load_blk(R3, src, d, r, r);
       if (t == 0) {
-        for (int n = 0; n < 4096 && ps_load(tflag) < k; ++n) {
+        for (int n = 0; n < 4096 && flag_load(tflag) < k; ++n) {
         }
         ps_wait(a, tflag, k);
       }
@@ -1125,7 +1112,7 @@ __global__ __launch_bounds__(SW_THREADS) void psweep_kernel(PsArgs a) {
       blk_store(r, k, R2);
       blk_store(r, r, R3);
       ps_publish(verA + r * nP + k, k);
-      if (t == 0) ps_store(verA + r * nP + r, k);
+      if (t == 0) flag_store(verA + r * nP + r, k);
     }
     return;
   }
@@ -1185,8 +1172,8 @@ __global__ __launch_bounds__(SW_THREADS) void psweep_kernel(PsArgs a) {
       blk_store(r, r, R3);
       ps_publish(verA + r * nP + (k - 1), k - 1);
       if (t == 0) {
-        ps_store(verA + r * nP + k, k - 1);
-        ps_store(verA + r * nP + r, k - 1);
+        flag_store(verA + r * nP + k, k - 1);
+        flag_store(verA + r * nP + r, k - 1);
       }
       // (r, k-1) is the next round's (k, k-2)
       float(*f0)[BP] = Kp;
@@ -1233,7 +1220,7 @@ __global__ __launch_bounds__(SW_THREADS) void psweep_kernel(PsArgs a) {
     const uint32_t toff = (uint32_t)(p * NB * NB * 4);
     auto load_t = [&]() {   // T_p into L2
       const int rr = t >> 4, c = (t & 15) * 4;
-      *(f32x4*)&L2[rr][c] = ps_ld4(rT, toff + (uint32_t)((rr * NB + c) * 4));
+      *(f32x4*)&L2[rr][c] = sc1_ld4(rT, toff + (uint32_t)((rr * NB + c) * 4));
     };
     if (q < nA) {
       // A task: (i, j) -= X_i X_j^T, X = (., p) T_p^T
