@@ -38,20 +38,6 @@ __device__ __forceinline__ P* at_layer(P* p, int64_t step_bytes) {
   return p ? (P*)((char*)p + (int64_t)blockIdx.y * step_bytes) : p;
 }
 
-// Partial sums of the five inner products of epsilon, fp64, one slot per wave of the block or tile
-// that forms them (every slot is written on each call that asks for epsilon):
-//   [4 n_r]        <W, R> of R block q (wave w: slot 4 q + w)
-//   [8 n_p]        <D, P> and <G, P> of the lower P block q - n_r (weight 2 below the diagonal)
-//   [8 nT^2]       <dW, R> and <dW, dW> of output tile t of the last product that writes dW
-// eps_kernel adds them in a fixed order, so the result does not depend on the schedule.
-__host__ __device__ __forceinline__ int dots_doubles(int nT) { return 4 * nT * nT + 4 * nT * (nT + 1) + 8 * nT * nT; }
-
-__device__ __forceinline__ double wave_sum(double x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
 // ------------------------------------------------------------------------------------------
 // Triangular fp32 GEMM on MFMA (32x32x2): C = alpha * op(A) B + beta * C for d x d row-major
 // matrices, op(A) = A lower triangular (TA = false: only k < m0 + 64 contributes to a row block at
@@ -79,11 +65,6 @@ struct TrGemm {
   void* Wn;
   int wdt;
   int64_t sa, sb, sc, sw;   // per-layer steps (bytes) of A, B, C and of W / Wn
-  // optional: per-wave partial sums <C, Rd> and <C, C> of the final C into dots (tile t, wave w:
-  // dots[2 (4 t + w) ..]); Rd and dots step by sd per layer
-  const float* Rd;
-  double* dots;
-  int64_t sd;
 };
 
 // Wn[e] = W[e] + v, rounded to nearest in W's dtype
@@ -111,8 +92,6 @@ __global__ __launch_bounds__(NT, 2) void trgemm_kernel(TrGemm g) {
   g.C = at_layer(g.C, g.sc);
   g.W = at_layer(g.W, g.sw);
   g.Wn = at_layer(g.Wn, g.sw);
-  g.Rd = at_layer(g.Rd, g.sd);
-  g.dots = at_layer(g.dots, g.sd);
   __shared__ __attribute__((aligned(16))) char a0[TG_STAGE], a1[TG_STAGE], a2[TG_STAGE], a3[TG_STAGE];
   __shared__ __attribute__((aligned(16))) char b0[TG_STAGE], b1[TG_STAGE], b2[TG_STAGE], b3[TG_STAGE];
   const int T = g.tiles, d = g.d;
@@ -212,33 +191,18 @@ __global__ __launch_bounds__(NT, 2) void trgemm_kernel(TrGemm g) {
     step(std::integral_constant<int, 3>{}, s + 3);
   }
   __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));   // loads past the last stage (zeros) have landed
-  const int col = n0 + 32 * wn + l32;   // d % 32 == 0: a wave's columns are all in range or all out
-  double s0 = 0.0, s1 = 0.0;
-  if (col < d) {
-    const int64_t e0 = (int64_t)(m0 + 32 * wm + 4 * hi) * d + col;
-    float* cb = g.C + e0;
-    const int rows = d - (m0 + 32 * wm + 4 * hi);
+  const int col = n0 + 32 * wn + l32;
+  if (col >= d) return;
+  const int64_t e0 = (int64_t)(m0 + 32 * wm + 4 * hi) * d + col;
+  float* cb = g.C + e0;
+  const int rows = d - (m0 + 32 * wm + 4 * hi);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 8 * (r >> 2) + (r & 3);
-      if (row < rows) {
-        const float v = g.beta == 0.f ? g.alpha * acc[r] : fmaf(g.alpha, acc[r], g.beta * cb[(int64_t)row * d]);
-        cb[(int64_t)row * d] = v;
-        if (g.Wn) fold_store(g, e0 + (int64_t)row * d, v);
-        if (g.dots) {
-          s0 += (double)v * g.Rd[e0 + (int64_t)row * d];
-          s1 += (double)v * v;
-        }
-      }
-    }
-  }
-  if (g.dots) {
-    s0 = wave_sum(s0);
-    s1 = wave_sum(s1);
-    if (lane == 0) {
-      double* o = g.dots + 2 * (4 * (bm * T + bn) + wave);
-      o[0] = s0;
-      o[1] = s1;
+  for (int r = 0; r < 16; ++r) {
+    const int row = 8 * (r >> 2) + (r & 3);
+    if (row < rows) {
+      const float v = g.beta == 0.f ? g.alpha * acc[r] : fmaf(g.alpha, acc[r], g.beta * cb[(int64_t)row * d]);
+      cb[(int64_t)row * d] = v;
+      if (g.Wn) fold_store(g, e0 + (int64_t)row * d, v);
     }
   }
 }
@@ -253,11 +217,9 @@ struct Steps {
 // C = alpha op(L) B + beta C with L = A lower triangular (op = identity or transpose), per layer
 hipError_t run_trgemm(bool transA, const float* A, int64_t sa, const float* B, int64_t sb, float* C, int64_t sc,
                       int d, float alpha, float beta, int batch, hipStream_t s, const void* W = nullptr,
-                      void* Wn = nullptr, int wdt = 0, int64_t sw = 0, const float* Rd = nullptr,
-                      double* dots = nullptr, int64_t sd = 0) {
+                      void* Wn = nullptr, int wdt = 0, int64_t sw = 0) {
   TrGemm g;
   g.W = W; g.Wn = Wn; g.wdt = wdt;
-  g.Rd = Rd; g.dots = dots; g.sd = sd;
   g.A = A; g.B = B; g.C = C;
   g.sa = sa; g.sb = sb; g.sc = sc; g.sw = sw;
   g.d = d;
@@ -449,14 +411,11 @@ __global__ __launch_bounds__(256) void split_kernel(const float* __restrict__ C,
 
 // One 64 x 64 output block q (R blocks first, then P's lower blocks), computed by the first 256
 // threads as 4 waves of 32 x 32 (every thread of the work-group takes part in the barriers); K steps
-// of 32 pass through registers, one step ahead, into LDS (every part of both operands).  With dots
-// set, each wave also leaves its part of <W, R> (W = the sum of its parts, exact in fp64) or of
-// <D, P> and <G, P>.
+// of 32 pass through registers, one step ahead, into LDS (every part of both operands).
 template <int WPARTS>
 __device__ __forceinline__ void rp_tile(const uint16_t* __restrict__ sp, float* __restrict__ R, float* __restrict__ P,
                                         int d, int n_r, int q, uint16_t (*As)[64][RP_PITCH],
-                                        uint16_t (*Bs)[64][RP_PITCH], const float* __restrict__ D,
-                                        const float* __restrict__ G, double* __restrict__ dots) {
+                                        uint16_t (*Bs)[64][RP_PITCH]) {
   const int64_t dd = (int64_t)d * d;
   const int nT = (d + 63) / 64, t = threadIdx.x;
   const bool on = t < 256;
@@ -518,51 +477,20 @@ __device__ __forceinline__ void rp_tile(const uint16_t* __restrict__ sp, float* 
   }
   float* out = is_p ? P : R;
   const int col = 64 * bj + 32 * wn + (lane & 31);
-  double s0 = 0.0, s1 = 0.0;
   if (on && col < d) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 64 * bi + 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (row < d) {
-        const int64_t e = (int64_t)row * d + col;
-        out[e] = acc[r];
-        if (dots) {
-          if (is_p) {
-            s0 += (double)D[e] * acc[r];
-            s1 += (double)G[e] * acc[r];
-          } else {
-            double w = 0.0;
-#pragma unroll
-            for (int i = 0; i < WPARTS; ++i) w += (double)Cvt<BF16>::to_f(sp[(3 + i) * dd + e]);
-            s0 += w * acc[r];
-          }
-        }
-      }
-    }
-  }
-  if (on && dots) {
-    s0 = wave_sum(s0);
-    s1 = wave_sum(s1);
-    if (lane == 0) {
-      if (is_p) {
-        const double wt = bi > bj ? 2.0 : 1.0;
-        double* o = dots + 4 * n_r + 8 * (q - n_r) + 2 * wave;
-        o[0] = wt * s0;
-        o[1] = wt * s1;
-      } else {
-        dots[4 * q + wave] = s0;
-      }
+      if (row < d) out[(int64_t)row * d + col] = acc[r];
     }
   }
 }
 
 template <int WPARTS>
 __global__ __launch_bounds__(256) void rp_kernel(const uint16_t* __restrict__ sp, float* __restrict__ R,
-                                                 float* __restrict__ P, int d, int n_r, Steps st, const float* D,
-                                                 const float* G, double* dots) {
+                                                 float* __restrict__ P, int d, int n_r, Steps st) {
   __shared__ __attribute__((aligned(16))) uint16_t As[3][64][RP_PITCH], Bs[WPARTS][64][RP_PITCH];
-  rp_tile<WPARTS>(at_layer(sp, st.ws), at_layer(R, st.ws), at_layer(P, st.ws), d, n_r, blockIdx.x, As, Bs,
-                  at_layer(D, st.mat), at_layer(G, st.mat), at_layer(dots, st.ws));
+  rp_tile<WPARTS>(at_layer(sp, st.ws), at_layer(R, st.ws), at_layer(P, st.ws), d, n_r, blockIdx.x, As, Bs);
 }
 
 // Quadrant qd (rows 16 (qd / 4) .., columns 16 (qd % 4) ..) of X op(Y) over k < 64 (op(Y) = Y^T when
@@ -918,8 +846,6 @@ struct PsArgs {
   float* Rc;            // R = C W
   float* P;             // lower block triangle of W W^T (with eps)
   int wparts, n_r, n_rp, rp_share;   // R blocks, R and P blocks, R/P blocks per panel
-  const float* D;                    // for the epsilon partial sums (dots), when asked for
-  double* dots;
   int* info;
   Scalars* sc;
   float lam;
@@ -1284,8 +1210,8 @@ __global__ __launch_bounds__(SW_THREADS) void psweep_kernel(PsArgs a) {
       // R / P block p * share + q
       uint16_t(*As)[64][RP_PITCH] = (uint16_t(*)[64][RP_PITCH]) & B0[0][0];
       uint16_t(*Bs)[64][RP_PITCH] = (uint16_t(*)[64][RP_PITCH]) & B1[0][0];
-      if (a.wparts == 1) rp_tile<1>(a.sp, a.Rc, a.P, d, a.n_r, p * a.rp_share + q, As, Bs, a.D, a.G, a.dots);
-      else rp_tile<3>(a.sp, a.Rc, a.P, d, a.n_r, p * a.rp_share + q, As, Bs, a.D, a.G, a.dots);
+      if (a.wparts == 1) rp_tile<1>(a.sp, a.Rc, a.P, d, a.n_r, p * a.rp_share + q, As, Bs);
+      else rp_tile<3>(a.sp, a.Rc, a.P, d, a.n_r, p * a.rp_share + q, As, Bs);
       __syncthreads();
       continue;
     }
@@ -1473,28 +1399,65 @@ __global__ __launch_bounds__(NT, 2) void gemm64_kernel(const float* A, int64_t s
       }
 }
 
-// epsilon from the partial sums (dots layout above), added in a fixed order: <D,P>, <G,P>, <W,R>,
-// <dW,R>, <dW,dW>.
-__global__ __launch_bounds__(NT) void eps_kernel(const double* dots, int nT, const Scalars* sc, float* eps,
+// Partial dot products for epsilon: <D,P>, <G,P>, <W,R>, <dW,R>, <dW,dW> (fp64 per block), row by row.
+// Only the lower 64-block triangle of P is formed; D and G are symmetric, so blocks below the
+// diagonal count twice and the upper ones are skipped.
+template <typename WT>
+__global__ __launch_bounds__(NT) void dots_kernel(const float* D, const float* G, const float* P,
+                                                  const typename WT::storage* W, const float* R, const float* dW,
+                                                  int d, double* part, Steps st) {
+  D = at_layer(D, st.mat);
+  G = at_layer(G, st.mat);
+  dW = at_layer(dW, st.mat);
+  P = at_layer(P, st.ws);
+  W = at_layer(W, st.wmat);
+  R = at_layer(R, st.ws);
+  part = at_layer(part, st.ws);
+  double s[5] = {0, 0, 0, 0, 0};
+  for (int r = blockIdx.x; r < d; r += gridDim.x)
+    for (int c = 4 * (int)threadIdx.x; c < d; c += 4 * NT) {
+      const int64_t e = (int64_t)r * d + c;
+      const f32x4 rv = *(const f32x4*)(R + e), dv = *(const f32x4*)(dW + e);
+      f32x4 wv;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) wv[u] = Cvt<WT>::to_f(W[e + u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s[2] += (double)wv[u] * rv[u];
+        s[3] += (double)dv[u] * rv[u];
+        s[4] += (double)dv[u] * dv[u];
+      }
+      const int rb = r / NB, cb = c / NB;
+      if (rb >= cb) {
+        const double wt = rb > cb ? 2.0 : 1.0;
+        const f32x4 pv = *(const f32x4*)(P + e), Dv = *(const f32x4*)(D + e), gv = *(const f32x4*)(G + e);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          s[0] += wt * ((double)Dv[u] * pv[u]);
+          s[1] += wt * ((double)gv[u] * pv[u]);
+        }
+      }
+    }
+  __shared__ double red[5][NT];
+  for (int q = 0; q < 5; ++q) red[q][threadIdx.x] = s[q];
+  __syncthreads();
+  for (int o = NT / 2; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o)
+      for (int q = 0; q < 5; ++q) red[q][threadIdx.x] += red[q][threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x < 5) part[blockIdx.x * 5 + threadIdx.x] = red[threadIdx.x][0];
+}
+
+__global__ __launch_bounds__(NT) void eps_kernel(const double* part, int nblk, const Scalars* sc, float* eps,
                                                  Steps st) {
-  dots = at_layer(dots, st.ws);
+  part = at_layer(part, st.ws);
   sc = at_layer(sc, st.ws);
   eps = at_layer(eps, (int64_t)sizeof(float));
-  const int n_r = nT * nT, n_p = nT * (nT + 1) / 2;
-  const double* dr = dots;
-  const double* dp = dots + 4 * n_r;
-  const double* dt = dp + 8 * n_p;
   __shared__ double red[5][NT];
   double t[5] = {0, 0, 0, 0, 0};
-  for (int b = threadIdx.x; b < 4 * n_p; b += NT) {
-    t[0] += dp[2 * b];
-    t[1] += dp[2 * b + 1];
-  }
-  for (int b = threadIdx.x; b < 4 * n_r; b += NT) {
-    t[2] += dr[b];
-    t[3] += dt[2 * b];
-    t[4] += dt[2 * b + 1];
-  }
+  for (int b = threadIdx.x; b < nblk; b += NT)
+    for (int q = 0; q < 5; ++q) t[q] += part[b * 5 + q];
   for (int q = 0; q < 5; ++q) red[q][threadIdx.x] = t[q];
   __syncthreads();
   for (int o = NT / 2; o > 0; o >>= 1) {
@@ -1510,6 +1473,8 @@ __global__ __launch_bounds__(NT) void eps_kernel(const double* dots, int nT, con
   }
 }
 
+constexpr int DOT_BLOCKS = 512;
+
 struct WsLayout {
   float* Mx;   // d x d
   float* Bx;   // d x d: I, then L^-1 (per-panel launches); the identity part as updated (one launch)
@@ -1519,7 +1484,7 @@ struct WsLayout {
   float* P;    // d x d (W W^T)
   float* T;    // NB x NB slots, one per panel (at least three)
   Scalars* sc;
-  double* dots;   // epsilon partial sums (dots_doubles)
+  double* part;
   double* R64; // d x d, C W accumulated in fp64 (refinement only)
   uint16_t* sp; // 9 d x d bf16: three parts of C, of W and of W^T (split_kernel)
   float* Linv; // d x d: L^-1 (one-launch sweep)
@@ -1545,7 +1510,7 @@ WsLayout carve(void* ws, int d) {
   w.T = (float*)p; p += t_slots_bytes(d);
   w.Xs = (float*)p; p += t_slots_bytes(d);
   w.sc = (Scalars*)p; p += 256;
-  w.dots = (double*)p; p += (dots_doubles(n_panels(d)) * sizeof(double) + 255) / 256 * 256;
+  w.part = (double*)p; p += DOT_BLOCKS * 5 * sizeof(double);
   w.R64 = (double*)p; p += (size_t)d * d * sizeof(double);
   w.st = (int*)p; p += (state_bytes(d) + 255) / 256 * 256;
   w.sp = (uint16_t*)p;
@@ -1590,8 +1555,7 @@ AuxStream* aux_stream() {
 }  // namespace
 
 size_t solve_workspace_bytes(int d) {
-  const size_t b = (size_t)d * d * sizeof(float) * 7 + 2 * t_slots_bytes(d) + 256 +
-                   (dots_doubles(n_panels(d)) * sizeof(double) + 255) / 256 * 256 +
+  const size_t b = (size_t)d * d * sizeof(float) * 7 + 2 * t_slots_bytes(d) + 256 + DOT_BLOCKS * 5 * sizeof(double) +
                    (size_t)d * d * sizeof(double) + (state_bytes(d) + 255) / 256 * 256 + (size_t)d * d * 18 + 256;
   return (b + 255) / 256 * 256;
 }
@@ -1608,10 +1572,6 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
   const int eb = (int)((dd + NT - 1) / NT > 2048 ? 2048 : (dd + NT - 1) / NT);
   const dim3 eg(eb, nb_l);
   const int nP = n_panels(d);
-  // epsilon partial sums: R and P blocks (from the R/P products), then the tiles of the last dW product
-  const int nT_all = nP;
-  double* dots = L.eps ? w.dots : nullptr;
-  double* dots_t = L.eps ? w.dots + 4 * nT_all * nT_all + 4 * nT_all * (nT_all + 1) : nullptr;
   // One layer with few panels: the whole sweep in one launch (the trailing updates then fit beside
   // the diagonal chain); otherwise one launch per panel, with the layers side by side.
   const bool one_launch = nb_l == 1 && nP <= PS_MAX_PANELS;
@@ -1654,8 +1614,7 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
     if (L.w_dtype == DT_BF16) {
       hipLaunchKernelGGL((split_kernel<1, BF16>), sg, dim3(256), 0, sr, L.C, (const uint16_t*)L.W, w.sp, d, st, state,
                          n_state, L.info);
-      if (!one_launch)
-        hipLaunchKernelGGL(rp_kernel<1>, rg, dim3(256), 0, sr, w.sp, w.Rc, w.P, d, n_r, st, L.D, L.G, dots);
+      if (!one_launch) hipLaunchKernelGGL(rp_kernel<1>, rg, dim3(256), 0, sr, w.sp, w.Rc, w.P, d, n_r, st);
     } else {
       if (L.w_dtype == DT_F16)
         hipLaunchKernelGGL((split_kernel<3, F16>), sg, dim3(256), 0, sr, L.C, (const uint16_t*)L.W, w.sp, d, st,
@@ -1663,8 +1622,7 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
       else
         hipLaunchKernelGGL((split_kernel<3, F32>), sg, dim3(256), 0, sr, L.C, (const float*)L.W, w.sp, d, st, state,
                            n_state, L.info);
-      if (!one_launch)
-        hipLaunchKernelGGL(rp_kernel<3>, rg, dim3(256), 0, sr, w.sp, w.Rc, w.P, d, n_r, st, L.D, L.G, dots);
+      if (!one_launch) hipLaunchKernelGGL(rp_kernel<3>, rg, dim3(256), 0, sr, w.sp, w.Rc, w.P, d, n_r, st);
     }
     ISPA_TRY(hipGetLastError());
     if (ax) ISPA_TRY(hipEventRecord(ax->join, sr));
@@ -1691,8 +1649,6 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
     a.Rc = w.Rc;
     a.P = w.P;
     a.wparts = L.w_dtype == DT_BF16 ? 1 : 3;
-    a.D = L.D;
-    a.dots = dots;
     a.n_r = nT * nT;
     a.n_rp = a.n_r + (L.eps ? nT * (nT + 1) / 2 : 0);
     a.rp_share = (a.n_rp + nP - 1) / nP;
@@ -1747,8 +1703,7 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
   // dW = (L^-1)^T Z   (op(A) upper triangular: only k >= m0 contributes)
   // (W_new = W + dW is written by the last product that updates dW)
   ISPA_TRY(run_trgemm(true, Li, st.ws, w.Mx, st.ws, L.delta_w, st.mat, d, 1.f, 0.f, nb_l, s, L.W,
-                      L.refine > 0 ? nullptr : L.w_new, L.w_dtype, st.wmat, w.Rc, L.refine > 0 ? nullptr : dots_t,
-                      st.ws));
+                      L.refine > 0 ? nullptr : L.w_new, L.w_dtype, st.wmat));
   if (L.refine > 0) {
     // iterative refinement: r = C W - (G + lambda I) dW with fp64 accumulation (C W formed once in
     // fp64), then dW += (L^-1)^T (L^-1 r) with the fp32 factor
@@ -1764,12 +1719,21 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
       // t = L^-1 r (into Mx, no longer needed), dW += (L^-1)^T t
       ISPA_TRY(run_trgemm(false, Li, st.ws, w.Rs, st.ws, w.Mx, st.ws, d, 1.f, 0.f, nb_l, s));
       ISPA_TRY(run_trgemm(true, Li, st.ws, w.Mx, st.ws, L.delta_w, st.mat, d, 1.f, 1.f, nb_l, s, L.W,
-                          it + 1 == L.refine ? L.w_new : nullptr, L.w_dtype, st.wmat, w.Rc,
-                          it + 1 == L.refine ? dots_t : nullptr, st.ws));
+                          it + 1 == L.refine ? L.w_new : nullptr, L.w_dtype, st.wmat));
     }
   }
   if (L.eps) {
-    hipLaunchKernelGGL(eps_kernel, dim3(1, nb_l), dim3(NT), 0, s, w.dots, nT_all, w.sc, L.eps, st);
+    if (L.w_dtype == DT_BF16)
+      hipLaunchKernelGGL(dots_kernel<BF16>, dim3(DOT_BLOCKS, nb_l), dim3(NT), 0, s, L.D, L.G, w.P,
+                         (const uint16_t*)L.W, w.Rc, L.delta_w, d, w.part, st);
+    else if (L.w_dtype == DT_F16)
+      hipLaunchKernelGGL(dots_kernel<F16>, dim3(DOT_BLOCKS, nb_l), dim3(NT), 0, s, L.D, L.G, w.P,
+                         (const uint16_t*)L.W, w.Rc, L.delta_w, d, w.part, st);
+    else
+      hipLaunchKernelGGL(dots_kernel<F32>, dim3(DOT_BLOCKS, nb_l), dim3(NT), 0, s, L.D, L.G, w.P, (const float*)L.W,
+                         w.Rc, L.delta_w, d, w.part, st);
+    ISPA_TRY(hipGetLastError());
+    hipLaunchKernelGGL(eps_kernel, dim3(1, nb_l), dim3(NT), 0, s, w.part, DOT_BLOCKS, w.sc, L.eps, st);
     ISPA_TRY(hipGetLastError());
   }
   return hipSuccess;
