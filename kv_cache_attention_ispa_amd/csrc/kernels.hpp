@@ -92,6 +92,11 @@ hipError_t launch_quant_rows(int dtype, const void* x, int64_t ldx, int rows, in
                              float* scales, hipStream_t s);
 hipError_t launch_quant_weight(int dtype, const void* w, int d_in, int d_out, uint8_t* wq_t, float* scales,
                                hipStream_t s);
+// out (fp32 d x d) = sum over n_seg segments g of A_g B_g^T, A_g / B_g the bf16 planes (d x d, row-major,
+// consecutive) numbered (a_planes >> 4 g) & 15 and (b_planes >> 4 g) & 15; layer y of batch at
+// planes + y layer_bytes and out + y layer_bytes.  d % 64 == 0, 9 d^2 * 2 bytes of planes < 2^32.
+hipError_t launch_nt_segments(const uint16_t* planes, float* out, int d, int n_seg, int a_planes, int b_planes,
+                              int batch, int64_t layer_bytes, hipStream_t s);
 hipError_t launch_proj8(int out_dtype, const uint8_t* aq, const float* sa, const uint8_t* wq_t, const float* sw,
                         void* out, int m, int n, int k, hipStream_t s);
 
@@ -118,5 +123,23 @@ struct SolveLaunch {
 };
 size_t solve_workspace_bytes(int d);
 hipError_t launch_solve(const SolveLaunch& L, hipStream_t s);
+
+// Refinement residual r = C W - (G + lambda I) dW from int8 digit products (refine.hip), per layer
+// (blockIdx.y) with byte steps s_mat (C, G, dW), s_wmat (W), s_ws (ws, r) and s_lambda (lambda).
+struct ResidualLaunch {
+  int batch, d;
+  const float* C;
+  const float* G;
+  const void* W;
+  int w_dtype;
+  const float* dW;
+  const float* lambda;   // device
+  float* r;
+  void* ws;              // residual_workspace_bytes(d) per layer
+  int rows_too;          // 1: (re)form the digits of [C | -G] (once per solve)
+  int64_t s_mat, s_wmat, s_ws, s_lambda;
+};
+size_t residual_workspace_bytes(int d);
+hipError_t launch_residual(const ResidualLaunch& L, hipStream_t s);
 
 }  // namespace ispa

@@ -40,12 +40,26 @@ constexpr int NT_ALOADS = NT_ATILE / 1024 / 4, NT_BLOADS = NT_BTILE / 1024 / 4; 
 constexpr int NT_LOADS = NT_ALOADS + NT_BLOADS;
 __device__ __forceinline__ int nt_off(int row, int chunk) { return row * NT_BK + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
-// KIND 0: E4M3 codes (scaled epilogue); otherwise the 16-bit type TIn.  TOut: type of out.
-// row_bytes: bytes of a row of either operand, a multiple of 128.
+// KIND 3 (segmented, for the solve's R = C W and P = W W^T): both operands are bf16 planes of one
+// d x d row-major array of planes (a == b), and the k sequence is n_seg segments of d values, segment
+// g pairing plane a_planes[g] of A with plane b_planes[g] of B (4 bits each); out is fp32 [m][n],
+// written directly; layer blockIdx.y at a + layer * layer_bytes and out + layer * layer_bytes.
+struct NtSeg {
+  int n_seg, a_planes, b_planes;
+  int64_t plane_bytes, layer_bytes;
+};
+
+// KIND 0: E4M3 codes (scaled epilogue); 1, 2: the 16-bit type TIn; 3: segmented (NtSeg).  TOut: type
+// of out.  row_bytes: bytes of a row of either operand, a multiple of 128.
 template <int KIND, typename TIn, typename TOut>
 __global__ __launch_bounds__(768, 1) void gemm_nt_kernel(const uint8_t* a, const uint8_t* b, const float* sa,
                                                           const float* sw, void* out, int m, int n, int row_bytes,
-                                                          int tiles_m, int tiles_n) {
+                                                          int tiles_m, int tiles_n, NtSeg seg) {
+  if constexpr (KIND == 3) {
+    a += (int64_t)blockIdx.y * seg.layer_bytes;
+    b = a;
+    out = (char*)out + (int64_t)blockIdx.y * seg.layer_bytes;
+  }
   __shared__ __attribute__((aligned(16))) uint8_t a0[NT_ATILE], a1[NT_ATILE], a2[NT_ATILE];
   __shared__ __attribute__((aligned(16))) uint8_t b0[NT_BTILE], b1[NT_BTILE], b2[NT_BTILE];
   __shared__ float sa_t[256], sw_t[128];
@@ -68,7 +82,8 @@ __global__ __launch_bounds__(768, 1) void gemm_nt_kernel(const uint8_t* a, const
     else return b2;
   };
   auto barrier = [&]() { lds_barrier(); };
-  const int n_st = row_bytes / NT_BK;
+  const int seg_st = row_bytes / NT_BK;                            // stages per segment (KIND 3)
+  const int n_st = KIND == 3 ? seg.n_seg * seg_st : row_bytes / NT_BK;
 
   // One barrier per stage: at barrier s, stage s is in LDS and the multipliers are done with stage
   // s - 1; the multipliers then run stage s while the loaders refill slot (s - 1) % 3 with stage s + 2
@@ -79,35 +94,51 @@ __global__ __launch_bounds__(768, 1) void gemm_nt_kernel(const uint8_t* a, const
       sa_t[t] = m0 + t < m ? sa[m0 + t] : 0.f;
       if (t < 128) sw_t[t] = n0 + t < n ? sw[n0 + t] : 0.f;
     }
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a + (int64_t)m0 * row_bytes), (short)0, min(256, m - m0) * row_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(b + (int64_t)n0 * row_bytes), (short)0, min(128, n - n0) * row_bytes, 0x00020000);
+    // KIND 3: one buffer over all planes of the layer; rows past the matrix load zeros through an
+    // out-of-range offset (the next plane follows them)
+    const __amdgpu_buffer_rsrc_t ra = KIND == 3
+        ? __builtin_amdgcn_make_buffer_rsrc((void*)a, (short)0, (int)0xFFFFFFF0u, 0x00020000)
+        : __builtin_amdgcn_make_buffer_rsrc((void*)(a + (int64_t)m0 * row_bytes), (short)0,
+                                            min(256, m - m0) * row_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = KIND == 3
+        ? __builtin_amdgcn_make_buffer_rsrc((void*)b, (short)0, (int)0xFFFFFFF0u, 0x00020000)
+        : __builtin_amdgcn_make_buffer_rsrc((void*)(b + (int64_t)n0 * row_bytes), (short)0,
+                                            min(128, n - n0) * row_bytes, 0x00020000);
     // load instruction i of a tile covers its rows 8 i .. 8 i + 7: lane l fills byte 16 l of that KiB,
     // i.e. row 8 i + l / 8 at physical chunk l % 8, which holds logical chunk (l % 8) ^ (4 (i % 2) + l / 16);
     // loader w issues A instructions 8 w .. 8 w + 7 and B instructions 4 w .. 4 w + 3
     uint32_t aoff[NT_ALOADS], boff[NT_BLOADS];
+    bool ain[NT_ALOADS], bin[NT_BLOADS];
 #pragma unroll
     for (int j = 0; j < NT_ALOADS; ++j) {
-      const int i = NT_ALOADS * w + j, c = (lane & 7) ^ (4 * (i & 1) + (lane >> 4));
-      aoff[j] = (uint32_t)((8 * i + (lane >> 3)) * row_bytes) + 16u * c;
+      const int i = NT_ALOADS * w + j, c = (lane & 7) ^ (4 * (i & 1) + (lane >> 4)), row = 8 * i + (lane >> 3);
+      aoff[j] = (uint32_t)(((KIND == 3 ? m0 : 0) + row) * row_bytes) + 16u * c;
+      ain[j] = KIND != 3 || m0 + row < m;
     }
 #pragma unroll
     for (int j = 0; j < NT_BLOADS; ++j) {
-      const int i = NT_BLOADS * w + j, c = (lane & 7) ^ (4 * (i & 1) + (lane >> 4));
-      boff[j] = (uint32_t)((8 * i + (lane >> 3)) * row_bytes) + 16u * c;
+      const int i = NT_BLOADS * w + j, c = (lane & 7) ^ (4 * (i & 1) + (lane >> 4)), row = 8 * i + (lane >> 3);
+      boff[j] = (uint32_t)(((KIND == 3 ? n0 : 0) + row) * row_bytes) + 16u * c;
+      bin[j] = KIND != 3 || n0 + row < n;
     }
+    constexpr uint32_t kOutOfRange = KIND == 3 ? 0xFFFFFFF0u : 0x80000000u;
     auto issue = [&](uint8_t* as, uint8_t* bs, int st) {
-      const uint32_t k0 = (uint32_t)st * NT_BK;
       const bool ok = st < n_st;
+      uint32_t ka = (uint32_t)st * NT_BK, kb = ka;
+      if constexpr (KIND == 3) {
+        const int g = ok ? st / seg_st : 0;
+        const uint32_t k0 = (uint32_t)(st - g * seg_st) * NT_BK;
+        ka = (uint32_t)(((seg.a_planes >> (4 * g)) & 15) * seg.plane_bytes) + k0;
+        kb = (uint32_t)(((seg.b_planes >> (4 * g)) & 15) * seg.plane_bytes) + k0;
+      }
 #pragma unroll
       for (int j = 0; j < NT_ALOADS; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(as + 1024 * (NT_ALOADS * w + j)), 16,
-                                                 ok ? aoff[j] + k0 : 0x80000000u, 0, 0, 0);
+                                                 ok && ain[j] ? aoff[j] + ka : kOutOfRange, 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < NT_BLOADS; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(bs + 1024 * (NT_BLOADS * w + j)), 16,
-                                                 ok ? boff[j] + k0 : 0x80000000u, 0, 0, 0);
+                                                 ok && bin[j] ? boff[j] + kb : kOutOfRange, 0, 0, 0);
     };
     issue(a0, b0, 0);
     issue(a1, b1, 1);
@@ -212,11 +243,28 @@ __global__ __launch_bounds__(768, 1) void gemm_nt_kernel(const uint8_t* a, const
     mstep(std::integral_constant<int, 2>{});
   }
   barrier();                                   // the ring is idle
-  uint8_t* mine = (wave < 4 ? a0 : a1) + 8192 * (wave & 3);
-  store_wave_tile_64<TOut>(acc, (char*)mine, (typename TOut::storage*)out, n, m0, n0, m, n, [&](int row, int col) {
-    if constexpr (KIND == 0) return sa_t[row] * sw_t[col];
-    else return 1.f;
-  });
+  if constexpr (KIND == 3) {
+    // fp32 out, register r of lane l of block (mi, ni): row 64 wm + 32 mi + 8 (r / 4) + 4 (l / 32) + r % 4,
+    // column 64 wn + 32 ni + l % 32
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int col = n0 + 64 * wn + 32 * ni + (lane & 31);
+        if (col >= n) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + 64 * wm + 32 * mi + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (row < m) ((float*)out)[(int64_t)row * n + col] = acc[mi][ni][r];
+        }
+      }
+  } else {
+    uint8_t* mine = (wave < 4 ? a0 : a1) + 8192 * (wave & 3);
+    store_wave_tile_64<TOut>(acc, (char*)mine, (typename TOut::storage*)out, n, m0, n0, m, n, [&](int row, int col) {
+      if constexpr (KIND == 0) return sa_t[row] * sw_t[col];
+      else return 1.f;
+    });
+  }
 }
 
 // W [k, n] 16-bit row-major -> W^T [n, k]; k and n are multiples of 16.  A work-group moves a
@@ -264,7 +312,7 @@ hipError_t launch_nt(const void* a, const void* b, const float* sa, const float*
                      int row_bytes, hipStream_t s) {
   const int tm = (m + 255) / 256, tn = (n + 127) / 128;
   hipLaunchKernelGGL((gemm_nt_kernel<KIND, TIn, TOut>), dim3(tm * tn), dim3(768), 0, s, (const uint8_t*)a,
-                     (const uint8_t*)b, sa, sw, out, m, n, row_bytes, tm, tn);
+                     (const uint8_t*)b, sa, sw, out, m, n, row_bytes, tm, tn, NtSeg{});
   return hipGetLastError();
 }
 
@@ -285,6 +333,20 @@ hipError_t launch_proj(const ProjLaunch& L, hipStream_t s) {
   const hipError_t e = launch_transpose16(L.b, L.k, L.n, L.bt, s);
   if (e != hipSuccess) return e;
   return launch_proj_nt(L.io, L.m, L.n, L.k, L.a, L.bt, L.out, s);
+}
+
+hipError_t launch_nt_segments(const uint16_t* planes, float* out, int d, int n_seg, int a_planes, int b_planes,
+                              int batch, int64_t layer_bytes, hipStream_t s) {
+  const int t = (d + 255) / 256, tn = (d + 127) / 128;
+  NtSeg g;
+  g.n_seg = n_seg;
+  g.a_planes = a_planes;
+  g.b_planes = b_planes;
+  g.plane_bytes = (int64_t)d * d * 2;
+  g.layer_bytes = layer_bytes;
+  hipLaunchKernelGGL((gemm_nt_kernel<3, BF16, F32>), dim3(t * tn, batch), dim3(768), 0, s, (const uint8_t*)planes,
+                     (const uint8_t*)planes, nullptr, nullptr, (void*)out, d, d, d * 2, t, tn, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_proj8(int out_dtype, const uint8_t* aq, const float* sa, const uint8_t* wq_t, const float* sw,

@@ -8,8 +8,8 @@
 //   R = C W;   G + lambda I = L L^T (blocked right-looking Cholesky, fp32);
 //   the sweep also carries the identity, which leaves L^-1 when it ends; then
 //   Z = L^-1 R and dW = (L^-1)^T Z are two triangular GEMMs.
-//   Optional iterative refinement (a given number of steps): r = C W - (G + lambda I) dW
-//   accumulated in fp64 (C W formed once in fp64), then dW += (L^-1)^T (L^-1 r).
+//   Optional iterative refinement (a given number of steps): r = C W - (G + lambda I) dW to about
+//   35 bits from exact int8 products of fixed-point digits (refine.hip), then dW += (L^-1)^T (L^-1 r).
 //
 // "Dynamic layer selection" ranks layers by the reconstruction error epsilon;
 // it is evaluated here from the statistics alone (D = dA^T dA, P = W W^T):
@@ -241,24 +241,16 @@ struct Scalars {
 };
 
 // Per-panel launches: Mx = G (lambda joins the diagonal blocks as the sweep factors them) and Bx = I
-// (becomes L^-1).  With refinement: Wf = W as fp32 (the fp64 product C W reads it).  Either part may
-// be off (null pointers).
-template <typename WT>
-__global__ __launch_bounds__(NT) void setup_kernel(const float* G, const typename WT::storage* W, int d, float* Mx,
-                                                   float* Bx, float* Wf, Steps st) {
+// (becomes L^-1).
+__global__ __launch_bounds__(NT) void setup_kernel(const float* G, int d, float* Mx, float* Bx, Steps st) {
   G = at_layer(G, st.mat);
-  W = at_layer(W, st.wmat);
   Mx = at_layer(Mx, st.ws);
   Bx = at_layer(Bx, st.ws);
-  Wf = at_layer(Wf, st.ws);
   const int64_t n = (int64_t)d * d;
   for (int64_t e = blockIdx.x * (int64_t)NT + threadIdx.x; e < n; e += (int64_t)gridDim.x * NT) {
-    if (Mx) {
-      const int i = (int)(e / d), j = (int)(e % d);
-      Mx[e] = G[e];
-      Bx[e] = (i == j) ? 1.f : 0.f;
-    }
-    if (Wf) Wf[e] = Cvt<WT>::to_f(W[e]);
+    const int i = (int)(e / d), j = (int)(e % d);
+    Mx[e] = G[e];
+    Bx[e] = (i == j) ? 1.f : 0.f;
   }
 }
 
@@ -1301,104 +1293,6 @@ __global__ __launch_bounds__(SW_THREADS) void psweep_kernel(PsArgs a) {
   }
 }
 
-// out = A B accumulated in fp64 (A, B fp32 [d, d] row-major; products of fp32 values are exact in
-// fp64) on v_mfma_f64_16x16x4f64.  128 x 128 tiles of 4 waves (2 x 2 of 64 x 64, each 4 x 4 blocks of
-// 16 x 16); k in stages of 16 staged through LDS as fp64 (A row-major with an odd pitch, so the 16
-// rows a quarter-wave reads at one k fall in distinct banks; B row-major), the next stage's global
-// loads held in registers while the current one multiplies; one barrier per stage.
-// MFMA operands: lane l holds A[16 i + l%16][4 s + l/16] and B[4 s + l/16][16 j + l%16]; result
-// register r of lane l is element (16 i + l/16 + 4 r, 16 j + l%16) (rows interleaved; a probe of the
-// instruction on the device fixed this).
-// MODE 0: R64 = A B (fp64 store).  MODE 1: the refinement residual r = R64 - lambda dW - A B with
-// A = G and B = dW (fp32 store).  d is a multiple of 32.
-typedef double f64x4 __attribute__((ext_vector_type(4)));
-typedef double f64x2 __attribute__((ext_vector_type(2)));
-constexpr int G64_AP = 17, G64_BP = 130;   // LDS pitches in doubles
-
-template <int MODE>
-__global__ __launch_bounds__(NT, 2) void gemm64_kernel(const float* A, int64_t sa, const float* B, int64_t sb, int d,
-                                                       const Scalars* sc, double* R64, float* r, int64_t sws) {
-  A = at_layer(A, sa);
-  B = at_layer(B, sb);
-  sc = at_layer(sc, sws);
-  R64 = at_layer(R64, sws);
-  r = at_layer(r, sws);
-  __shared__ double as[2][128 * G64_AP];
-  __shared__ __attribute__((aligned(16))) double bs[2][16 * G64_BP];
-  const int tpd = (d + 127) / 128;
-  const int i0 = (blockIdx.x / tpd) * 128, j0 = (blockIdx.x % tpd) * 128;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, lr = lane & 15, lk = lane >> 4;
-  f64x4 acc[4][4];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f64x4{0.0, 0.0, 0.0, 0.0};
-  // stage loads: A rows i0 + q/4, columns k0 + 4 (q%4) .. +3; B row k0 + q/32, columns j0 + 4 (q%32) .. +3
-  f32x4 ra[2], rb[2];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int q = tid + NT * h;
-      const int ar = q >> 2, ac = 4 * (q & 3), br = q >> 5, bc = 4 * (q & 31);
-      ra[h] = i0 + ar < d ? *(const f32x4*)(A + (int64_t)(i0 + ar) * d + k0 + ac) : f32x4{0.f, 0.f, 0.f, 0.f};
-      rb[h] = j0 + bc < d ? *(const f32x4*)(B + (int64_t)(k0 + br) * d + j0 + bc) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int q = tid + NT * h;
-      const int ar = q >> 2, ac = 4 * (q & 3), br = q >> 5, bc = 4 * (q & 31);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) as[buf][ar * G64_AP + ac + e] = (double)ra[h][e];
-      double* bp = &bs[buf][br * G64_BP + bc];
-      *(f64x2*)bp = f64x2{(double)rb[h][0], (double)rb[h][1]};
-      *(f64x2*)(bp + 2) = f64x2{(double)rb[h][2], (double)rb[h][3]};
-    }
-  };
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  const int n_st = d / 16;
-  for (int st = 0; st < n_st; ++st) {
-    const int cur = st & 1;
-    if (st + 1 < n_st) gload(16 * (st + 1));
-    const double* ap = &as[cur][(64 * wm + lr) * G64_AP + lk];
-    const double* bp = &bs[cur][lk * G64_BP + 64 * wn + lr];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      double af[4], bf[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) af[mi] = ap[16 * mi * G64_AP + 4 * kk];
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) bf[ni] = bp[4 * kk * G64_BP + 16 * ni];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = __builtin_amdgcn_mfma_f64_16x16x4f64(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
-    }
-    if (st + 1 < n_st) sstore(cur ^ 1);
-    __syncthreads();
-  }
-  const double lam = MODE == 1 ? (double)sc->lambda : 0.0;
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i = i0 + 64 * wm + 16 * mi + lk + 4 * q, j = j0 + 64 * wn + 16 * ni + lr;
-        if (i < d && j < d) {
-          const int64_t e = (int64_t)i * d + j;
-          if (MODE == 0)
-            R64[e] = acc[mi][ni][q];
-          else
-            r[e] = (float)(R64[e] - lam * (double)B[e] - acc[mi][ni][q]);
-        }
-      }
-}
-
 // Partial dot products for epsilon: <D,P>, <G,P>, <W,R>, <dW,R>, <dW,dW> (fp64 per block), row by row.
 // Only the lower 64-block triangle of P is formed; D and G are symmetric, so blocks below the
 // diagonal count twice and the upper ones are skipped.
@@ -1480,12 +1374,11 @@ struct WsLayout {
   float* Bx;   // d x d: I, then L^-1 (per-panel launches); the identity part as updated (one launch)
   float* Rs;   // d x d: refinement residual
   float* Rc;   // d x d
-  float* Wf;   // d x d
   float* P;    // d x d (W W^T)
   float* T;    // NB x NB slots, one per panel (at least three)
   Scalars* sc;
   double* part;
-  double* R64; // d x d, C W accumulated in fp64 (refinement only)
+  void* rz;    // refinement residual: int8 digit planes of [C | -G] and [W ; dW] (residual_workspace_bytes)
   uint16_t* sp; // 9 d x d bf16: three parts of C, of W and of W^T (split_kernel)
   float* Linv; // d x d: L^-1 (one-launch sweep)
   float* Xs;   // NB x NB slots, one per panel (one-launch sweep)
@@ -1504,14 +1397,13 @@ WsLayout carve(void* ws, int d) {
   w.Bx = (float*)p; p += dd;
   w.Rs = (float*)p; p += dd;
   w.Rc = (float*)p; p += dd;
-  w.Wf = (float*)p; p += dd;
   w.P = (float*)p; p += dd;
   w.Linv = (float*)p; p += dd;
   w.T = (float*)p; p += t_slots_bytes(d);
   w.Xs = (float*)p; p += t_slots_bytes(d);
   w.sc = (Scalars*)p; p += 256;
   w.part = (double*)p; p += DOT_BLOCKS * 5 * sizeof(double);
-  w.R64 = (double*)p; p += (size_t)d * d * sizeof(double);
+  w.rz = p; p += (residual_workspace_bytes(d) + 255) / 256 * 256;
   w.st = (int*)p; p += (state_bytes(d) + 255) / 256 * 256;
   w.sp = (uint16_t*)p;
   return w;
@@ -1555,8 +1447,9 @@ AuxStream* aux_stream() {
 }  // namespace
 
 size_t solve_workspace_bytes(int d) {
-  const size_t b = (size_t)d * d * sizeof(float) * 7 + 2 * t_slots_bytes(d) + 256 + DOT_BLOCKS * 5 * sizeof(double) +
-                   (size_t)d * d * sizeof(double) + (state_bytes(d) + 255) / 256 * 256 + (size_t)d * d * 18 + 256;
+  const size_t b = (size_t)d * d * sizeof(float) * 6 + 2 * t_slots_bytes(d) + 256 + DOT_BLOCKS * 5 * sizeof(double) +
+                   (residual_workspace_bytes(d) + 255) / 256 * 256 + (state_bytes(d) + 255) / 256 * 256 +
+                   (size_t)d * d * 18 + 256;
   return (b + 255) / 256 * 256;
 }
 
@@ -1578,18 +1471,10 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
   int* state = one_launch ? w.st : nullptr;
   const int n_state = PS_STATE_INTS + 2 * nP * nP;
 
-  // Mx and Bx for the per-panel launches, W as fp32 for the refinement (the one-launch sweep reads G
-  // itself and starts the identity part implicitly)
-  if (!one_launch || L.refine > 0) {
-    float* Mx = one_launch ? nullptr : w.Mx;
-    float* Bx = one_launch ? nullptr : w.Bx;
-    float* Wf = L.refine > 0 ? w.Wf : nullptr;
-    if (L.w_dtype == DT_BF16)
-      hipLaunchKernelGGL(setup_kernel<BF16>, eg, dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, Mx, Bx, Wf, st);
-    else if (L.w_dtype == DT_F16)
-      hipLaunchKernelGGL(setup_kernel<F16>, eg, dim3(NT), 0, s, L.G, (const uint16_t*)L.W, d, Mx, Bx, Wf, st);
-    else
-      hipLaunchKernelGGL(setup_kernel<F32>, eg, dim3(NT), 0, s, L.G, (const float*)L.W, d, Mx, Bx, Wf, st);
+  // Mx and Bx for the per-panel launches (the one-launch sweep reads G itself and starts the identity
+  // part implicitly)
+  if (!one_launch) {
+    hipLaunchKernelGGL(setup_kernel, eg, dim3(NT), 0, s, L.G, d, w.Mx, w.Bx, st);
     ISPA_TRY(hipGetLastError());
   }
 
@@ -1611,10 +1496,15 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
   {
     const int nT = (d + 63) / 64, n_r = nT * nT, n_p = L.eps ? nT * (nT + 1) / 2 : 0;
     const dim3 sg(n_r, nb_l), rg(n_r + n_p, nb_l);
-    if (L.w_dtype == DT_BF16) {
+    // Layers with more panels than one launch takes: R and P on the projection's NT kernel, as
+    // sums of products of the bf16 planes (C0 C1 C2 | W0 W1 W2 | W^T0 W^T1 W^T2), smallest terms first
+    // (the same terms as rp_tile; P in full).  Its 32-bit offsets span all planes up to d = 8192.
+    const bool nt_rp = nP > PS_MAX_PANELS && d % 64 == 0 && d <= 8192;
+    const bool bf16w = L.w_dtype == DT_BF16;
+    if (bf16w) {
       hipLaunchKernelGGL((split_kernel<1, BF16>), sg, dim3(256), 0, sr, L.C, (const uint16_t*)L.W, w.sp, d, st, state,
                          n_state, L.info);
-      if (!one_launch) hipLaunchKernelGGL(rp_kernel<1>, rg, dim3(256), 0, sr, w.sp, w.Rc, w.P, d, n_r, st);
+      if (!one_launch && !nt_rp) hipLaunchKernelGGL(rp_kernel<1>, rg, dim3(256), 0, sr, w.sp, w.Rc, w.P, d, n_r, st);
     } else {
       if (L.w_dtype == DT_F16)
         hipLaunchKernelGGL((split_kernel<3, F16>), sg, dim3(256), 0, sr, L.C, (const uint16_t*)L.W, w.sp, d, st,
@@ -1622,7 +1512,18 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
       else
         hipLaunchKernelGGL((split_kernel<3, F32>), sg, dim3(256), 0, sr, L.C, (const float*)L.W, w.sp, d, st, state,
                            n_state, L.info);
-      if (!one_launch) hipLaunchKernelGGL(rp_kernel<3>, rg, dim3(256), 0, sr, w.sp, w.Rc, w.P, d, n_r, st);
+      if (!one_launch && !nt_rp) hipLaunchKernelGGL(rp_kernel<3>, rg, dim3(256), 0, sr, w.sp, w.Rc, w.P, d, n_r, st);
+    }
+    if (nt_rp) {
+      ISPA_TRY(hipGetLastError());
+      // R = C W: A planes C_i (0..2), B planes W^T_j (6..8), i + j <= 2; P = W W^T: planes W_i (3..5)
+      if (bf16w) {
+        ISPA_TRY(launch_nt_segments(w.sp, w.Rc, d, 3, 0x012, 0x666, nb_l, st.ws, sr));
+        if (n_p) ISPA_TRY(launch_nt_segments(w.sp, w.P, d, 1, 0x3, 0x3, nb_l, st.ws, sr));
+      } else {
+        ISPA_TRY(launch_nt_segments(w.sp, w.Rc, d, 6, 0x010210, 0x667678, nb_l, st.ws, sr));
+        if (n_p) ISPA_TRY(launch_nt_segments(w.sp, w.P, d, 6, 0x343543, 0x334345, nb_l, st.ws, sr));
+      }
     }
     ISPA_TRY(hipGetLastError());
     if (ax) ISPA_TRY(hipEventRecord(ax->join, sr));
@@ -1705,17 +1606,26 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
   ISPA_TRY(run_trgemm(true, Li, st.ws, w.Mx, st.ws, L.delta_w, st.mat, d, 1.f, 0.f, nb_l, s, L.W,
                       L.refine > 0 ? nullptr : L.w_new, L.w_dtype, st.wmat));
   if (L.refine > 0) {
-    // iterative refinement: r = C W - (G + lambda I) dW with fp64 accumulation (C W formed once in
-    // fp64), then dW += (L^-1)^T (L^-1 r) with the fp32 factor
-    const int tpd = (d + 127) / 128;
-    const dim3 g64(tpd * tpd, nb_l);
-    hipLaunchKernelGGL(gemm64_kernel<0>, g64, dim3(NT), 0, s, L.C, st.mat, w.Wf, st.ws, d, w.sc, w.R64,
-                       (float*)nullptr, st.ws);
-    ISPA_TRY(hipGetLastError());
+    // iterative refinement: r = C W - (G + lambda I) dW from exact int8 products of fixed-point digits
+    // (refine.hip), then dW += (L^-1)^T (L^-1 r) with the fp32 factor
     for (int it = 0; it < L.refine; ++it) {
-      hipLaunchKernelGGL(gemm64_kernel<1>, g64, dim3(NT), 0, s, L.G, st.mat, L.delta_w, st.mat, d, w.sc, w.R64,
-                         w.Rs, st.ws);
-      ISPA_TRY(hipGetLastError());
+      ResidualLaunch R;
+      R.batch = nb_l;
+      R.d = d;
+      R.C = L.C;
+      R.G = L.G;
+      R.W = L.W;
+      R.w_dtype = L.w_dtype;
+      R.dW = L.delta_w;
+      R.lambda = &w.sc->lambda;
+      R.r = w.Rs;
+      R.ws = w.rz;
+      R.rows_too = it == 0;
+      R.s_mat = st.mat;
+      R.s_wmat = st.wmat;
+      R.s_ws = st.ws;
+      R.s_lambda = st.ws;
+      ISPA_TRY(launch_residual(R, s));
       // t = L^-1 r (into Mx, no longer needed), dW += (L^-1)^T t
       ISPA_TRY(run_trgemm(false, Li, st.ws, w.Rs, st.ws, w.Mx, st.ws, d, 1.f, 0.f, nb_l, s));
       ISPA_TRY(run_trgemm(true, Li, st.ws, w.Mx, st.ws, L.delta_w, st.mat, d, 1.f, 1.f, nb_l, s, L.W,

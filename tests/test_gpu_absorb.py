@@ -104,9 +104,10 @@ def _solve_gpu(G, C, D, W, lam, relative, w_dtype="f32", refine=False):
             "info": int(info.item())}
 
 
-@pytest.mark.parametrize("d,n", [(32, 50), (96, 70), (128, 400), (160, 500), (256, 200), (320, 2000)])
+@pytest.mark.parametrize("d,n", [(32, 50), (96, 70), (128, 400), (160, 500), (256, 200), (320, 2000), (2112, 2500)])
 @pytest.mark.parametrize("refine", [False, True])
 def test_solve_matches_oracle(d, n, refine):
+    """d <= 2048: one launch factorises; 2112 (33 panels): per-panel launches, R and P on the NT kernel."""
     G, C, D, W = _spd_problem(d, n, d + n)
     lam = oracle.ridge_lambda(G, 1e-3, True)
     got = _solve_gpu(G, C, D, W, 1e-3, True, refine=refine)
@@ -120,9 +121,10 @@ def test_solve_matches_oracle(d, n, refine):
     assert abs(got["eps"] - eps) <= 1e-2 * eps
 
 
+@pytest.mark.parametrize("d", [192, 2112])
 @pytest.mark.parametrize("w_dtype", ["bf16", "f16"])
-def test_solve_16bit_weights(w_dtype):
-    G, C, D, W = _spd_problem(192, 300, 5, w_dtype)
+def test_solve_16bit_weights(w_dtype, d):
+    G, C, D, W = _spd_problem(d, 300 if d < 1024 else 2500, 5, w_dtype)
     got = _solve_gpu(G, C, D, W, 0.05, False, w_dtype=w_dtype)
     dW = oracle.solve_delta_w(G, C, W, 0.05)
     assert got["info"] == 0 and abs(got["lambda"] - 0.05) < 1e-9
