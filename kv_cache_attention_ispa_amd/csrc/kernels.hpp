@@ -95,8 +95,9 @@ hipError_t launch_quant_weight(int dtype, const void* w, int d_in, int d_out, ui
 // out (fp32 d x d) = sum over n_seg segments g of A_g B_g^T, A_g / B_g the bf16 planes (d x d, row-major,
 // consecutive) numbered (a_planes >> 4 g) & 15 and (b_planes >> 4 g) & 15; layer y of batch at
 // planes + y layer_bytes and out + y layer_bytes.  d % 64 == 0, 9 d^2 * 2 bytes of planes < 2^32.
+// lower: only the 64 x 64 blocks on and below the diagonal are needed (others may stay unwritten).
 hipError_t launch_nt_segments(const uint16_t* planes, float* out, int d, int n_seg, int a_planes, int b_planes,
-                              int batch, int64_t layer_bytes, hipStream_t s);
+                              int batch, int64_t layer_bytes, bool lower, hipStream_t s);
 hipError_t launch_proj8(int out_dtype, const uint8_t* aq, const float* sa, const uint8_t* wq_t, const float* sw,
                         void* out, int m, int n, int k, hipStream_t s);
 

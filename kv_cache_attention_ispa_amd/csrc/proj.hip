@@ -47,6 +47,7 @@ __device__ __forceinline__ int nt_off(int row, int chunk) { return row * NT_BK +
 struct NtSeg {
   int n_seg, a_planes, b_planes;
   int64_t plane_bytes, layer_bytes;
+  int lower;   // 1: only tiles that meet the lower triangle of 64 x 64 blocks (the others return)
 };
 
 // KIND 0: E4M3 codes (scaled epilogue); 1, 2: the 16-bit type TIn; 3: segmented (NtSeg).  TOut: type
@@ -67,6 +68,10 @@ __global__ __launch_bounds__(768, 1) void gemm_nt_kernel(const uint8_t* a, const
   const int logical = xcd_remap(blockIdx.x, tiles_m * tiles_n);
   const int bm = logical / tiles_n, bn = logical % tiles_n;
   const int m0 = bm * 256, n0 = bn * 128;
+  if constexpr (KIND == 3) {
+    // the tile covers 64-blocks rows 4 bm .. 4 bm + 3 and columns 2 bn, 2 bn + 1
+    if (seg.lower && 2 * bn > 4 * bm + 3) return;
+  }
   const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   auto aslot = [&](auto J) -> uint8_t* {
@@ -336,7 +341,7 @@ hipError_t launch_proj(const ProjLaunch& L, hipStream_t s) {
 }
 
 hipError_t launch_nt_segments(const uint16_t* planes, float* out, int d, int n_seg, int a_planes, int b_planes,
-                              int batch, int64_t layer_bytes, hipStream_t s) {
+                              int batch, int64_t layer_bytes, bool lower, hipStream_t s) {
   const int t = (d + 255) / 256, tn = (d + 127) / 128;
   NtSeg g;
   g.n_seg = n_seg;
@@ -344,6 +349,7 @@ hipError_t launch_nt_segments(const uint16_t* planes, float* out, int d, int n_s
   g.b_planes = b_planes;
   g.plane_bytes = (int64_t)d * d * 2;
   g.layer_bytes = layer_bytes;
+  g.lower = lower ? 1 : 0;
   hipLaunchKernelGGL((gemm_nt_kernel<3, BF16, F32>), dim3(t * tn, batch), dim3(768), 0, s, (const uint8_t*)planes,
                      (const uint8_t*)planes, nullptr, nullptr, (void*)out, d, d, d * 2, t, tn, g);
   return hipGetLastError();

@@ -1498,7 +1498,8 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
     const dim3 sg(n_r, nb_l), rg(n_r + n_p, nb_l);
     // Layers with more panels than one launch takes: R and P on the projection's NT kernel, as
     // sums of products of the bf16 planes (C0 C1 C2 | W0 W1 W2 | W^T0 W^T1 W^T2), smallest terms first
-    // (the same terms as rp_tile; P in full).  Its 32-bit offsets span all planes up to d = 8192.
+    // (the same terms as rp_tile; P in the tiles that meet its lower block triangle, which is all that
+    // epsilon reads).  Its 32-bit offsets span all planes up to d = 8192.
     const bool nt_rp = nP > PS_MAX_PANELS && d % 64 == 0 && d <= 8192;
     const bool bf16w = L.w_dtype == DT_BF16;
     if (bf16w) {
@@ -1518,11 +1519,11 @@ hipError_t launch_solve(const SolveLaunch& L, hipStream_t s) {
       ISPA_TRY(hipGetLastError());
       // R = C W: A planes C_i (0..2), B planes W^T_j (6..8), i + j <= 2; P = W W^T: planes W_i (3..5)
       if (bf16w) {
-        ISPA_TRY(launch_nt_segments(w.sp, w.Rc, d, 3, 0x012, 0x666, nb_l, st.ws, sr));
-        if (n_p) ISPA_TRY(launch_nt_segments(w.sp, w.P, d, 1, 0x3, 0x3, nb_l, st.ws, sr));
+        ISPA_TRY(launch_nt_segments(w.sp, w.Rc, d, 3, 0x012, 0x666, nb_l, st.ws, false, sr));
+        if (n_p) ISPA_TRY(launch_nt_segments(w.sp, w.P, d, 1, 0x3, 0x3, nb_l, st.ws, true, sr));
       } else {
-        ISPA_TRY(launch_nt_segments(w.sp, w.Rc, d, 6, 0x010210, 0x667678, nb_l, st.ws, sr));
-        if (n_p) ISPA_TRY(launch_nt_segments(w.sp, w.P, d, 6, 0x343543, 0x334345, nb_l, st.ws, sr));
+        ISPA_TRY(launch_nt_segments(w.sp, w.Rc, d, 6, 0x010210, 0x667678, nb_l, st.ws, false, sr));
+        if (n_p) ISPA_TRY(launch_nt_segments(w.sp, w.P, d, 6, 0x343543, 0x334345, nb_l, st.ws, true, sr));
       }
     }
     ISPA_TRY(hipGetLastError());
