@@ -203,7 +203,7 @@ def test_bf16_small_end_to_end():
     assert abs(got["eps"] - eps) <= 1e-2 * eps
 
 
-@pytest.mark.parametrize("d,layers,refine", [(96, 2, 0), (256, 3, 0), (1536, 4, 0), (320, 2, 1), (2048, 2, 0)])
+@pytest.mark.parametrize("d,layers,refine", [(96, 2, 0), (256, 3, 0), (1536, 4, 0), (320, 2, 1), (2048, 2, 0), (2112, 2, 1)])
 def test_batched_solve_equals_per_layer_calls(d, layers, refine):
     """ispa_absorb_solve_batched: every layer's dW, W_new, eps, lambda and info equal those of a
     separate ispa_absorb_solve call, bit for bit; one layer is indefinite (info set, others intact);
