@@ -443,6 +443,10 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void attn_mfma_kernel(AttnParams p
   const int hi = lane >> 5;
   const int qrow = qblk * BM + wave * 32 + (lane & 31);
   const bool qok = qrow < p.n_q;
+  // A wave whose 32 queries all lie past n_q (the last query block of a head) still issues its share
+  // of the tile loads and meets every barrier, but runs no matrix or softmax work: the chip runs at a
+  // power-limited clock, so idle matrix cores let the busy ones run faster.
+  const bool live = qblk * BM + wave * 32 < p.n_q;
   const int col0 = head * HD;
 
   // Q^T B-operand fragments: lane (n = query, k = 16 ks + 8 hi + 0..7)
@@ -498,7 +502,7 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void attn_mfma_kernel(AttnParams p
   // M(n-1) only needs PV(n-1): its QK result is never used.
   auto matrix = [&](auto J, int t) {   // J = (t + 1) % 3
     constexpr int j = decltype(J)::value;
-    matrix_phase<T, TP>(kslot(J), vslot(std::integral_constant<int, (j + 2) % 3>{}), kbase, vbase, qf, pf, s, st.o);
+    if (live) matrix_phase<T, TP>(kslot(J), vslot(std::integral_constant<int, (j + 2) % 3>{}), kbase, vbase, qf, pf, s, st.o);
     if (t < 0) st.reset();
   };
   // load group i+2 (J = i % 3)
@@ -508,7 +512,7 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void attn_mfma_kernel(AttnParams p
                       vslot(std::integral_constant<int, (j + 1) % 3>{})), wave);
   };
   auto softmax = [&](int t) {
-    if (t < 0 || t >= sc.n) return;
+    if (!live || t < 0 || t >= sc.n) return;
     if (MODE == 0 && t == sc.t_hist) {
       // first history tile: the local branch is complete
       m_loc = st.m;
@@ -564,6 +568,7 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void attn_mfma_kernel(AttnParams p
     }
   }
 
+  if (!live) return;   // no barrier follows the loop
   if (MODE != 0) {
     close_branch(st);
     store_token_major<T>(p.a_full, p.d, col0, qrow, qok, st.o);

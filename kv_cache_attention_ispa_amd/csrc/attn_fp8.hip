@@ -362,6 +362,8 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fp8_kernel(Fp8Params p) {
   const int grp = wave >> 2, hi = lane >> 5;
   const int qrow = qblk * BM + wave * 32 + (lane & 31);
   const bool qok = qrow < p.n_q;
+  // a wave with no query below n_q issues its loads and meets every barrier, and multiplies nothing
+  const bool live = qblk * BM + wave * 32 < p.n_q;
   const int col0 = head * HD;
 
   // Q codes for the B operand of MFMA h: this lane's query, head dims 64 h + 32 hi + 0..31
@@ -435,7 +437,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fp8_kernel(Fp8Params p) {
   // the schedule of the 16-bit kernel: M(t) = QK(t+1) + PV(t) reads K slot (t+1) % 3 and V slot t % 3
   auto matrix = [&](auto J, int t) {
     constexpr int j = decltype(J)::value;
-    matrix8(kslot(J), vslot(std::integral_constant<int, (j + 2) % 3>{}), kbase, vbase, qf, pf, ones, s, st);
+    if (live) matrix8(kslot(J), vslot(std::integral_constant<int, (j + 2) % 3>{}), kbase, vbase, qf, pf, ones, s, st);
     if (t < 0) reset();
   };
   auto issue_ahead = [&](auto J, int i) {
@@ -444,7 +446,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fp8_kernel(Fp8Params p) {
                       vslot(std::integral_constant<int, (j + 1) % 3>{})), wave);
   };
   auto softmax = [&](int t) {
-    if (t < 0 || t >= sc.n) return;
+    if (!live || t < 0 || t >= sc.n) return;
     softmax8(s, sc.valid(t), c, hi, st, pf);
   };
   auto phase_end = [&]() { lds_barrier(); };
@@ -486,6 +488,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_fp8_kernel(Fp8Params p) {
     }
   }
 
+  if (!live) return;   // no barrier follows the loop
   // O = s_v O / l; l sits in register 0 of lanes 0-31
   const uint32_t lu = __float_as_uint(st.lacc[0]);
   const auto lr = __builtin_amdgcn_permlane32_swap(lu, lu, false, false);
