@@ -34,4 +34,5 @@ from .absorb import (gram_stats, ridge_lambda, solve_delta_w, recon_error_direct
                      recon_error_traces, select_local_layers, fold_weights, local_layer_output,
                      normal_equation_residual)
 from .accounting import attn_flops, kv_cache_bytes, kv_removed_fraction  # noqa: F401
-from .fp8 import local_layer_output_w8a8, local_attention_fp8  # noqa: F401
+from .fp8 import (local_layer_output_w8a8, local_attention_fp8, local_layer_output_w8a8_fp8attn,  # noqa: F401
+                  quantize_weight)

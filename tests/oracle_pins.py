@@ -389,6 +389,23 @@ def check_golden_w8a8_l_layer(impl):
     assert np.array_equal(out, np.array(g["expect"]["out"]))
 
 
+def check_golden_w8a8_fp8attn_l_layer(impl):
+    """W8A8 converted-layer step with FP8 attention: exact FP8 attention (Q = 0, four local rows), bf16
+    storage that decides an activation code, a non-symmetric W; then the W8A8 fixture's inputs, where the
+    FP8 coding of V decides a code; and the weight codes of a non-square W."""
+    g = _golden("w8a8_fp8attn_l_layer_hand.json")
+    q, k, v, w = (np.array(g[x], dtype=np.float64) for x in ("q", "k", "v", "w"))
+    out = impl.local_layer_output_w8a8_fp8attn(q, k, v, g["n_sink"], g["n_cur"], g["n_heads"], w)
+    assert np.array_equal(out, np.array(g["expect"]["out"]))
+    h = _golden("w8a8_l_layer_hand.json")
+    q, k, v, w = (np.array(h[x], dtype=np.float64) for x in ("q", "k", "v", "w"))
+    out = impl.local_layer_output_w8a8_fp8attn(q, k, v, h["n_sink"], h["n_cur"], h["n_heads"], w)
+    assert np.array_equal(out, np.array(g["expect"]["case2_out"]))
+    qw = g["quantize_weight"]
+    codes, scales = impl.quantize_weight(np.array(qw["w"]))
+    assert np.array_equal(np.asarray(codes), np.array(qw["codes"])) and np.array_equal(np.asarray(scales), np.array(qw["scales"]))
+
+
 def check_golden_fp8_attention(impl):
     """Hand-worked FP8 attention of a converted layer: dominant key, rounding against the integer
     reference, Q = 0."""
@@ -459,6 +476,6 @@ ABSORB_PINS = [check_golden_ridge, check_residual, check_augmented_lstsq, check_
                check_relative_lambda, check_linearity_in_w, check_optimality, check_rowspace,
                check_eps_two_ways, check_zero_absorb, check_gram_associativity, check_selection,
                check_golden_l_layer, check_golden_residual_and_fold, check_golden_w8a8_l_layer,
-               check_golden_fp8_attention, check_fp8_attention_structure]
+               check_golden_fp8_attention, check_fp8_attention_structure, check_golden_w8a8_fp8attn_l_layer]
 ACCOUNTING_PINS = [check_kv_bytes, check_flops]
 ALL_PINS = ATTENTION_PINS + ABSORB_PINS + ACCOUNTING_PINS

@@ -18,10 +18,11 @@ NAMES = ["branch_rows", "softmax_attention", "dual_stream", "lse_merge", "gram_s
          "solve_delta_w", "normal_equation_residual", "recon_error_direct", "recon_error_traces",
          "select_local_layers", "fold_weights", "local_layer_output", "attn_flops", "kv_cache_bytes",
          "kv_removed_fraction", "default_scale", "local_layer_output_w8a8", "local_attention_fp8"]
+FP8_NAMES = ["local_layer_output_w8a8_fp8attn", "quantize_weight"]
 
 
 def _ns(**over):
-    ns = types.SimpleNamespace(**{n: getattr(oracle, n) for n in NAMES})
+    ns = types.SimpleNamespace(**{n: getattr(oracle, n) for n in NAMES}, **{n: getattr(fp8, n) for n in FP8_NAMES})
     for k, v in over.items():
         setattr(ns, k, v)
     return ns
@@ -168,6 +169,23 @@ def _w8a8_no_bf16_rounding(q, k, v, n_sink, n_cur, n_heads, W, scale=None, threa
     return fp8.w8a8_matmul(a.astype(np.float32), W)
 
 
+def _fp8attn_layer_no_bf16(q, k, v, n_sink, n_cur, n_heads, W, scale=None):
+    a = fp8.local_attention_fp8(q, k, v, n_sink, n_cur, n_heads, scale)
+    return fp8.w8a8_matmul(a.astype(np.float32), W)
+
+
+def _fp8attn_layer_float_attention(q, k, v, n_sink, n_cur, n_heads, W, scale=None):
+    return fp8.local_layer_output_w8a8(q, k, v, n_sink, n_cur, n_heads, W, scale)
+
+
+def _fp8attn_layer_w_transposed(q, k, v, n_sink, n_cur, n_heads, W, scale=None):
+    return fp8.local_layer_output_w8a8_fp8attn(q, k, v, n_sink, n_cur, n_heads, np.asarray(W).T, scale)
+
+
+def _quantize_weight_untransposed(W):
+    return fp8.quantize_rows(np.asarray(W, dtype=np.float32))
+
+
 def _fp8_attention_variant(reference="ceil", p_scale=256.0, l_from="codes", k_scale="head"):
     def attn(q, k, v, n_sink, n_cur, n_heads, scale=None, quantize=True):
         if not quantize:   # the planted mistakes are in the rounding only
@@ -236,6 +254,10 @@ MUTANTS = {
     "residual_returns_zero": dict(normal_equation_residual=_residual_zero),
     "residual_drops_lambda": dict(normal_equation_residual=_residual_no_lambda),
     "w8a8_skips_bf16_storage": dict(local_layer_output_w8a8=_w8a8_no_bf16_rounding),
+    "fp8attn_layer_skips_bf16_storage": dict(local_layer_output_w8a8_fp8attn=_fp8attn_layer_no_bf16),
+    "fp8attn_layer_float_attention": dict(local_layer_output_w8a8_fp8attn=_fp8attn_layer_float_attention),
+    "fp8attn_layer_w_transposed": dict(local_layer_output_w8a8_fp8attn=_fp8attn_layer_w_transposed),
+    "weight_codes_per_input_channel": dict(quantize_weight=_quantize_weight_untransposed),
     "fp8_reference_not_integer": dict(local_attention_fp8=_fp8_attention_variant(reference="max")),
     "fp8_probabilities_scaled_448": dict(local_attention_fp8=_fp8_attention_variant(p_scale=448.0)),
     "fp8_row_sum_unquantised": dict(local_attention_fp8=_fp8_attention_variant(l_from="exact")),
