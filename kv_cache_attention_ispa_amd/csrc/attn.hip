@@ -443,10 +443,12 @@ __global__ __launch_bounds__(MFMA_THREADS, 2) void attn_mfma_kernel(AttnParams p
   const int hi = lane >> 5;
   const int qrow = qblk * BM + wave * 32 + (lane & 31);
   const bool qok = qrow < p.n_q;
-  // A wave whose 32 queries all lie past n_q (the last query block of a head) still issues its share
-  // of the tile loads and meets every barrier, but runs no matrix or softmax work: the chip runs at a
-  // power-limited clock, so idle matrix cores let the busy ones run faster.
-  const bool live = qblk * BM + wave * 32 < p.n_q;
+  // Local-only mode: a wave whose 32 queries all lie past n_q (the last query block of a head) still
+  // issues its share of the tile loads and meets every barrier, but runs no matrix or softmax work
+  // (the chip runs at a power-limited clock, so idle matrix cores let the busy ones run faster).  The
+  // dual and full modes keep every wave working: a block that ran ahead of the other blocks of its
+  // head would stop sharing their K and V lines in L2 (HBM fetches per dual call rose by a quarter).
+  const bool live = MODE != 2 || qblk * BM + wave * 32 < p.n_q;
   const int col0 = head * HD;
 
   // Q^T B-operand fragments: lane (n = query, k = 16 ks + 8 hi + 0..7)

@@ -155,11 +155,9 @@ def test_fp8_layer_step_time():
     """At the 1.3B converted layer: the W8A8 step with FP8 attention (pre-pass, attention, activation
     codes, FP8 product) against the 16-bit step and the W8A8 step with 16-bit attention.  Times are
     the best of three rounds of 20-call medians, the variants alternating, so a clock change hits them
-    alike.  Measured without a profiler the FP8 step runs 2-4% faster than the 16-bit one: the FP8
-    attention kernel is about 10% faster than the 16-bit one, but both are bound by the softmax and
-    the pipeline rather than the matrix cores, and the FP8 pre-pass costs 22 us.  That margin is
-    within run-to-run noise, so the test bounds the FP8 step at 1.05 x the 16-bit step (a slowdown
-    such as a register spill fails it) and prints the ratio."""
+    alike.  The FP8 step has measured 0.83-0.84 x the 16-bit one (its attention kernel 129-133 us
+    against 165-167 us; the FP8 pre-pass costs 21 us), so the test asserts a gain: at most 0.93 x the
+    16-bit step, and prints the ratio."""
     import kv_cache_attention_ispa_amd as ispa
     t = torch()
     s = wl.LAYER_1P3B.shape
@@ -203,4 +201,4 @@ def test_fp8_layer_step_time():
             ms[name] = min(ms.get(name, med), med)
     print("1.3B converted layer step (ms): " + ", ".join(f"{n} {v:.4f}" for n, v in ms.items()) +
           f"; FP8 / 16-bit step {ms['w8a8_fp8_attention'] / ms['bf16']:.3f}")
-    assert ms["w8a8_fp8_attention"] <= 1.05 * ms["bf16"]
+    assert ms["w8a8_fp8_attention"] <= 0.93 * ms["bf16"]
