@@ -6,7 +6,9 @@ file per workload in this directory.
 
 * layer_1p3b_bf16 / layer_14b_bf16: lambda, ||dW||_F, the reconstruction error
   epsilon, and a Gaussian sketch S^T dW X (S, X seeded [d, 16]) from which the
-  tests estimate ||dW_gpu - dW||_F / ||dW||_F without storing dW.
+  tests estimate ||dW_gpu - dW||_F / ||dW||_F without storing dW; for the 14B
+  layer also four seeded whole rows and four whole columns of dW (float32), which
+  the test compares element by element.
 * warmup_1p3b_30x4: for each of the 30 layers (4 warmup chunks of 3 frames,
   per-layer temporal correlation), lambda, epsilon, ||dW||_F, the sketch of
   dW, and G, C, D (accumulated over the 4 x 4680 warmup tokens) at seeded
@@ -52,6 +54,12 @@ def sample_entries(d: int, n: int = 64, n_diag: int = 16):
     return np.concatenate([ii, dg]), np.concatenate([jj, dg])
 
 
+def sample_lines(d: int, n: int = 4):
+    """Seeded row and column indices of dW stored whole."""
+    rng = np.random.default_rng(np.random.SeedSequence([wl.ROOT_SEED, SKETCH_CFG, d, 3]))
+    return np.sort(rng.choice(d, n, replace=False)), np.sort(rng.choice(d, n, replace=False))
+
+
 def layer_golden(w: wl.Workload) -> dict:
     s = w.shape
     t0 = time.time()
@@ -61,7 +69,13 @@ def layer_golden(w: wl.Workload) -> dict:
     lam = oracle.ridge_lambda(G, w.lam, w.lam_relative)
     dW = oracle.solve_delta_w(G, C, x["w"], lam)
     S, X = sketch_mats(s.d)
+    lines = {}
+    if w.name == wl.LAYER_14B.name:
+        rows, cols = sample_lines(s.d)
+        lines = {"dw_rows": {"index": rows.tolist(), "values": dW[rows].astype(np.float32).tolist()},
+                 "dw_cols": {"index": cols.tolist(), "values": dW[:, cols].T.astype(np.float32).tolist()}}
     return {
+        **lines,
         "workload": w.name,
         "lambda": lam,
         "dw_fro": float(np.linalg.norm(dW)),

@@ -6,10 +6,12 @@ is one of:
   * properties that hold at any size (the normal equations of the solve, sketched
     with a seeded Gaussian block so the host work stays small);
   * values stored by tests/golden/make_golden.py, which calls only the oracle
-    (lambda, epsilon, ||dW|| and a Gaussian sketch S^T dW X of dW);
+    (lambda, epsilon, ||dW||, a Gaussian sketch S^T dW X of dW, and at the 14B layer four
+    whole rows and four whole columns of dW);
   * at the 1.3B layer, the whole dW from the oracle run in the test.
 Tolerances follow the bf16 workloads: attention max-rel 2e-2, dW rel-Frobenius 1e-2
-(the whole matrix at the 1.3B layer, the 16 x 16 sketch at the 14B layer), epsilon relative 1e-2.
+(the whole matrix at the 1.3B layer; the 16 x 16 sketch and the eight stored lines at the 14B
+layer), epsilon relative 1e-2.
 The 30-layer warmup workload runs through the driver in test_gpu_runtime.py.
 """
 import json
@@ -155,14 +157,21 @@ def test_layer_1p3b_full_size(stat_dtype):
 
 def test_layer_14b_full_size():
     """The ill-conditioned case (4680 tokens < 5120 features, cond ~ 2e6): fp16 statistics, fp16
-    probabilities in the PV product and one refinement step keep dW within 1e-2."""
+    probabilities in the PV product and one refinement step keep dW within 1e-2, on the sketch and
+    element by element on four whole rows and four whole columns of the oracle's dW."""
     w = wl.LAYER_14B
     L, dW, S, X = _check_layer(w, refine=True)
     g = _golden(w.name)
     ref = np.array(g["dw_sketch"])
     err = np.linalg.norm(S.T @ dW @ X - ref) / np.linalg.norm(ref)
-    print(f"14B layer: dW sketch rel-Frobenius {err:.3e}, eps {float(L.eps.item()):.6f} vs {g['eps']:.6f}")
+    rows, cols = np.array(g["dw_rows"]["index"]), np.array(g["dw_cols"]["index"])
+    got = np.concatenate([dW[rows], dW[:, cols].T])
+    want = np.concatenate([np.array(g["dw_rows"]["values"]), np.array(g["dw_cols"]["values"])])
+    err_lines = relfro(got, want)
+    print(f"14B layer: dW sketch rel-Frobenius {err:.3e}, on 4 rows + 4 columns {err_lines:.3e}, "
+          f"eps {float(L.eps.item()):.6f} vs {g['eps']:.6f}")
     assert err <= 1e-2
+    assert err_lines <= 1e-2
     assert abs(float(L.eps.item()) - g["eps"]) <= 1e-2 * g["eps"]
 
 
