@@ -133,6 +133,57 @@ def test_solve_16bit_weights(w_dtype, d):
     assert maxrel(got["w_new"], wl.round_to(W + got["dW"], w_dtype)) <= 1e-2
 
 
+def test_solve_large_lambda_limit():
+    """lambda -> infinity: dW = (G + lambda I)^-1 C W -> C W / lambda, and ||dW|| <= ||C W|| / lambda
+    (G is positive semi-definite), against the oracle at lambda = 1e6 tr(G) / d."""
+    d = 256
+    G, C, D, W = _spd_problem(d, 400, 21)
+    lam = oracle.ridge_lambda(G, 1e6, True)
+    got = _solve_gpu(G, C, D, W, 1e6, True)
+    assert got["info"] == 0 and abs(got["lambda"] - lam) <= 1e-6 * lam
+    cw = C @ W
+    assert np.linalg.norm(got["dW"]) <= np.linalg.norm(cw) / lam * (1 + 1e-5)
+    assert relfro(got["dW"], oracle.solve_delta_w(G, C, W, lam)) <= 1e-3
+    assert relfro(got["dW"], cw / lam) <= 1e-3    # first order in 1 / lambda: ||G|| / lambda ~ 1e-6 d
+
+
+@pytest.mark.parametrize("d,n", [(256, 100), (640, 300)])
+@pytest.mark.parametrize("refine", [False, True])
+def test_solve_fewer_tokens_than_features(d, n, refine):
+    """n < d (as at the 14B layer): G has rank n, so lambda = 1e-3 tr(G) / d alone lifts its null space
+    and cond(G + lambda I) is about 1e3 d / n.  dW within 1e-3 of the float64 solve.
+
+    epsilon is small here (the few tokens are fitted almost exactly), and the library evaluates it
+    by the trace formula that holds at the optimum, num^2 = <D,P> - <dW,R> - lambda ||dW||^2
+    (P = W W^T, R = C W).  An error e in dW moves that by -<e, R + 2 lambda dW> - lambda ||e||^2,
+    to first order, where the exact formula would move to second order; so num^2 is held to that
+    bound, computed from the measured e, plus 1e-6 of the traces for their fp32 inputs.  The
+    formula itself, evaluated in float64 on the kernel's own dW, must match the kernel's num^2 to
+    5e-7 of its traces (fp32 R and P; measured 1e-8 to 1e-7).  Here num^2 is itself only about 3e-7
+    of the traces, so a small epsilon is known to a few percent at best from fp32 statistics."""
+    G, C, D, W = _spd_problem(d, n, d + 3 * n)
+    lam = oracle.ridge_lambda(G, 1e-3, True)
+    got = _solve_gpu(G, C, D, W, 1e-3, True, refine=refine)
+    assert got["info"] == 0
+    dW = oracle.solve_delta_w(G, C, W, lam)
+    err = relfro(got["dW"], dW)
+    eps = oracle.recon_error_traces(G, C, D, W, dW, lam)
+    Rm = C @ W
+    den2 = np.sum(W * ((G + C + C.T + D) @ W))
+    e = np.linalg.norm(got["dW"] - dW)
+    slack = (e * np.linalg.norm(Rm + 2.0 * lam * dW) + lam * e * e
+             + 1e-6 * (abs(np.sum(W * (D @ W))) + abs(np.sum(dW * Rm))))
+    print(f"d={d} n={n} refine={refine}: dW rel-Frobenius {err:.2e}; eps {got['eps']:.4e} vs {eps:.4e}, "
+          f"num^2 off by {abs(got['eps'] ** 2 - eps ** 2) * den2:.2e} of a {slack:.2e} bound")
+    assert err <= 1e-3
+    assert abs(got["eps"] ** 2 - eps ** 2) * den2 <= slack
+    g = got["dW"]
+    dp, gr, gg = np.sum(W * (D @ W)), np.sum(g * Rm), lam * np.sum(g * g)
+    dev_rel = abs(got["eps"] ** 2 * den2 - (dp - gr - gg)) / (abs(dp) + abs(gr) + gg)
+    print(f"  kernel num^2 against the formula on its own dW: {dev_rel:.2e} of the traces")
+    assert dev_rel <= 5e-7
+
+
 @pytest.mark.parametrize("bad", [1, 70, 129])
 def test_solve_reports_first_nonpositive_pivot(bad):
     """info = k (1-based) when the leading minor of order k of G + lambda I is not positive definite."""
